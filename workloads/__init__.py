@@ -1,0 +1,308 @@
+"""Seeded synthetic inputs shaped like the captured MLA decode calls.
+
+This module only draws and lays out inputs: lengths, index lists, pool rows,
+queries and scales.  It holds none of the attention arithmetic, and it is the
+one module that both the HIP path's tests / benchmark and the oracle's tests
+use.  Inputs are drawn with a seeded ``torch.Generator`` on the requested
+device; a CPU oracle reads back exactly the bytes the device path consumes.
+
+Shapes follow "[Kimi-K3 MLA TP8] MLA performance" (ROCm/aiter issue 4541),
+Sec. 4.1 / 4.2 "Arguments" (q (B, 16, 576) e4m3fn, a 5,283,840-entry token-major
+pool, a 4,718,592-entry index buffer, per-request lengths ~68,43x with a
+63,911-token shared prefix) and Sec. 5.4 (prefix slots shared by every request).
+Value distributions, seeds and the other workloads are this project's choices,
+stated in the design notes.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+ROW_DIM = 576
+LATENT_DIM = 512
+E4M3FN_MAX = 448.0
+POOL_ENTRIES = 5_283_840  # [Issue] Sec. 4.1, kv_buffer (5283840, 1, 1, 576)
+INDEX_BUFFER = 4_718_592  # [Issue] Sec. 4.1, kv_indices (4718592,)
+SHARED_PREFIX = 63_911  # [Issue] Sec. 1, workload row
+UNIQUE_INPUT = 4_089  # [Issue] Sec. 1, workload row
+SM_SCALE_F64 = 192.0 ** -0.5  # [Issue] Sec. 2, sm_scale = 1/sqrt(192)
+
+
+def fp32(x: float) -> float:
+    """Round a Python float to the nearest binary32 value (returned as float)."""
+    return float(torch.tensor(x, dtype=torch.float32).item())
+
+
+SM_SCALE = fp32(SM_SCALE_F64)
+
+
+@dataclass
+class Workload:
+    """One decode call's inputs (device tensors) plus the recipe that made them."""
+
+    name: str
+    dtype: str  # 'fp8' or 'bf16' storage of q and the pool
+    q: torch.Tensor  # (T, H, 576)
+    kv_pool: torch.Tensor  # (N, 576)
+    qo_indptr: torch.Tensor  # (B+1,) int32
+    kv_indptr: torch.Tensor  # (B+1,) int32
+    kv_indices: torch.Tensor  # (>= kv_indptr[B],) int32
+    kv_last_page_lens: torch.Tensor  # (B,) int32, all ones
+    q_scale: torch.Tensor  # 0-d fp32
+    kv_scale: torch.Tensor  # 0-d fp32
+    sm_scale: float
+    num_heads: int
+    real_heads: int
+    max_seqlen_q: int
+    return_lse: bool
+    lengths: list[int]
+    qlens: list[int]
+    recipe: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return len(self.lengths)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def total_kv(self) -> int:
+        return int(sum(self.lengths))
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _fill_values(shape, std: float, dtype: str, seed: int, device, chunk_rows: int = 1 << 17):
+    """N(0, std) values, clamped to the e4m3fn range, stored as ``dtype``.
+
+    Drawn in row chunks so a multi-GB pool never needs a full fp32 copy.
+    """
+    tdtype = torch.float8_e4m3fn if dtype == "fp8" else torch.bfloat16
+    out = torch.empty(shape, dtype=tdtype, device=device)
+    g = _gen(seed, device)
+    rows = shape[0]
+    flat = out.view(rows, -1)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        x = torch.randn((r1 - r0, flat.shape[1]), generator=g, device=device, dtype=torch.float32)
+        x.mul_(std).clamp_(-E4M3FN_MAX, E4M3FN_MAX)
+        flat[r0:r1] = x.to(tdtype)
+    return out
+
+
+def _scale(lo_hi, seed: int, device) -> torch.Tensor:
+    if lo_hi is None:
+        return torch.ones((), dtype=torch.float32, device=device)
+    lo, hi = lo_hi
+    g = _gen(seed, device)
+    return (torch.rand((), generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo)
+
+
+def build(
+    name: str,
+    lengths: list[int],
+    *,
+    num_heads: int = 16,
+    real_heads: int | None = None,
+    qlens: list[int] | None = None,
+    pool_entries: int = 4096,
+    dtype: str = "fp8",
+    kv_std: float = 1.0,
+    q_std: float = 1.0,
+    scale_range=None,
+    shared_prefix: int = 0,
+    layout: str = "random",
+    index_buffer: int | None = None,
+    return_lse: bool = True,
+    seed: int = 0,
+    device="cpu",
+) -> Workload:
+    """Assemble a decode call.
+
+    lengths:       KV length (tokens) of each request.
+    qlens:         query tokens per request (default all 1).
+    shared_prefix: the first ``shared_prefix`` entries of every request use the
+                   same pool slots (prefix caching); the rest are disjoint.
+    layout:        'random' scatters slots by a seeded permutation of the pool;
+                   'blocked' hands out runs of 128 consecutive slots (the
+                   allocator's block size) in a seeded random block order.
+    Seeds: lengths are the caller's; KV uses seed+1, q seed+2, indices seed+3,
+    scales seed+4 (q_scale) and seed+5 (kv_scale).
+    """
+    B = len(lengths)
+    lengths = [int(n) for n in lengths]
+    qlens = [1] * B if qlens is None else [int(x) for x in qlens]
+    real_heads = num_heads if real_heads is None else real_heads
+    T = sum(qlens)
+    uniq = [max(0, n - shared_prefix) for n in lengths]
+    need = shared_prefix + sum(uniq)
+    if need > pool_entries:
+        raise ValueError(f"workload needs {need} distinct slots, pool has {pool_entries}")
+
+    # Indices: a seeded permutation (or block permutation) of the pool.
+    gi = _gen(seed + 3, device)
+    if layout == "random":
+        perm = torch.randperm(pool_entries, generator=gi, device=device, dtype=torch.int64)
+    elif layout == "blocked":
+        nblk = pool_entries // 128
+        bperm = torch.randperm(nblk, generator=gi, device=device, dtype=torch.int64)
+        perm = (bperm[:, None] * 128 + torch.arange(128, device=device)[None, :]).reshape(-1)
+    else:
+        raise ValueError(layout)
+    prefix = perm[:shared_prefix]
+    parts = []
+    off = shared_prefix
+    for n, u in zip(lengths, uniq):
+        parts.append(prefix[: min(n, shared_prefix)])
+        parts.append(perm[off : off + u])
+        off += u
+    used = torch.cat(parts) if parts else torch.empty(0, dtype=torch.int64, device=device)
+    total = int(used.numel())
+    buf_len = max(total, index_buffer or 0, 1)
+    kv_indices = torch.zeros(buf_len, dtype=torch.int32, device=device)
+    kv_indices[:total] = used.to(torch.int32)
+
+    kv_indptr = torch.zeros(B + 1, dtype=torch.int32)
+    kv_indptr[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    qo_indptr = torch.zeros(B + 1, dtype=torch.int32)
+    qo_indptr[1:] = torch.cumsum(torch.tensor(qlens, dtype=torch.int64), 0).to(torch.int32)
+
+    kv_pool = _fill_values((pool_entries, ROW_DIM), kv_std, dtype, seed + 1, device)
+    q = _fill_values((T, num_heads, ROW_DIM), q_std, dtype, seed + 2, device, chunk_rows=1 << 12)
+    if real_heads < num_heads:
+        q[:, real_heads:, :] = torch.zeros((), dtype=q.dtype, device=device)
+
+    return Workload(
+        name=name,
+        dtype=dtype,
+        q=q,
+        kv_pool=kv_pool,
+        qo_indptr=qo_indptr.to(device),
+        kv_indptr=kv_indptr.to(device),
+        kv_indices=kv_indices,
+        kv_last_page_lens=torch.ones(B, dtype=torch.int32, device=device),
+        q_scale=_scale(scale_range, seed + 4, device),
+        kv_scale=_scale(scale_range, seed + 5, device),
+        sm_scale=SM_SCALE,
+        num_heads=num_heads,
+        real_heads=real_heads,
+        max_seqlen_q=max(qlens) if qlens else 1,
+        return_lse=return_lse,
+        lengths=lengths,
+        qlens=qlens,
+        recipe=dict(
+            seed=seed, pool_entries=pool_entries, kv_std=kv_std, q_std=q_std,
+            scale_range=scale_range, shared_prefix=shared_prefix, layout=layout,
+            index_buffer=buf_len, dtype=dtype,
+        ),
+    )
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size.  Config k draws lengths from seed 1000*k.
+# ---------------------------------------------------------------------------
+
+
+def tiny(device="cpu") -> Workload:
+    """B=2, 16 heads (12 real + 4 zero), kv 64 and 100, pool 256 entries, N(0,1)."""
+    return build(
+        "tiny", [64, 100], num_heads=16, real_heads=12, pool_entries=256, dtype="fp8",
+        kv_std=1.0, q_std=1.0, scale_range=None, seed=1000, device=device,
+    )
+
+
+def c16_lengths() -> list[int]:
+    """63,911 shared + 4,089 unique + 430 + (b mod 5) decoded, b = 0..15."""
+    return [SHARED_PREFIX + UNIQUE_INPUT + 430 + (b % 5) for b in range(16)]
+
+
+def c16(device="cpu", variant: str = "shared", return_lse: bool = False) -> Workload:
+    """Batch 16 at kv ~68,430 (the headline decode call), fp8, N(0,0.5) KV.
+
+    variant: 'shared' (prefix slots shared by all requests, as captured),
+             'unshared' (every request's prefix uses its own slots),
+             'blocked' (shared prefix, slots handed out in 128-slot runs).
+    """
+    lengths = c16_lengths()
+    shared = 0 if variant == "unshared" else SHARED_PREFIX
+    layout = "blocked" if variant == "blocked" else "random"
+    return build(
+        f"c16-{variant}", lengths, num_heads=16, real_heads=12, pool_entries=POOL_ENTRIES,
+        dtype="fp8", kv_std=0.5, q_std=1.0, scale_range=(0.5, 2.0), shared_prefix=shared,
+        layout=layout, index_buffer=INDEX_BUFFER, return_lse=return_lse, seed=2000,
+        device=device,
+    )
+
+
+def c24_lengths() -> list[int]:
+    g = _gen(3000, "cpu")
+    dec = torch.randint(0, 351, (24,), generator=g).tolist()
+    return [SHARED_PREFIX + UNIQUE_INPUT + int(d) for d in dec]
+
+
+def c24(device="cpu", return_lse: bool = False) -> Workload:
+    """Batch 24, shared 63,911 prefix + 4,089 unique + U{0..350} decoded, fp8."""
+    return build(
+        "c24", c24_lengths(), num_heads=16, real_heads=12, pool_entries=POOL_ENTRIES,
+        dtype="fp8", kv_std=0.5, q_std=1.0, scale_range=(0.5, 2.0),
+        shared_prefix=SHARED_PREFIX, index_buffer=INDEX_BUFFER, return_lse=return_lse,
+        seed=3000, device=device,
+    )
+
+
+def mixed_lengths() -> list[int]:
+    g = _gen(4000, "cpu")
+    u = torch.rand(64, generator=g, dtype=torch.float64)
+    lo, hi = math.log(1024.0), math.log(142_000.0)
+    return [int(math.floor(math.exp(lo + (hi - lo) * float(x)))) for x in u]
+
+
+def mixed(device="cpu", dtype: str = "fp8", return_lse: bool = False) -> Workload:
+    """Batch 64, kv log-uniform in [1,024, 142,000], disjoint slots, N(0,1)."""
+    return build(
+        f"mixed-{dtype}", mixed_lengths(), num_heads=16, real_heads=12,
+        pool_entries=POOL_ENTRIES, dtype=dtype, kv_std=1.0, q_std=1.0, scale_range=None,
+        return_lse=return_lse, seed=4000, device=device,
+    )
+
+
+DCP_LOCAL = 142_000 // 8  # 17,750 positions per request on one DCP8 rank
+
+
+def dcp_share(device="cpu") -> Workload:
+    """One DCP8 rank: batch 8, 96 heads, 4 query tokens (causal), kv 17,750."""
+    return build(
+        "dcp-share", [DCP_LOCAL] * 8, num_heads=96, real_heads=96, qlens=[4] * 8,
+        pool_entries=POOL_ENTRIES, dtype="fp8", kv_std=0.5, q_std=1.0,
+        scale_range=(0.5, 2.0), return_lse=True, seed=5000, device=device,
+    )
+
+
+def merge_shards(
+    num_parts: int = 8, num_tokens: int = 32, num_heads: int = 96, parts_dtype: str = "fp32",
+    seed: int = 5100, device="cpu", kv_local: int = DCP_LOCAL,
+):
+    """Synthetic DCP partial answers: o ~ N(0,1), lse ~ N(ln kv_local, 1).
+
+    One (shard, token, head) row per shard is forced to -inf (an empty shard),
+    and one (token, head) row is -inf in every shard.
+    Returns (o_parts (S,T,H,512), lse_parts (S,T,H) fp32).
+    """
+    g = _gen(seed, device)
+    tdtype = torch.float32 if parts_dtype == "fp32" else torch.bfloat16
+    o = torch.randn((num_parts, num_tokens, num_heads, LATENT_DIM), generator=g, device=device)
+    lse = torch.randn((num_parts, num_tokens, num_heads), generator=g, device=device)
+    lse = lse + math.log(kv_local)
+    for s in range(num_parts):
+        lse[s, s % num_tokens, (7 * s) % num_heads] = -math.inf
+    lse[:, num_tokens - 1, num_heads - 1] = -math.inf
+    return o.to(tdtype), lse.to(torch.float32)

@@ -1,0 +1,54 @@
+"""Algorithmic bytes and FLOPs of one decode call (benchmark bookkeeping).
+
+The accounting follows "[Kimi-K3 MLA TP8] MLA performance" (ROCm/aiter issue
+4541), Sec. 5.3 "Strongly memory-bound": every gathered token slot costs one
+576-wide pool row plus one int32 index; q is read once and o written once;
+FLOPs count 2 * rows * (576 + 512) per (query row, visible entry), padded heads
+included.  Shared-prefix reuse is not subtracted: the method gathers per
+request.
+"""
+
+from __future__ import annotations
+
+ROW_DIM = 576
+LATENT_DIM = 512
+INDEX_BYTES = 4
+
+_ELEM = {"fp8": 1, "bf16": 2, "fp32": 4}
+
+
+def row_bytes(dtype: str) -> int:
+    return ROW_DIM * _ELEM[dtype]
+
+
+def visible(n: int, qlen: int, j: int) -> int:
+    return max(0, n - (qlen - 1 - j))
+
+
+def decode_bytes(lengths, qlens, num_heads, dtype="fp8", return_lse=False) -> int:
+    """HBM bytes the method must move for one call."""
+    T = sum(qlens)
+    kv = sum(lengths) * (row_bytes(dtype) + INDEX_BYTES)
+    q = T * num_heads * ROW_DIM * _ELEM[dtype]
+    o = T * num_heads * LATENT_DIM * 2
+    lse = T * num_heads * 4 if return_lse else 0
+    return kv + q + o + lse
+
+
+def decode_flops(lengths, qlens, num_heads) -> int:
+    """2 * heads * sum over query tokens of visible entries * (576 + 512)."""
+    vis = sum(visible(n, ql, j) for n, ql in zip(lengths, qlens) for j in range(ql))
+    return 2 * num_heads * vis * (ROW_DIM + LATENT_DIM)
+
+
+def merge_bytes(num_parts, num_tokens, num_heads, parts_dtype="fp32", with_lse_out=True) -> int:
+    rows = num_tokens * num_heads
+    return rows * (num_parts * (LATENT_DIM * _ELEM[parts_dtype] + 4) + LATENT_DIM * 2 + (4 if with_lse_out else 0))
+
+
+def workload_bytes(w) -> int:
+    return decode_bytes(w.lengths, w.qlens, w.num_heads, w.dtype, w.return_lse)
+
+
+def workload_flops(w) -> int:
+    return decode_flops(w.lengths, w.qlens, w.num_heads)
