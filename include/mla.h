@@ -1,0 +1,176 @@
+/*
+ * mla.h - C ABI of the MI355X (gfx950) latent-MLA decode library.
+ *
+ * The operation: absorbed (latent) multi-head latent attention decode over a
+ * token-major paged cache, as described on the page "[Kimi-K3 MLA TP8] MLA
+ * performance" (ROCm/aiter issue 4541):
+ *   - Sec. 2 "K3 MLA geometry": every cached token is one 576-wide latent row
+ *     (512 latent + 64 rope) shared by all query heads; scores use all 576
+ *     dims, the output is the softmax-weighted sum of the first 512 dims;
+ *     sm_scale = 1/sqrt(192).
+ *   - Sec. 3 "Entry point" and Sec. 4.1 "Arguments": the call's tensors
+ *     (q, kv_buffer, o, qo_indptr, kv_indptr, kv_indices, kv_last_page_lens,
+ *     sm_scale, q_scale, kv_scale, return_lse) and their layouts.
+ *   - Sec. 5.2 "The kernel runs with page_size = 1": kv_indptr deltas are KV
+ *     lengths in tokens, kv_indices holds one pool entry per token.
+ * The merge of partial answers follows "Kimi K3 on AMD Instinct MI355X: vLLM
+ * Serving Matches NVIDIA HGX B300 Throughput per GPU on AgentX", Sec. "1.
+ * Cache: keep conversation state available for reuse" (partial answers carry
+ * normalisation information and are merged with softmax weights).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers to caller-owned, contiguous,
+ *     row-major memory on the current HIP device.  The library allocates and
+ *     frees nothing on the call path and keeps no state between calls other
+ *     than a cached per-device property query.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream) and the call returns without synchronising.  The host
+ *     never reads device memory, so the calls can be captured in a HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     violation returns a status code and enqueues nothing.  A failed launch
+ *     returns MLA_ERR_HIP.  No C++ exception crosses this interface.
+ *   - Device-side contents (indptr monotonicity, index ranges) are the
+ *     caller's contract.  The kernels clamp every index they read to the
+ *     buffer it addresses, so a violation gives wrong numbers, never an
+ *     out-of-bounds access.
+ *   - Concurrent calls on different streams need distinct workspaces.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage types. FP8 is OCP float8_e4m3fn (the KV cache dtype of Sec. 1). */
+typedef enum {
+  MLA_DTYPE_FP8_E4M3FN = 0,
+  MLA_DTYPE_BF16 = 1,
+  MLA_DTYPE_FP32 = 2
+} mla_dtype;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL_POINTER = 1,
+  MLA_ERR_BAD_SHAPE = 2,
+  MLA_ERR_BAD_DTYPE = 3,
+  MLA_ERR_UNSUPPORTED = 4,
+  MLA_ERR_WORKSPACE_TOO_SMALL = 5,
+  MLA_ERR_HIP = 6
+} mla_status;
+
+/* Width of one cache row and of the output (Sec. 2 "K3 MLA geometry"). */
+#define MLA_ROW_DIM 576
+#define MLA_LATENT_DIM 512
+/* Heads are processed in groups of 16; callers pad 12 -> 16 (Sec. 5.1). */
+#define MLA_HEAD_GROUP 16
+
+/*
+ * Workspace bytes mla_decode needs on the current device for this call shape.
+ * The workspace holds fp32 partial answers of the KV splits (at most two per
+ * worker workgroup); its size depends only on the device's compute-unit count
+ * and the arguments below, not on KV lengths.  Returns 0 for invalid shapes.
+ */
+size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, int max_seqlen_q);
+
+/*
+ * MLA decode (Sec. 3 entry point; Sec. 4.1 argument layouts).
+ *
+ *  q              (num_q_tokens, num_heads, 576) of q_dtype.  Heads beyond the
+ *                 model's real count are caller padding; each head attends
+ *                 independently, so padding never changes a real head.
+ *  kv_pool        (pool_entries, 576) of kv_dtype, i.e. the (N,1,1,576) cache
+ *                 viewed token-major (page_size 1).
+ *  o              (num_q_tokens, num_heads, 512) bfloat16, written
+ *                 (round to nearest even).
+ *  qo_indptr      (batch+1) int32: request b owns query tokens
+ *                 [qo_indptr[b], qo_indptr[b+1]); qo_indptr[batch] must equal
+ *                 num_q_tokens and every request at most max_seqlen_q tokens.
+ *  kv_indptr      (batch+1) int32 offsets into kv_indices; deltas are each
+ *                 request's KV length in tokens.
+ *  kv_indices     (kv_indices_len) int32 pool entry of every cached token.
+ *  kv_last_page_lens (batch) int32, all ones for page_size 1; not read
+ *                 (may be NULL).
+ *  sm_scale       host float, the softmax scale (1/sqrt(192) for K3).
+ *  q_scale, kv_scale  device fp32 scalars (0-d tensors); real = stored*scale.
+ *                 NULL means 1.0.
+ *  return_lse, lse  if return_lse != 0, lse (num_q_tokens, num_heads) fp32
+ *                 receives ln(sum_i exp(s_i)) of each row; it may be NULL
+ *                 otherwise.
+ *  workspace      device scratch of at least
+ *                 mla_decode_workspace_bytes(batch, num_q_tokens, num_heads,
+ *                 max_seqlen_q) bytes, 256-byte aligned; contents on entry do
+ *                 not matter.
+ *
+ * Query token j of a request with qlen tokens and n cached entries sees the
+ * first n - (qlen - 1 - j) entries (bottom-right causal alignment for
+ * multi-token verification).  A row that sees nothing gets o = 0 and
+ * lse = -inf.  Supported: q_dtype == kv_dtype, either FP8_E4M3FN or BF16;
+ * num_heads a positive multiple of 16; 1 <= max_seqlen_q <= 64.
+ */
+mla_status mla_decode(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                      int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                      const int32_t* kv_indptr, const int32_t* kv_indices,
+                      int64_t kv_indices_len, const int32_t* kv_last_page_lens, int batch,
+                      int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
+                      const float* q_scale, const float* kv_scale, int return_lse, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode with an explicit number of worker workgroups (0 = the library's
+ * choice, one per compute unit).  The KV work is cut into `num_workers` equal
+ * contiguous ranges; results agree with mla_decode within rounding.  The
+ * workspace must hold mla_decode_workspace_bytes_ex(..., num_workers) bytes.
+ */
+mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                         int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                         const int32_t* kv_indptr, const int32_t* kv_indices,
+                         int64_t kv_indices_len, const int32_t* kv_last_page_lens, int batch,
+                         int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
+                         const float* q_scale, const float* kv_scale, int return_lse,
+                         float* lse, void* workspace, size_t workspace_bytes, int num_workers,
+                         void* stream);
+
+size_t mla_decode_workspace_bytes_ex(int batch, int num_q_tokens, int num_heads,
+                                     int max_seqlen_q, int num_workers);
+
+/*
+ * LSE-weighted merge of partial answers over disjoint KV shards (the DCP
+ * merge of the blog's Sec. 1; the same math combines the decode's own splits).
+ *
+ *  o_parts    (num_parts, num_q_tokens, num_heads, 512) of parts_dtype
+ *             (BF16 or FP32), each shard's normalised output.
+ *  lse_parts  (num_parts, num_q_tokens, num_heads) fp32, each shard's lse;
+ *             -inf marks an empty shard, whose o_parts row is not read.
+ *  o          (num_q_tokens, num_heads, 512) bf16, written.
+ *  lse        (num_q_tokens, num_heads) fp32, written if not NULL.
+ * For each row: M = max_s lse_s, L = M + ln sum_s exp(lse_s - M),
+ * o = sum_s exp(lse_s - L) o_s, lse = L; a row empty in every shard gets
+ * o = 0, lse = -inf.
+ */
+mla_status mla_merge_partials(const void* o_parts, int parts_dtype, const float* lse_parts,
+                              int num_parts, int num_q_tokens, int num_heads, void* o,
+                              float* lse, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* mla_status_string(int status);
+
+/*
+ * Host mirror of the work planner, for tests: given host copies of qo_indptr
+ * and kv_indptr, fill `out` (capacity `out_cap` pieces, 8 int64 each:
+ * worker, token, head_group, kv_begin, kv_end, unit_len, slot, is_complete)
+ * with the pieces every worker processes, in worker order.  slot is the
+ * partial-answer slot (-1 for complete pieces).  Returns the number of pieces
+ * (which may exceed out_cap; only out_cap are written), or -1 on bad input.
+ */
+int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
+                      int num_heads, int num_workers, int64_t* out, int64_t out_cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

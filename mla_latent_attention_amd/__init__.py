@@ -1,0 +1,196 @@
+"""MI355X-native latent MLA decode: a thin binding over libmla.so (include/mla.h).
+
+This module only marshals arguments: it checks devices, dtypes and contiguity,
+allocates a workspace when the caller passes none, and hands raw device
+pointers plus the current HIP stream to the C ABI.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import DTYPE_BF16, DTYPE_FP8, DTYPE_FP32, MLAError
+
+__all__ = [
+    "decode",
+    "merge_partials",
+    "workspace_bytes",
+    "plan_host",
+    "MLAError",
+    "library_path",
+]
+
+ROW_DIM = 576
+LATENT_DIM = 512
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _storage_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float8_e4m3fn:
+        return DTYPE_FP8
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    raise TypeError(f"unsupported storage dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, device, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_bytes(batch: int, num_q_tokens: int, num_heads: int, max_seqlen_q: int = 1,
+                    num_workers: int = 0) -> int:
+    L = _lib.lib()
+    if num_workers:
+        n = L.mla_decode_workspace_bytes_ex(batch, num_q_tokens, num_heads, max_seqlen_q, num_workers)
+    else:
+        n = L.mla_decode_workspace_bytes(batch, num_q_tokens, num_heads, max_seqlen_q)
+    if n == 0:
+        raise ValueError("invalid shape for the decode workspace (or no HIP device)")
+    return int(n)
+
+
+def decode(
+    q: torch.Tensor,
+    kv_pool: torch.Tensor,
+    qo_indptr: torch.Tensor,
+    kv_indptr: torch.Tensor,
+    kv_indices: torch.Tensor,
+    kv_last_page_lens: torch.Tensor | None,
+    sm_scale: float,
+    q_scale: torch.Tensor | None = None,
+    kv_scale: torch.Tensor | None = None,
+    return_lse: bool = False,
+    *,
+    o: torch.Tensor | None = None,
+    lse: torch.Tensor | None = None,
+    max_seqlen_q: int | None = None,
+    workspace: torch.Tensor | None = None,
+    num_workers: int = 0,
+):
+    """Latent MLA decode; returns o (T, H, 512) bf16, or (o, lse) if return_lse.
+
+    q: (T, H, 576) float8_e4m3fn or bfloat16; kv_pool: (N, 576) or (N, 1, 1, 576)
+    of the same dtype; indptr / indices int32; q_scale / kv_scale 0-d fp32
+    device tensors (None = 1.0).  max_seqlen_q defaults to the largest
+    qo_indptr delta, which costs a device-to-host copy: pass it to avoid that.
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a device tensor")
+    if q.dim() != 3 or q.shape[2] != ROW_DIM:
+        raise ValueError(f"q must be (T, H, {ROW_DIM})")
+    T, H, _ = q.shape
+    if kv_pool.dim() == 4:
+        if tuple(kv_pool.shape[1:]) != (1, 1, ROW_DIM):
+            raise ValueError("a 4-d kv_pool must be (N, 1, 1, 576)")
+        kv_pool = kv_pool.view(kv_pool.shape[0], ROW_DIM)
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_DIM:
+        raise ValueError(f"kv_pool must be (N, {ROW_DIM})")
+    _need(q, "q", dev)
+    _need(kv_pool, "kv_pool", dev)
+    B = qo_indptr.numel() - 1
+    _need(qo_indptr, "qo_indptr", dev, torch.int32, (B + 1,))
+    _need(kv_indptr, "kv_indptr", dev, torch.int32, (B + 1,))
+    _need(kv_indices, "kv_indices", dev, torch.int32)
+    if kv_last_page_lens is not None:
+        _need(kv_last_page_lens, "kv_last_page_lens", dev, torch.int32, (B,))
+    for name, s in (("q_scale", q_scale), ("kv_scale", kv_scale)):
+        if s is not None:
+            _need(s, name, dev, torch.float32)
+            if s.numel() != 1:
+                raise ValueError(f"{name} must hold one value")
+    if o is None:
+        o = torch.empty((T, H, LATENT_DIM), dtype=torch.bfloat16, device=dev)
+    _need(o, "o", dev, torch.bfloat16, (T, H, LATENT_DIM))
+    if return_lse:
+        if lse is None:
+            lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        _need(lse, "lse", dev, torch.float32, (T, H))
+    if max_seqlen_q is None:
+        max_seqlen_q = int((qo_indptr[1:] - qo_indptr[:-1]).max().item()) if B > 0 else 1
+    ws_need = workspace_bytes(B, T, H, max_seqlen_q, num_workers)
+    if workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    L = _lib.lib()
+    qdt, kdt = _storage_dtype(q), _storage_dtype(kv_pool)
+    status = L.mla_decode_ex(
+        _ptr(q), qdt, _ptr(kv_pool), kdt, kv_pool.shape[0], _ptr(o), _ptr(qo_indptr),
+        _ptr(kv_indptr), _ptr(kv_indices), kv_indices.numel(), _ptr(kv_last_page_lens),
+        B, T, H, max_seqlen_q, float(sm_scale), _ptr(q_scale), _ptr(kv_scale),
+        1 if return_lse else 0, _ptr(lse) if return_lse else None, _ptr(workspace), ws_len,
+        int(num_workers), _stream(dev),
+    )
+    _lib.check(status, "mla_decode")
+    return (o, lse) if return_lse else o
+
+
+def merge_partials(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, o=None, lse=None,
+                   return_lse: bool = True):
+    """LSE merge of S shards: o_parts (S, T, H, 512) bf16|fp32, lse_parts (S, T, H) fp32."""
+    dev = o_parts.device
+    if o_parts.dim() != 4 or o_parts.shape[3] != LATENT_DIM:
+        raise ValueError("o_parts must be (S, T, H, 512)")
+    S, T, H, _ = o_parts.shape
+    _need(o_parts, "o_parts", dev)
+    _need(lse_parts, "lse_parts", dev, torch.float32, (S, T, H))
+    if o is None:
+        o = torch.empty((T, H, LATENT_DIM), dtype=torch.bfloat16, device=dev)
+    _need(o, "o", dev, torch.bfloat16, (T, H, LATENT_DIM))
+    if return_lse:
+        if lse is None:
+            lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        _need(lse, "lse", dev, torch.float32, (T, H))
+    status = _lib.lib().mla_merge_partials(
+        _ptr(o_parts), _storage_dtype(o_parts), _ptr(lse_parts), S, T, H, _ptr(o),
+        _ptr(lse) if return_lse else None, _stream(dev),
+    )
+    _lib.check(status, "mla_merge_partials")
+    return (o, lse) if return_lse else o
+
+
+PLAN_FIELDS = ("worker", "token", "head_group", "kv_begin", "kv_end", "unit_len", "slot", "complete")
+
+
+def plan_host(qo_indptr, kv_indptr, num_heads: int, num_workers: int) -> np.ndarray:
+    """The planner's pieces for host indptr arrays: int64 array (pieces, 8), columns PLAN_FIELDS."""
+    qo = np.ascontiguousarray(np.asarray(qo_indptr, dtype=np.int32))
+    kv = np.ascontiguousarray(np.asarray(kv_indptr, dtype=np.int32))
+    B = len(qo) - 1
+    L = _lib.lib()
+    n = L.mla_plan_host(qo.ctypes.data, kv.ctypes.data, B, num_heads, num_workers, None, 0)
+    if n < 0:
+        raise ValueError("invalid planner input")
+    out = np.zeros((max(n, 1), 8), dtype=np.int64)
+    n2 = L.mla_plan_host(qo.ctypes.data, kv.ctypes.data, B, num_heads, num_workers,
+                         out.ctypes.data, n)
+    assert n2 == n
+    return out[:n]

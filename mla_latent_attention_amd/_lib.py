@@ -1,0 +1,68 @@
+"""ctypes view of libmla.so: symbol signatures exactly as include/mla.h declares."""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla.so")
+
+STATUS = {
+    0: "MLA_OK",
+    1: "MLA_ERR_NULL_POINTER",
+    2: "MLA_ERR_BAD_SHAPE",
+    3: "MLA_ERR_BAD_DTYPE",
+    4: "MLA_ERR_UNSUPPORTED",
+    5: "MLA_ERR_WORKSPACE_TOO_SMALL",
+    6: "MLA_ERR_HIP",
+}
+DTYPE_FP8, DTYPE_BF16, DTYPE_FP32 = 0, 1, 2
+
+_vp, _i32p, _f32p, _i64p = C.c_void_p, C.POINTER(C.c_int32), C.c_void_p, C.POINTER(C.c_int64)
+
+_DECODE_ARGS = [
+    _vp, C.c_int, _vp, C.c_int, C.c_int64, _vp, _vp, _vp, _vp, C.c_int64, _vp,
+    C.c_int, C.c_int, C.c_int, C.c_int, C.c_float, _vp, _vp, C.c_int, _vp, _vp, C.c_size_t,
+]
+
+SIGNATURES = {
+    "mla_decode": (C.c_int, _DECODE_ARGS + [_vp]),
+    "mla_decode_ex": (C.c_int, _DECODE_ARGS + [C.c_int, _vp]),
+    "mla_decode_workspace_bytes": (C.c_size_t, [C.c_int] * 4),
+    "mla_decode_workspace_bytes_ex": (C.c_size_t, [C.c_int] * 5),
+    "mla_merge_partials": (C.c_int, [_vp, C.c_int, _vp, C.c_int, C.c_int, C.c_int, _vp, _vp, _vp]),
+    "mla_status_string": (C.c_char_p, [C.c_int]),
+    "mla_plan_host": (C.c_int64, [_vp, _vp, C.c_int, C.c_int, C.c_int, _vp, C.c_int64]),
+}
+
+_lib = None
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+def lib() -> C.CDLL:
+    """Load libmla.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -m mla_latent_attention_amd.build)"
+            )
+        handle = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def check(status: int, where: str) -> None:
+    if status != 0:
+        raise MLAError(status, where)

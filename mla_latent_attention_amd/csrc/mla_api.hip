@@ -1,0 +1,217 @@
+// mla_api.hip - the extern "C" boundary declared in include/mla.h: argument
+// validation, workspace sizing, the per-device property cache and launches.
+// Every check runs before anything is enqueued; no HIP call is made for an
+// invalid argument, so the error paths run without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <vector>
+
+#include "../../include/mla.h"
+#include "mla_internal.h"
+#include "mla_plan.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+
+// Compute units of the current device (cached), or 0 if HIP fails.
+int current_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool shape_ok(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
+  if (batch < 1 || num_q_tokens < 1 || num_heads < 1) return false;
+  if (max_seqlen_q < 1 || max_seqlen_q > 64) return false;
+  if (num_q_tokens > (int64_t)batch * max_seqlen_q) return false;
+  // token * heads * 576 must stay addressable with 64-bit offsets and the
+  // combine grid (tokens * head groups) within one grid dimension.
+  if ((int64_t)num_q_tokens * (num_heads / mla::kGroup) > 0x7FFFFFFF) return false;
+  return true;
+}
+
+constexpr int kMaxWorkers = 1 << 16;
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL_POINTER: return "MLA_ERR_NULL_POINTER: a required pointer is NULL";
+    case MLA_ERR_BAD_SHAPE: return "MLA_ERR_BAD_SHAPE: a size argument is out of range";
+    case MLA_ERR_BAD_DTYPE: return "MLA_ERR_BAD_DTYPE: unsupported storage type combination";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: num_heads must be a multiple of 16";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+size_t mla_decode_workspace_bytes_ex(int batch, int num_q_tokens, int num_heads,
+                                     int max_seqlen_q, int num_workers) {
+  if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
+  if (num_workers < 1 || num_workers > kMaxWorkers) return 0;
+  return mla::workspace_bytes(num_workers);
+}
+
+size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
+  if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
+  const int cus = current_cu_count();
+  if (cus <= 0) return 0;
+  return mla::workspace_bytes(cus);
+}
+
+mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                         int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                         const int32_t* kv_indptr, const int32_t* kv_indices,
+                         int64_t kv_indices_len, const int32_t* kv_last_page_lens, int batch,
+                         int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
+                         const float* q_scale, const float* kv_scale, int return_lse,
+                         float* lse, void* workspace, size_t workspace_bytes, int num_workers,
+                         void* stream) {
+  (void)kv_last_page_lens;  // page_size 1: all ones by contract, never read
+  if (!q || !kv_pool || !o || !qo_indptr || !kv_indptr || !kv_indices)
+    return MLA_ERR_NULL_POINTER;
+  if (return_lse && !lse) return MLA_ERR_NULL_POINTER;
+  if (q_dtype != kv_dtype) return MLA_ERR_BAD_DTYPE;
+  if (q_dtype != MLA_DTYPE_FP8_E4M3FN && q_dtype != MLA_DTYPE_BF16) return MLA_ERR_BAD_DTYPE;
+  if (num_heads % mla::kGroup != 0 || num_heads <= 0) return MLA_ERR_UNSUPPORTED;
+  if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return MLA_ERR_BAD_SHAPE;
+  if (pool_entries < 1 || kv_indices_len < 0 || kv_indices_len > 0x7FFFFFFF)
+    return MLA_ERR_BAD_SHAPE;
+  if (num_workers < 0 || num_workers > kMaxWorkers) return MLA_ERR_BAD_SHAPE;
+  if (q_dtype == MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;  // fp8 path only for now
+  if (!workspace) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (num_workers > 0 && workspace_bytes < mla::workspace_bytes(num_workers))
+    return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+  if (num_workers == 0) {
+    num_workers = current_cu_count();
+    if (num_workers <= 0) return MLA_ERR_HIP;
+    if (workspace_bytes < mla::workspace_bytes(num_workers)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  }
+
+  mla::DecodeParams p;
+  p.q = static_cast<const uint8_t*>(q);
+  p.kv = static_cast<const uint8_t*>(kv_pool);
+  p.pool_entries = pool_entries;
+  p.o = static_cast<uint16_t*>(o);
+  p.qo_indptr = qo_indptr;
+  p.kv_indptr = kv_indptr;
+  p.kv_indices = kv_indices;
+  p.kv_indices_len = (int)kv_indices_len;
+  p.batch = batch;
+  p.num_tokens = num_q_tokens;
+  p.num_heads = num_heads;
+  p.sm_scale = sm_scale;
+  p.q_scale = q_scale;
+  p.kv_scale = kv_scale;
+  p.lse = return_lse ? lse : nullptr;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        mla::part_o_bytes(num_workers));
+  p.num_workers = num_workers;
+  const int kdt = (kv_dtype == MLA_DTYPE_FP8_E4M3FN) ? 0 : 1;
+  if (mla::launch_decode(p, kdt, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+mla_status mla_decode(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                      int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                      const int32_t* kv_indptr, const int32_t* kv_indices,
+                      int64_t kv_indices_len, const int32_t* kv_last_page_lens, int batch,
+                      int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
+                      const float* q_scale, const float* kv_scale, int return_lse, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode_ex(q, q_dtype, kv_pool, kv_dtype, pool_entries, o, qo_indptr, kv_indptr,
+                       kv_indices, kv_indices_len, kv_last_page_lens, batch, num_q_tokens,
+                       num_heads, max_seqlen_q, sm_scale, q_scale, kv_scale, return_lse, lse,
+                       workspace, workspace_bytes, 0, stream);
+}
+
+mla_status mla_merge_partials(const void* o_parts, int parts_dtype, const float* lse_parts,
+                              int num_parts, int num_q_tokens, int num_heads, void* o,
+                              float* lse, void* stream) {
+  if (!o_parts || !lse_parts || !o) return MLA_ERR_NULL_POINTER;
+  if (parts_dtype != MLA_DTYPE_FP32 && parts_dtype != MLA_DTYPE_BF16) return MLA_ERR_BAD_DTYPE;
+  if (num_parts < 1 || num_q_tokens < 1 || num_heads < 1) return MLA_ERR_BAD_SHAPE;
+  const int64_t rows = (int64_t)num_q_tokens * num_heads;
+  if ((rows + 3) / 4 > 0x7FFFFFFF) return MLA_ERR_BAD_SHAPE;
+  if (mla::launch_merge(o_parts, parts_dtype == MLA_DTYPE_FP32, lse_parts, num_parts, rows,
+                        static_cast<uint16_t*>(o), lse,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
+                      int num_heads, int num_workers, int64_t* out, int64_t out_cap) {
+  using namespace mla;
+  if (!qo_indptr || !kv_indptr || batch < 1 || num_heads < kGroup || num_heads % kGroup ||
+      num_workers < 1 || (out_cap > 0 && !out))
+    return -1;
+  const int G = num_heads / kGroup;
+  const int T = qo_indptr[batch];
+  const int kv_cap = kv_indptr[batch];
+  if (T < 0 || kv_cap < 0) return -1;
+  std::vector<int64_t> cum(batch + 1, 0);
+  for (int b = 0; b < batch; ++b) {
+    const Req r = load_req(qo_indptr, kv_indptr, b, kv_cap, T);
+    cum[b + 1] = cum[b] + (int64_t)G * request_rows(r.n, r.qlen);
+  }
+  const int64_t W = cum[batch];
+  if (W == 0) return 0;
+  const int nw = effective_workers(W, num_workers);
+  int64_t count = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int64_t p0 = worker_begin(w, W, nw), p1 = worker_begin(w + 1, W, nw);
+    if (p0 >= p1) continue;
+    int b = 0;
+    while (!(cum[b] <= p0 && p0 < cum[b + 1])) ++b;
+    Cursor c;
+    cursor_in_request(c, b, load_req(qo_indptr, kv_indptr, b, kv_cap, T), p0 - cum[b], G);
+    int64_t pos = p0;
+    int piece = 0;
+    while (pos < p1) {
+      const int v = visible(c.r.n, c.r.qlen, c.j);
+      const int len = (int)lmin((int64_t)(v - c.k), p1 - pos);
+      if (len <= 0) return -1;
+      const bool complete = (c.k == 0 && len == v);
+      const int slot = complete ? -1 : (piece == 0 ? 2 * w : 2 * w + 1);
+      if (count < out_cap) {
+        int64_t* rec = out + 8 * count;
+        rec[0] = w;
+        rec[1] = c.r.q_base + c.j;
+        rec[2] = c.g;
+        rec[3] = c.k;
+        rec[4] = c.k + len;
+        rec[5] = v;
+        rec[6] = slot;
+        rec[7] = complete ? 1 : 0;
+      }
+      ++count;
+      pos += len;
+      c.k += len;
+      ++piece;
+      if (pos < p1 && c.k == v && !cursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G))
+        return -1;
+    }
+  }
+  return count;
+}
+
+}  // extern "C"

@@ -1,0 +1,659 @@
+// mla_decode.hip - split-KV latent MLA decode for gfx950 (MI355X / CDNA4).
+//
+// What is computed ("[Kimi-K3 MLA TP8] MLA performance", ROCm/aiter issue
+// 4541, Sec. 2 "K3 MLA geometry" and Sec. 5.2 "The kernel runs with
+// page_size = 1"): for every query row (token t, head h) of request b,
+//   s_i = sm_scale * q_scale * kv_scale * sum_{d<576} q[t,h,d] * pool[L_b[i], d]
+//   o[t,h,:] = kv_scale * sum_i softmax(s)_i * pool[L_b[i], 0:512]
+// over the entries L_b[i] the token may see, with lse = ln sum_i exp(s_i).
+//
+// Design (our own; the pages' assembly kernel is not available):
+//   * One workgroup (4 waves, one per SIMD) per worker; the planner in
+//     mla_plan.h hands each worker an equal share of the KV stream.
+//   * Inside a piece the 4 waves take interleaved 32-row tiles and run
+//     independent online softmaxes, merged through LDS at the piece's end.
+//   * Per tile a wave gathers 32 pool rows with 16-byte loads straight into
+//     VGPRs, two tiles ahead of use.  Lane l loads row (l%16) (+16), bytes
+//     [64c + 16*(l/16), +16) for c = 0..8, which is exactly the A-operand
+//     layout of v_mfma_f32_16x16x32_fp8_fp8, so Q.K^T runs from registers:
+//     S^T (kv x 16 rows) = K (kv x 576) . Q^T.
+//   * The latent 512 bytes of each row go to a per-wave LDS tile (row-major,
+//     padded stride); P.V reads 16 bytes from each of 8 rows and transposes
+//     4x4 byte blocks in registers (v_perm) to build the V^T A-operand, so the
+//     contraction runs as O^T (512 x 16 rows) += V^T . P^T on fp8 MFMA.
+//   * P is fed as two e4m3 terms, P*256 = hi + lo (hi = e4m3(P*256),
+//     lo = e4m3(P*256 - hi)), so the fp8 P.V keeps ~8 significant bits of P;
+//     a single e4m3 P (4 bits) would not meet the output tolerance.
+//   * Scores are kept in base 2 (log2(e) folded into the scale).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+#include "mla_plan.h"
+
+namespace mla {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTile = 32;                          // KV rows per wave iteration
+constexpr int kVStride = 528;                      // LDS bytes per staged V row (512 + pad)
+constexpr int kVWaveBytes = kTile * kVStride;      // 16,896
+constexpr int kCombBytes = kWaves * 32 * 64 * 16;  // 131,072: every wave's O^T
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kPScale = 256.0f;                  // P*256 uses the e4m3 range
+static_assert(kWaves * kVWaveBytes <= kCombBytes, "V staging must fit in the LDS buffer");
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite).
+__device__ __forceinline__ u32 bf16_bits(float f) {
+  u32 u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ long as_long(u32 lo, u32 hi) {
+  return (long)((uint64_t)lo | ((uint64_t)hi << 32));
+}
+
+// Orders this wave's LDS accesses (writes by some lanes, reads by others).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// 4x4 byte transpose: out_k = (a.byte k, b.byte k, c.byte k, d.byte k).
+__device__ __forceinline__ void transpose4x4(u32 a, u32 b, u32 c, u32 d, u32& o0, u32& o1, u32& o2,
+                                             u32& o3) {
+  const u32 t0 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  const u32 t1 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+  const u32 t2 = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
+  const u32 t3 = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
+  o0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);           // a0 b0 c0 d0
+  o1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);           // a1 b1 c1 d1
+  o2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);           // a2 b2 c2 d2
+  o3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);           // a3 b3 c3 d3
+}
+
+// ---------------------------------------------------------------- block helpers
+
+__device__ int64_t block_sum_i64(int64_t v, int64_t* red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  const int wv = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wv] = v;
+  __syncthreads();
+  int64_t s = 0;
+  for (int i = 0; i < kWaves; ++i) s += red[i];
+  return s;
+}
+
+// Exclusive prefix sum over the block's 256 values; `total` gets the sum.
+__device__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int64_t x = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    int64_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) red[wv] = x;
+  __syncthreads();
+  int64_t before = 0;
+  total = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < wv) before += red[i];
+    total += red[i];
+  }
+  return before + x - v;
+}
+
+// Total stream length W = sum over requests of G * request_rows.
+__device__ int64_t plan_total(const DecodeParams& p, int G, int64_t* red) {
+  int64_t acc = 0;
+  for (int b = threadIdx.x; b < p.batch; b += kThreads) {
+    Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
+    acc += (int64_t)G * request_rows(r.n, r.qlen);
+  }
+  return block_sum_i64(acc, red);
+}
+
+// Request containing stream position pos (and its stream start); false if none.
+__device__ bool plan_locate(const DecodeParams& p, int G, int64_t pos, int64_t* red, int* s_b,
+                            int64_t* s_cum) {
+  if (threadIdx.x == 0) *s_b = -1;
+  int64_t carry = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += kThreads) {
+    const int b = b0 + threadIdx.x;
+    int64_t R = 0;
+    if (b < p.batch) {
+      Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
+      R = (int64_t)G * request_rows(r.n, r.qlen);
+    }
+    int64_t total;
+    const int64_t cum = carry + block_excl_scan_i64(R, red, total);
+    if (R > 0 && pos >= cum && pos < cum + R) {
+      *s_b = b;
+      *s_cum = cum;
+    }
+    carry += total;
+    __syncthreads();
+    if (*s_b >= 0) break;
+  }
+  __syncthreads();
+  return *s_b >= 0;
+}
+
+// Request owning query token t (-1 if none) and the stream start of that request.
+__device__ void plan_token(const DecodeParams& p, int G, int t, int64_t* red, int* s_b,
+                           int64_t* s_cum) {
+  if (threadIdx.x == 0) *s_b = -1;
+  int64_t carry = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += kThreads) {
+    const int b = b0 + threadIdx.x;
+    int64_t R = 0;
+    bool mine = false;
+    if (b < p.batch) {
+      Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
+      R = (int64_t)G * request_rows(r.n, r.qlen);
+      mine = t >= r.q_base && t < r.q_base + r.qlen;
+    }
+    int64_t total;
+    const int64_t cum = carry + block_excl_scan_i64(R, red, total);
+    if (mine) {
+      *s_b = b;
+      *s_cum = cum;
+    }
+    carry += total;
+    __syncthreads();
+    if (*s_b >= 0) break;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- fp8 decode
+
+struct TileIdx {
+  int i0, i1;  // pool rows for tile rows (lane%16) and (16 + lane%16); -1 = past the end
+};
+
+__device__ __forceinline__ TileIdx fetch_idx(const int32_t* idxp, int rows, int tile, int n) {
+  TileIdx t;
+  const int e0 = tile * kTile + n, e1 = e0 + 16;
+  t.i0 = -1;
+  t.i1 = -1;
+  if (e0 < rows) t.i0 = idxp[e0];
+  if (e1 < rows) t.i1 = idxp[e1];
+  return t;
+}
+
+__device__ __forceinline__ void issue_rows(uint4 (&B)[18], const uint8_t* kv, int64_t pool_entries,
+                                           TileIdx ti, int gq) {
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  const int64_t last = pool_entries - 1;
+  if (ti.i0 >= 0) {
+    const int64_t r = (int64_t)ti.i0 < last ? (int64_t)ti.i0 : last;
+    const uint8_t* src = kv + r * kRowDim + 16 * gq;
+#pragma unroll
+    for (int c = 0; c < 9; ++c) B[c] = *(const uint4*)(src + 64 * c);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 9; ++c) B[c] = z;
+  }
+  if (ti.i1 >= 0) {
+    const int64_t r = (int64_t)ti.i1 < last ? (int64_t)ti.i1 : last;
+    const uint8_t* src = kv + r * kRowDim + 16 * gq;
+#pragma unroll
+    for (int c = 0; c < 9; ++c) B[9 + c] = *(const uint4*)(src + 64 * c);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 9; ++c) B[9 + c] = z;
+  }
+}
+
+struct WaveState {
+  v4f O[32];  // O^T blocks: block (half*16 + t) element i = row (lane%16),
+              // dim 256*half + 64*(lane/16) + 16*i + t
+  float m;    // running max of base-2 scores of row (lane%16)
+  float l;    // this lane's partial sum of 2^(s - m)
+};
+
+// One 32-row tile: scores, online softmax, P.V.  B holds the tile's rows and is
+// refilled with the rows of `next` before the softmax work starts.
+__device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx& next,
+                                         const long (&qlo)[9], const long (&qhi)[9],
+                                         uint8_t* vst, const DecodeParams& p, const int32_t* idxp,
+                                         int rows, int tile, float cs, int n, int gq) {
+  // ---- S^T = K . Q^T for kv rows [0,16) and [16,32) of the tile
+  v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 9; ++c) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].x, B[c].y), qlo[c], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].x, B[9 + c].y), qlo[c], s1, 0, 0,
+                                                    0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].z, B[c].w), qhi[c], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].z, B[9 + c].w), qhi[c], s1, 0,
+                                                    0, 0);
+  }
+
+  // ---- stage the latent 512 bytes of both 16-row blocks in LDS
+  wave_lds_sync();  // the previous tile's V reads are complete
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    *(uint4*)(vst + n * kVStride + 64 * c + 16 * gq) = B[c];
+    *(uint4*)(vst + (16 + n) * kVStride + 64 * c + 16 * gq) = B[9 + c];
+  }
+
+  // ---- refill B two tiles ahead; fetch the indices of the tile after that
+  issue_rows(B, p.kv, p.pool_entries, next, gq);
+  next = fetch_idx(idxp, rows, tile + 4 * kWaves, n);
+
+  // ---- online softmax (row = lane%16; this lane holds kv rows 4gq+i, 16+4gq+i)
+  const int base = tile * kTile + 4 * gq;
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sc[i] = (base + i < rows) ? s0[i] * cs : neg_inf();
+    sc[4 + i] = (base + 16 + i < rows) ? s1[i] * cs : neg_inf();
+  }
+  float tmax = sc[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float mnew = fmaxf(st.m, tmax);  // finite: row 0 of a live tile is valid
+  const float alpha = fast_exp2(st.m - mnew);
+  float x[8], psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float pr = fast_exp2(sc[i] - mnew);
+    psum += pr;
+    x[i] = pr * kPScale;
+  }
+  st.l = st.l * alpha + psum;
+  st.m = mnew;
+  if (alpha != 1.0f) {
+#pragma unroll
+    for (int b = 0; b < 32; ++b) st.O[b] *= alpha;
+  }
+
+  // ---- P*256 = hi + lo in e4m3; byte k of the operand = kv row kappa(gq, k)
+  u32 h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+  h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h0, true);
+  u32 h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+  h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], h1, true);
+  float r[8];
+  r[0] = x[0] - __builtin_amdgcn_cvt_f32_fp8(h0, 0);
+  r[1] = x[1] - __builtin_amdgcn_cvt_f32_fp8(h0, 1);
+  r[2] = x[2] - __builtin_amdgcn_cvt_f32_fp8(h0, 2);
+  r[3] = x[3] - __builtin_amdgcn_cvt_f32_fp8(h0, 3);
+  r[4] = x[4] - __builtin_amdgcn_cvt_f32_fp8(h1, 0);
+  r[5] = x[5] - __builtin_amdgcn_cvt_f32_fp8(h1, 1);
+  r[6] = x[6] - __builtin_amdgcn_cvt_f32_fp8(h1, 2);
+  r[7] = x[7] - __builtin_amdgcn_cvt_f32_fp8(h1, 3);
+  u32 l0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+  l0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], l0, true);
+  u32 l1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[4], r[5], 0, false);
+  l1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], l1, true);
+  const long phi = as_long(h0, h1), plo = as_long(l0, l1);
+
+  // ---- O^T += V^T . P^T; the kv row of operand byte k is kappa(gq, k):
+  //      4gq + k for k < 4, 16 + 4gq + (k - 4) otherwise.
+  wave_lds_sync();  // all lanes' V writes are in LDS
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int row = (k < 4) ? (4 * gq + k) : (16 + 4 * gq + (k - 4));
+      v[k] = *(const uint4*)(vst + row * kVStride + 16 * n + 256 * half);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32 a0, a1, a2, a3, b0, b1, b2, b3;
+      const u32* w0 = (const u32*)&v[0];
+      const u32* w1 = (const u32*)&v[1];
+      const u32* w2 = (const u32*)&v[2];
+      const u32* w3 = (const u32*)&v[3];
+      const u32* w4 = (const u32*)&v[4];
+      const u32* w5 = (const u32*)&v[5];
+      const u32* w6 = (const u32*)&v[6];
+      const u32* w7 = (const u32*)&v[7];
+      transpose4x4(w0[q], w1[q], w2[q], w3[q], a0, a1, a2, a3);
+      transpose4x4(w4[q], w5[q], w6[q], w7[q], b0, b1, b2, b3);
+      const long A[4] = {as_long(a0, b0), as_long(a1, b1), as_long(a2, b2), as_long(a3, b3)};
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int blk = half * 16 + 4 * q + bb;
+        st.O[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(A[bb], phi, st.O[blk], 0, 0, 0);
+        st.O[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(A[bb], plo, st.O[blk], 0, 0, 0);
+      }
+    }
+  }
+}
+
+struct alignas(16) DecodeShared {
+  uint8_t buf[kCombBytes];  // V staging during the tile loop, O^T exchange after it
+  int64_t red[kWaves];
+  float m[kWaves][16];
+  float l[kWaves][16];
+  int b;
+  int64_t cum;
+};
+
+// One piece: KV positions [kv_pos0, kv_pos0 + rows) of unit (token t, head group g).
+__device__ __forceinline__ void fp8_piece(const DecodeParams& p, DecodeShared& sh, int t, int g,
+                                          int kv_pos0, int rows, int slot, float cs, float ks) {
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
+  __syncthreads();  // the previous piece is done with the LDS buffer
+
+  long qlo[9], qhi[9];
+  {
+    const uint8_t* qrow = p.q + ((int64_t)t * p.num_heads + g * kGroup + n) * kRowDim + 16 * gq;
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      const uint4 x = *(const uint4*)(qrow + 64 * c);
+      qlo[c] = as_long(x.x, x.y);
+      qhi[c] = as_long(x.z, x.w);
+    }
+  }
+
+  WaveState st;
+#pragma unroll
+  for (int b = 0; b < 32; ++b) st.O[b] = v4f{0.f, 0.f, 0.f, 0.f};
+  st.m = neg_inf();
+  st.l = 0.f;
+
+  const int ntiles = (rows + kTile - 1) / kTile;
+  const int32_t* idxp = p.kv_indices + kv_pos0;
+  uint8_t* vst = sh.buf + wv * kVWaveBytes;
+
+  int tile = wv;
+  uint4 bufA[18], bufB[18];
+  TileIdx nextA, nextB;
+  {
+    const TileIdx t0 = fetch_idx(idxp, rows, tile, n);
+    const TileIdx t1 = fetch_idx(idxp, rows, tile + kWaves, n);
+    issue_rows(bufA, p.kv, p.pool_entries, t0, gq);
+    issue_rows(bufB, p.kv, p.pool_entries, t1, gq);
+    nextA = fetch_idx(idxp, rows, tile + 2 * kWaves, n);
+    nextB = fetch_idx(idxp, rows, tile + 3 * kWaves, n);
+  }
+  while (tile < ntiles) {
+    fp8_tile(st, bufA, nextA, qlo, qhi, vst, p, idxp, rows, tile, cs, n, gq);
+    tile += kWaves;
+    if (tile >= ntiles) break;
+    fp8_tile(st, bufB, nextB, qlo, qhi, vst, p, idxp, rows, tile, cs, n, gq);
+    tile += kWaves;
+  }
+
+  // ---- merge the 4 waves' online-softmax states
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+  __syncthreads();  // every wave is done with its V staging
+  if (gq == 0) {
+    sh.m[wv][n] = st.m;
+    sh.l[wv][n] = st.l;
+  }
+  v4f* comb = (v4f*)sh.buf;
+#pragma unroll
+  for (int b = 0; b < 32; ++b) comb[(wv * 32 + b) * 64 + lane] = st.O[b];
+  __syncthreads();
+
+  float mw[kWaves], M = neg_inf();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    mw[w] = sh.m[w][n];
+    M = fmaxf(M, mw[w]);
+  }
+  float fw[kWaves], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    fw[w] = (mw[w] == neg_inf()) ? 0.f : fast_exp2(mw[w] - M);
+    L += sh.l[w][n] * fw[w];
+  }
+  const float oscale = ks / (kPScale * L);
+
+  // This wave writes O^T blocks [8wv, 8wv + 8): half = wv/2, t = 8(wv%2) + bb;
+  // element i of block bb is dim 256*half + 64*gq + 16*i + 8*(wv%2) + bb.
+  float acc[8][4];
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    v4f a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) a += fw[w] * comb[(w * 32 + 8 * wv + bb) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[bb][i] = a[i] * oscale;
+  }
+  const int half = wv >> 1;
+  const int dim0 = 256 * half + 64 * gq + 8 * (wv & 1);
+  const int64_t orow = (int64_t)t * p.num_heads + g * kGroup + n;
+  const float lse_val = (M + fast_log2(L)) * kLn2;
+  if (slot < 0) {
+    uint16_t* dst = p.o + orow * kLatent + dim0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 pk;
+      pk.x = bf16_bits(acc[0][i]) | (bf16_bits(acc[1][i]) << 16);
+      pk.y = bf16_bits(acc[2][i]) | (bf16_bits(acc[3][i]) << 16);
+      pk.z = bf16_bits(acc[4][i]) | (bf16_bits(acc[5][i]) << 16);
+      pk.w = bf16_bits(acc[6][i]) | (bf16_bits(acc[7][i]) << 16);
+      *(uint4*)(dst + 16 * i) = pk;
+    }
+    if (p.lse != nullptr && wv == 0 && gq == 0) p.lse[orow] = lse_val;
+  } else {
+    float* dst = p.part_o + ((int64_t)slot * kGroup + n) * kLatent + dim0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(float4*)(dst + 16 * i) = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+      *(float4*)(dst + 16 * i + 4) = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
+    }
+    if (wv == 0 && gq == 0) p.part_lse[(int64_t)slot * kGroup + n] = lse_val;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_fp8_kernel(const DecodeParams p) {
+  __shared__ DecodeShared sh;
+  const int G = p.num_heads / kGroup;
+  const int64_t W = plan_total(p, G, sh.red);
+  if (W == 0) return;
+  const int nw = effective_workers(W, p.num_workers);
+  const int w = blockIdx.x;
+  if (w >= nw) return;
+  const int64_t p0 = worker_begin(w, W, nw), p1 = worker_begin(w + 1, W, nw);
+  if (p0 >= p1) return;
+  if (!plan_locate(p, G, p0, sh.red, &sh.b, &sh.cum)) return;
+
+  Cursor c;
+  {
+    const int b = sh.b;
+    const Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
+    cursor_in_request(c, b, r, p0 - sh.cum, G);
+  }
+  const float qs = p.q_scale ? *p.q_scale : 1.0f;
+  const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
+  const float cs = p.sm_scale * kLog2e * qs * ks;
+
+  int64_t pos = p0;
+  int piece = 0;
+  while (pos < p1) {
+    const int v = visible(c.r.n, c.r.qlen, c.j);
+    const int len = (int)lmin((int64_t)(v - c.k), p1 - pos);
+    if (len <= 0) break;  // not reached with a consistent plan
+    const bool complete = (c.k == 0 && len == v);
+    const int slot = complete ? -1 : (piece == 0 ? 2 * w : 2 * w + 1);
+    fp8_piece(p, sh, c.r.q_base + c.j, c.g, c.r.kv_base + c.k, len, slot, cs, ks);
+    pos += len;
+    c.k += len;
+    ++piece;
+    if (pos < p1 && c.k == v) {
+      if (!cursor_next_unit(c, p.qo_indptr, p.kv_indptr, p.batch, p.kv_indices_len, p.num_tokens,
+                            G))
+        break;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- split combine
+
+// grid (T * G, 4): block (u, y) merges rows 4y..4y+3 of unit u = t * G + g, one
+// row per wave, 8 dims per lane.  Writes o = 0 / lse = -inf for empty units and
+// leaves units finished inside one worker alone.
+__global__ __launch_bounds__(kThreads) void mla_combine_kernel(const DecodeParams p) {
+  __shared__ int64_t red[kWaves];
+  __shared__ int s_b;
+  __shared__ int64_t s_cum;
+  const int G = p.num_heads / kGroup;
+  const int u = blockIdx.x;
+  const int t = u / G, g = u % G;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = 4 * blockIdx.y + wv;
+  const int64_t orow = (int64_t)t * p.num_heads + g * kGroup + n;
+
+  const int64_t W = plan_total(p, G, red);
+  plan_token(p, G, t, red, &s_b, &s_cum);
+  const int b = s_b;
+  int v = 0;
+  int64_t ustart = 0;
+  if (b >= 0) {
+    const Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
+    const int j = t - r.q_base;
+    v = visible(r.n, r.qlen, j);
+    ustart = s_cum;
+    for (int jj = first_visible_token(r); jj < j; ++jj) ustart += (int64_t)G * visible(r.n, r.qlen, jj);
+    ustart += (int64_t)g * v;
+  }
+  uint16_t* dst = p.o + orow * kLatent + 8 * lane;
+  if (v == 0 || W == 0) {
+    *(uint4*)dst = make_uint4(0, 0, 0, 0);
+    if (p.lse != nullptr && lane == 0) p.lse[orow] = neg_inf();
+    return;
+  }
+  const int nw = effective_workers(W, p.num_workers);
+  const int wlo = worker_of(ustart, W, nw), whi = worker_of(ustart + v - 1, W, nw);
+  if (wlo == whi) return;
+
+  float M = neg_inf();
+  for (int w = wlo; w <= whi; ++w) {
+    const int slot = (w == wlo && worker_begin(w, W, nw) < ustart) ? 2 * w + 1 : 2 * w;
+    M = fmaxf(M, p.part_lse[(int64_t)slot * kGroup + n]);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float S = 0.f;
+  for (int w = wlo; w <= whi; ++w) {
+    const int slot = (w == wlo && worker_begin(w, W, nw) < ustart) ? 2 * w + 1 : 2 * w;
+    const float wt = fast_exp2((p.part_lse[(int64_t)slot * kGroup + n] - M) * kLog2e);
+    S += wt;
+    const float* src = p.part_o + ((int64_t)slot * kGroup + n) * kLatent + 8 * lane;
+    const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
+    acc[0] += wt * x0.x;
+    acc[1] += wt * x0.y;
+    acc[2] += wt * x0.z;
+    acc[3] += wt * x0.w;
+    acc[4] += wt * x1.x;
+    acc[5] += wt * x1.y;
+    acc[6] += wt * x1.z;
+    acc[7] += wt * x1.w;
+  }
+  const float inv = 1.0f / S;
+  uint4 pk;
+  pk.x = bf16_bits(acc[0] * inv) | (bf16_bits(acc[1] * inv) << 16);
+  pk.y = bf16_bits(acc[2] * inv) | (bf16_bits(acc[3] * inv) << 16);
+  pk.z = bf16_bits(acc[4] * inv) | (bf16_bits(acc[5] * inv) << 16);
+  pk.w = bf16_bits(acc[6] * inv) | (bf16_bits(acc[7] * inv) << 16);
+  *(uint4*)dst = pk;
+  if (p.lse != nullptr && lane == 0) p.lse[orow] = M + fast_log2(S) * kLn2;
+}
+
+// ---------------------------------------------------------------- shard merge
+
+// One wave per (token, head) row, 8 dims per lane.
+template <bool kFp32Parts>
+__global__ __launch_bounds__(kThreads) void mla_merge_kernel(const void* o_parts,
+                                                             const float* lse_parts, int S,
+                                                             int64_t rows, uint16_t* o,
+                                                             float* lse) {
+  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float M = neg_inf();
+  for (int s = 0; s < S; ++s) M = fmaxf(M, lse_parts[(int64_t)s * rows + row]);
+  uint16_t* dst = o + row * kLatent + 8 * lane;
+  if (M == neg_inf()) {
+    *(uint4*)dst = make_uint4(0, 0, 0, 0);
+    if (lse != nullptr && lane == 0) lse[row] = neg_inf();
+    return;
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float ls = lse_parts[(int64_t)s * rows + row];
+    if (ls == neg_inf()) continue;  // empty shard: its o row is not read
+    const float wt = fast_exp2((ls - M) * kLog2e);
+    sum += wt;
+    const int64_t off = ((int64_t)s * rows + row) * kLatent + 8 * lane;
+    if constexpr (kFp32Parts) {
+      const float* src = (const float*)o_parts + off;
+      const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
+      acc[0] += wt * x0.x;
+      acc[1] += wt * x0.y;
+      acc[2] += wt * x0.z;
+      acc[3] += wt * x0.w;
+      acc[4] += wt * x1.x;
+      acc[5] += wt * x1.y;
+      acc[6] += wt * x1.z;
+      acc[7] += wt * x1.w;
+    } else {
+      const uint4 x = *(const uint4*)((const uint16_t*)o_parts + off);
+      const u32 wds[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] += wt * __uint_as_float(wds[k] << 16);
+        acc[2 * k + 1] += wt * __uint_as_float(wds[k] & 0xFFFF0000u);
+      }
+    }
+  }
+  const float inv = 1.0f / sum;
+  uint4 pk;
+  pk.x = bf16_bits(acc[0] * inv) | (bf16_bits(acc[1] * inv) << 16);
+  pk.y = bf16_bits(acc[2] * inv) | (bf16_bits(acc[3] * inv) << 16);
+  pk.z = bf16_bits(acc[4] * inv) | (bf16_bits(acc[5] * inv) << 16);
+  pk.w = bf16_bits(acc[6] * inv) | (bf16_bits(acc[7] * inv) << 16);
+  *(uint4*)dst = pk;
+  if (lse != nullptr && lane == 0) lse[row] = M + fast_log2(sum) * kLn2;
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, hipStream_t stream) {
+  if (kv_dtype != 0) return hipErrorNotSupported;
+  const int G = p.num_heads / kGroup;
+  hipLaunchKernelGGL(mla_decode_fp8_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(p.num_tokens * G), 4), dim3(kThreads), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const void* o_parts, int parts_fp32, const float* lse_parts, int num_parts,
+                        int64_t rows, uint16_t* o, float* lse, hipStream_t stream) {
+  const unsigned grid = (unsigned)((rows + kWaves - 1) / kWaves);
+  if (parts_fp32)
+    hipLaunchKernelGGL(mla_merge_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, o_parts,
+                       lse_parts, num_parts, rows, o, lse);
+  else
+    hipLaunchKernelGGL(mla_merge_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, o_parts,
+                       lse_parts, num_parts, rows, o, lse);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,45 @@
+// mla_internal.h - parameters shared between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeParams {
+  const uint8_t* q;         // (T, H, 576) elements of the storage type
+  const uint8_t* kv;        // (pool_entries, 576)
+  int64_t pool_entries;
+  uint16_t* o;              // (T, H, 512) bf16
+  const int32_t* qo_indptr;  // (B+1)
+  const int32_t* kv_indptr;  // (B+1)
+  const int32_t* kv_indices;
+  int kv_indices_len;
+  int batch;
+  int num_tokens;
+  int num_heads;
+  float sm_scale;
+  const float* q_scale;     // device scalar or nullptr (1.0)
+  const float* kv_scale;    // device scalar or nullptr (1.0)
+  float* lse;               // (T, H) or nullptr
+  float* part_o;            // workspace: (2*num_workers, 16, 512) fp32
+  float* part_lse;          // workspace: (2*num_workers, 16) fp32
+  int num_workers;
+};
+
+// Workspace layout for `num_workers` workers.
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline size_t part_o_bytes(int num_workers) { return align256(size_t(2) * num_workers * 16 * 512 * 4); }
+inline size_t part_lse_bytes(int num_workers) { return align256(size_t(2) * num_workers * 16 * 4); }
+inline size_t workspace_bytes(int num_workers) {
+  return part_o_bytes(num_workers) + part_lse_bytes(num_workers);
+}
+
+// kv_dtype: 0 = fp8 e4m3fn, 1 = bf16.
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, hipStream_t stream);
+
+hipError_t launch_merge(const void* o_parts, int parts_fp32, const float* lse_parts, int num_parts,
+                        int64_t rows, uint16_t* o, float* lse, hipStream_t stream);
+
+}  // namespace mla

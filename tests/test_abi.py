@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every symbol include/mla.h declares, and
+rejects bad arguments on the host before touching HIP (no GPU needed)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from mla_latent_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(mla_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("mla_decode", "mla_merge_partials", "mla_decode_workspace_bytes",
+                     "mla_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} declared in mla.h but not exported"
+        assert name in _lib.SIGNATURES, f"binding has no signature for {name}"
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for code, name in _lib.STATUS.items():
+        assert L.mla_status_string(code).decode().startswith(name)
+    assert L.mla_status_string(99).decode() == "MLA_ERR_UNKNOWN"
+
+
+def test_workspace_size_is_pure_and_bounded():
+    L = _lib.lib()
+    ws = L.mla_decode_workspace_bytes_ex(16, 16, 16, 1, 256)
+    assert ws >= 2 * 256 * 16 * (512 + 1) * 4
+    assert ws % 256 == 0
+    assert L.mla_decode_workspace_bytes_ex(0, 16, 16, 1, 256) == 0
+    assert L.mla_decode_workspace_bytes_ex(16, 16, 16, 0, 256) == 0
+    assert L.mla_decode_workspace_bytes_ex(16, 16, 16, 1, 0) == 0
+    assert L.mla_decode_workspace_bytes_ex(2, 9, 16, 4, 8) == 0  # more tokens than 2 * 4
+
+
+FAKE = C.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _decode(**over):
+    args = dict(
+        q=FAKE, q_dtype=0, kv=FAKE, kv_dtype=0, pool=256, o=FAKE, qo=FAKE, kvp=FAKE, idx=FAKE,
+        idx_len=164, lpl=None, batch=2, T=2, H=16, qmax=1, sm=0.072, qs=None, ks=None, rl=0,
+        lse=None, ws=FAKE, ws_len=1 << 30, nw=8, stream=None,
+    )
+    args.update(over)
+    return _lib.lib().mla_decode_ex(*args.values())
+
+
+@pytest.mark.parametrize(
+    "over,status",
+    [
+        (dict(q=None), 1),
+        (dict(kv=None), 1),
+        (dict(o=None), 1),
+        (dict(idx=None), 1),
+        (dict(rl=1, lse=None), 1),
+        (dict(q_dtype=1, kv_dtype=0), 3),
+        (dict(q_dtype=2, kv_dtype=2), 3),
+        (dict(H=12), 4),
+        (dict(H=0), 4),
+        (dict(batch=0), 2),
+        (dict(qmax=0), 2),
+        (dict(qmax=65), 2),
+        (dict(T=3, qmax=1), 2),
+        (dict(pool=0), 2),
+        (dict(nw=-1), 2),
+        (dict(ws=None), 5),
+        (dict(ws_len=1024), 5),
+    ],
+)
+def test_decode_rejects_bad_arguments_before_any_launch(over, status):
+    assert _decode(**over) == status
+
+
+@pytest.mark.parametrize(
+    "args,status",
+    [
+        ((None, 2, FAKE, 8, 32, 96, FAKE, FAKE, None), 1),
+        ((FAKE, 0, FAKE, 8, 32, 96, FAKE, FAKE, None), 3),
+        ((FAKE, 2, FAKE, 0, 32, 96, FAKE, FAKE, None), 2),
+        ((FAKE, 2, None, 8, 32, 96, FAKE, FAKE, None), 1),
+    ],
+)
+def test_merge_rejects_bad_arguments(args, status):
+    assert _lib.lib().mla_merge_partials(*args) == status

@@ -1,0 +1,248 @@
+"""GPU parity of mla_decode / mla_merge_partials against the float64 oracle.
+
+Every call goes through the C ABI (libmla.so via the ctypes binding).  Inputs
+come from the shared seeded generators; the oracle reads back exactly the
+bytes the kernels consumed.  Small cases are compared in full; the full-size
+workloads are compared on sampled requests in the launch configuration the
+benchmark times (one worker per compute unit).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import io as oio
+from oracle import mla as omla
+from tests.parity import assert_gate, bf16_abs_tol, metrics
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU machines too
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import mla_latent_attention_amd as mla  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run(w, num_workers=0, return_lse=True, q=None):
+    torch.cuda.synchronize()
+    out = mla.decode(
+        w.q if q is None else q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
+        w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale, return_lse=return_lse,
+        max_seqlen_q=w.max_seqlen_q, num_workers=num_workers,
+    )
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle(w, requests=None):
+    a = oio.workload_args(w, requests)
+    toks = a["tokens"]
+    o, lse = oio.call_decode(a)
+    return toks, o, lse
+
+
+def check(w, requests=None, num_workers=0, where=""):
+    say(f"[parity] {w.name} requests={requests} workers={num_workers}")
+    o, lse = run(w, num_workers)
+    toks, o_ref, lse_ref = oracle(w, requests)
+    m = metrics(o[toks], o_ref, lse[toks], lse_ref)
+    say(f"[parity] {w.name}: {m}")
+    assert_gate(m, where or w.name)
+    return o, lse, m
+
+
+# ------------------------------------------------------------------ small cases
+
+
+def test_tiny_workload_full():
+    check(workloads.tiny(DEV))
+
+
+def small_shared(seed=0, B=4, H=16, qlens=None, real_heads=12):
+    rng = np.random.default_rng(seed)
+    lengths = [2000 + 1100 + int(x) for x in rng.integers(0, 400, size=B)]
+    return workloads.build(
+        f"small-shared-{seed}", lengths, num_heads=H, real_heads=real_heads, qlens=qlens,
+        pool_entries=1 << 15, kv_std=0.5, q_std=1.0, scale_range=(0.5, 2.0), shared_prefix=2000,
+        seed=100 + seed, device=DEV,
+    )
+
+
+@pytest.mark.parametrize("nw", [0, 1, 2, 3, 16, 256])
+def test_small_shared_prefix_any_worker_count(nw):
+    check(small_shared(), num_workers=nw, where=f"small nw={nw}")
+
+
+def test_ragged_lengths_and_empty_requests():
+    lengths = [0, 1, 31, 32, 33, 100, 1000, 4097, 0, 2]
+    qlens = [1, 1, 1, 1, 1, 1, 1, 1, 1, 1]
+    w = workloads.build("ragged", lengths, num_heads=16, real_heads=12, qlens=qlens,
+                        pool_entries=8192, kv_std=1.0, scale_range=(0.5, 2.0), seed=7, device=DEV)
+    for nw in (0, 5):
+        o, lse, _ = check(w, num_workers=nw, where=f"ragged nw={nw}")
+        assert torch.all(o[0] == 0) and torch.all(o[8] == 0)
+        assert torch.all(torch.isneginf(lse[0])) and torch.all(torch.isneginf(lse[8]))
+
+
+def test_multi_token_causal_many_heads():
+    w = workloads.build("mt-96", [700, 1333, 3], num_heads=96, real_heads=96, qlens=[4, 3, 4],
+                        pool_entries=4096, kv_std=0.5, scale_range=(0.5, 2.0), seed=8, device=DEV)
+    for nw in (0, 7):
+        check(w, num_workers=nw, where=f"mt-96 nw={nw}")
+
+
+def test_peaky_scores():
+    """Stress case outside the benchmark distributions: |o| reaches ~5, where a
+    bf16 unit in the last place (2^-5) exceeds 1e-2, so the absolute bound is
+    bf16's own resolution at that magnitude; row-relative and lse gates hold."""
+    w = workloads.build("peaky", [5000, 77], num_heads=32, real_heads=32, pool_entries=8192,
+                        kv_std=2.0, q_std=4.0, scale_range=(0.5, 2.0), seed=9, device=DEV)
+    o, lse = run(w)
+    _, o_ref, lse_ref = oracle(w)
+    m = metrics(o, o_ref, lse, lse_ref)
+    say(f"[parity] peaky: {m}")
+    assert_gate(m, "peaky", abs_tol=bf16_abs_tol(m["ref_absmax"]))
+
+
+# ------------------------------------------------------------------ invariants
+
+
+def test_pad_heads_do_not_change_real_heads_bitwise():
+    w = small_shared(1)
+    o_zero, lse_zero = run(w)
+    q_rand = w.q.clone()
+    g = torch.Generator(device=DEV).manual_seed(5)
+    noise = torch.randn(q_rand[:, 12:].shape, generator=g, device=DEV).clamp(-448, 448)
+    q_rand[:, 12:] = noise.to(torch.float8_e4m3fn)
+    o_r, lse_r = run(w, q=q_rand)
+    assert torch.equal(o_r[:, :12], o_zero[:, :12])
+    assert torch.equal(lse_r[:, :12], lse_zero[:, :12])
+
+
+def test_run_to_run_bitwise_deterministic():
+    w = small_shared(2)
+    a = run(w)
+    b = run(w)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_power_of_two_scale_exchange_is_bitwise():
+    w = small_shared(3)
+    o1, lse1 = run(w)
+    w2 = workloads.Workload(**{**w.__dict__, "kv_scale": w.kv_scale * 2, "sm_scale": w.sm_scale / 2})
+    o2, lse2 = run(w2)
+    assert torch.equal(o2.float(), 2 * o1.float())
+    assert torch.equal(lse2, lse1)
+
+
+def test_kv_permutation_within_requests():
+    w = small_shared(4)
+    o1, lse1 = run(w)
+    idx = w.kv_indices.clone()
+    kvp = w.kv_indptr.cpu().tolist()
+    g = torch.Generator(device=DEV).manual_seed(3)
+    for b in range(w.batch):
+        s, e = kvp[b], kvp[b + 1]
+        idx[s:e] = idx[s:e][torch.randperm(e - s, generator=g, device=DEV)]
+    w2 = workloads.Workload(**{**w.__dict__, "kv_indices": idx})
+    o2, lse2 = run(w2)
+    m = metrics(o2, o1.float().cpu().numpy().astype(np.float64), lse2, lse1.cpu().numpy())
+    assert_gate(m, "permutation")
+
+
+def test_dcp_shards_plus_merge_equal_the_full_call():
+    """8 KV shards decoded with return_lse, merged by mla_merge_partials."""
+    full = workloads.build("dcp-mini", [1600, 2400], num_heads=32, real_heads=32, qlens=[1, 1],
+                           pool_entries=8192, kv_std=0.5, scale_range=(0.5, 2.0), seed=10, device=DEV)
+    o_full, lse_full = run(full)
+    kvp = full.kv_indptr.cpu().tolist()
+    S = 8
+    parts_o, parts_l = [], []
+    for s in range(S):
+        pieces, lens = [], []
+        for b in range(full.batch):
+            n = kvp[b + 1] - kvp[b]
+            lo, hi = n * s // S, n * (s + 1) // S
+            pieces.append(full.kv_indices[kvp[b] + lo: kvp[b] + hi])
+            lens.append(hi - lo)
+        ind = torch.cat(pieces)
+        kv_indptr = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+        ws = workloads.Workload(**{**full.__dict__, "kv_indices": ind, "kv_indptr": kv_indptr, "lengths": lens})
+        o_s, l_s = run(ws)
+        parts_o.append(o_s)
+        parts_l.append(l_s)
+    o_m, lse_m = mla.merge_partials(torch.stack(parts_o), torch.stack(parts_l))
+    toks, o_ref, lse_ref = oracle(full)
+    assert_gate(metrics(o_m, o_ref, lse_m, lse_ref), "dcp merged vs oracle")
+    assert_gate(metrics(o_full, o_ref, lse_full, lse_ref), "dcp full vs oracle")
+
+
+# ------------------------------------------------------------------ merge
+
+
+@pytest.mark.parametrize("parts_dtype", ["fp32", "bf16"])
+def test_merge_partials_full_size(parts_dtype):
+    o_p, lse_p = workloads.merge_shards(parts_dtype=parts_dtype, device=DEV)
+    o, lse = mla.merge_partials(o_p, lse_p)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = omla.merge_partials(oio.codes(o_p).astype(np.float64) if parts_dtype == "fp32"
+                                         else _bf16_to_f64(o_p), lse_p.cpu().numpy().astype(np.float64))
+    m = metrics(o, ref_o, lse, ref_lse)
+    say(f"[merge] {parts_dtype}: {m}")
+    assert_gate(m, f"merge {parts_dtype}")
+
+
+def _bf16_to_f64(t):
+    from oracle import codecs
+    return codecs.decode_bf16(oio.codes(t))
+
+
+# ------------------------------------------------------------------ full sizes (sampled)
+
+
+def test_headline_batch16_sampled():
+    w = workloads.c16(DEV, "shared", return_lse=True)
+    check(w, requests=[0, 7, 15])
+    del w
+
+
+def test_headline_batch16_unshared_prefix_sampled():
+    w = workloads.c16(DEV, "unshared", return_lse=True)
+    check(w, requests=[3, 12])
+
+
+def test_batch24_sampled():
+    w = workloads.c24(DEV, return_lse=True)
+    check(w, requests=[0, 11, 23])
+
+
+def test_mixed_lengths_fp8_sampled():
+    w = workloads.mixed(DEV, "fp8", return_lse=True)
+    L = np.array(w.lengths)
+    check(w, requests=[int(L.argmax()), int(L.argmin()), 17])
+
+
+def test_dcp_share_sampled():
+    w = workloads.dcp_share(DEV)
+    check(w, requests=[0, 5])
+
+
+def test_captured_argument_layout_is_accepted():
+    """The exact tensors of the captured call, including the (N,1,1,576) view."""
+    w = workloads.c16(DEV, "shared")
+    kv4 = w.kv_pool.view(-1, 1, 1, 576)
+    assert tuple(kv4.stride()) == (576, 576, 576, 1)
+    o = mla.decode(w.q, kv4, w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_lens,
+                   w.sm_scale, w.q_scale, w.kv_scale, max_seqlen_q=1)
+    torch.cuda.synchronize()
+    assert o.shape == (16, 16, 512) and o.dtype == torch.bfloat16 and o.stride() == (8192, 512, 1)
+    assert w.kv_indices.numel() == workloads.INDEX_BUFFER

@@ -1,0 +1,129 @@
+"""Properties of the work planner (host mirror of the device planner; no GPU).
+
+Every unit (query token, head group) must be covered exactly once by pieces,
+every worker must get an equal share of the stream, partial pieces may only sit
+at a worker's two ends, and the split combine's slot rule must name exactly the
+slots the decode workers write.
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+from mla_latent_attention_amd import plan_host
+
+MIN_WORKER_ROWS = 512
+
+
+def visible(n, qlen, j):
+    return max(0, n - (qlen - 1 - j))
+
+
+def units(qo, kv, G):
+    """(token, group, length, stream start) in stream order, skipping nothing."""
+    out, pos = [], 0
+    for b in range(len(qo) - 1):
+        n, ql = kv[b + 1] - kv[b], qo[b + 1] - qo[b]
+        for j in range(ql):
+            v = visible(n, ql, j)
+            for g in range(G):
+                out.append((qo[b] + j, g, v, pos))
+                pos += v
+    return out, pos
+
+
+def check_plan(qo, kv, H, nw_req):
+    G = H // 16
+    us, W = units(qo, kv, G)
+    pieces = plan_host(qo, kv, H, nw_req)
+    if W == 0:
+        assert len(pieces) == 0
+        return pieces
+    nw = min(nw_req, max(1, -(-W // MIN_WORKER_ROWS)))
+    cover = {}
+    for w, t, g, kb, ke, ul, slot, comp in pieces:
+        assert 0 <= kb < ke <= ul
+        cover.setdefault((t, g), []).append((kb, ke, w, slot, comp))
+    # coverage: each non-empty unit exactly tiled, in worker order
+    for t, g, v, start in us:
+        if v == 0:
+            assert (t, g) not in cover
+            continue
+        segs = sorted(cover[(t, g)])
+        assert segs[0][0] == 0 and segs[-1][1] == v
+        for (a0, a1, *_), (b0, b1, *_) in zip(segs, segs[1:]):
+            assert a1 == b0
+        if len(segs) == 1:
+            assert segs[0][4] == 1 and segs[0][3] == -1
+        else:
+            assert all(s[4] == 0 for s in segs)
+            # the combine's rule: worker range [wlo, whi]; slot 2w+1 only for a
+            # first worker that started before the unit
+            begin = lambda w: w * W // nw  # noqa: E731
+            owner = lambda p: ((p + 1) * nw - 1) // W  # noqa: E731
+            wlo, whi = owner(start), owner(start + v - 1)
+            want = {(2 * w + 1) if (w == wlo and begin(w) < start) else 2 * w for w in range(wlo, whi + 1)}
+            assert {s[3] for s in segs} == want
+            assert [s[2] for s in segs] == list(range(wlo, whi + 1))
+    # balance: worker w processes exactly its stream share
+    per_worker = np.zeros(nw, dtype=np.int64)
+    for w, t, g, kb, ke, *_ in pieces:
+        per_worker[w] += ke - kb
+    shares = np.array([(w + 1) * W // nw - w * W // nw for w in range(nw)])
+    assert np.array_equal(per_worker, shares)
+    # partial pieces only at a worker's ends; slots unique
+    slots = [p[6] for p in pieces if p[6] >= 0]
+    assert len(slots) == len(set(slots))
+    for w in range(nw):
+        mine = pieces[pieces[:, 0] == w]
+        for i, p in enumerate(mine):
+            if p[7] == 0:
+                assert i in (0, len(mine) - 1)
+                assert p[6] == (2 * w if i == 0 else 2 * w + 1)
+    return pieces
+
+
+def indptr(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+
+
+@pytest.mark.parametrize("nw", [1, 7, 256])
+def test_headline_batch(nw):
+    L = workloads.c16_lengths()
+    p = check_plan(indptr([1] * 16), indptr(L), 16, nw)
+    if nw == 256:
+        w_rows = sum(L) // 256
+        assert abs(w_rows - 4276) <= 1
+
+
+def test_c24_and_mixed_lengths():
+    check_plan(indptr([1] * 24), indptr(workloads.c24_lengths()), 16, 256)
+    check_plan(indptr([1] * 64), indptr(workloads.mixed_lengths()), 16, 256)
+
+
+def test_dcp_share_multi_token_many_heads():
+    pieces = check_plan(indptr([4] * 8), indptr([17_750] * 8), 96, 256)
+    assert pieces[:, 2].max() == 5
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_ragged_plans(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    lengths = rng.integers(0, 3000, size=B)
+    lengths[rng.random(B) < 0.2] = 0
+    qlens = rng.integers(1, 5, size=B)
+    H = 16 * int(rng.integers(1, 4))
+    check_plan(indptr(qlens), indptr(lengths), H, int(rng.integers(1, 300)))
+
+
+def test_empty_and_tiny_inputs():
+    check_plan(indptr([1, 1]), indptr([0, 0]), 16, 256)
+    p = check_plan(indptr([1, 1]), indptr([64, 100]), 16, 256)
+    assert len(p) == 2 and all(p[:, 7] == 1)  # one worker does everything
+    check_plan(indptr([4, 3]), indptr([2, 1]), 16, 8)  # early draft tokens see nothing
+
+
+def test_rejects_bad_planner_input():
+    with pytest.raises(ValueError):
+        plan_host(indptr([1]), indptr([10]), 12, 4)
