@@ -1,11 +1,15 @@
 """Benchmark: latent MLA decode on one MI355X, batch 16 at kv ~68,430, fp8.
 
 One step = one mla_decode call (plan, index fetch, row gather, QK^T, online
-softmax, P.V, split epilogue and combine) over one layer's inputs.  Like a
+softmax, P.V, split epilogue and combine) over one layer's inputs.  As in a
 model step, consecutive steps cycle through `--layers` independent layer
 caches (same requests and index lists, separate pools and queries), so a
-layer's distinct rows are evicted from the last-level cache before the same
-layer comes round again.  Inputs are resident in HBM before timing starts.
+layer's distinct rows have left the last-level cache before that layer comes
+round again.  Inputs are resident in HBM before timing starts.
+
+The calls are captured once in a HIP graph (as a serving loop would) and the
+graph is replayed, so the timing is the GPU's, not the Python binding's; the
+eager per-call time is reported beside it.
 
 Prints one JSON line.  `value` is algorithmic GB/s: per call,
 sum(kv_len) * (576 + 4) + |q| + |o| bytes (the issue's own accounting) over
@@ -30,17 +34,37 @@ PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--layers", type=int, default=8, help="distinct layer caches cycled per step")
     ap.add_argument("--variant", default="shared", choices=["shared", "unshared", "blocked"])
+    ap.add_argument("--eager", action="store_true", help="time eager calls instead of graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the extra timing lines")
     ap.add_argument("--cpu-requests", type=int, default=2, help="requests in the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain fp32 copy-like kernel (out = -in) over BYTES, "
+                         "to calibrate HBM byte counters, and exit")
     return ap.parse_args()
 
 
+def calibrate_copy(nbytes, steps):
+    """A plain elementwise kernel reading and writing exactly nbytes each."""
+    import torch
+
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}),
+          flush=True)
+
+
 def make_layers(n_layers, variant, dev):
+    """n_layers decode calls over the same requests with separate pools and q."""
     import torch
 
     import workloads
@@ -57,8 +81,62 @@ def make_layers(n_layers, variant, dev):
     return layers
 
 
-def time_calls(calls, steps, warmup):
-    """Wall time per call over `steps` calls and per-call HIP-event durations."""
+def with_indices(layers, variant, dev):
+    """The same layers with another variant's index lists."""
+    import workloads
+
+    shared = 0 if variant == "unshared" else workloads.SHARED_PREFIX
+    layout = "blocked" if variant == "blocked" else "random"
+    idx = workloads.make_indices(layers[0].lengths, shared, layers[0].kv_pool.shape[0], layout,
+                                 2000 + 3, dev, workloads.INDEX_BUFFER)
+    return [workloads.Workload(**{**w.__dict__, "kv_indices": idx}) for w in layers]
+
+
+def make_calls(mla, layers, o, ws):
+    def call_for(w):
+        return lambda: mla.decode(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                  w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale,
+                                  o=o, max_seqlen_q=1, workspace=ws)
+
+    return [call_for(w) for w in layers]
+
+
+def time_graph(calls, steps, warmup):
+    """Capture all calls once and replay; (wall s/call, event s/call per replay, calls)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    L = len(calls)
+    reps = max(1, steps // L)
+    for _ in range(max(1, warmup // L)):
+        g.replay()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(reps):
+        starts[i].record()
+        g.replay()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / (reps * L)
+    ev = [s.elapsed_time(e) * 1e-3 / L for s, e in zip(starts, ends)]
+    del g
+    return wall, ev, reps * L
+
+
+def time_eager(calls, steps, warmup):
     import torch
 
     for i in range(warmup):
@@ -75,13 +153,11 @@ def time_calls(calls, steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     ev = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
-    return wall, ev
+    return wall, ev, steps
 
 
 def cpu_baseline(w, n_req):
     """The float64 oracle on `n_req` full-length requests of the same call."""
-    import numpy as np
-
     from oracle import io as oio
 
     try:
@@ -90,8 +166,7 @@ def cpu_baseline(w, n_req):
         cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    reqs = list(range(n_req))
-    args = oio.workload_args(w, reqs)
+    args = oio.workload_args(w, list(range(n_req)))
     t0 = time.perf_counter()
     reps = 0
     while True:
@@ -101,11 +176,43 @@ def cpu_baseline(w, n_req):
             break
     per_sample = (time.perf_counter() - t0) / reps
     per_call = per_sample * w.batch / n_req
-    return per_call, cores, f"{n_req} of {w.batch} requests (all {sum(w.lengths[:n_req])} KV rows, 16 heads), {reps} reps; scaled x{w.batch / n_req:g} to one call"
+    rows = sum(w.lengths[:n_req])
+    sample = (f"{n_req} of {w.batch} requests ({rows} KV rows x 16 heads), {reps} reps; "
+              f"scaled x{w.batch / n_req:g} to one call")
+    return per_call, cores, sample
+
+
+def measured_traffic(variant):
+    """HBM bytes per call from the committed counter runs, if they were taken on
+    this exact kernel source and workload variant; else None."""
+    import hashlib
+
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic_c16.json")) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, rec["kernel_source"]), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    if sha != rec.get("kernel_source_sha256") or variant != rec.get("variant"):
+        return None
+    return int(rec["fetch_bytes_per_call"]) + int(rec["write_bytes_per_call"])
+
+
+def stats_us(ev):
+    import numpy as np
+
+    return {"mean": round(float(np.mean(ev)) * 1e6, 2),
+            "p10": round(float(np.percentile(ev, 10)) * 1e6, 2),
+            "median": round(float(np.median(ev)) * 1e6, 2),
+            "p90": round(float(np.percentile(ev, 90)) * 1e6, 2)}
 
 
 def main():
     a = parse()
+    if a.calibrate_copy:
+        calibrate_copy(a.calibrate_copy, max(1, a.steps))
+        return
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
               "(multi-GPU sharding is design-only)", file=sys.stderr)
@@ -124,17 +231,11 @@ def main():
     flops = accounting.workload_flops(w0)
     T, H = w0.num_tokens, w0.num_heads
     o = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(mla.workspace_bytes(w0.batch, T, H, 1), dtype=torch.uint8, device=dev)
-
-    def call_for(w):
-        return lambda: mla.decode(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
-                                  w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale,
-                                  o=o, max_seqlen_q=1, workspace=ws)
-
-    calls = [call_for(w) for w in layers]
-    wall, ev = time_calls(calls, a.steps, a.warmup)
+    ws = mla.new_workspace(mla.workspace_bytes(w0.batch, T, H, 1), dev)
+    calls = make_calls(mla, layers, o, ws)
+    timer = time_eager if a.eager else time_graph
+    wall, ev, steps = timer(calls, a.steps, a.warmup)
     ev_mean = float(np.mean(ev))
-    us = wall * 1e6
     value = nbytes / wall / 1e9
     achieved = nbytes / ev_mean / 1e9
     out = {
@@ -142,7 +243,7 @@ def main():
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": a.steps,
+        "steps": steps,
         "warmup": a.warmup,
         "ms_per_step": round(wall * 1e3, 5),
         "higher_is_better": True,
@@ -153,36 +254,46 @@ def main():
         "config": {
             "workload": f"c16 decode, {a.variant} prefix: batch 16, 16 heads (12 real + 4 zero), "
                         f"qlen 1, kv {min(w0.lengths)}-{max(w0.lengths)} (63,911 shared-prefix slots), "
-                        f"fp8 e4m3 pool 5,283,840 x 576, {a.layers} layer caches cycled",
+                        f"fp8 e4m3 pool 5,283,840 x 576, {a.layers} layer caches cycled, "
+                        f"{'eager calls' if a.eager else 'HIP graph replay'}",
             "global_batch": w0.batch,
             "seq_len": int(np.mean(w0.lengths)),
             "kv_rows_per_call": w0.total_kv,
             "layers_cycled": a.layers,
             "parallelism": "single GPU",
         },
-        "us_per_call": round(us, 2),
+        "us_per_call": round(wall * 1e6, 2),
         "pct_of_8TBs": round(100 * value / PEAK_GBS, 2),
         "algorithmic_bytes_per_call": nbytes,
         "flops_per_call": flops,
-        "event_us_per_call": {"mean": round(ev_mean * 1e6, 2),
-                              "p10": round(float(np.percentile(ev, 10)) * 1e6, 2),
-                              "median": round(float(np.median(ev)) * 1e6, 2),
-                              "p90": round(float(np.percentile(ev, 90)) * 1e6, 2)},
+        "event_us_per_call": stats_us(ev),
         "roofline": {
             "bound": "hbm",
-            "kernel": "mla_decode call (decode kernel + split combine kernel)",
+            "kernel": "mla_decode call: mla_decode_fp8_kernel + mla_combine_kernel",
             "achieved": round(achieved, 2),
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(a.variant) if a.layers == 8 else None,
         },
     }
     if not a.no_variants:
         variants = {}
-        wall1, ev1 = time_calls(calls[:1], max(20, a.steps // 4), 5)
+        wall1, ev1, _ = timer(calls[:1] * 4, max(16, a.steps // 8), 4)
         variants["same_layer_back_to_back"] = {"us_per_call": round(wall1 * 1e6, 2),
                                                "GB_s": round(nbytes / wall1 / 1e9, 2)}
+        if not a.eager:
+            wall_e, ev_e, _ = time_eager(calls, max(16, a.steps // 4), 4)
+            variants["eager_calls_incl_host_overhead"] = {"us_per_call": round(wall_e * 1e6, 2),
+                                                          "event_us": stats_us(ev_e)}
+        for var in ("unshared", "blocked"):
+            if var == a.variant:
+                continue
+            vcalls = make_calls(mla, with_indices(layers, var, dev), o, ws)
+            wv, evv, _ = timer(vcalls, max(16, a.steps // 4), a.warmup)
+            variants[f"{var}_prefix"] = {"us_per_call": round(wv * 1e6, 2),
+                                         "GB_s": round(nbytes / wv / 1e9, 2),
+                                         "pct_of_8TBs": round(100 * nbytes / wv / 1e9 / PEAK_GBS, 2)}
         out["variants"] = variants
     if not a.no_cpu_baseline:
         per_call, cores, sample = cpu_baseline(w0, a.cpu_requests)

@@ -71,8 +71,9 @@ typedef enum {
 /*
  * Workspace bytes mla_decode needs on the current device for this call shape.
  * The workspace holds fp32 partial answers of the KV splits (at most two per
- * worker workgroup); its size depends only on the device's compute-unit count
- * and the arguments below, not on KV lengths.  Returns 0 for invalid shapes.
+ * worker workgroup) and one 16-byte split descriptor per worker; its size
+ * depends only on the device's compute-unit count and the arguments below, not
+ * on KV lengths.  Returns 0 for invalid shapes.
  */
 size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, int max_seqlen_q);
 
@@ -103,7 +104,7 @@ size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, in
  *  workspace      device scratch of at least
  *                 mla_decode_workspace_bytes(batch, num_q_tokens, num_heads,
  *                 max_seqlen_q) bytes, 256-byte aligned; contents on entry do
- *                 not matter.
+ *                 not matter (every byte read is written earlier in the call).
  *
  * Query token j of a request with qlen tokens and n cached entries sees the
  * first n - (qlen - 1 - j) entries (bottom-right causal alignment for

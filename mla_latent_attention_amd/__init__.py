@@ -21,6 +21,7 @@ __all__ = [
     "merge_partials",
     "workspace_bytes",
     "plan_host",
+    "new_workspace",
     "MLAError",
     "library_path",
 ]
@@ -74,6 +75,11 @@ def workspace_bytes(batch: int, num_q_tokens: int, num_heads: int, max_seqlen_q:
     if n == 0:
         raise ValueError("invalid shape for the decode workspace (or no HIP device)")
     return int(n)
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A decode workspace (its contents on entry do not matter)."""
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def decode(
@@ -137,7 +143,7 @@ def decode(
         max_seqlen_q = int((qo_indptr[1:] - qo_indptr[:-1]).max().item()) if B > 0 else 1
     ws_need = workspace_bytes(B, T, H, max_seqlen_q, num_workers)
     if workspace is None:
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+        workspace = new_workspace(ws_need, dev)
     _need(workspace, "workspace", dev)
     ws_len = workspace.numel() * workspace.element_size()
     L = _lib.lib()

@@ -41,7 +41,7 @@ bool shape_ok(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
   return true;
 }
 
-constexpr int kMaxWorkers = 1 << 16;
+using mla::kMaxWorkers;
 
 }  // namespace
 
@@ -64,14 +64,14 @@ size_t mla_decode_workspace_bytes_ex(int batch, int num_q_tokens, int num_heads,
                                      int max_seqlen_q, int num_workers) {
   if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
   if (num_workers < 1 || num_workers > kMaxWorkers) return 0;
-  return mla::workspace_bytes(num_workers);
+  return mla::workspace_bytes(num_workers, (int64_t)num_q_tokens * (num_heads / mla::kGroup));
 }
 
 size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
   if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
   const int cus = current_cu_count();
   if (cus <= 0) return 0;
-  return mla::workspace_bytes(cus);
+  return mla::workspace_bytes(cus, (int64_t)num_q_tokens * (num_heads / mla::kGroup));
 }
 
 mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
@@ -94,14 +94,16 @@ mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv
     return MLA_ERR_BAD_SHAPE;
   if (num_workers < 0 || num_workers > kMaxWorkers) return MLA_ERR_BAD_SHAPE;
   if (q_dtype == MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;  // fp8 path only for now
+  const int64_t num_units = (int64_t)num_q_tokens * (num_heads / mla::kGroup);
   if (!workspace) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  if (num_workers > 0 && workspace_bytes < mla::workspace_bytes(num_workers))
+  if (num_workers > 0 && workspace_bytes < mla::workspace_bytes(num_workers, num_units))
     return MLA_ERR_WORKSPACE_TOO_SMALL;
 
   if (num_workers == 0) {
     num_workers = current_cu_count();
     if (num_workers <= 0) return MLA_ERR_HIP;
-    if (workspace_bytes < mla::workspace_bytes(num_workers)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace_bytes < mla::workspace_bytes(num_workers, num_units))
+      return MLA_ERR_WORKSPACE_TOO_SMALL;
   }
 
   mla::DecodeParams p;
@@ -120,8 +122,10 @@ mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv
   p.q_scale = q_scale;
   p.kv_scale = kv_scale;
   p.lse = return_lse ? lse : nullptr;
-  p.part_o = static_cast<float*>(workspace);
-  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+  char* ws = static_cast<char*>(workspace);
+  p.desc = reinterpret_cast<int4*>(ws);
+  p.part_o = reinterpret_cast<float*>(ws + mla::desc_bytes(num_units));
+  p.part_lse = reinterpret_cast<float*>(ws + mla::desc_bytes(num_units) +
                                         mla::part_o_bytes(num_workers));
   p.num_workers = num_workers;
   const int kdt = (kv_dtype == MLA_DTYPE_FP8_E4M3FN) ? 0 : 1;

@@ -21,10 +21,20 @@
 //     padded stride); P.V reads 16 bytes from each of 8 rows and transposes
 //     4x4 byte blocks in registers (v_perm) to build the V^T A-operand, so the
 //     contraction runs as O^T (512 x 16 rows) += V^T . P^T on fp8 MFMA.
-//   * P is fed as two e4m3 terms, P*256 = hi + lo (hi = e4m3(P*256),
-//     lo = e4m3(P*256 - hi)), so the fp8 P.V keeps ~8 significant bits of P;
+//   * P is fed as two e4m3 terms, P*128 = hi + lo (hi = e4m3(P*128),
+//     lo = e4m3(P*128 - hi)), so the fp8 P.V keeps ~8 significant bits of P;
 //     a single e4m3 P (4 bits) would not meet the output tolerance.
-//   * Scores are kept in base 2 (log2(e) folded into the scale).
+//   * Scores are kept in base 2 (log2(e) folded into the scale).  The running
+//     max is only raised when a row's max grows by more than 2x, so the O^T
+//     accumulators are rescaled on few tiles.
+//   * Every load of the tile loop is unconditional (tail positions repeat the
+//     piece's last entry and are masked), so the outstanding-load count is
+//     static and the two-tile prefetch survives compilation.
+//   * Split-KV partials are merged by a second, small kernel: each worker
+//     leaves a descriptor for the split unit that starts in it, and the
+//     combine kernel merges exactly those units by LSE.  (Merging inside the
+//     decode would need device-scope fences, which write back and invalidate
+//     the L2 of every XCD under the still-running workers.)
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -43,9 +53,11 @@ constexpr int kTile = 32;                          // KV rows per wave iteration
 constexpr int kVStride = 528;                      // LDS bytes per staged V row (512 + pad)
 constexpr int kVWaveBytes = kTile * kVStride;      // 16,896
 constexpr int kCombBytes = kWaves * 32 * 64 * 16;  // 131,072: every wave's O^T
+constexpr int kIdxSeg = 7168;                      // kv_indices staged in LDS per segment
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kPScale = 256.0f;                  // P*256 uses the e4m3 range
+constexpr float kLazy = 1.0f;                       // rescale when a row max grows > 2^kLazy
+constexpr float kPScale = 128.0f;                  // P * kPScale <= 2^kLazy * 128 = 256 < 448
 static_assert(kWaves * kVWaveBytes <= kCombBytes, "V staging must fit in the LDS buffer");
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
@@ -115,16 +127,6 @@ __device__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) 
   return before + x - v;
 }
 
-// Total stream length W = sum over requests of G * request_rows.
-__device__ int64_t plan_total(const DecodeParams& p, int G, int64_t* red) {
-  int64_t acc = 0;
-  for (int b = threadIdx.x; b < p.batch; b += kThreads) {
-    Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
-    acc += (int64_t)G * request_rows(r.n, r.qlen);
-  }
-  return block_sum_i64(acc, red);
-}
-
 // Request containing stream position pos (and its stream start); false if none.
 __device__ bool plan_locate(const DecodeParams& p, int G, int64_t pos, int64_t* red, int* s_b,
                             int64_t* s_cum) {
@@ -151,87 +153,59 @@ __device__ bool plan_locate(const DecodeParams& p, int G, int64_t pos, int64_t* 
   return *s_b >= 0;
 }
 
-// Request owning query token t (-1 if none) and the stream start of that request.
-__device__ void plan_token(const DecodeParams& p, int G, int t, int64_t* red, int* s_b,
-                           int64_t* s_cum) {
-  if (threadIdx.x == 0) *s_b = -1;
-  int64_t carry = 0;
-  for (int b0 = 0; b0 < p.batch; b0 += kThreads) {
-    const int b = b0 + threadIdx.x;
-    int64_t R = 0;
-    bool mine = false;
-    if (b < p.batch) {
-      Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
-      R = (int64_t)G * request_rows(r.n, r.qlen);
-      mine = t >= r.q_base && t < r.q_base + r.qlen;
-    }
-    int64_t total;
-    const int64_t cum = carry + block_excl_scan_i64(R, red, total);
-    if (mine) {
-      *s_b = b;
-      *s_cum = cum;
-    }
-    carry += total;
-    __syncthreads();
-    if (*s_b >= 0) break;
-  }
-  __syncthreads();
-}
-
 // ---------------------------------------------------------------- fp8 decode
 
 struct TileIdx {
-  int i0, i1;  // pool rows for tile rows (lane%16) and (16 + lane%16); -1 = past the end
+  int i0, i1;  // pool rows of tile rows (lane%16) and (16 + lane%16)
 };
 
-__device__ __forceinline__ TileIdx fetch_idx(const int32_t* idxp, int rows, int tile, int n) {
+// Indices of a tile's rows, read from the LDS copy of the current segment.
+// Positions past the segment repeat its last entry, so every row load is
+// issued unconditionally (the outstanding-load count stays static and the
+// compiler keeps the prefetch pipeline); those rows' scores are masked to
+// -inf, so their (finite, referenced) contents never contribute.  Keeping the
+// indices in LDS also keeps them off the in-order vector-memory counter.
+__device__ __forceinline__ TileIdx fetch_idx(const int32_t* sidx, int rows, int tile, int n) {
+  const int e0 = imin(tile * kTile + n, rows - 1);
+  const int e1 = imin(tile * kTile + 16 + n, rows - 1);
   TileIdx t;
-  const int e0 = tile * kTile + n, e1 = e0 + 16;
-  t.i0 = -1;
-  t.i1 = -1;
-  if (e0 < rows) t.i0 = idxp[e0];
-  if (e1 < rows) t.i1 = idxp[e1];
+  t.i0 = sidx[e0];
+  t.i1 = sidx[e1];
   return t;
+}
+
+__device__ __forceinline__ const uint8_t* row_ptr(const uint8_t* kv, int64_t pool_entries, int idx,
+                                                  int gq) {
+  int64_t r = idx < 0 ? 0 : (int64_t)idx;
+  r = r < pool_entries ? r : pool_entries - 1;
+  return kv + r * kRowDim + 16 * gq;
 }
 
 __device__ __forceinline__ void issue_rows(uint4 (&B)[18], const uint8_t* kv, int64_t pool_entries,
                                            TileIdx ti, int gq) {
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  const int64_t last = pool_entries - 1;
-  if (ti.i0 >= 0) {
-    const int64_t r = (int64_t)ti.i0 < last ? (int64_t)ti.i0 : last;
-    const uint8_t* src = kv + r * kRowDim + 16 * gq;
+  const uint8_t* s0 = row_ptr(kv, pool_entries, ti.i0, gq);
+  const uint8_t* s1 = row_ptr(kv, pool_entries, ti.i1, gq);
 #pragma unroll
-    for (int c = 0; c < 9; ++c) B[c] = *(const uint4*)(src + 64 * c);
-  } else {
+  for (int c = 0; c < 9; ++c) B[c] = *(const uint4*)(s0 + 64 * c);
 #pragma unroll
-    for (int c = 0; c < 9; ++c) B[c] = z;
-  }
-  if (ti.i1 >= 0) {
-    const int64_t r = (int64_t)ti.i1 < last ? (int64_t)ti.i1 : last;
-    const uint8_t* src = kv + r * kRowDim + 16 * gq;
-#pragma unroll
-    for (int c = 0; c < 9; ++c) B[9 + c] = *(const uint4*)(src + 64 * c);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 9; ++c) B[9 + c] = z;
-  }
+  for (int c = 0; c < 9; ++c) B[9 + c] = *(const uint4*)(s1 + 64 * c);
 }
 
 struct WaveState {
   v4f O[32];  // O^T blocks: block (half*16 + t) element i = row (lane%16),
-              // dim 256*half + 64*(lane/16) + 16*i + t
-  float m;    // running max of base-2 scores of row (lane%16)
+              // dim 256*half + 64*(lane/16) + 16*i + t; scaled by kPScale
+  float m;    // (possibly stale) running max of base-2 scores of row lane%16
   float l;    // this lane's partial sum of 2^(s - m)
 };
 
-// One 32-row tile: scores, online softmax, P.V.  B holds the tile's rows and is
-// refilled with the rows of `next` before the softmax work starts.
+// One 32-row tile: S^T = K.Q^T, online softmax, O^T += V^T.P^T.  With kRefill,
+// B is refilled with the rows of `next` (two tiles ahead for this wave) right
+// after its contents are consumed, and the indices four tiles ahead are fetched.
+template <bool kRefill>
 __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx& next,
                                          const long (&qlo)[9], const long (&qhi)[9],
-                                         uint8_t* vst, const DecodeParams& p, const int32_t* idxp,
+                                         uint8_t* vst, const DecodeParams& p, const int32_t* sidx,
                                          int rows, int tile, float cs, int n, int gq) {
-  // ---- S^T = K . Q^T for kv rows [0,16) and [16,32) of the tile
   v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < 9; ++c) {
@@ -243,19 +217,19 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
                                                     0, 0);
   }
 
-  // ---- stage the latent 512 bytes of both 16-row blocks in LDS
+  // Stage the latent 512 bytes of both 16-row blocks in this wave's LDS tile.
   wave_lds_sync();  // the previous tile's V reads are complete
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     *(uint4*)(vst + n * kVStride + 64 * c + 16 * gq) = B[c];
     *(uint4*)(vst + (16 + n) * kVStride + 64 * c + 16 * gq) = B[9 + c];
   }
+  if constexpr (kRefill) {
+    issue_rows(B, p.kv, p.pool_entries, next, gq);
+    next = fetch_idx(sidx, rows, tile + 4 * kWaves, n);
+  }
 
-  // ---- refill B two tiles ahead; fetch the indices of the tile after that
-  issue_rows(B, p.kv, p.pool_entries, next, gq);
-  next = fetch_idx(idxp, rows, tile + 4 * kWaves, n);
-
-  // ---- online softmax (row = lane%16; this lane holds kv rows 4gq+i, 16+4gq+i)
+  // Online softmax for row lane%16; this lane holds kv rows 4gq+i and 16+4gq+i.
   const int base = tile * kTile + 4 * gq;
   float sc[8];
 #pragma unroll
@@ -268,23 +242,27 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
   for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  const float mnew = fmaxf(st.m, tmax);  // finite: row 0 of a live tile is valid
-  const float alpha = fast_exp2(st.m - mnew);
+  // Lazy rescale: keep a stale max unless a row's max grew by more than
+  // 2^kLazy; P = 2^(s - m) then stays <= 2^kLazy and P * kPScale <= 256 fits e4m3.
+  const bool grow = tmax > st.m + kLazy;  // first tile: m = -inf
+  if (__any(grow)) {
+    const float mset = grow ? tmax : st.m;
+    const float alpha = fast_exp2(st.m - mset);  // 1 for rows that keep m, 0 on the first tile
+#pragma unroll
+    for (int b = 0; b < 32; ++b) st.O[b] *= alpha;
+    st.l *= alpha;
+    st.m = mset;
+  }
   float x[8], psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float pr = fast_exp2(sc[i] - mnew);
+    const float pr = fast_exp2(sc[i] - st.m);
     psum += pr;
     x[i] = pr * kPScale;
   }
-  st.l = st.l * alpha + psum;
-  st.m = mnew;
-  if (alpha != 1.0f) {
-#pragma unroll
-    for (int b = 0; b < 32; ++b) st.O[b] *= alpha;
-  }
+  st.l += psum;
 
-  // ---- P*256 = hi + lo in e4m3; byte k of the operand = kv row kappa(gq, k)
+  // P*kPScale = hi + lo in e4m3; byte k of the operand = kv row kappa(gq, k).
   u32 h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
   h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h0, true);
   u32 h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
@@ -304,8 +282,8 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
   l1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], l1, true);
   const long phi = as_long(h0, h1), plo = as_long(l0, l1);
 
-  // ---- O^T += V^T . P^T; the kv row of operand byte k is kappa(gq, k):
-  //      4gq + k for k < 4, 16 + 4gq + (k - 4) otherwise.
+  // O^T += V^T . P^T; the kv row of operand byte k is kappa(gq, k):
+  // 4gq + k for k < 4, 16 + 4gq + (k - 4) otherwise.
   wave_lds_sync();  // all lanes' V writes are in LDS
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -341,6 +319,7 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
 
 struct alignas(16) DecodeShared {
   uint8_t buf[kCombBytes];  // V staging during the tile loop, O^T exchange after it
+  int32_t idx[kIdxSeg];     // kv_indices of the current segment of the piece
   int64_t red[kWaves];
   float m[kWaves][16];
   float l[kWaves][16];
@@ -348,15 +327,30 @@ struct alignas(16) DecodeShared {
   int64_t cum;
 };
 
-// One piece: KV positions [kv_pos0, kv_pos0 + rows) of unit (token t, head group g).
-__device__ __forceinline__ void fp8_piece(const DecodeParams& p, DecodeShared& sh, int t, int g,
+// The unit (query token, head group) a piece belongs to.
+struct UnitRef {
+  int t, g;
+};
+
+__device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&a)[8]) {
+  uint4 pk;
+  pk.x = bf16_bits(a[0]) | (bf16_bits(a[1]) << 16);
+  pk.y = bf16_bits(a[2]) | (bf16_bits(a[3]) << 16);
+  pk.z = bf16_bits(a[4]) | (bf16_bits(a[5]) << 16);
+  pk.w = bf16_bits(a[6]) | (bf16_bits(a[7]) << 16);
+  *(uint4*)dst = pk;
+}
+
+// One piece: KV positions [kv_pos0, kv_pos0 + rows) of unit u.  slot < 0 means
+// the piece is the whole unit and o / lse are written directly.
+__device__ __forceinline__ void fp8_piece(const DecodeParams& p, DecodeShared& sh, const UnitRef& u,
                                           int kv_pos0, int rows, int slot, float cs, float ks) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
   __syncthreads();  // the previous piece is done with the LDS buffer
 
   long qlo[9], qhi[9];
   {
-    const uint8_t* qrow = p.q + ((int64_t)t * p.num_heads + g * kGroup + n) * kRowDim + 16 * gq;
+    const uint8_t* qrow = p.q + ((int64_t)u.t * p.num_heads + u.g * kGroup + n) * kRowDim + 16 * gq;
 #pragma unroll
     for (int c = 0; c < 9; ++c) {
       const uint4 x = *(const uint4*)(qrow + 64 * c);
@@ -371,27 +365,48 @@ __device__ __forceinline__ void fp8_piece(const DecodeParams& p, DecodeShared& s
   st.m = neg_inf();
   st.l = 0.f;
 
-  const int ntiles = (rows + kTile - 1) / kTile;
-  const int32_t* idxp = p.kv_indices + kv_pos0;
   uint8_t* vst = sh.buf + wv * kVWaveBytes;
-
-  int tile = wv;
-  uint4 bufA[18], bufB[18];
-  TileIdx nextA, nextB;
-  {
-    const TileIdx t0 = fetch_idx(idxp, rows, tile, n);
-    const TileIdx t1 = fetch_idx(idxp, rows, tile + kWaves, n);
-    issue_rows(bufA, p.kv, p.pool_entries, t0, gq);
-    issue_rows(bufB, p.kv, p.pool_entries, t1, gq);
-    nextA = fetch_idx(idxp, rows, tile + 2 * kWaves, n);
-    nextB = fetch_idx(idxp, rows, tile + 3 * kWaves, n);
-  }
-  while (tile < ntiles) {
-    fp8_tile(st, bufA, nextA, qlo, qhi, vst, p, idxp, rows, tile, cs, n, gq);
-    tile += kWaves;
-    if (tile >= ntiles) break;
-    fp8_tile(st, bufB, nextB, qlo, qhi, vst, p, idxp, rows, tile, cs, n, gq);
-    tile += kWaves;
+  for (int seg0 = 0; seg0 < rows; seg0 += kIdxSeg) {
+    const int srows = imin(kIdxSeg, rows - seg0);
+    __syncthreads();  // the previous segment's index reads are done
+    for (int i = tid; i < srows; i += kThreads) sh.idx[i] = p.kv_indices[kv_pos0 + seg0 + i];
+    __syncthreads();
+    const int32_t* sidx = sh.idx;
+    const int ntiles = (srows + kTile - 1) / kTile;
+    const int m = ntiles > wv ? (ntiles - wv + kWaves - 1) / kWaves : 0;  // this wave's tiles
+    if (m > 0) {
+      // wave tile k is tile wv + 4k; even k live in bufA, odd k in bufB.
+      uint4 bufA[18], bufB[18];
+      TileIdx nextA, nextB;
+      {
+        const TileIdx t0 = fetch_idx(sidx, srows, wv, n);
+        const TileIdx t1 = fetch_idx(sidx, srows, wv + kWaves, n);
+        issue_rows(bufA, p.kv, p.pool_entries, t0, gq);
+        issue_rows(bufB, p.kv, p.pool_entries, t1, gq);
+        nextA = fetch_idx(sidx, srows, wv + 2 * kWaves, n);
+        nextB = fetch_idx(sidx, srows, wv + 3 * kWaves, n);
+      }
+      int k = 0;
+      for (; k + 3 < m; k += 2) {
+        fp8_tile<true>(st, bufA, nextA, qlo, qhi, vst, p, sidx, srows, wv + kWaves * k, cs, n, gq);
+        fp8_tile<true>(st, bufB, nextB, qlo, qhi, vst, p, sidx, srows, wv + kWaves * (k + 1), cs, n,
+                       gq);
+      }
+      const int rem = m - k;
+      if (rem == 3) {
+        fp8_tile<true>(st, bufA, nextA, qlo, qhi, vst, p, sidx, srows, wv + kWaves * k, cs, n, gq);
+        fp8_tile<false>(st, bufB, nextB, qlo, qhi, vst, p, sidx, srows, wv + kWaves * (k + 1), cs, n,
+                        gq);
+        fp8_tile<false>(st, bufA, nextA, qlo, qhi, vst, p, sidx, srows, wv + kWaves * (k + 2), cs, n,
+                        gq);
+      } else if (rem == 2) {
+        fp8_tile<false>(st, bufA, nextA, qlo, qhi, vst, p, sidx, srows, wv + kWaves * k, cs, n, gq);
+        fp8_tile<false>(st, bufB, nextB, qlo, qhi, vst, p, sidx, srows, wv + kWaves * (k + 1), cs, n,
+                        gq);
+      } else if (rem == 1) {
+        fp8_tile<false>(st, bufA, nextA, qlo, qhi, vst, p, sidx, srows, wv + kWaves * k, cs, n, gq);
+      }
+    }
   }
 
   // ---- merge the 4 waves' online-softmax states
@@ -423,39 +438,45 @@ __device__ __forceinline__ void fp8_piece(const DecodeParams& p, DecodeShared& s
 
   // This wave writes O^T blocks [8wv, 8wv + 8): half = wv/2, t = 8(wv%2) + bb;
   // element i of block bb is dim 256*half + 64*gq + 16*i + 8*(wv%2) + bb.
-  float acc[8][4];
+  float acc[4][8];
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) {
     v4f a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) a += fw[w] * comb[(w * 32 + 8 * wv + bb) * 64 + lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[bb][i] = a[i] * oscale;
+    for (int i = 0; i < 4; ++i) acc[i][bb] = a[i] * oscale;
   }
-  const int half = wv >> 1;
-  const int dim0 = 256 * half + 64 * gq + 8 * (wv & 1);
-  const int64_t orow = (int64_t)t * p.num_heads + g * kGroup + n;
+  const int dim0 = 256 * (wv >> 1) + 64 * gq + 8 * (wv & 1);
   const float lse_val = (M + fast_log2(L)) * kLn2;
   if (slot < 0) {
+    const int64_t orow = (int64_t)u.t * p.num_heads + u.g * kGroup + n;
     uint16_t* dst = p.o + orow * kLatent + dim0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 pk;
-      pk.x = bf16_bits(acc[0][i]) | (bf16_bits(acc[1][i]) << 16);
-      pk.y = bf16_bits(acc[2][i]) | (bf16_bits(acc[3][i]) << 16);
-      pk.z = bf16_bits(acc[4][i]) | (bf16_bits(acc[5][i]) << 16);
-      pk.w = bf16_bits(acc[6][i]) | (bf16_bits(acc[7][i]) << 16);
-      *(uint4*)(dst + 16 * i) = pk;
-    }
+    for (int i = 0; i < 4; ++i) store_bf16x8(dst + 16 * i, acc[i]);
     if (p.lse != nullptr && wv == 0 && gq == 0) p.lse[orow] = lse_val;
-  } else {
-    float* dst = p.part_o + ((int64_t)slot * kGroup + n) * kLatent + dim0;
+    return;
+  }
+  float* dst = p.part_o + ((int64_t)slot * kGroup + n) * kLatent + dim0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(float4*)(dst + 16 * i) = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
-      *(float4*)(dst + 16 * i + 4) = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
-    }
-    if (wv == 0 && gq == 0) p.part_lse[(int64_t)slot * kGroup + n] = lse_val;
+  for (int i = 0; i < 4; ++i) {
+    *(float4*)(dst + 16 * i) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    *(float4*)(dst + 16 * i + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+  }
+  if (wv == 0 && gq == 0) p.part_lse[(int64_t)slot * kGroup + n] = lse_val;
+
+}
+
+// Query rows that see no entry get o = 0, lse = -inf; the block owning token t
+// (t mod gridDim.x) writes them.  Rare: empty requests or early draft tokens.
+__device__ void zero_token(const DecodeParams& p, int t) {
+  const int G = p.num_heads / kGroup;
+  for (int g = 0; g < G; ++g) p.desc[(int64_t)t * G + g] = make_int4(0, 0, 0, 0);
+  for (int h = 0; h < p.num_heads; ++h) {
+    const int64_t orow = (int64_t)t * p.num_heads + h;
+    uint4* dst = (uint4*)(p.o + orow * kLatent);
+    for (int k = 0; k < kLatent / 8; ++k) dst[k] = make_uint4(0, 0, 0, 0);
+    if (p.lse != nullptr) p.lse[orow] = neg_inf();
   }
 }
 
@@ -463,14 +484,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void mla_decode_fp8_kernel(const DecodeParams p) {
   __shared__ DecodeShared sh;
   const int G = p.num_heads / kGroup;
-  const int64_t W = plan_total(p, G, sh.red);
+
+  // Pass 1 over requests: stream length W; zero this block's empty tokens.
+  int64_t acc = 0;
+  for (int b = threadIdx.x; b < p.batch; b += kThreads) {
+    const Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
+    acc += (int64_t)G * request_rows(r.n, r.qlen);
+    const int nempty = imin(r.qlen, imax(0, r.qlen - r.n));
+    for (int j = 0; j < nempty; ++j)
+      if ((r.q_base + j) % (int)gridDim.x == (int)blockIdx.x) zero_token(p, r.q_base + j);
+  }
+  const int64_t W = block_sum_i64(acc, sh.red);
+  const int w = blockIdx.x;
   if (W == 0) return;
   const int nw = effective_workers(W, p.num_workers);
-  const int w = blockIdx.x;
-  if (w >= nw) return;
   const int64_t p0 = worker_begin(w, W, nw), p1 = worker_begin(w + 1, W, nw);
-  if (p0 >= p1) return;
-  if (!plan_locate(p, G, p0, sh.red, &sh.b, &sh.cum)) return;
+  if (w >= nw || p0 >= p1 || !plan_locate(p, G, p0, sh.red, &sh.b, &sh.cum)) return;
 
   Cursor c;
   {
@@ -490,7 +519,18 @@ void mla_decode_fp8_kernel(const DecodeParams p) {
     if (len <= 0) break;  // not reached with a consistent plan
     const bool complete = (c.k == 0 && len == v);
     const int slot = complete ? -1 : (piece == 0 ? 2 * w : 2 * w + 1);
-    fp8_piece(p, sh, c.r.q_base + c.j, c.g, c.r.kv_base + c.k, len, slot, cs, ks);
+    UnitRef u;
+    u.t = c.r.q_base + c.j;
+    u.g = c.g;
+    fp8_piece(p, sh, u, c.r.kv_base + c.k, len, slot, cs, ks);
+    if (c.k == 0 && threadIdx.x == 0) {
+      // The worker holding a unit's first piece describes it for the combine
+      // pass: a split unit is merged from this worker's slot and slot 2w' of
+      // every later worker w' up to the last one.
+      p.desc[(int64_t)u.t * G + u.g] =
+          complete ? make_int4(0, 0, 0, 0)
+                   : make_int4(w, worker_of(pos + v - 1, W, nw), slot, 1);
+    }
     pos += len;
     c.k += len;
     ++piece;
@@ -504,73 +544,68 @@ void mla_decode_fp8_kernel(const DecodeParams p) {
 
 // ---------------------------------------------------------------- split combine
 
-// grid (T * G, 4): block (u, y) merges rows 4y..4y+3 of unit u = t * G + g, one
-// row per wave, 8 dims per lane.  Writes o = 0 / lse = -inf for empty units and
-// leaves units finished inside one worker alone.
-__global__ __launch_bounds__(kThreads) void mla_combine_kernel(const DecodeParams p) {
-  __shared__ int64_t red[kWaves];
-  __shared__ int s_b;
-  __shared__ int64_t s_cum;
+// grid (units, 32) of single waves: block (u, 2n + h) merges row n, dims
+// [256h, 256h + 256) of unit u = t * G + g if it was split, 4 dims per lane:
+// M = max lse_s, o = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
+// The slots are the first worker's own and slot 2w' of each later worker.
+constexpr int kCombineThreads = 64;
+
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const DecodeParams p) {
+  const int64_t u = blockIdx.x;
+  const int4 d = p.desc[u];
+  if (d.w == 0) return;
   const int G = p.num_heads / kGroup;
-  const int u = blockIdx.x;
-  const int t = u / G, g = u % G;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = 4 * blockIdx.y + wv;
-  const int64_t orow = (int64_t)t * p.num_heads + g * kGroup + n;
+  const int lane = threadIdx.x;
+  const int n = blockIdx.y >> 1, h = blockIdx.y & 1;
+  const int w0 = d.x, S = d.y - d.x + 1;
+  auto slot_of = [&](int i) -> int64_t { return i == 0 ? (int64_t)d.z : 2 * (int64_t)(w0 + i); };
 
-  const int64_t W = plan_total(p, G, red);
-  plan_token(p, G, t, red, &s_b, &s_cum);
-  const int b = s_b;
-  int v = 0;
-  int64_t ustart = 0;
-  if (b >= 0) {
-    const Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
-    const int j = t - r.q_base;
-    v = visible(r.n, r.qlen, j);
-    ustart = s_cum;
-    for (int jj = first_visible_token(r); jj < j; ++jj) ustart += (int64_t)G * visible(r.n, r.qlen, jj);
-    ustart += (int64_t)g * v;
+  // Slots in batches of 16: every load of a batch is issued before any is
+  // used, with an online rescale across batches.
+  float M = neg_inf(), sum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  constexpr int kBatch = 16;
+  for (int i0 = 0; i0 < S; i0 += kBatch) {
+    float4 x[kBatch];
+    float ls[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {  // past-the-end slots reload the last one, weight 0
+      const int64_t slot = slot_of(imin(i0 + j, S - 1));
+      ls[j] = p.part_lse[slot * kGroup + n];
+      x[j] = *(const float4*)(p.part_o + (slot * kGroup + n) * kLatent + 256 * h + 4 * lane);
+    }
+    // Keep the scheduler from interleaving these loads with their uses, which
+    // would leave only a couple in flight at a time.
+    __builtin_amdgcn_sched_barrier(0);
+    float bm = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (i0 + j < S) bm = fmaxf(bm, ls[j]);
+    const float alpha = (M == neg_inf()) ? 0.f : fast_exp2((M - bm) * kLog2e);
+    sum *= alpha;
+    acc.x *= alpha;
+    acc.y *= alpha;
+    acc.z *= alpha;
+    acc.w *= alpha;
+    M = bm;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float wt = (i0 + j < S) ? fast_exp2((ls[j] - M) * kLog2e) : 0.f;
+      sum += wt;
+      acc.x += wt * x[j].x;
+      acc.y += wt * x[j].y;
+      acc.z += wt * x[j].z;
+      acc.w += wt * x[j].w;
+    }
   }
-  uint16_t* dst = p.o + orow * kLatent + 8 * lane;
-  if (v == 0 || W == 0) {
-    *(uint4*)dst = make_uint4(0, 0, 0, 0);
-    if (p.lse != nullptr && lane == 0) p.lse[orow] = neg_inf();
-    return;
-  }
-  const int nw = effective_workers(W, p.num_workers);
-  const int wlo = worker_of(ustart, W, nw), whi = worker_of(ustart + v - 1, W, nw);
-  if (wlo == whi) return;
-
-  float M = neg_inf();
-  for (int w = wlo; w <= whi; ++w) {
-    const int slot = (w == wlo && worker_begin(w, W, nw) < ustart) ? 2 * w + 1 : 2 * w;
-    M = fmaxf(M, p.part_lse[(int64_t)slot * kGroup + n]);
-  }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float S = 0.f;
-  for (int w = wlo; w <= whi; ++w) {
-    const int slot = (w == wlo && worker_begin(w, W, nw) < ustart) ? 2 * w + 1 : 2 * w;
-    const float wt = fast_exp2((p.part_lse[(int64_t)slot * kGroup + n] - M) * kLog2e);
-    S += wt;
-    const float* src = p.part_o + ((int64_t)slot * kGroup + n) * kLatent + 8 * lane;
-    const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
-    acc[0] += wt * x0.x;
-    acc[1] += wt * x0.y;
-    acc[2] += wt * x0.z;
-    acc[3] += wt * x0.w;
-    acc[4] += wt * x1.x;
-    acc[5] += wt * x1.y;
-    acc[6] += wt * x1.z;
-    acc[7] += wt * x1.w;
-  }
-  const float inv = 1.0f / S;
-  uint4 pk;
-  pk.x = bf16_bits(acc[0] * inv) | (bf16_bits(acc[1] * inv) << 16);
-  pk.y = bf16_bits(acc[2] * inv) | (bf16_bits(acc[3] * inv) << 16);
-  pk.z = bf16_bits(acc[4] * inv) | (bf16_bits(acc[5] * inv) << 16);
-  pk.w = bf16_bits(acc[6] * inv) | (bf16_bits(acc[7] * inv) << 16);
-  *(uint4*)dst = pk;
-  if (p.lse != nullptr && lane == 0) p.lse[orow] = M + fast_log2(S) * kLn2;
+  const float inv = 1.0f / sum;
+  const int64_t t = u / G, g = u % G;
+  const int64_t orow = t * p.num_heads + g * kGroup + n;
+  uint2 pk;
+  pk.x = bf16_bits(acc.x * inv) | (bf16_bits(acc.y * inv) << 16);
+  pk.y = bf16_bits(acc.z * inv) | (bf16_bits(acc.w * inv) << 16);
+  *(uint2*)(p.o + orow * kLatent + 256 * h + 4 * lane) = pk;
+  if (p.lse != nullptr && h == 0 && lane == 0) p.lse[orow] = M + fast_log2(sum) * kLn2;
 }
 
 // ---------------------------------------------------------------- shard merge
@@ -635,12 +670,12 @@ __global__ __launch_bounds__(kThreads) void mla_merge_kernel(const void* o_parts
 
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, hipStream_t stream) {
   if (kv_dtype != 0) return hipErrorNotSupported;
-  const int G = p.num_heads / kGroup;
   hipLaunchKernelGGL(mla_decode_fp8_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(p.num_tokens * G), 4), dim3(kThreads), 0,
-                     stream, p);
+  const unsigned units = (unsigned)(p.num_tokens * (p.num_heads / kGroup));
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(units, 2 * kGroup), dim3(kCombineThreads), 0, stream,
+                     p);
   return hipGetLastError();
 }
 

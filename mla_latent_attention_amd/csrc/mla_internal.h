@@ -25,15 +25,24 @@ struct DecodeParams {
   float* lse;               // (T, H) or nullptr
   float* part_o;            // workspace: (2*num_workers, 16, 512) fp32
   float* part_lse;          // workspace: (2*num_workers, 16) fp32
+  int4* desc;               // workspace: (tokens * head groups) split-unit descriptors
   int num_workers;
 };
 
-// Workspace layout for `num_workers` workers.
+// Workspace layout for `num_workers` workers and `num_units` = tokens * head
+// groups (every byte the kernels read is written earlier in the same call, so
+// no clearing is ever needed):
+//   desc     (num_units) int4 per unit {first worker, last worker, slot of the
+//            first worker, 1} for a unit split over several workers, w = 0 else
+//   part_o   (2*num_workers, 16, 512) fp32 partial outputs
+//   part_lse (2*num_workers, 16) fp32 partial lse
+constexpr int kMaxWorkers = 1 << 16;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline size_t desc_bytes(int64_t num_units) { return align256(size_t(num_units) * 16); }
 inline size_t part_o_bytes(int num_workers) { return align256(size_t(2) * num_workers * 16 * 512 * 4); }
 inline size_t part_lse_bytes(int num_workers) { return align256(size_t(2) * num_workers * 16 * 4); }
-inline size_t workspace_bytes(int num_workers) {
-  return part_o_bytes(num_workers) + part_lse_bytes(num_workers);
+inline size_t workspace_bytes(int num_workers, int64_t num_units) {
+  return desc_bytes(num_units) + part_o_bytes(num_workers) + part_lse_bytes(num_workers);
 }
 
 // kv_dtype: 0 = fp8 e4m3fn, 1 = bf16.

@@ -128,6 +128,56 @@ def test_pad_heads_do_not_change_real_heads_bitwise():
     assert torch.equal(lse_r[:, :12], lse_zero[:, :12])
 
 
+def test_workspace_reused_across_calls():
+    """One workspace serves consecutive calls of different shapes and worker
+    counts (nothing in it survives from one call to the next)."""
+    ws = mla.new_workspace(mla.workspace_bytes(64, 64, 96, 4, num_workers=300), DEV)
+    cases = [(small_shared(5), 300), (small_shared(6, B=3), 37), (small_shared(5), 300),
+             (workloads.build("reuse-mt", [900, 40], num_heads=32, real_heads=32, qlens=[2, 4],
+                              pool_entries=4096, scale_range=(0.5, 2.0), seed=12, device=DEV), 11)]
+    for w, nw in cases:
+        o, lse = mla.decode(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                            w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale,
+                            return_lse=True, max_seqlen_q=w.max_seqlen_q, workspace=ws,
+                            num_workers=nw)
+        torch.cuda.synchronize()
+        _, o_ref, lse_ref = oracle(w)
+        assert_gate(metrics(o, o_ref, lse, lse_ref), f"reuse {w.name} nw={nw}")
+
+
+def test_graph_replay_matches_eager_bitwise():
+    """A decode captured in a HIP graph and replayed (with eager work between
+    replays) gives the eager result bit for bit on every replay."""
+    w = small_shared(7)
+    o_eager, lse_eager = run(w)
+    o = torch.empty_like(o_eager)
+    lse = torch.empty_like(lse_eager)
+    ws = mla.new_workspace(mla.workspace_bytes(w.batch, w.num_tokens, w.num_heads, 1), DEV)
+
+    def call():
+        mla.decode(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_lens,
+                   w.sm_scale, w.q_scale, w.kv_scale, return_lse=True, o=o, lse=lse,
+                   max_seqlen_q=1, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        o.zero_()
+        lse.fill_(7.0)
+        run(small_shared(8))  # unrelated eager work on the same device
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_eager), f"replay {rep}"
+        assert torch.equal(lse, lse_eager), f"replay {rep}"
+
+
 def test_run_to_run_bitwise_deterministic():
     w = small_shared(2)
     a = run(w)

@@ -107,6 +107,35 @@ def _scale(lo_hi, seed: int, device) -> torch.Tensor:
     return (torch.rand((), generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo)
 
 
+def make_indices(lengths, shared_prefix, pool_entries, layout, seed, device, index_buffer=None):
+    """kv_indices for `lengths`: a seeded permutation (or 128-slot block
+    permutation) of the pool; the first `shared_prefix` entries of every request
+    are the same slots, the rest are disjoint.  Buffer length >= the sum."""
+    gi = _gen(seed, device)
+    if layout == "random":
+        perm = torch.randperm(pool_entries, generator=gi, device=device, dtype=torch.int64)
+    elif layout == "blocked":
+        nblk = pool_entries // 128
+        bperm = torch.randperm(nblk, generator=gi, device=device, dtype=torch.int64)
+        perm = (bperm[:, None] * 128 + torch.arange(128, device=device)[None, :]).reshape(-1)
+    else:
+        raise ValueError(layout)
+    prefix = perm[:shared_prefix]
+    parts = []
+    off = shared_prefix
+    for n in lengths:
+        u = max(0, n - shared_prefix)
+        parts.append(prefix[: min(n, shared_prefix)])
+        parts.append(perm[off : off + u])
+        off += u
+    used = torch.cat(parts) if parts else torch.empty(0, dtype=torch.int64, device=device)
+    total = int(used.numel())
+    buf_len = max(total, index_buffer or 0, 1)
+    kv_indices = torch.zeros(buf_len, dtype=torch.int32, device=device)
+    kv_indices[:total] = used.to(torch.int32)
+    return kv_indices
+
+
 def build(
     name: str,
     lengths: list[int],
@@ -148,28 +177,9 @@ def build(
     if need > pool_entries:
         raise ValueError(f"workload needs {need} distinct slots, pool has {pool_entries}")
 
-    # Indices: a seeded permutation (or block permutation) of the pool.
-    gi = _gen(seed + 3, device)
-    if layout == "random":
-        perm = torch.randperm(pool_entries, generator=gi, device=device, dtype=torch.int64)
-    elif layout == "blocked":
-        nblk = pool_entries // 128
-        bperm = torch.randperm(nblk, generator=gi, device=device, dtype=torch.int64)
-        perm = (bperm[:, None] * 128 + torch.arange(128, device=device)[None, :]).reshape(-1)
-    else:
-        raise ValueError(layout)
-    prefix = perm[:shared_prefix]
-    parts = []
-    off = shared_prefix
-    for n, u in zip(lengths, uniq):
-        parts.append(prefix[: min(n, shared_prefix)])
-        parts.append(perm[off : off + u])
-        off += u
-    used = torch.cat(parts) if parts else torch.empty(0, dtype=torch.int64, device=device)
-    total = int(used.numel())
-    buf_len = max(total, index_buffer or 0, 1)
-    kv_indices = torch.zeros(buf_len, dtype=torch.int32, device=device)
-    kv_indices[:total] = used.to(torch.int32)
+    kv_indices = make_indices(lengths, shared_prefix, pool_entries, layout, seed + 3, device,
+                              index_buffer)
+    buf_len = int(kv_indices.numel())
 
     kv_indptr = torch.zeros(B + 1, dtype=torch.int32)
     kv_indptr[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
