@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the extra timing lines")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations (c24, mixed fp8/bf16, DCP share, merge)")
     ap.add_argument("--cpu-requests", type=int, default=2, help="requests in the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain fp32 copy-like kernel (out = -in) over BYTES, "
@@ -90,6 +92,83 @@ def with_indices(layers, variant, dev):
     idx = workloads.make_indices(layers[0].lengths, shared, layers[0].kv_pool.shape[0], layout,
                                  2000 + 3, dev, workloads.INDEX_BUFFER)
     return [workloads.Workload(**{**w.__dict__, "kv_indices": idx}) for w in layers]
+
+
+def extra_layers(base, n_layers, kv_std, seed0, dev):
+    """base plus n_layers - 1 copies with separate pools and q (same indices)."""
+    import torch
+
+    import workloads
+
+    layers = [base]
+    for k in range(1, n_layers):
+        pool = workloads._fill_values(tuple(base.kv_pool.shape), kv_std, base.dtype,
+                                      seed0 + 100 * k + 1, dev)
+        q = workloads._fill_values(tuple(base.q.shape), 1.0, base.dtype, seed0 + 100 * k + 2, dev,
+                                   chunk_rows=1 << 12)
+        if base.real_heads < base.num_heads:
+            q[:, base.real_heads:, :] = torch.zeros((), dtype=q.dtype, device=dev)
+        layers.append(workloads.Workload(**{**base.__dict__, "kv_pool": pool, "q": q,
+                                            "name": f"{base.name}-layer{k}"}))
+    return layers
+
+
+def config_lines(mla, dev, steps, warmup, n_layers=4):
+    """Time the other decode configurations and the shard merge, each cycling
+    n_layers independent inputs under graph replay."""
+    import torch
+
+    import workloads
+    from workloads import accounting
+
+    out = {}
+    cases = [
+        ("c24_batch24_fp8", lambda: workloads.c24(dev), 0.5),
+        ("mixed_batch64_fp8", lambda: workloads.mixed(dev, "fp8"), 1.0),
+        ("mixed_batch64_bf16", lambda: workloads.mixed(dev, "bf16"), 1.0),
+        ("dcp_share_96heads_qlen4_fp8", lambda: workloads.dcp_share(dev), 0.5),
+    ]
+    for name, make, std in cases:
+        base = make()
+        layers = extra_layers(base, n_layers, std, 7000, dev)
+        T, H = base.num_tokens, base.num_heads
+        o = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev) if base.return_lse else None
+        ws = mla.new_workspace(mla.workspace_bytes(base.batch, T, H, base.max_seqlen_q), dev)
+
+        def call_for(w):
+            return lambda: mla.decode(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                      w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale,
+                                      return_lse=w.return_lse, o=o, lse=lse,
+                                      max_seqlen_q=w.max_seqlen_q, workspace=ws)
+
+        wall, ev, n = time_graph([call_for(w) for w in layers], steps, warmup)
+        nbytes = accounting.workload_bytes(base)
+        flops = accounting.workload_flops(base)
+        out[name] = {"us_per_call": round(wall * 1e6, 2), "event_us": stats_us(ev),
+                     "GB_s": round(nbytes / wall / 1e9, 2),
+                     "pct_of_8TBs": round(100 * nbytes / wall / 1e9 / PEAK_GBS, 2),
+                     "TFLOP_s": round(flops / wall / 1e12, 2),
+                     "algorithmic_bytes_per_call": nbytes, "kv_rows": base.total_kv,
+                     "dtype": base.dtype, "calls": n}
+        del layers, base, o, lse, ws
+        torch.cuda.empty_cache()
+    for parts_dtype in ("fp32", "bf16"):
+        sets = [workloads.merge_shards(parts_dtype=parts_dtype, seed=5100 + k, device=dev)
+                for k in range(8)]
+        o = torch.empty((32, 96, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((32, 96), dtype=torch.float32, device=dev)
+        calls = [(lambda op=op, lp=lp: mla.merge_partials(op, lp, o=o, lse=lse))
+                 for op, lp in sets]
+        wall, ev, n = time_graph(calls, steps, warmup)
+        nbytes = accounting.merge_bytes(8, 32, 96, parts_dtype)
+        out[f"merge_8_shards_{parts_dtype}"] = {
+            "us_per_call": round(wall * 1e6, 2), "event_us": stats_us(ev),
+            "GB_s": round(nbytes / wall / 1e9, 2),
+            "pct_of_8TBs": round(100 * nbytes / wall / 1e9 / PEAK_GBS, 2),
+            "algorithmic_bytes_per_call": nbytes, "calls": n}
+        del sets
+    return out
 
 
 def make_calls(mla, layers, o, ws):
@@ -295,6 +374,10 @@ def main():
                                          "GB_s": round(nbytes / wv / 1e9, 2),
                                          "pct_of_8TBs": round(100 * nbytes / wv / 1e9 / PEAK_GBS, 2)}
         out["variants"] = variants
+    if not a.no_configs:
+        del calls, layers
+        torch.cuda.empty_cache()
+        out["configs"] = config_lines(mla, dev, max(64, a.steps // 4), 8)
     if not a.no_cpu_baseline:
         per_call, cores, sample = cpu_baseline(w0, a.cpu_requests)
         out["cpu_baseline"] = {"value": round(nbytes / per_call / 1e9, 4), "unit": "GB/s",

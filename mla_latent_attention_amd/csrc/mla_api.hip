@@ -93,7 +93,6 @@ mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv
   if (pool_entries < 1 || kv_indices_len < 0 || kv_indices_len > 0x7FFFFFFF)
     return MLA_ERR_BAD_SHAPE;
   if (num_workers < 0 || num_workers > kMaxWorkers) return MLA_ERR_BAD_SHAPE;
-  if (q_dtype == MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;  // fp8 path only for now
   const int64_t num_units = (int64_t)num_q_tokens * (num_heads / mla::kGroup);
   if (!workspace) return MLA_ERR_WORKSPACE_TOO_SMALL;
   if (num_workers > 0 && workspace_bytes < mla::workspace_bytes(num_workers, num_units))

@@ -10,20 +10,19 @@
 // Design (our own; the pages' assembly kernel is not available):
 //   * One workgroup (4 waves, one per SIMD) per worker; the planner in
 //     mla_plan.h hands each worker an equal share of the KV stream.
-//   * Inside a piece the 4 waves take interleaved 32-row tiles and run
-//     independent online softmaxes, merged through LDS at the piece's end.
-//   * Per tile a wave gathers 32 pool rows with 16-byte loads straight into
-//     VGPRs, two tiles ahead of use.  Lane l loads row (l%16) (+16), bytes
-//     [64c + 16*(l/16), +16) for c = 0..8, which is exactly the A-operand
-//     layout of v_mfma_f32_16x16x32_fp8_fp8, so Q.K^T runs from registers:
-//     S^T (kv x 16 rows) = K (kv x 576) . Q^T.
-//   * The latent 512 bytes of each row go to a per-wave LDS tile (row-major,
-//     padded stride); P.V reads 16 bytes from each of 8 rows and transposes
-//     4x4 byte blocks in registers (v_perm) to build the V^T A-operand, so the
-//     contraction runs as O^T (512 x 16 rows) += V^T . P^T on fp8 MFMA.
-//   * P is fed as two e4m3 terms, P*128 = hi + lo (hi = e4m3(P*128),
-//     lo = e4m3(P*128 - hi)), so the fp8 P.V keeps ~8 significant bits of P;
-//     a single e4m3 P (4 bits) would not meet the output tolerance.
+//   * Inside a piece the 4 waves take interleaved tiles of 18 KB of gathered
+//     rows (32 fp8 rows or 16 bf16 rows) and run independent online softmaxes,
+//     merged through LDS at the piece's end.
+//   * Per tile a wave gathers its rows with 16-byte loads straight into VGPRs,
+//     two tiles ahead of use, laid out as the A operand of the QK MFMA, so
+//     Q.K^T runs from registers as S^T (kv x 16 rows) = K (kv x 576) . Q^T.
+//   * The latent part of each row goes to a per-wave LDS tile (row-major,
+//     padded stride); P.V reads it back transposed into the V^T A operand
+//     (v_perm byte or half-word selects), so the contraction runs as
+//     O^T (512 x 16 rows) += V^T . P^T on MFMA.
+//   * P is fed as two terms, P = hi + lo (e4m3 for the fp8 path, bf16 for the
+//     bf16 path), so the contraction sees ~8 (fp8) or ~16 (bf16) significant
+//     bits of P; a single e4m3 P (4 bits) would not meet the output tolerance.
 //   * Scores are kept in base 2 (log2(e) folded into the scale).  The running
 //     max is only raised when a row's max grows by more than 2x, so the O^T
 //     accumulators are rescaled on few tiles.
@@ -49,16 +48,11 @@ typedef uint32_t u32;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTile = 32;                          // KV rows per wave iteration
-constexpr int kVStride = 528;                      // LDS bytes per staged V row (512 + pad)
-constexpr int kVWaveBytes = kTile * kVStride;      // 16,896
 constexpr int kCombBytes = kWaves * 32 * 64 * 16;  // 131,072: every wave's O^T
 constexpr int kIdxSeg = 7168;                      // kv_indices staged in LDS per segment
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLazy = 1.0f;                       // rescale when a row max grows > 2^kLazy
-constexpr float kPScale = 128.0f;                  // P * kPScale <= 2^kLazy * 128 = 256 < 448
-static_assert(kWaves * kVWaveBytes <= kCombBytes, "V staging must fit in the LDS buffer");
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
@@ -153,97 +147,55 @@ __device__ bool plan_locate(const DecodeParams& p, int G, int64_t pos, int64_t* 
   return *s_b >= 0;
 }
 
-// ---------------------------------------------------------------- fp8 decode
+// ---------------------------------------------------------------- tile loop
 
-struct TileIdx {
-  int i0, i1;  // pool rows of tile rows (lane%16) and (16 + lane%16)
+struct alignas(16) DecodeShared {
+  uint8_t buf[kCombBytes];  // V staging during the tile loop, O^T exchange after it
+  int32_t idx[kIdxSeg];     // kv_indices of the current segment of the piece
+  int64_t red[kWaves];
+  float m[kWaves][16];
+  float l[kWaves][16];
+  int b;
+  int64_t cum;
 };
 
-// Indices of a tile's rows, read from the LDS copy of the current segment.
-// Positions past the segment repeat its last entry, so every row load is
-// issued unconditionally (the outstanding-load count stays static and the
-// compiler keeps the prefetch pipeline); those rows' scores are masked to
-// -inf, so their (finite, referenced) contents never contribute.  Keeping the
-// indices in LDS also keeps them off the in-order vector-memory counter.
-__device__ __forceinline__ TileIdx fetch_idx(const int32_t* sidx, int rows, int tile, int n) {
-  const int e0 = imin(tile * kTile + n, rows - 1);
-  const int e1 = imin(tile * kTile + 16 + n, rows - 1);
-  TileIdx t;
-  t.i0 = sidx[e0];
-  t.i1 = sidx[e1];
-  return t;
-}
+// The unit (query token, head group) a piece belongs to.
+struct UnitRef {
+  int t, g;
+};
 
-__device__ __forceinline__ const uint8_t* row_ptr(const uint8_t* kv, int64_t pool_entries, int idx,
-                                                  int gq) {
-  int64_t r = idx < 0 ? 0 : (int64_t)idx;
-  r = r < pool_entries ? r : pool_entries - 1;
-  return kv + r * kRowDim + 16 * gq;
-}
-
-__device__ __forceinline__ void issue_rows(uint4 (&B)[18], const uint8_t* kv, int64_t pool_entries,
-                                           TileIdx ti, int gq) {
-  const uint8_t* s0 = row_ptr(kv, pool_entries, ti.i0, gq);
-  const uint8_t* s1 = row_ptr(kv, pool_entries, ti.i1, gq);
-#pragma unroll
-  for (int c = 0; c < 9; ++c) B[c] = *(const uint4*)(s0 + 64 * c);
-#pragma unroll
-  for (int c = 0; c < 9; ++c) B[9 + c] = *(const uint4*)(s1 + 64 * c);
-}
+struct TileIdx {
+  int i0, i1;  // pool rows this lane gathers: tile row (lane%16) and, for
+               // 32-row tiles, tile row (16 + lane%16)
+};
 
 struct WaveState {
-  v4f O[32];  // O^T blocks: block (half*16 + t) element i = row (lane%16),
-              // dim 256*half + 64*(lane/16) + 16*i + t; scaled by kPScale
+  v4f O[32];  // O^T blocks (the dim of each element depends on the path);
+              // scaled by the path's kPScale
   float m;    // (possibly stale) running max of base-2 scores of row lane%16
   float l;    // this lane's partial sum of 2^(s - m)
 };
 
-// One 32-row tile: S^T = K.Q^T, online softmax, O^T += V^T.P^T.  With kRefill,
-// B is refilled with the rows of `next` (two tiles ahead for this wave) right
-// after its contents are consumed, and the indices four tiles ahead are fetched.
-template <bool kRefill>
-__device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx& next,
-                                         const long (&qlo)[9], const long (&qhi)[9],
-                                         uint8_t* vst, const DecodeParams& p, const int32_t* sidx,
-                                         int rows, int tile, float cs, int n, int gq) {
-  v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < 9; ++c) {
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].x, B[c].y), qlo[c], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].x, B[9 + c].y), qlo[c], s1, 0, 0,
-                                                    0);
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].z, B[c].w), qhi[c], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].z, B[9 + c].w), qhi[c], s1, 0,
-                                                    0, 0);
-  }
+// Clamped address of byte 16*gq of pool row idx.
+template <int kRowBytes>
+__device__ __forceinline__ const uint8_t* row_ptr(const uint8_t* kv, int64_t pool_entries, int idx,
+                                                  int gq) {
+  int64_t r = idx < 0 ? 0 : (int64_t)idx;
+  r = r < pool_entries ? r : pool_entries - 1;
+  return kv + r * kRowBytes + 16 * gq;
+}
 
-  // Stage the latent 512 bytes of both 16-row blocks in this wave's LDS tile.
-  wave_lds_sync();  // the previous tile's V reads are complete
+// Online-softmax update for row lane%16 from this lane's N scores (already
+// masked to -inf past the piece).  Returns P = 2^(s - m) in x.  The running
+// max is only raised when a row's max grows by more than 2^kLazy, so P stays
+// <= 2^kLazy and the accumulators are rescaled on few tiles.
+template <int N>
+__device__ __forceinline__ void softmax_update(WaveState& st, float (&x)[N]) {
+  float tmax = x[0];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    *(uint4*)(vst + n * kVStride + 64 * c + 16 * gq) = B[c];
-    *(uint4*)(vst + (16 + n) * kVStride + 64 * c + 16 * gq) = B[9 + c];
-  }
-  if constexpr (kRefill) {
-    issue_rows(B, p.kv, p.pool_entries, next, gq);
-    next = fetch_idx(sidx, rows, tile + 4 * kWaves, n);
-  }
-
-  // Online softmax for row lane%16; this lane holds kv rows 4gq+i and 16+4gq+i.
-  const int base = tile * kTile + 4 * gq;
-  float sc[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sc[i] = (base + i < rows) ? s0[i] * cs : neg_inf();
-    sc[4 + i] = (base + 16 + i < rows) ? s1[i] * cs : neg_inf();
-  }
-  float tmax = sc[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
+  for (int i = 1; i < N; ++i) tmax = fmaxf(tmax, x[i]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  // Lazy rescale: keep a stale max unless a row's max grew by more than
-  // 2^kLazy; P = 2^(s - m) then stays <= 2^kLazy and P * kPScale <= 256 fits e4m3.
   const bool grow = tmax > st.m + kLazy;  // first tile: m = -inf
   if (__any(grow)) {
     const float mset = grow ? tmax : st.m;
@@ -253,16 +205,96 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
     st.l *= alpha;
     st.m = mset;
   }
-  float x[8], psum = 0.f;
+  float psum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float pr = fast_exp2(sc[i] - st.m);
-    psum += pr;
-    x[i] = pr * kPScale;
+  for (int i = 0; i < N; ++i) {
+    x[i] = fast_exp2(x[i] - st.m);
+    psum += x[i];
   }
   st.l += psum;
+}
 
-  // P*kPScale = hi + lo in e4m3; byte k of the operand = kv row kappa(gq, k).
+// ---- fp8 e4m3 path: 32-row tiles of 576-byte rows.
+//
+// Lane l gathers tile rows (l%16) and (16 + l%16), bytes [64c + 16*(l/16), +16)
+// for c = 0..8: two K-blocks of 32 dims of the A operand of
+// v_mfma_f32_16x16x32_fp8_fp8 per load, so Q.K^T runs from registers as
+// S^T (kv x 16 rows) = K . Q^T.  The latent 512 bytes go to a per-wave LDS
+// tile; P.V reads 16 bytes from each of 8 rows and transposes 4x4 byte blocks
+// (v_perm) into the V^T A operand: O^T (512 x 16 rows) += V^T . P^T.  P enters
+// as two e4m3 terms, P*128 = hi + lo, which keeps ~8 significant bits of P (a
+// single e4m3 P, 4 bits, would not meet the output tolerance).
+
+constexpr int kFp8Tile = 32;
+constexpr int kFp8VStride = 528;  // LDS bytes per staged V row (512 + pad)
+
+__device__ __forceinline__ TileIdx fp8_fetch_idx(const int32_t* sidx, int rows, int tile, int n) {
+  const int e0 = imin(tile * kFp8Tile + n, rows - 1);
+  const int e1 = imin(tile * kFp8Tile + 16 + n, rows - 1);
+  TileIdx t;
+  t.i0 = sidx[e0];
+  t.i1 = sidx[e1];
+  return t;
+}
+
+__device__ __forceinline__ void fp8_issue_rows(uint4 (&B)[18], const uint8_t* kv,
+                                               int64_t pool_entries, TileIdx ti, int gq) {
+  const uint8_t* s0 = row_ptr<kRowDim>(kv, pool_entries, ti.i0, gq);
+  const uint8_t* s1 = row_ptr<kRowDim>(kv, pool_entries, ti.i1, gq);
+#pragma unroll
+  for (int c = 0; c < 9; ++c) B[c] = *(const uint4*)(s0 + 64 * c);
+#pragma unroll
+  for (int c = 0; c < 9; ++c) B[9 + c] = *(const uint4*)(s1 + 64 * c);
+}
+
+struct Fp8Q {
+  long lo[9], hi[9];  // q row lane%16, bytes [64c + 16*(lane/16), +8) and [+8, +16)
+};
+
+// One 32-row tile: S^T = K.Q^T, online softmax, O^T += V^T.P^T.  With kRefill,
+// B is refilled with the rows of `next` (two tiles ahead for this wave) right
+// after its contents are consumed, and the indices four tiles ahead are fetched.
+template <bool kRefill>
+__device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx& next,
+                                         const Fp8Q& q, uint8_t* vst, const DecodeParams& p,
+                                         const int32_t* sidx, int rows, int tile, float cs, int n,
+                                         int gq) {
+  v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 9; ++c) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].x, B[c].y), q.lo[c], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].x, B[9 + c].y), q.lo[c], s1, 0,
+                                                    0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].z, B[c].w), q.hi[c], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].z, B[9 + c].w), q.hi[c], s1, 0,
+                                                    0, 0);
+  }
+
+  // Stage the latent 512 bytes of both 16-row blocks in this wave's LDS tile.
+  wave_lds_sync();  // the previous tile's V reads are complete
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    *(uint4*)(vst + n * kFp8VStride + 64 * c + 16 * gq) = B[c];
+    *(uint4*)(vst + (16 + n) * kFp8VStride + 64 * c + 16 * gq) = B[9 + c];
+  }
+  if constexpr (kRefill) {
+    fp8_issue_rows(B, p.kv, p.pool_entries, next, gq);
+    next = fp8_fetch_idx(sidx, rows, tile + 4 * kWaves, n);
+  }
+
+  // Row lane%16; this lane holds kv rows 4gq+i and 16+4gq+i.
+  const int base = tile * kFp8Tile + 4 * gq;
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = (base + i < rows) ? s0[i] * cs : neg_inf();
+    x[4 + i] = (base + 16 + i < rows) ? s1[i] * cs : neg_inf();
+  }
+  softmax_update<8>(st, x);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] *= 128.0f;  // P * 128 <= 2^kLazy * 128 = 256 < 448
+
+  // P*128 = hi + lo in e4m3; byte k of the operand = kv row kappa(gq, k).
   u32 h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
   h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h0, true);
   u32 h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
@@ -291,10 +323,10 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int row = (k < 4) ? (4 * gq + k) : (16 + 4 * gq + (k - 4));
-      v[k] = *(const uint4*)(vst + row * kVStride + 16 * n + 256 * half);
+      v[k] = *(const uint4*)(vst + row * kFp8VStride + 16 * n + 256 * half);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int qq = 0; qq < 4; ++qq) {
       u32 a0, a1, a2, a3, b0, b1, b2, b3;
       const u32* w0 = (const u32*)&v[0];
       const u32* w1 = (const u32*)&v[1];
@@ -304,12 +336,12 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
       const u32* w5 = (const u32*)&v[5];
       const u32* w6 = (const u32*)&v[6];
       const u32* w7 = (const u32*)&v[7];
-      transpose4x4(w0[q], w1[q], w2[q], w3[q], a0, a1, a2, a3);
-      transpose4x4(w4[q], w5[q], w6[q], w7[q], b0, b1, b2, b3);
+      transpose4x4(w0[qq], w1[qq], w2[qq], w3[qq], a0, a1, a2, a3);
+      transpose4x4(w4[qq], w5[qq], w6[qq], w7[qq], b0, b1, b2, b3);
       const long A[4] = {as_long(a0, b0), as_long(a1, b1), as_long(a2, b2), as_long(a3, b3)};
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        const int blk = half * 16 + 4 * q + bb;
+        const int blk = half * 16 + 4 * qq + bb;
         st.O[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(A[bb], phi, st.O[blk], 0, 0, 0);
         st.O[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(A[bb], plo, st.O[blk], 0, 0, 0);
       }
@@ -317,20 +349,226 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
   }
 }
 
-struct alignas(16) DecodeShared {
-  uint8_t buf[kCombBytes];  // V staging during the tile loop, O^T exchange after it
-  int32_t idx[kIdxSeg];     // kv_indices of the current segment of the piece
-  int64_t red[kWaves];
-  float m[kWaves][16];
-  float l[kWaves][16];
-  int b;
-  int64_t cum;
+struct Fp8Path {
+  static constexpr int kRowBytes = kRowDim;
+  static constexpr int kTile = kFp8Tile;
+  static constexpr int kVStride = kFp8VStride;
+  static constexpr float kPScale = 128.0f;
+  using Q = Fp8Q;
+  // Q stays in registers: lane l holds row l%16 of the unit's head group.
+  static __device__ __forceinline__ void load_q(Q& q, const DecodeParams& p, DecodeShared&,
+                                                const UnitRef& u, int n, int gq) {
+    const uint8_t* qrow =
+        p.q + ((int64_t)u.t * p.num_heads + u.g * kGroup + n) * kRowBytes + 16 * gq;
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      const uint4 x = *(const uint4*)(qrow + 64 * c);
+      q.lo[c] = as_long(x.x, x.y);
+      q.hi[c] = as_long(x.z, x.w);
+    }
+  }
+  static __device__ __forceinline__ TileIdx fetch_idx(const int32_t* sidx, int rows, int tile,
+                                                      int n) {
+    return fp8_fetch_idx(sidx, rows, tile, n);
+  }
+  static __device__ __forceinline__ void issue_rows(uint4 (&B)[18], const uint8_t* kv,
+                                                    int64_t pool_entries, TileIdx ti, int gq) {
+    fp8_issue_rows(B, kv, pool_entries, ti, gq);
+  }
+  template <bool kRefill>
+  static __device__ __forceinline__ void tile(WaveState& st, uint4 (&B)[18], TileIdx& next,
+                                              const Q& q, uint8_t* vst, const DecodeParams& p,
+                                              const int32_t* sidx, int rows, int t, float cs,
+                                              int n, int gq) {
+    fp8_tile<kRefill>(st, B, next, q, vst, p, sidx, rows, t, cs, n, gq);
+  }
+  // O^T block b = 16*half + 4*qq + bb, element i, at lane (n, gq) is dim
+  // 256*half + 64*gq + 16*i + 4*qq + bb.  Wave wv owns blocks [8wv, 8wv + 8):
+  // dims first_dim(wv, gq) + kDimStride*i + (block - 8wv).
+  static constexpr int kDimStride = 16;
+  static __device__ __forceinline__ int first_dim(int wv, int gq) {
+    return 256 * (wv >> 1) + 64 * gq + 8 * (wv & 1);
+  }
 };
 
-// The unit (query token, head group) a piece belongs to.
-struct UnitRef {
-  int t, g;
+// ---- bf16 path: 16-row tiles of 1152-byte rows (the same 18 KB per tile).
+//
+// Lane l gathers tile row (l%16), bytes [64c + 16*(l/16), +16) for c = 0..17:
+// eight bf16 dims 32c + 8*(l/16) + j, the A operand of v_mfma_f32_16x16x32_bf16
+// for K-block c, so S^T (16 kv x 16 rows) = K . Q^T runs from registers.  The
+// S^T accumulator (lane holds kv rows 4*(l/16) + i of row l%16) is exactly the
+// B operand of v_mfma_f32_16x16x16_bf16 (P^T), so P needs no reshuffle; the
+// V^T A operand (dim l%16 of a block, kv rows 4*(l/16) + j) comes from four
+// 16-byte LDS reads per lane and 16-bit v_perm selects.  P enters as
+// P = hi + lo in bf16 (~16 significant bits).
+
+constexpr int kBf16Tile = 16;
+constexpr int kBf16RowBytes = 2 * kRowDim;  // 1152
+constexpr int kBf16VStride = 1040;          // LDS bytes per staged V row (1024 + pad)
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef u32 v4u __attribute__((ext_vector_type(4)));
+typedef u32 v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v8bf as_v8bf(uint4 x) {
+  return __builtin_bit_cast(v8bf, v4u{x.x, x.y, x.z, x.w});
+}
+__device__ __forceinline__ v4s as_v4s(u32 lo, u32 hi) {
+  return __builtin_bit_cast(v4s, v2u{lo, hi});
+}
+
+__device__ __forceinline__ TileIdx bf16_fetch_idx(const int32_t* sidx, int rows, int tile, int n) {
+  TileIdx t;
+  t.i0 = sidx[imin(tile * kBf16Tile + n, rows - 1)];
+  t.i1 = t.i0;
+  return t;
+}
+
+__device__ __forceinline__ void bf16_issue_rows(uint4 (&B)[18], const uint8_t* kv,
+                                                int64_t pool_entries, TileIdx ti, int gq) {
+  const uint8_t* s0 = row_ptr<kBf16RowBytes>(kv, pool_entries, ti.i0, gq);
+#pragma unroll
+  for (int c = 0; c < 18; ++c) B[c] = *(const uint4*)(s0 + 64 * c);
+}
+
+// Q is staged once per piece in LDS, past the V tiles, in lane order: entry
+// 64c + l holds q row l%16, bytes [64c + 16*(l/16), +16), so a wave reads the
+// B operand of K-block c as 64 consecutive 16-byte words.  (Kept in registers
+// it would cost 72 VGPRs per lane, which this path does not have.)
+constexpr int kBf16QOffset = kWaves * kBf16Tile * kBf16VStride;  // 66,560
+struct Bf16Q {
+  const uint4* lds;  // this lane's entry of K-block 0
 };
+
+template <bool kRefill>
+__device__ __forceinline__ void bf16_tile(WaveState& st, uint4 (&B)[18], TileIdx& next,
+                                          const Bf16Q& q, uint8_t* vst, const DecodeParams& p,
+                                          const int32_t* sidx, int rows, int tile, float cs, int n,
+                                          int gq) {
+  // Q operands come from LDS in groups of 6 K-blocks; the scheduling fences
+  // keep the compiler from hoisting all 18 reads (72 VGPRs) at once.
+  v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c0 = 0; c0 < 9; c0 += 3) {
+#pragma unroll
+    for (int c = c0; c < c0 + 3; ++c) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(B[c]), as_v8bf(q.lds[64 * c]), s0, 0, 0,
+                                                   0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(B[9 + c]), as_v8bf(q.lds[64 * (9 + c)]),
+                                                   s1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Stage the latent 1024 bytes of the 16 rows in this wave's LDS tile.
+  wave_lds_sync();  // the previous tile's V reads are complete
+#pragma unroll
+  for (int c = 0; c < 16; ++c) *(uint4*)(vst + n * kBf16VStride + 64 * c + 16 * gq) = B[c];
+  if constexpr (kRefill) {
+    bf16_issue_rows(B, p.kv, p.pool_entries, next, gq);
+    next = bf16_fetch_idx(sidx, rows, tile + 4 * kWaves, n);
+  }
+
+  // Row lane%16; this lane holds kv rows 4gq+i.
+  const int base = tile * kBf16Tile + 4 * gq;
+  float x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (base + i < rows) ? (s0[i] + s1[i]) * cs : neg_inf();
+  softmax_update<4>(st, x);
+
+  // P = hi + lo, both bf16; element j of the operand is kv row 4gq + j.
+  u32 hb[4], lb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hb[i] = bf16_bits(x[i]);
+    lb[i] = bf16_bits(x[i] - __uint_as_float(hb[i] << 16));
+  }
+  const v4s phi = as_v4s(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+  const v4s plo = as_v4s(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+
+  // O^T += V^T . P^T.  For c = 0..3 the lane reads dims [8m, 8m + 8) with
+  // m = n + 16c of kv rows 4gq + j; word w of those 16 bytes holds dims 8m + 2w
+  // (low half) and 8m + 2w + 1 (high half).  Block 8c + t takes dim 8m + t,
+  // so O^T block 8c + t, element i, at lane (n, gq) is dim
+  // 8 * (4gq + i + 16c) + t.
+  wave_lds_sync();  // all lanes' V writes are in LDS
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = *(const uint4*)(vst + (4 * gq + j) * kBf16VStride + 16 * n + 256 * c);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u32 r0 = ((const u32*)&v[0])[w], r1 = ((const u32*)&v[1])[w];
+      const u32 r2 = ((const u32*)&v[2])[w], r3 = ((const u32*)&v[3])[w];
+      const v4s ae = as_v4s(__builtin_amdgcn_perm(r1, r0, 0x05040100u),
+                            __builtin_amdgcn_perm(r3, r2, 0x05040100u));
+      const v4s ao = as_v4s(__builtin_amdgcn_perm(r1, r0, 0x07060302u),
+                            __builtin_amdgcn_perm(r3, r2, 0x07060302u));
+      const int be = 8 * c + 2 * w, bo = be + 1;
+      st.O[be] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, phi, st.O[be], 0, 0, 0);
+      st.O[bo] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, phi, st.O[bo], 0, 0, 0);
+      st.O[be] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, plo, st.O[be], 0, 0, 0);
+      st.O[bo] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, plo, st.O[bo], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+struct Bf16Path {
+  static constexpr int kRowBytes = kBf16RowBytes;
+  static constexpr int kTile = kBf16Tile;
+  static constexpr int kVStride = kBf16VStride;
+  static constexpr float kPScale = 1.0f;
+  using Q = Bf16Q;
+  // Cooperative copy of the unit's 16 q rows into LDS; the caller synchronises
+  // the block before the first tile reads it.
+  static __device__ __forceinline__ void load_q(Q& q, const DecodeParams& p, DecodeShared& sh,
+                                                const UnitRef& u, int, int) {
+    uint4* dst = (uint4*)(sh.buf + kBf16QOffset);
+    const uint8_t* q0 = p.q + ((int64_t)u.t * p.num_heads + u.g * kGroup) * kRowBytes;
+    constexpr int kEntries = 18 * 64, kPer = (kEntries + kThreads - 1) / kThreads;
+    uint4 v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {  // all loads first; the tail rereads the last entry
+      const int e = imin(k * kThreads + (int)threadIdx.x, kEntries - 1);
+      const int c = e >> 6, l = e & 63;
+      v[k] = *(const uint4*)(q0 + (l & 15) * kRowBytes + 64 * c + 16 * (l >> 4));
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = k * kThreads + threadIdx.x;
+      if (e < kEntries) dst[e] = v[k];
+    }
+    q.lds = dst + (threadIdx.x & 63);
+  }
+  static __device__ __forceinline__ TileIdx fetch_idx(const int32_t* sidx, int rows, int tile,
+                                                      int n) {
+    return bf16_fetch_idx(sidx, rows, tile, n);
+  }
+  static __device__ __forceinline__ void issue_rows(uint4 (&B)[18], const uint8_t* kv,
+                                                    int64_t pool_entries, TileIdx ti, int gq) {
+    bf16_issue_rows(B, kv, pool_entries, ti, gq);
+  }
+  template <bool kRefill>
+  static __device__ __forceinline__ void tile(WaveState& st, uint4 (&B)[18], TileIdx& next,
+                                              const Q& q, uint8_t* vst, const DecodeParams& p,
+                                              const int32_t* sidx, int rows, int t, float cs,
+                                              int n, int gq) {
+    bf16_tile<kRefill>(st, B, next, q, vst, p, sidx, rows, t, cs, n, gq);
+  }
+  // Block 8c + t, element i, at lane (n, gq) is dim 128c + 32gq + 8i + t; wave
+  // wv owns blocks [8wv, 8wv + 8), i.e. c = wv.
+  static constexpr int kDimStride = 8;
+  static __device__ __forceinline__ int first_dim(int wv, int gq) { return 128 * wv + 32 * gq; }
+};
+
+static_assert(kWaves * kFp8Tile * kFp8VStride <= kCombBytes, "fp8 V staging must fit in LDS");
+static_assert(kBf16QOffset + 18 * 64 * 16 <= kCombBytes, "bf16 V staging and Q must fit in LDS");
+
+// ---------------------------------------------------------------- pieces
 
 __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&a)[8]) {
   uint4 pk;
@@ -341,23 +579,42 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&a)[8])
   *(uint4*)dst = pk;
 }
 
+// Copies n (>= 1) indices to LDS.  Each thread issues kIdxBatch loads before
+// its first store (past-the-end positions reload the last index), so a
+// segment costs ceil(n / 2048) memory round trips instead of one per 256.
+constexpr int kIdxBatch = 8;
+__device__ __forceinline__ void stage_indices(int32_t* dst, const int32_t* src, int n) {
+  for (int i0 = 0; i0 < n; i0 += kThreads * kIdxBatch) {
+    int32_t v[kIdxBatch];
+#pragma unroll
+    for (int j = 0; j < kIdxBatch; ++j) v[j] = src[imin(i0 + j * kThreads + (int)threadIdx.x, n - 1)];
+#pragma unroll
+    for (int j = 0; j < kIdxBatch; ++j) {
+      const int i = i0 + j * kThreads + threadIdx.x;
+      if (i < n) dst[i] = v[j];
+    }
+  }
+}
+
 // One piece: KV positions [kv_pos0, kv_pos0 + rows) of unit u.  slot < 0 means
 // the piece is the whole unit and o / lse are written directly.
-__device__ __forceinline__ void fp8_piece(const DecodeParams& p, DecodeShared& sh, const UnitRef& u,
-                                          int kv_pos0, int rows, int slot, float cs, float ks) {
+//
+// The 4 waves take interleaved tiles (wave wv: tiles wv, wv + 4, ...) and run
+// independent online softmaxes over them, merged through LDS at the end.  A
+// wave keeps two tiles of rows in flight in registers (bufA / bufB), each
+// refilled right after its contents are consumed; every load is unconditional
+// (positions past the segment repeat its last index and are masked), so the
+// outstanding-load count stays static and the prefetch survives compilation.
+// Indices are staged in LDS per segment, off the vector-memory counter.
+template <class Path>
+__device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared& sh,
+                                             const UnitRef& u, int kv_pos0, int rows, int slot,
+                                             float cs, float ks) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
   __syncthreads();  // the previous piece is done with the LDS buffer
 
-  long qlo[9], qhi[9];
-  {
-    const uint8_t* qrow = p.q + ((int64_t)u.t * p.num_heads + u.g * kGroup + n) * kRowDim + 16 * gq;
-#pragma unroll
-    for (int c = 0; c < 9; ++c) {
-      const uint4 x = *(const uint4*)(qrow + 64 * c);
-      qlo[c] = as_long(x.x, x.y);
-      qhi[c] = as_long(x.z, x.w);
-    }
-  }
+  typename Path::Q q;
+  Path::load_q(q, p, sh, u, n, gq);
 
   WaveState st;
 #pragma unroll
@@ -365,46 +622,50 @@ __device__ __forceinline__ void fp8_piece(const DecodeParams& p, DecodeShared& s
   st.m = neg_inf();
   st.l = 0.f;
 
-  uint8_t* vst = sh.buf + wv * kVWaveBytes;
+  uint8_t* vst = sh.buf + wv * Path::kTile * Path::kVStride;
   for (int seg0 = 0; seg0 < rows; seg0 += kIdxSeg) {
     const int srows = imin(kIdxSeg, rows - seg0);
     __syncthreads();  // the previous segment's index reads are done
-    for (int i = tid; i < srows; i += kThreads) sh.idx[i] = p.kv_indices[kv_pos0 + seg0 + i];
+    stage_indices(sh.idx, p.kv_indices + kv_pos0 + seg0, srows);
     __syncthreads();
     const int32_t* sidx = sh.idx;
-    const int ntiles = (srows + kTile - 1) / kTile;
+    const int ntiles = (srows + Path::kTile - 1) / Path::kTile;
     const int m = ntiles > wv ? (ntiles - wv + kWaves - 1) / kWaves : 0;  // this wave's tiles
     if (m > 0) {
       // wave tile k is tile wv + 4k; even k live in bufA, odd k in bufB.
       uint4 bufA[18], bufB[18];
       TileIdx nextA, nextB;
       {
-        const TileIdx t0 = fetch_idx(sidx, srows, wv, n);
-        const TileIdx t1 = fetch_idx(sidx, srows, wv + kWaves, n);
-        issue_rows(bufA, p.kv, p.pool_entries, t0, gq);
-        issue_rows(bufB, p.kv, p.pool_entries, t1, gq);
-        nextA = fetch_idx(sidx, srows, wv + 2 * kWaves, n);
-        nextB = fetch_idx(sidx, srows, wv + 3 * kWaves, n);
+        const TileIdx t0 = Path::fetch_idx(sidx, srows, wv, n);
+        const TileIdx t1 = Path::fetch_idx(sidx, srows, wv + kWaves, n);
+        Path::issue_rows(bufA, p.kv, p.pool_entries, t0, gq);
+        Path::issue_rows(bufB, p.kv, p.pool_entries, t1, gq);
+        nextA = Path::fetch_idx(sidx, srows, wv + 2 * kWaves, n);
+        nextB = Path::fetch_idx(sidx, srows, wv + 3 * kWaves, n);
       }
       int k = 0;
       for (; k + 3 < m; k += 2) {
-        fp8_tile<true>(st, bufA, nextA, qlo, qhi, vst, p, sidx, srows, wv + kWaves * k, cs, n, gq);
-        fp8_tile<true>(st, bufB, nextB, qlo, qhi, vst, p, sidx, srows, wv + kWaves * (k + 1), cs, n,
-                       gq);
+        Path::template tile<true>(st, bufA, nextA, q, vst, p, sidx, srows, wv + kWaves * k, cs, n,
+                                  gq);
+        Path::template tile<true>(st, bufB, nextB, q, vst, p, sidx, srows, wv + kWaves * (k + 1),
+                                  cs, n, gq);
       }
       const int rem = m - k;
       if (rem == 3) {
-        fp8_tile<true>(st, bufA, nextA, qlo, qhi, vst, p, sidx, srows, wv + kWaves * k, cs, n, gq);
-        fp8_tile<false>(st, bufB, nextB, qlo, qhi, vst, p, sidx, srows, wv + kWaves * (k + 1), cs, n,
-                        gq);
-        fp8_tile<false>(st, bufA, nextA, qlo, qhi, vst, p, sidx, srows, wv + kWaves * (k + 2), cs, n,
-                        gq);
+        Path::template tile<true>(st, bufA, nextA, q, vst, p, sidx, srows, wv + kWaves * k, cs, n,
+                                  gq);
+        Path::template tile<false>(st, bufB, nextB, q, vst, p, sidx, srows, wv + kWaves * (k + 1),
+                                   cs, n, gq);
+        Path::template tile<false>(st, bufA, nextA, q, vst, p, sidx, srows, wv + kWaves * (k + 2),
+                                   cs, n, gq);
       } else if (rem == 2) {
-        fp8_tile<false>(st, bufA, nextA, qlo, qhi, vst, p, sidx, srows, wv + kWaves * k, cs, n, gq);
-        fp8_tile<false>(st, bufB, nextB, qlo, qhi, vst, p, sidx, srows, wv + kWaves * (k + 1), cs, n,
-                        gq);
+        Path::template tile<false>(st, bufA, nextA, q, vst, p, sidx, srows, wv + kWaves * k, cs, n,
+                                   gq);
+        Path::template tile<false>(st, bufB, nextB, q, vst, p, sidx, srows, wv + kWaves * (k + 1),
+                                   cs, n, gq);
       } else if (rem == 1) {
-        fp8_tile<false>(st, bufA, nextA, qlo, qhi, vst, p, sidx, srows, wv + kWaves * k, cs, n, gq);
+        Path::template tile<false>(st, bufA, nextA, q, vst, p, sidx, srows, wv + kWaves * k, cs, n,
+                                   gq);
       }
     }
   }
@@ -434,10 +695,10 @@ __device__ __forceinline__ void fp8_piece(const DecodeParams& p, DecodeShared& s
     fw[w] = (mw[w] == neg_inf()) ? 0.f : fast_exp2(mw[w] - M);
     L += sh.l[w][n] * fw[w];
   }
-  const float oscale = ks / (kPScale * L);
+  const float oscale = ks / (Path::kPScale * L);
 
-  // This wave writes O^T blocks [8wv, 8wv + 8): half = wv/2, t = 8(wv%2) + bb;
-  // element i of block bb is dim 256*half + 64*gq + 16*i + 8*(wv%2) + bb.
+  // This wave writes O^T blocks [8wv, 8wv + 8); element i of block 8wv + bb is
+  // dim first_dim + kDimStride*i + bb.
   float acc[4][8];
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) {
@@ -447,24 +708,24 @@ __device__ __forceinline__ void fp8_piece(const DecodeParams& p, DecodeShared& s
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][bb] = a[i] * oscale;
   }
-  const int dim0 = 256 * (wv >> 1) + 64 * gq + 8 * (wv & 1);
+  const int dim0 = Path::first_dim(wv, gq);
   const float lse_val = (M + fast_log2(L)) * kLn2;
   if (slot < 0) {
     const int64_t orow = (int64_t)u.t * p.num_heads + u.g * kGroup + n;
     uint16_t* dst = p.o + orow * kLatent + dim0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) store_bf16x8(dst + 16 * i, acc[i]);
+    for (int i = 0; i < 4; ++i) store_bf16x8(dst + Path::kDimStride * i, acc[i]);
     if (p.lse != nullptr && wv == 0 && gq == 0) p.lse[orow] = lse_val;
     return;
   }
   float* dst = p.part_o + ((int64_t)slot * kGroup + n) * kLatent + dim0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    *(float4*)(dst + 16 * i) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-    *(float4*)(dst + 16 * i + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+    float* d = dst + Path::kDimStride * i;
+    *(float4*)d = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    *(float4*)(d + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
   }
   if (wv == 0 && gq == 0) p.part_lse[(int64_t)slot * kGroup + n] = lse_val;
-
 }
 
 // Query rows that see no entry get o = 0, lse = -inf; the block owning token t
@@ -480,9 +741,9 @@ __device__ void zero_token(const DecodeParams& p, int t) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mla_decode_fp8_kernel(const DecodeParams p) {
-  __shared__ DecodeShared sh;
+// One worker: locate its share of the KV stream and run its pieces.
+template <class Path>
+__device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShared& sh) {
   const int G = p.num_heads / kGroup;
 
   // Pass 1 over requests: stream length W; zero this block's empty tokens.
@@ -522,7 +783,7 @@ void mla_decode_fp8_kernel(const DecodeParams p) {
     UnitRef u;
     u.t = c.r.q_base + c.j;
     u.g = c.g;
-    fp8_piece(p, sh, u, c.r.kv_base + c.k, len, slot, cs, ks);
+    decode_piece<Path>(p, sh, u, c.r.kv_base + c.k, len, slot, cs, ks);
     if (c.k == 0 && threadIdx.x == 0) {
       // The worker holding a unit's first piece describes it for the combine
       // pass: a split unit is merged from this worker's slot and slot 2w' of
@@ -540,6 +801,18 @@ void mla_decode_fp8_kernel(const DecodeParams p) {
         break;
     }
   }
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_fp8_kernel(const DecodeParams p) {
+  __shared__ DecodeShared sh;
+  decode_worker<Fp8Path>(p, sh);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_bf16_kernel(const DecodeParams p) {
+  __shared__ DecodeShared sh;
+  decode_worker<Bf16Path>(p, sh);
 }
 
 // ---------------------------------------------------------------- split combine
@@ -669,8 +942,12 @@ __global__ __launch_bounds__(kThreads) void mla_merge_kernel(const void* o_parts
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, hipStream_t stream) {
-  if (kv_dtype != 0) return hipErrorNotSupported;
-  hipLaunchKernelGGL(mla_decode_fp8_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream, p);
+  if (kv_dtype == 0)
+    hipLaunchKernelGGL(mla_decode_fp8_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream, p);
+  else if (kv_dtype == 1)
+    hipLaunchKernelGGL(mla_decode_bf16_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream, p);
+  else
+    return hipErrorNotSupported;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned units = (unsigned)(p.num_tokens * (p.num_heads / kGroup));
