@@ -145,7 +145,8 @@ size_t mla_decode_workspace_bytes_ex(int batch, int num_q_tokens, int num_heads,
  *  o_parts    (num_parts, num_q_tokens, num_heads, 512) of parts_dtype
  *             (BF16 or FP32), each shard's normalised output.
  *  lse_parts  (num_parts, num_q_tokens, num_heads) fp32, each shard's lse;
- *             -inf marks an empty shard, whose o_parts row is not read.
+ *             -inf marks an empty shard: its o_parts row is read but given
+ *             weight 0 by a select, so its contents (even NaN) never matter.
  *  o          (num_q_tokens, num_heads, 512) bf16, written.
  *  lse        (num_q_tokens, num_heads) fp32, written if not NULL.
  * For each row: M = max_s lse_s, L = M + ln sum_s exp(lse_s - M),

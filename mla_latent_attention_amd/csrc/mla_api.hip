@@ -180,13 +180,28 @@ int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int ba
   if (W == 0) return 0;
   const int nw = effective_workers(W, num_workers);
   int64_t count = 0;
-  for (int w = 0; w < nw; ++w) {
-    const int64_t p0 = worker_begin(w, W, nw), p1 = worker_begin(w + 1, W, nw);
-    if (p0 >= p1) continue;
+  // Cursor at stream position x (0 <= x < W), as the kernel's locate does.
+  auto locate = [&](int64_t x, Cursor& c) {
     int b = 0;
-    while (!(cum[b] <= p0 && p0 < cum[b + 1])) ++b;
-    Cursor c;
-    cursor_in_request(c, b, load_req(qo_indptr, kv_indptr, b, kv_cap, T), p0 - cum[b], G);
+    while (!(cum[b] <= x && x < cum[b + 1])) ++b;
+    cursor_in_request(c, b, load_req(qo_indptr, kv_indptr, b, kv_cap, T), x - cum[b], G);
+  };
+  for (int w = 0; w < nw; ++w) {
+    const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
+    Cursor c, c1;
+    locate(x0, c);
+    int64_t p1 = W;
+    if (x1 < W) {
+      locate(x1, c1);
+      p1 = snap_at(x1, c1);
+    }
+    const int64_t p0 = snap_at(x0, c);
+    if (p0 >= p1) continue;
+    if (p0 < x0) {
+      c.k = 0;
+    } else if (p0 > x0) {
+      if (!cursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G)) continue;
+    }
     int64_t pos = p0;
     int piece = 0;
     while (pos < p1) {

@@ -90,6 +90,27 @@ __device__ __forceinline__ void transpose4x4(u32 a, u32 b, u32 c, u32 d, u32& o0
 
 // ---------------------------------------------------------------- block helpers
 
+// Block-uniform values read from memory arrive in vector registers; moving
+// them to scalar registers keeps the planner state (live across the whole
+// tile loop) out of the vector register budget of the loop.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void uniformize(Cursor& c) {
+  c.b = uniform(c.b);
+  c.j = uniform(c.j);
+  c.g = uniform(c.g);
+  c.k = uniform(c.k);
+  c.r.kv_base = uniform(c.r.kv_base);
+  c.r.n = uniform(c.r.n);
+  c.r.q_base = uniform(c.r.q_base);
+  c.r.qlen = uniform(c.r.qlen);
+}
+
 __device__ int64_t block_sum_i64(int64_t v, int64_t* red) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   const int wv = threadIdx.x >> 6;
@@ -121,10 +142,12 @@ __device__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) 
   return before + x - v;
 }
 
-// Request containing stream position pos (and its stream start); false if none.
-__device__ bool plan_locate(const DecodeParams& p, int G, int64_t pos, int64_t* red, int* s_b,
-                            int64_t* s_cum) {
-  if (threadIdx.x == 0) *s_b = -1;
+// Requests containing stream positions x[0] and x[1] (a negative position is
+// not looked up): sb[i] = request (-1 if not found, -2 if not looked up) and
+// scum[i] = that request's first stream position.
+__device__ void plan_locate2(const DecodeParams& p, int G, const int64_t (&x)[2], int64_t* red,
+                             int* sb, int64_t* scum) {
+  if (threadIdx.x < 2) sb[threadIdx.x] = x[threadIdx.x] < 0 ? -2 : -1;
   int64_t carry = 0;
   for (int b0 = 0; b0 < p.batch; b0 += kThreads) {
     const int b = b0 + threadIdx.x;
@@ -135,16 +158,18 @@ __device__ bool plan_locate(const DecodeParams& p, int G, int64_t pos, int64_t* 
     }
     int64_t total;
     const int64_t cum = carry + block_excl_scan_i64(R, red, total);
-    if (R > 0 && pos >= cum && pos < cum + R) {
-      *s_b = b;
-      *s_cum = cum;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (R > 0 && x[i] >= cum && x[i] < cum + R) {
+        sb[i] = b;
+        scum[i] = cum;
+      }
     }
     carry += total;
     __syncthreads();
-    if (*s_b >= 0) break;
+    if (sb[0] != -1 && sb[1] != -1) break;
   }
   __syncthreads();
-  return *s_b >= 0;
 }
 
 // ---------------------------------------------------------------- tile loop
@@ -155,8 +180,8 @@ struct alignas(16) DecodeShared {
   int64_t red[kWaves];
   float m[kWaves][16];
   float l[kWaves][16];
-  int b;
-  int64_t cum;
+  int pb[2];
+  int64_t pcum[2];
 };
 
 // The unit (query token, head group) a piece belongs to.
@@ -214,6 +239,50 @@ __device__ __forceinline__ void softmax_update(WaveState& st, float (&x)[N]) {
   st.l += psum;
 }
 
+// Copies a head group's 16 q rows (kLoads 16-byte loads per lane, row stride
+// kRowBytes) from q0 into LDS at dst in lane order: entry 64c + l holds row
+// l%16, bytes [64c + 16*(l/16), +16).  All loads are issued before the first
+// store (the tail rereads the last entry).  Returns this lane's entry 0.
+//
+// The first kIdxBatch * kThreads kv_indices of the piece (n of them, n >= 1)
+// are copied to idx_dst in the same pass, so the piece's start costs one
+// memory round trip; the caller copies the rest.
+constexpr int kIdxBatch = 8;
+__device__ __forceinline__ void stage_first_indices(int32_t* idx_dst, const int32_t* idx_src,
+                                                    int n) {
+  int32_t iv[kIdxBatch];
+#pragma unroll
+  for (int j = 0; j < kIdxBatch; ++j) iv[j] = idx_src[imin(j * kThreads + (int)threadIdx.x, n - 1)];
+#pragma unroll
+  for (int j = 0; j < kIdxBatch; ++j) idx_dst[imin(j * kThreads + (int)threadIdx.x, n - 1)] = iv[j];
+}
+
+template <int kLoads, int kRowBytes>
+__device__ __forceinline__ const uint4* stage_q(uint8_t* dst_bytes, const uint8_t* q0,
+                                                int32_t* idx_dst, const int32_t* idx_src, int n) {
+  // Thread (wave wv, lane l) copies entries 64c + l for c = wv, wv + 4, ...:
+  // one per-lane base address plus a wave-uniform offset per load.  Waves
+  // past the last c repeat it (the same value to the same entry).
+  uint4* dst = (uint4*)dst_bytes;
+  constexpr int kPer = (kLoads + kWaves - 1) / kWaves;
+  const int lane = threadIdx.x & 63, wv = uniform((int)(threadIdx.x >> 6));
+  const uint8_t* src = q0 + (lane & 15) * kRowBytes + 16 * (lane >> 4);
+  uint4 v[kPer];
+  int32_t iv[kIdxBatch];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) v[k] = *(const uint4*)(src + 64 * imin(kWaves * k + wv, kLoads - 1));
+#pragma unroll
+  for (int j = 0; j < kIdxBatch; ++j) iv[j] = idx_src[imin(j * kThreads + (int)threadIdx.x, n - 1)];
+  // Stores are unconditional too (past-the-end lanes rewrite the last entry
+  // with the value its owner writes): a conditional store would let the
+  // compiler sink each load into its branch and serialise the round trips.
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) dst[64 * imin(kWaves * k + wv, kLoads - 1) + lane] = v[k];
+#pragma unroll
+  for (int j = 0; j < kIdxBatch; ++j) idx_dst[imin(j * kThreads + (int)threadIdx.x, n - 1)] = iv[j];
+  return dst + lane;
+}
+
 // ---- fp8 e4m3 path: 32-row tiles of 576-byte rows.
 //
 // Lane l gathers tile rows (l%16) and (16 + l%16), bytes [64c + 16*(l/16), +16)
@@ -262,12 +331,13 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
   v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < 9; ++c) {
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].x, B[c].y), q.lo[c], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].x, B[9 + c].y), q.lo[c], s1, 0,
-                                                    0, 0);
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].z, B[c].w), q.hi[c], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].z, B[9 + c].w), q.hi[c], s1, 0,
-                                                    0, 0);
+    const long qlo = q.lo[c], qhi = q.hi[c];
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].x, B[c].y), qlo, s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].x, B[9 + c].y), qlo, s1, 0, 0,
+                                                    0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].z, B[c].w), qhi, s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].z, B[9 + c].w), qhi, s1, 0, 0,
+                                                    0);
   }
 
   // Stage the latent 512 bytes of both 16-row blocks in this wave's LDS tile.
@@ -355,16 +425,22 @@ struct Fp8Path {
   static constexpr int kVStride = kFp8VStride;
   static constexpr float kPScale = 128.0f;
   using Q = Fp8Q;
-  // Q stays in registers: lane l holds row l%16 of the unit's head group.
-  static __device__ __forceinline__ void load_q(Q& q, const DecodeParams& p, DecodeShared&,
-                                                const UnitRef& u, int n, int gq) {
-    const uint8_t* qrow =
-        p.q + ((int64_t)u.t * p.num_heads + u.g * kGroup + n) * kRowBytes + 16 * gq;
+  // Q stays in registers (lane l: row l%16 of the unit's head group); its
+  // loads go out with the piece's first index batch.
+  static __device__ __forceinline__ void load_q(Q& q, const DecodeParams& p, DecodeShared& sh,
+                                                const UnitRef& u, const int32_t* idx, int n) {
+    const int lane = threadIdx.x & 63;
+    const uint8_t* qrow = p.q +
+                          ((int64_t)u.t * p.num_heads + u.g * kGroup + (lane & 15)) * kRowBytes +
+                          16 * (lane >> 4);
+    uint4 x[9];
+#pragma unroll
+    for (int c = 0; c < 9; ++c) x[c] = *(const uint4*)(qrow + 64 * c);
+    stage_first_indices(sh.idx, idx, n);
 #pragma unroll
     for (int c = 0; c < 9; ++c) {
-      const uint4 x = *(const uint4*)(qrow + 64 * c);
-      q.lo[c] = as_long(x.x, x.y);
-      q.hi[c] = as_long(x.z, x.w);
+      q.lo[c] = as_long(x[c].x, x[c].y);
+      q.hi[c] = as_long(x[c].z, x[c].w);
     }
   }
   static __device__ __forceinline__ TileIdx fetch_idx(const int32_t* sidx, int rows, int tile,
@@ -526,23 +602,10 @@ struct Bf16Path {
   // Cooperative copy of the unit's 16 q rows into LDS; the caller synchronises
   // the block before the first tile reads it.
   static __device__ __forceinline__ void load_q(Q& q, const DecodeParams& p, DecodeShared& sh,
-                                                const UnitRef& u, int, int) {
-    uint4* dst = (uint4*)(sh.buf + kBf16QOffset);
-    const uint8_t* q0 = p.q + ((int64_t)u.t * p.num_heads + u.g * kGroup) * kRowBytes;
-    constexpr int kEntries = 18 * 64, kPer = (kEntries + kThreads - 1) / kThreads;
-    uint4 v[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {  // all loads first; the tail rereads the last entry
-      const int e = imin(k * kThreads + (int)threadIdx.x, kEntries - 1);
-      const int c = e >> 6, l = e & 63;
-      v[k] = *(const uint4*)(q0 + (l & 15) * kRowBytes + 64 * c + 16 * (l >> 4));
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int e = k * kThreads + threadIdx.x;
-      if (e < kEntries) dst[e] = v[k];
-    }
-    q.lds = dst + (threadIdx.x & 63);
+                                                const UnitRef& u, const int32_t* idx, int n) {
+    q.lds = stage_q<18, kRowBytes>(sh.buf + kBf16QOffset,
+                                   p.q + ((int64_t)u.t * p.num_heads + u.g * kGroup) * kRowBytes,
+                                   sh.idx, idx, n);
   }
   static __device__ __forceinline__ TileIdx fetch_idx(const int32_t* sidx, int rows, int tile,
                                                       int n) {
@@ -579,20 +642,17 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&a)[8])
   *(uint4*)dst = pk;
 }
 
-// Copies n (>= 1) indices to LDS.  Each thread issues kIdxBatch loads before
-// its first store (past-the-end positions reload the last index), so a
-// segment costs ceil(n / 2048) memory round trips instead of one per 256.
-constexpr int kIdxBatch = 8;
-__device__ __forceinline__ void stage_indices(int32_t* dst, const int32_t* src, int n) {
-  for (int i0 = 0; i0 < n; i0 += kThreads * kIdxBatch) {
+// Copies indices [from, n) of src (n >= 1) to the same positions of dst.
+// Each thread issues kIdxBatch loads before its first store (past-the-end
+// positions reload the last index), so a segment costs one memory round trip
+// per 2048 indices instead of one per 256.
+__device__ __forceinline__ void stage_indices(int32_t* dst, const int32_t* src, int from, int n) {
+  for (int i0 = from; i0 < n; i0 += kThreads * kIdxBatch) {
     int32_t v[kIdxBatch];
 #pragma unroll
     for (int j = 0; j < kIdxBatch; ++j) v[j] = src[imin(i0 + j * kThreads + (int)threadIdx.x, n - 1)];
 #pragma unroll
-    for (int j = 0; j < kIdxBatch; ++j) {
-      const int i = i0 + j * kThreads + threadIdx.x;
-      if (i < n) dst[i] = v[j];
-    }
+    for (int j = 0; j < kIdxBatch; ++j) dst[imin(i0 + j * kThreads + (int)threadIdx.x, n - 1)] = v[j];
   }
 }
 
@@ -614,7 +674,7 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
   __syncthreads();  // the previous piece is done with the LDS buffer
 
   typename Path::Q q;
-  Path::load_q(q, p, sh, u, n, gq);
+  Path::load_q(q, p, sh, u, p.kv_indices + kv_pos0, imin(rows, kIdxSeg));
 
   WaveState st;
 #pragma unroll
@@ -625,8 +685,10 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
   uint8_t* vst = sh.buf + wv * Path::kTile * Path::kVStride;
   for (int seg0 = 0; seg0 < rows; seg0 += kIdxSeg) {
     const int srows = imin(kIdxSeg, rows - seg0);
-    __syncthreads();  // the previous segment's index reads are done
-    stage_indices(sh.idx, p.kv_indices + kv_pos0 + seg0, srows);
+    if (seg0 > 0) __syncthreads();  // the previous segment's index reads are done
+    // The first kIdxBatch * kThreads indices of segment 0 came with Q.
+    stage_indices(sh.idx, p.kv_indices + kv_pos0 + seg0, seg0 == 0 ? kIdxBatch * kThreads : 0,
+                  srows);
     __syncthreads();
     const int32_t* sidx = sh.idx;
     const int ntiles = (srows + Path::kTile - 1) / Path::kTile;
@@ -755,18 +817,39 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
     for (int j = 0; j < nempty; ++j)
       if ((r.q_base + j) % (int)gridDim.x == (int)blockIdx.x) zero_token(p, r.q_base + j);
   }
-  const int64_t W = block_sum_i64(acc, sh.red);
+  const int64_t W = uniform(block_sum_i64(acc, sh.red));
   const int w = blockIdx.x;
   if (W == 0) return;
   const int nw = effective_workers(W, p.num_workers);
-  const int64_t p0 = worker_begin(w, W, nw), p1 = worker_begin(w + 1, W, nw);
-  if (w >= nw || p0 >= p1 || !plan_locate(p, G, p0, sh.red, &sh.b, &sh.cum)) return;
-
+  if (w >= nw) return;
+  // This worker's range [p0, p1): the equal-share boundaries, each snapped to
+  // a unit boundary within kSnapRows (0 and W are boundaries already).
+  const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
+  const int64_t xs[2] = {x0, x1 < W ? x1 : -1};
+  plan_locate2(p, G, xs, sh.red, sh.pb, sh.pcum);
+  const int b0 = uniform(sh.pb[0]), b1 = uniform(sh.pb[1]);
+  if (b0 < 0 || b1 == -1) return;  // not reached with consistent indptr
   Cursor c;
-  {
-    const int b = sh.b;
-    const Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
-    cursor_in_request(c, b, r, p0 - sh.cum, G);
+  cursor_in_request(c, b0, load_req(p.qo_indptr, p.kv_indptr, b0, p.kv_indices_len, p.num_tokens),
+                    x0 - uniform(sh.pcum[0]), G);
+  uniformize(c);
+  int64_t p1 = W;
+  if (x1 < W) {
+    Cursor c1;
+    cursor_in_request(c1, b1, load_req(p.qo_indptr, p.kv_indptr, b1, p.kv_indices_len, p.num_tokens),
+                      x1 - uniform(sh.pcum[1]), G);
+    uniformize(c1);
+    p1 = snap_at(x1, c1);
+  }
+  const int64_t p0 = snap_at(x0, c);
+  if (p0 >= p1) return;
+  if (p0 < x0) {
+    c.k = 0;  // moved back to the start of its unit
+  } else if (p0 > x0) {  // moved forward past the end of its unit
+    if (!cursor_next_unit(c, p.qo_indptr, p.kv_indptr, p.batch, p.kv_indices_len, p.num_tokens,
+                          G))
+      return;
+    uniformize(c);
   }
   const float qs = p.q_scale ? *p.q_scale : 1.0f;
   const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
@@ -783,15 +866,22 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
     UnitRef u;
     u.t = c.r.q_base + c.j;
     u.g = c.g;
-    decode_piece<Path>(p, sh, u, c.r.kv_base + c.k, len, slot, cs, ks);
-    if (c.k == 0 && threadIdx.x == 0) {
-      // The worker holding a unit's first piece describes it for the combine
-      // pass: a split unit is merged from this worker's slot and slot 2w' of
-      // every later worker w' up to the last one.
-      p.desc[(int64_t)u.t * G + u.g] =
-          complete ? make_int4(0, 0, 0, 0)
-                   : make_int4(w, worker_of(pos + v - 1, W, nw), slot, 1);
+    if (threadIdx.x == 0) {
+      // Split-unit descriptor for the combine pass {first worker, last worker,
+      // slot of the first worker, split?}: the worker holding the unit's first
+      // piece writes fields 0, 2 and 3, the one holding its last piece field 1.
+      // The unit is merged from the first worker's slot and slot 2w' of every
+      // later worker w' up to the last.  (Written before the piece runs, so
+      // none of this stays live across its tile loop.)
+      int* d = (int*)(p.desc + ((int64_t)u.t * G + u.g));
+      if (c.k == 0) {
+        d[0] = w;
+        d[2] = slot;
+        d[3] = complete ? 0 : 1;
+      }
+      if (!complete && c.k + len == v) d[1] = w;
     }
+    decode_piece<Path>(p, sh, u, c.r.kv_base + c.k, len, slot, cs, ks);
     pos += len;
     c.k += len;
     ++piece;
@@ -799,6 +889,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
       if (!cursor_next_unit(c, p.qo_indptr, p.kv_indptr, p.batch, p.kv_indices_len, p.num_tokens,
                             G))
         break;
+      uniformize(c);
     }
   }
 }
@@ -883,7 +974,31 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const Deco
 
 // ---------------------------------------------------------------- shard merge
 
-// One wave per (token, head) row, 8 dims per lane.
+// One wave per (token, head) row, 8 dims per lane.  Shards are taken in
+// batches of kMergeBatch: all lse loads of a batch, then all row loads, are in
+// flight before any is used (indices past S reload shard S-1 with weight 0),
+// with an online rescale across batches.  An empty shard (lse = -inf) gets
+// weight 0 through a select, so whatever its row holds (even NaN) is ignored.
+constexpr int kMergeBatch = 8;
+
+template <bool kFp32Parts>
+__device__ __forceinline__ void load_part_row(const void* o_parts, int64_t off, float (&x)[8]) {
+  if constexpr (kFp32Parts) {
+    const float* src = (const float*)o_parts + off;
+    const float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else {
+    const uint4 v = *(const uint4*)((const uint16_t*)o_parts + off);
+    const u32 wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(wds[k] << 16);
+      x[2 * k + 1] = __uint_as_float(wds[k] & 0xFFFF0000u);
+    }
+  }
+}
+
 template <bool kFp32Parts>
 __global__ __launch_bounds__(kThreads) void mla_merge_kernel(const void* o_parts,
                                                              const float* lse_parts, int S,
@@ -892,42 +1007,43 @@ __global__ __launch_bounds__(kThreads) void mla_merge_kernel(const void* o_parts
   const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
-  float M = neg_inf();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lse_parts[(int64_t)s * rows + row]);
+  float M = neg_inf(), sum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+    float ls[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      ls[j] = lse_parts[(int64_t)imin(s0 + j, S - 1) * rows + row];
+    float x[kMergeBatch][8];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      load_part_row<kFp32Parts>(o_parts, ((int64_t)imin(s0 + j, S - 1) * rows + row) * kLatent +
+                                             8 * lane, x[j]);
+    __builtin_amdgcn_sched_barrier(0);
+    float bm = M;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (s0 + j < S) bm = fmaxf(bm, ls[j]);
+    if (bm == neg_inf()) continue;  // every shard so far is empty
+    const float alpha = (M == neg_inf()) ? 0.f : fast_exp2((M - bm) * kLog2e);
+    sum *= alpha;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[d] *= alpha;
+    M = bm;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const bool live = (s0 + j < S) && ls[j] != neg_inf();
+      const float wt = live ? fast_exp2((ls[j] - M) * kLog2e) : 0.f;
+      sum += wt;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[d] += live ? wt * x[j][d] : 0.f;
+    }
+  }
   uint16_t* dst = o + row * kLatent + 8 * lane;
   if (M == neg_inf()) {
     *(uint4*)dst = make_uint4(0, 0, 0, 0);
     if (lse != nullptr && lane == 0) lse[row] = neg_inf();
     return;
-  }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float sum = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float ls = lse_parts[(int64_t)s * rows + row];
-    if (ls == neg_inf()) continue;  // empty shard: its o row is not read
-    const float wt = fast_exp2((ls - M) * kLog2e);
-    sum += wt;
-    const int64_t off = ((int64_t)s * rows + row) * kLatent + 8 * lane;
-    if constexpr (kFp32Parts) {
-      const float* src = (const float*)o_parts + off;
-      const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
-      acc[0] += wt * x0.x;
-      acc[1] += wt * x0.y;
-      acc[2] += wt * x0.z;
-      acc[3] += wt * x0.w;
-      acc[4] += wt * x1.x;
-      acc[5] += wt * x1.y;
-      acc[6] += wt * x1.z;
-      acc[7] += wt * x1.w;
-    } else {
-      const uint4 x = *(const uint4*)((const uint16_t*)o_parts + off);
-      const u32 wds[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[2 * k] += wt * __uint_as_float(wds[k] << 16);
-        acc[2 * k + 1] += wt * __uint_as_float(wds[k] & 0xFFFF0000u);
-      }
-    }
   }
   const float inv = 1.0f / sum;
   uint4 pk;

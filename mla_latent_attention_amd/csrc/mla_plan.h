@@ -16,6 +16,10 @@
 //     [floor(w*W/NW), floor((w+1)*W/NW)), so every worker gets the same number
 //     of KV rows (+-1) whatever the length mix; the range may cross unit and
 //     request boundaries.  The part of a unit inside one worker is a "piece".
+//   * A worker boundary that falls within kSnapRows rows of a unit boundary
+//     is moved onto it, so no worker pays the fixed cost of a piece of a few
+//     rows (with equal shares, unit boundaries drift a few rows past worker
+//     boundaries).  Boundaries stay >= 256 rows apart, so they never cross.
 //   * Only a worker's first and last piece can be partial: a partial first
 //     piece writes its (o, lse) to workspace slot 2w, a partial last piece to
 //     slot 2w+1.  Complete pieces write o (and lse) directly.
@@ -60,10 +64,19 @@ MLA_HD int effective_workers(int64_t W, int nw) {
   return (int)lmin(need, (int64_t)nw);
 }
 
+// Unsnapped start of worker w's range.
 MLA_HD int64_t worker_begin(int w, int64_t W, int nw) { return (int64_t)w * W / nw; }
 
-// Worker whose range contains stream position p (0 <= p < W).
-MLA_HD int worker_of(int64_t p, int64_t W, int nw) { return (int)(((p + 1) * nw - 1) / W); }
+constexpr int kSnapRows = 64;
+
+// Snapped position for stream position x lying k rows into a unit of length
+// v: the nearer unit boundary if it is within kSnapRows rows, else x.
+MLA_HD int64_t snap_position(int64_t x, int k, int v) {
+  if (k == 0) return x;
+  if (k <= kSnapRows && k <= v - k) return x - k;
+  if (v - k <= kSnapRows) return x + (v - k);
+  return x;
+}
 
 // One request's bounds, clamped so that no later read can leave its buffer.
 struct Req {
@@ -115,6 +128,11 @@ MLA_HD void cursor_in_request(Cursor& c, int b, const Req& r, int64_t off, int G
   c.j = r.qlen;  // not reached for a valid offset
   c.g = 0;
   c.k = 0;
+}
+
+// Snap stream position x whose cursor is c (set by cursor_in_request).
+MLA_HD int64_t snap_at(int64_t x, const Cursor& c) {
+  return snap_position(x, c.k, visible(c.r.n, c.r.qlen, c.j));
 }
 
 // Move to the start of the next non-empty unit.  Returns false past the end.

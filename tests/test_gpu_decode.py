@@ -312,6 +312,24 @@ def test_merge_partials_full_size(parts_dtype):
     assert_gate(m, f"merge {parts_dtype}")
 
 
+@pytest.mark.parametrize("parts_dtype", ["fp32", "bf16"])
+def test_merge_ignores_empty_shard_rows(parts_dtype):
+    """Rows of shards marked empty (lse = -inf) may hold anything, NaN included."""
+    o_p, lse_p = workloads.merge_shards(num_parts=11, num_tokens=5, num_heads=32,
+                                        parts_dtype=parts_dtype, seed=77, device=DEV)
+    o_ref_in = o_p.clone()
+    o_p[torch.isneginf(lse_p)] = float("nan")
+    o, lse = mla.merge_partials(o_p, lse_p)
+    o2, lse2 = mla.merge_partials(o_ref_in, lse_p)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    ref_o, ref_lse = omla.merge_partials(
+        oio.codes(o_ref_in).astype(np.float64) if parts_dtype == "fp32" else _bf16_to_f64(o_ref_in),
+        lse_p.cpu().numpy().astype(np.float64))
+    assert_gate(metrics(o, ref_o, lse, ref_lse), f"merge empty rows {parts_dtype}")
+
+
 def _bf16_to_f64(t):
     from oracle import codecs
     return codecs.decode_bf16(oio.codes(t))

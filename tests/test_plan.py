@@ -13,6 +13,7 @@ import workloads
 from mla_latent_attention_amd import plan_host
 
 MIN_WORKER_ROWS = 512
+SNAP_ROWS = 64
 
 
 def visible(n, qlen, j):
@@ -32,6 +33,28 @@ def units(qo, kv, G):
     return out, pos
 
 
+def snapped_bounds(us, W, nw):
+    """Worker boundaries: w*W//nw, moved onto a unit boundary within SNAP_ROWS
+    (the nearer one; back on a tie)."""
+    starts = [st for _, _, v, st in us if v > 0]
+    lens = [v for _, _, v, _ in us if v > 0]
+    bounds = [0]
+    for w in range(1, nw):
+        x = w * W // nw
+        i = int(np.searchsorted(starts, x, side="right")) - 1
+        k, v = x - starts[i], lens[i]
+        if k == 0:
+            bounds.append(x)
+        elif k <= SNAP_ROWS and k <= v - k:
+            bounds.append(x - k)
+        elif v - k <= SNAP_ROWS:
+            bounds.append(x + v - k)
+        else:
+            bounds.append(x)
+    bounds.append(W)
+    return bounds
+
+
 def check_plan(qo, kv, H, nw_req):
     G = H // 16
     us, W = units(qo, kv, G)
@@ -40,6 +63,8 @@ def check_plan(qo, kv, H, nw_req):
         assert len(pieces) == 0
         return pieces
     nw = min(nw_req, max(1, -(-W // MIN_WORKER_ROWS)))
+    S = snapped_bounds(us, W, nw)
+    assert all(a < b for a, b in zip(S, S[1:]))
     cover = {}
     for w, t, g, kb, ke, ul, slot, comp in pieces:
         assert 0 <= kb < ke <= ul
@@ -59,8 +84,8 @@ def check_plan(qo, kv, H, nw_req):
             assert all(s[4] == 0 for s in segs)
             # the combine's rule: worker range [wlo, whi]; slot 2w+1 only for a
             # first worker that started before the unit
-            begin = lambda w: w * W // nw  # noqa: E731
-            owner = lambda p: ((p + 1) * nw - 1) // W  # noqa: E731
+            begin = lambda w: S[w]  # noqa: E731
+            owner = lambda p: int(np.searchsorted(S, p, side="right")) - 1  # noqa: E731
             wlo, whi = owner(start), owner(start + v - 1)
             want = {(2 * w + 1) if (w == wlo and begin(w) < start) else 2 * w for w in range(wlo, whi + 1)}
             assert {s[3] for s in segs} == want
@@ -69,8 +94,15 @@ def check_plan(qo, kv, H, nw_req):
     per_worker = np.zeros(nw, dtype=np.int64)
     for w, t, g, kb, ke, *_ in pieces:
         per_worker[w] += ke - kb
-    shares = np.array([(w + 1) * W // nw - w * W // nw for w in range(nw)])
+    shares = np.array([S[w + 1] - S[w] for w in range(nw)])
     assert np.array_equal(per_worker, shares)
+    assert np.all(np.abs(shares - W / nw) <= 2 * SNAP_ROWS + 1)
+    # no piece starts or ends within SNAP_ROWS of an interior unit boundary
+    for w, t, g, kb, ke, ul, *_ in pieces:
+        if kb > 0:
+            assert kb > SNAP_ROWS and ul - kb > SNAP_ROWS
+        if ke < ul:
+            assert ke > SNAP_ROWS and ul - ke > SNAP_ROWS
     # partial pieces only at a worker's ends; slots unique
     slots = [p[6] for p in pieces if p[6] >= 0]
     assert len(slots) == len(set(slots))
@@ -94,6 +126,8 @@ def test_headline_batch(nw):
     if nw == 256:
         w_rows = sum(L) // 256
         assert abs(w_rows - 4276) <= 1
+        # 16 workers per request, one piece each: no worker pays for a sliver
+        assert len(p) == 256 and sorted(p[:, 0].tolist()) == list(range(256))
 
 
 def test_c24_and_mixed_lengths():
