@@ -28,6 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode µs/call + HBM GB/s (% of 8 TB/s), bs16 kv≈68K fp8, 1 GPU"
+CONFIG_NAMES = ("c24_batch24_fp8", "mixed_batch64_fp8", "mixed_batch64_bf16",
+                "dcp_share_96heads_qlen4_fp8", "merge_8_shards_fp32", "merge_8_shards_bf16")
 PEAK_GBS = 8000.0
 
 
@@ -43,6 +45,8 @@ def parse():
     ap.add_argument("--no-variants", action="store_true", help="skip the extra timing lines")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other configurations (c24, mixed fp8/bf16, DCP share, merge)")
+    ap.add_argument("--only", default=None, choices=sorted(CONFIG_NAMES),
+                    help="time just this other configuration and print its line (for profiling)")
     ap.add_argument("--cpu-requests", type=int, default=2, help="requests in the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain fp32 copy-like kernel (out = -in) over BYTES, "
@@ -113,9 +117,9 @@ def extra_layers(base, n_layers, kv_std, seed0, dev):
     return layers
 
 
-def config_lines(mla, dev, steps, warmup, n_layers=4):
+def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
     """Time the other decode configurations and the shard merge, each cycling
-    n_layers independent inputs under graph replay."""
+    n_layers independent inputs under graph replay (only: just that one)."""
     import torch
 
     import workloads
@@ -129,6 +133,8 @@ def config_lines(mla, dev, steps, warmup, n_layers=4):
         ("dcp_share_96heads_qlen4_fp8", lambda: workloads.dcp_share(dev), 0.5),
     ]
     for name, make, std in cases:
+        if only is not None and name != only:
+            continue
         base = make()
         layers = extra_layers(base, n_layers, std, 7000, dev)
         T, H = base.num_tokens, base.num_heads
@@ -154,6 +160,8 @@ def config_lines(mla, dev, steps, warmup, n_layers=4):
         del layers, base, o, lse, ws
         torch.cuda.empty_cache()
     for parts_dtype in ("fp32", "bf16"):
+        if only is not None and only != f"merge_8_shards_{parts_dtype}":
+            continue
         sets = [workloads.merge_shards(parts_dtype=parts_dtype, seed=5100 + k, device=dev)
                 for k in range(8)]
         o = torch.empty((32, 96, 512), dtype=torch.bfloat16, device=dev)
@@ -304,6 +312,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.only:
+        line = config_lines(mla, dev, max(64, a.steps // 4), 8, only=a.only)
+        print(json.dumps({"config_only": a.only, **line[a.only]}), flush=True)
+        return
     layers = make_layers(a.layers, a.variant, dev)
     w0 = layers[0]
     nbytes = accounting.workload_bytes(w0)

@@ -70,10 +70,19 @@ typedef enum {
 
 /*
  * Workspace bytes mla_decode needs on the current device for this call shape.
- * The workspace holds fp32 partial answers of the KV splits (at most two per
- * worker workgroup) and one 16-byte split descriptor per worker; its size
- * depends only on the device's compute-unit count and the arguments below, not
- * on KV lengths.  Returns 0 for invalid shapes.
+ * The workspace holds fp32 partial answers of the KV splits and one 16-byte
+ * split descriptor per (query token, head group); its size depends only on
+ * the device's compute-unit count and the arguments below, not on KV lengths
+ * or the storage type.  Returns 0 for invalid shapes.
+ *
+ * Two kernels serve mla_decode.  The standard one gives each worker
+ * workgroup a contiguous range of (token, head group) rows, at most two of
+ * them partial (two 16x512 fp32 partial slots per worker), one worker per
+ * compute unit.  When num_heads / 16 * max_seqlen_q >= 4 and the storage is
+ * FP8, the group-mode kernel instead walks 4 row groups of one request over a
+ * single shared KV range, so each gathered cache row feeds 64 query rows; it
+ * runs two workers per compute unit with eight partial slots each.  The
+ * workspace is sized for the larger layout whenever the shape qualifies.
  */
 size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, int max_seqlen_q);
 
@@ -122,9 +131,10 @@ mla_status mla_decode(const void* q, int q_dtype, const void* kv_pool, int kv_dt
 
 /*
  * mla_decode with an explicit number of worker workgroups (0 = the library's
- * choice, one per compute unit).  The KV work is cut into `num_workers` equal
- * contiguous ranges; results agree with mla_decode within rounding.  The
- * workspace must hold mla_decode_workspace_bytes_ex(..., num_workers) bytes.
+ * choice: one per compute unit, two in group mode).  The KV work is cut into
+ * `num_workers` equal contiguous ranges; results agree with mla_decode within
+ * rounding.  The workspace must hold mla_decode_workspace_bytes_ex(...,
+ * num_workers) bytes.
  */
 mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
                          int64_t pool_entries, void* o, const int32_t* qo_indptr,
@@ -170,6 +180,18 @@ const char* mla_status_string(int status);
  */
 int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
                       int num_heads, int num_workers, int64_t* out, int64_t out_cap);
+
+/*
+ * Host mirror of the group-mode planner (the fp8 path when num_heads / 16 *
+ * max_seqlen_q >= 4), for tests.  A unit is 4 consecutive row groups
+ * rg = j * (num_heads / 16) + g of one request (token j, head group g), as
+ * long as the last of them sees.  Records as for mla_plan_host but with
+ * columns: worker, request, unit, kv_begin, kv_end, unit_len, slot_base,
+ * is_complete; slot_base is the first of the piece's 4 partial slots (one per
+ * row group), -1 for complete pieces.  Same return convention.
+ */
+int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
+                             int num_heads, int num_workers, int64_t* out, int64_t out_cap);
 
 #ifdef __cplusplus
 }

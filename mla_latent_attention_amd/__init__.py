@@ -21,6 +21,7 @@ __all__ = [
     "merge_partials",
     "workspace_bytes",
     "plan_host",
+    "plan_groups_host",
     "new_workspace",
     "MLAError",
     "library_path",
@@ -186,17 +187,28 @@ def merge_partials(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, o=None, ls
 PLAN_FIELDS = ("worker", "token", "head_group", "kv_begin", "kv_end", "unit_len", "slot", "complete")
 
 
-def plan_host(qo_indptr, kv_indptr, num_heads: int, num_workers: int) -> np.ndarray:
-    """The planner's pieces for host indptr arrays: int64 array (pieces, 8), columns PLAN_FIELDS."""
+GROUP_PLAN_FIELDS = ("worker", "request", "unit", "kv_begin", "kv_end", "unit_len", "slot_base",
+                     "complete")
+
+
+def _plan(fn, qo_indptr, kv_indptr, num_heads, num_workers):
     qo = np.ascontiguousarray(np.asarray(qo_indptr, dtype=np.int32))
     kv = np.ascontiguousarray(np.asarray(kv_indptr, dtype=np.int32))
     B = len(qo) - 1
-    L = _lib.lib()
-    n = L.mla_plan_host(qo.ctypes.data, kv.ctypes.data, B, num_heads, num_workers, None, 0)
+    n = fn(qo.ctypes.data, kv.ctypes.data, B, num_heads, num_workers, None, 0)
     if n < 0:
         raise ValueError("invalid planner input")
     out = np.zeros((max(n, 1), 8), dtype=np.int64)
-    n2 = L.mla_plan_host(qo.ctypes.data, kv.ctypes.data, B, num_heads, num_workers,
-                         out.ctypes.data, n)
+    n2 = fn(qo.ctypes.data, kv.ctypes.data, B, num_heads, num_workers, out.ctypes.data, n)
     assert n2 == n
     return out[:n]
+
+
+def plan_host(qo_indptr, kv_indptr, num_heads: int, num_workers: int) -> np.ndarray:
+    """The planner's pieces for host indptr arrays: int64 array (pieces, 8), columns PLAN_FIELDS."""
+    return _plan(_lib.lib().mla_plan_host, qo_indptr, kv_indptr, num_heads, num_workers)
+
+
+def plan_groups_host(qo_indptr, kv_indptr, num_heads: int, num_workers: int) -> np.ndarray:
+    """The group-mode planner's pieces: int64 array (pieces, 8), columns GROUP_PLAN_FIELDS."""
+    return _plan(_lib.lib().mla_plan_groups_host, qo_indptr, kv_indptr, num_heads, num_workers)

@@ -34,6 +34,7 @@ SIGNATURES = {
     "mla_merge_partials": (C.c_int, [_vp, C.c_int, _vp, C.c_int, C.c_int, C.c_int, _vp, _vp, _vp]),
     "mla_status_string": (C.c_char_p, [C.c_int]),
     "mla_plan_host": (C.c_int64, [_vp, _vp, C.c_int, C.c_int, C.c_int, _vp, C.c_int64]),
+    "mla_plan_groups_host": (C.c_int64, [_vp, _vp, C.c_int, C.c_int, C.c_int, _vp, C.c_int64]),
 }
 
 _lib = None

@@ -43,6 +43,19 @@ bool shape_ok(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
 
 using mla::kMaxWorkers;
 
+// Partial slots per worker for a call shape (group mode applies to the fp8
+// kernels; the layout is sized the same for both storage types).
+int slots_for(int num_heads, int max_seqlen_q) {
+  return mla::slots_per_worker(mla::use_group_mode(num_heads / mla::kGroup, max_seqlen_q));
+}
+
+// Default worker count: one per CU, two per CU for the group-mode kernel
+// (which runs two workgroups per CU).  Sizing uses the larger count for every
+// group-mode shape, whatever the storage type.
+int workers_for(int num_heads, int max_seqlen_q, int cus) {
+  return mla::use_group_mode(num_heads / mla::kGroup, max_seqlen_q) ? 2 * cus : cus;
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,14 +77,17 @@ size_t mla_decode_workspace_bytes_ex(int batch, int num_q_tokens, int num_heads,
                                      int max_seqlen_q, int num_workers) {
   if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
   if (num_workers < 1 || num_workers > kMaxWorkers) return 0;
-  return mla::workspace_bytes(num_workers, (int64_t)num_q_tokens * (num_heads / mla::kGroup));
+  return mla::workspace_bytes(num_workers, (int64_t)num_q_tokens * (num_heads / mla::kGroup),
+                              slots_for(num_heads, max_seqlen_q));
 }
 
 size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
   if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
   const int cus = current_cu_count();
   if (cus <= 0) return 0;
-  return mla::workspace_bytes(cus, (int64_t)num_q_tokens * (num_heads / mla::kGroup));
+  return mla::workspace_bytes(workers_for(num_heads, max_seqlen_q, cus),
+                              (int64_t)num_q_tokens * (num_heads / mla::kGroup),
+                              slots_for(num_heads, max_seqlen_q));
 }
 
 mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
@@ -94,14 +110,18 @@ mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv
     return MLA_ERR_BAD_SHAPE;
   if (num_workers < 0 || num_workers > kMaxWorkers) return MLA_ERR_BAD_SHAPE;
   const int64_t num_units = (int64_t)num_q_tokens * (num_heads / mla::kGroup);
+  const int slots = slots_for(num_heads, max_seqlen_q);
   if (!workspace) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  if (num_workers > 0 && workspace_bytes < mla::workspace_bytes(num_workers, num_units))
+  if (num_workers > 0 && workspace_bytes < mla::workspace_bytes(num_workers, num_units, slots))
     return MLA_ERR_WORKSPACE_TOO_SMALL;
 
+  const int kdt = (kv_dtype == MLA_DTYPE_FP8_E4M3FN) ? 0 : 1;
+  const bool group_mode = kdt == 0 && mla::use_group_mode(num_heads / mla::kGroup, max_seqlen_q);
   if (num_workers == 0) {
-    num_workers = current_cu_count();
-    if (num_workers <= 0) return MLA_ERR_HIP;
-    if (workspace_bytes < mla::workspace_bytes(num_workers, num_units))
+    const int cus = current_cu_count();
+    if (cus <= 0) return MLA_ERR_HIP;
+    num_workers = group_mode ? 2 * cus : cus;
+    if (workspace_bytes < mla::workspace_bytes(num_workers, num_units, slots))
       return MLA_ERR_WORKSPACE_TOO_SMALL;
   }
 
@@ -125,10 +145,9 @@ mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv
   p.desc = reinterpret_cast<int4*>(ws);
   p.part_o = reinterpret_cast<float*>(ws + mla::desc_bytes(num_units));
   p.part_lse = reinterpret_cast<float*>(ws + mla::desc_bytes(num_units) +
-                                        mla::part_o_bytes(num_workers));
+                                        mla::part_o_bytes(num_workers, slots));
   p.num_workers = num_workers;
-  const int kdt = (kv_dtype == MLA_DTYPE_FP8_E4M3FN) ? 0 : 1;
-  if (mla::launch_decode(p, kdt, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (mla::launch_decode(p, kdt, group_mode, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }
@@ -226,6 +245,75 @@ int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int ba
       c.k += len;
       ++piece;
       if (pos < p1 && c.k == v && !cursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G))
+        return -1;
+    }
+  }
+  return count;
+}
+
+int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
+                             int num_heads, int num_workers, int64_t* out, int64_t out_cap) {
+  using namespace mla;
+  if (!qo_indptr || !kv_indptr || batch < 1 || num_heads < kGroup || num_heads % kGroup ||
+      num_workers < 1 || (out_cap > 0 && !out))
+    return -1;
+  const int G = num_heads / kGroup;
+  const int T = qo_indptr[batch];
+  const int kv_cap = kv_indptr[batch];
+  if (T < 0 || kv_cap < 0) return -1;
+  std::vector<int64_t> cum(batch + 1, 0);
+  for (int b = 0; b < batch; ++b)
+    cum[b + 1] = cum[b] + group_request_rows(load_req(qo_indptr, kv_indptr, b, kv_cap, T), G);
+  const int64_t W = cum[batch];
+  if (W == 0) return 0;
+  const int nw = effective_workers(W, num_workers);
+  const int slots = slots_per_worker(true);
+  int64_t count = 0;
+  auto locate = [&](int64_t x, GCursor& c) {
+    int b = 0;
+    while (!(cum[b] <= x && x < cum[b + 1])) ++b;
+    gcursor_in_request(c, b, load_req(qo_indptr, kv_indptr, b, kv_cap, T), x - cum[b], G);
+  };
+  for (int w = 0; w < nw; ++w) {
+    const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
+    GCursor c, c1;
+    locate(x0, c);
+    int64_t p1 = W;
+    if (x1 < W) {
+      locate(x1, c1);
+      p1 = gsnap_at(x1, c1, G);
+    }
+    const int64_t p0 = gsnap_at(x0, c, G);
+    if (p0 >= p1) continue;
+    if (p0 < x0) {
+      c.k = 0;
+    } else if (p0 > x0) {
+      if (!gcursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G)) continue;
+    }
+    int64_t pos = p0;
+    int piece = 0;
+    while (pos < p1) {
+      const int L = group_unit_len(c.r, G, c.u);
+      const int len = (int)lmin((int64_t)(L - c.k), p1 - pos);
+      if (len <= 0) return -1;
+      const bool complete = (c.k == 0 && len == L);
+      const int slot = complete ? -1 : slots * w + (piece == 0 ? 0 : slots / 2);
+      if (count < out_cap) {
+        int64_t* rec = out + 8 * count;
+        rec[0] = w;
+        rec[1] = c.b;
+        rec[2] = c.u;
+        rec[3] = c.k;
+        rec[4] = c.k + len;
+        rec[5] = L;
+        rec[6] = slot;
+        rec[7] = complete ? 1 : 0;
+      }
+      ++count;
+      pos += len;
+      c.k += len;
+      ++piece;
+      if (pos < p1 && c.k == L && !gcursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G))
         return -1;
     }
   }

@@ -1,0 +1,233 @@
+// mla_device.h - device helpers shared by the decode kernels: arithmetic
+// helpers, block-wide scans, the planner's request lookup, the online-softmax
+// state and the staging of q and kv_indices.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+#include "mla_plan.h"
+
+namespace mla {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kCombBytes = kWaves * 32 * 64 * 16;  // 131,072: every wave's O^T
+constexpr int kIdxSeg = 7168;                      // kv_indices staged in LDS per segment
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kLazy = 1.0f;                       // rescale when a row max grows > 2^kLazy
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite).
+__device__ __forceinline__ u32 bf16_bits(float f) {
+  u32 u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ long as_long(u32 lo, u32 hi) {
+  return (long)((uint64_t)lo | ((uint64_t)hi << 32));
+}
+
+// Orders this wave's LDS accesses (writes by some lanes, reads by others).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// 4x4 byte transpose: out_k = (a.byte k, b.byte k, c.byte k, d.byte k).
+__device__ __forceinline__ void transpose4x4(u32 a, u32 b, u32 c, u32 d, u32& o0, u32& o1, u32& o2,
+                                             u32& o3) {
+  const u32 t0 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  const u32 t1 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+  const u32 t2 = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
+  const u32 t3 = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
+  o0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);           // a0 b0 c0 d0
+  o1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);           // a1 b1 c1 d1
+  o2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);           // a2 b2 c2 d2
+  o3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);           // a3 b3 c3 d3
+}
+
+// ---------------------------------------------------------------- block helpers
+
+// Block-uniform values read from memory arrive in vector registers; moving
+// them to scalar registers keeps the planner state (live across the whole
+// tile loop) out of the vector register budget of the loop.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void uniformize(Cursor& c) {
+  c.b = uniform(c.b);
+  c.j = uniform(c.j);
+  c.g = uniform(c.g);
+  c.k = uniform(c.k);
+  c.r.kv_base = uniform(c.r.kv_base);
+  c.r.n = uniform(c.r.n);
+  c.r.q_base = uniform(c.r.q_base);
+  c.r.qlen = uniform(c.r.qlen);
+}
+
+__device__ int64_t block_sum_i64(int64_t v, int64_t* red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  const int wv = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wv] = v;
+  __syncthreads();
+  int64_t s = 0;
+  for (int i = 0; i < kWaves; ++i) s += red[i];
+  return s;
+}
+
+// Exclusive prefix sum over the block's 256 values; `total` gets the sum.
+__device__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int64_t x = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    int64_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) red[wv] = x;
+  __syncthreads();
+  int64_t before = 0;
+  total = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < wv) before += red[i];
+    total += red[i];
+  }
+  return before + x - v;
+}
+
+// Requests containing stream positions x[0] and x[1] (a negative position is
+// not looked up), where request r holds rows_of(r) stream rows: sb[i] =
+// request (-1 if not found, -2 if not looked up) and scum[i] = that request's
+// first stream position.
+template <class RowsOf>
+__device__ void plan_locate2(const DecodeParams& p, RowsOf rows_of, const int64_t (&x)[2],
+                             int64_t* red, int* sb, int64_t* scum) {
+  if (threadIdx.x < 2) sb[threadIdx.x] = x[threadIdx.x] < 0 ? -2 : -1;
+  int64_t carry = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += kThreads) {
+    const int b = b0 + threadIdx.x;
+    int64_t R = 0;
+    if (b < p.batch) {
+      R = rows_of(load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens));
+    }
+    int64_t total;
+    const int64_t cum = carry + block_excl_scan_i64(R, red, total);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (R > 0 && x[i] >= cum && x[i] < cum + R) {
+        sb[i] = b;
+        scum[i] = cum;
+      }
+    }
+    carry += total;
+    __syncthreads();
+    if (sb[0] != -1 && sb[1] != -1) break;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- softmax state
+
+struct WaveState {
+  v4f O[32];  // O^T blocks (the dim of each element depends on the path);
+              // scaled by the path's kPScale
+  float m;    // (possibly stale) running max of base-2 scores of row lane%16
+  float l;    // this lane's partial sum of 2^(s - m)
+};
+
+// Online-softmax update for row lane%16 from this lane's N scores (already
+// masked to -inf past the piece).  Returns P = 2^(s - m) in x.  The running
+// max is only raised when a row's max grows by more than 2^kLazy, so P stays
+// <= 2^kLazy and the accumulators are rescaled on few tiles.
+template <int N>
+__device__ __forceinline__ void softmax_update(WaveState& st, float (&x)[N]) {
+  float tmax = x[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) tmax = fmaxf(tmax, x[i]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const bool grow = tmax > st.m + kLazy;  // first tile: m = -inf
+  if (__any(grow)) {
+    const float mset = grow ? tmax : st.m;
+    const float alpha = fast_exp2(st.m - mset);  // 1 for rows that keep m, 0 on the first tile
+#pragma unroll
+    for (int b = 0; b < 32; ++b) st.O[b] *= alpha;
+    st.l *= alpha;
+    st.m = mset;
+  }
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    x[i] = fast_exp2(x[i] - st.m);
+    psum += x[i];
+  }
+  st.l += psum;
+}
+
+// ---------------------------------------------------------------- staging
+
+// kv_indices loads issued per thread before the first store.
+constexpr int kIdxBatch = 8;
+
+__device__ __forceinline__ void stage_first_indices(int32_t* idx_dst, const int32_t* idx_src,
+                                                    int n) {
+  int32_t iv[kIdxBatch];
+#pragma unroll
+  for (int j = 0; j < kIdxBatch; ++j) iv[j] = idx_src[imin(j * kThreads + (int)threadIdx.x, n - 1)];
+#pragma unroll
+  for (int j = 0; j < kIdxBatch; ++j) idx_dst[imin(j * kThreads + (int)threadIdx.x, n - 1)] = iv[j];
+}
+
+__device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&a)[8]) {
+  uint4 pk;
+  pk.x = bf16_bits(a[0]) | (bf16_bits(a[1]) << 16);
+  pk.y = bf16_bits(a[2]) | (bf16_bits(a[3]) << 16);
+  pk.z = bf16_bits(a[4]) | (bf16_bits(a[5]) << 16);
+  pk.w = bf16_bits(a[6]) | (bf16_bits(a[7]) << 16);
+  *(uint4*)dst = pk;
+}
+
+// Copies indices [from, n) of src (n >= 1) to the same positions of dst.
+// Each thread issues kIdxBatch loads before its first store (past-the-end
+// positions reload the last index), so a segment costs one memory round trip
+// per 2048 indices instead of one per 256.
+__device__ __forceinline__ void stage_indices(int32_t* dst, const int32_t* src, int from, int n) {
+  for (int i0 = from; i0 < n; i0 += kThreads * kIdxBatch) {
+    int32_t v[kIdxBatch];
+#pragma unroll
+    for (int j = 0; j < kIdxBatch; ++j) v[j] = src[imin(i0 + j * kThreads + (int)threadIdx.x, n - 1)];
+#pragma unroll
+    for (int j = 0; j < kIdxBatch; ++j) dst[imin(i0 + j * kThreads + (int)threadIdx.x, n - 1)] = v[j];
+  }
+}
+
+// Query rows that see no entry get o = 0, lse = -inf; the block owning token t
+// (t mod gridDim.x) writes them.  Rare: empty requests or early draft tokens.
+__device__ void zero_token(const DecodeParams& p, int t) {
+  const int G = p.num_heads / kGroup;
+  for (int g = 0; g < G; ++g) p.desc[(int64_t)t * G + g] = make_int4(0, 0, 0, 0);
+  for (int h = 0; h < p.num_heads; ++h) {
+    const int64_t orow = (int64_t)t * p.num_heads + h;
+    uint4* dst = (uint4*)(p.o + orow * kLatent);
+    for (int k = 0; k < kLatent / 8; ++k) dst[k] = make_uint4(0, 0, 0, 0);
+    if (p.lse != nullptr) p.lse[orow] = neg_inf();
+  }
+}
+
+}  // namespace mla

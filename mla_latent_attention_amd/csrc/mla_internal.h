@@ -23,30 +23,43 @@ struct DecodeParams {
   const float* q_scale;     // device scalar or nullptr (1.0)
   const float* kv_scale;    // device scalar or nullptr (1.0)
   float* lse;               // (T, H) or nullptr
-  float* part_o;            // workspace: (2*num_workers, 16, 512) fp32
-  float* part_lse;          // workspace: (2*num_workers, 16) fp32
+  float* part_o;            // workspace: (slots*num_workers, 16, 512) fp32
+  float* part_lse;          // workspace: (slots*num_workers, 16) fp32
   int4* desc;               // workspace: (tokens * head groups) split-unit descriptors
   int num_workers;
 };
 
-// Workspace layout for `num_workers` workers and `num_units` = tokens * head
-// groups (every byte the kernels read is written earlier in the same call, so
-// no clearing is ever needed):
-//   desc     (num_units) int4 per unit {first worker, last worker, slot of the
-//            first worker, 1} for a unit split over several workers, w = 0 else
-//   part_o   (2*num_workers, 16, 512) fp32 partial outputs
-//   part_lse (2*num_workers, 16) fp32 partial lse
+// Partial-answer slots per worker: a worker holds at most two partial pieces,
+// each covering one row group, or kGroupsPerUnit (4) row groups in group mode.
+inline int slots_per_worker(bool group_mode) { return group_mode ? 8 : 2; }
+
+// Workspace layout for `num_workers` workers, `slots` partial slots per worker
+// and `num_units` = tokens * head groups (every byte the kernels read is
+// written earlier in the same call, so no clearing is ever needed):
+//   desc     (num_units) int4 per row group {first worker, last worker, slot
+//            of the first worker, 1} for a row group split over several
+//            workers, w = 0 else
+//   part_o   (slots * num_workers, 16, 512) fp32 partial outputs
+//   part_lse (slots * num_workers, 16) fp32 partial lse
 constexpr int kMaxWorkers = 1 << 16;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline size_t desc_bytes(int64_t num_units) { return align256(size_t(num_units) * 16); }
-inline size_t part_o_bytes(int num_workers) { return align256(size_t(2) * num_workers * 16 * 512 * 4); }
-inline size_t part_lse_bytes(int num_workers) { return align256(size_t(2) * num_workers * 16 * 4); }
-inline size_t workspace_bytes(int num_workers, int64_t num_units) {
-  return desc_bytes(num_units) + part_o_bytes(num_workers) + part_lse_bytes(num_workers);
+inline size_t part_o_bytes(int num_workers, int slots) {
+  return align256(size_t(slots) * num_workers * 16 * 512 * 4);
+}
+inline size_t part_lse_bytes(int num_workers, int slots) {
+  return align256(size_t(slots) * num_workers * 16 * 4);
+}
+inline size_t workspace_bytes(int num_workers, int64_t num_units, int slots) {
+  return desc_bytes(num_units) + part_o_bytes(num_workers, slots) +
+         part_lse_bytes(num_workers, slots);
 }
 
-// kv_dtype: 0 = fp8 e4m3fn, 1 = bf16.
-hipError_t launch_decode(const DecodeParams& p, int kv_dtype, hipStream_t stream);
+// kv_dtype: 0 = fp8 e4m3fn, 1 = bf16.  group_mode selects the group-mode
+// kernels (fp8 only; the workspace then has 8 slots per worker).
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, bool group_mode, hipStream_t stream);
+// The group-mode decode kernel alone (mla_decode_groups.hip).
+hipError_t launch_decode_groups(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_merge(const void* o_parts, int parts_fp32, const float* lse_parts, int num_parts,
                         int64_t rows, uint16_t* o, float* lse, hipStream_t stream);

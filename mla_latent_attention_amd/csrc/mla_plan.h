@@ -155,4 +155,80 @@ MLA_HD bool cursor_next_unit(Cursor& c, const int32_t* qo, const int32_t* kvp, i
   return false;
 }
 
+// ---- Group mode: a unit is kGroupsPerUnit consecutive row groups of one
+// request, processed by one workgroup over one shared KV range (each wave one
+// row group).  Row group rg = j * G + g (token j, head group g); unit u covers
+// row groups [4u, 4u + 4) of the request's qlen * G and is as long as the
+// last of them sees (the others mask the entries they may not see).  Used when
+// a request has several row groups (many heads or several query tokens), where
+// a unit per row group would gather the same rows once per row group.
+constexpr int kGroupsPerUnit = 4;
+
+MLA_HD bool use_group_mode(int G, int max_seqlen_q) {
+  return (int64_t)G * max_seqlen_q >= kGroupsPerUnit;
+}
+
+MLA_HD int group_units(const Req& r, int G) {
+  return (r.qlen * G + kGroupsPerUnit - 1) / kGroupsPerUnit;
+}
+
+MLA_HD int group_unit_len(const Req& r, int G, int u) {
+  const int last = imin(kGroupsPerUnit * u + kGroupsPerUnit - 1, r.qlen * G - 1);
+  return visible(r.n, r.qlen, last / G);
+}
+
+// Stream rows of request r in group mode.
+MLA_HD int64_t group_request_rows(const Req& r, int G) {
+  int64_t s = 0;
+  const int U = group_units(r, G);
+  for (int u = 0; u < U; ++u) s += group_unit_len(r, G, u);
+  return s;
+}
+
+// Position in the group-mode stream: request b, its unit u, offset k.
+struct GCursor {
+  int b, u, k;
+  Req r;
+};
+
+MLA_HD void gcursor_in_request(GCursor& c, int b, const Req& r, int64_t off, int G) {
+  c.b = b;
+  c.r = r;
+  const int U = group_units(r, G);
+  for (int u = 0; u < U; ++u) {
+    const int v = group_unit_len(r, G, u);
+    if (off < v) {
+      c.u = u;
+      c.k = (int)off;
+      return;
+    }
+    off -= v;
+  }
+  c.u = U;  // not reached for a valid offset
+  c.k = 0;
+}
+
+// Move to the start of the next non-empty unit (unit lengths never shrink
+// within a request).  Returns false past the end.
+MLA_HD bool gcursor_next_unit(GCursor& c, const int32_t* qo, const int32_t* kvp, int B, int kv_cap,
+                              int T, int G) {
+  c.k = 0;
+  if (++c.u < group_units(c.r, G)) return true;
+  for (int b = c.b + 1; b < B; ++b) {
+    Req r = load_req(qo, kvp, b, kv_cap, T);
+    if (group_request_rows(r, G) > 0) {
+      c.b = b;
+      c.r = r;
+      c.u = 0;
+      while (group_unit_len(r, G, c.u) == 0) ++c.u;
+      return true;
+    }
+  }
+  return false;
+}
+
+MLA_HD int64_t gsnap_at(int64_t x, const GCursor& c, int G) {
+  return snap_position(x, c.k, group_unit_len(c.r, G, c.u));
+}
+
 }  // namespace mla

@@ -5,6 +5,15 @@
   use puts spill traffic next to the gather stream (a spill inside the tile
   loop costs several per cent).  The bf16 kernel may keep a few per-piece
   values in scratch, never more than a small bound.
+* The group-mode kernel keeps everything in registers too (two waves per
+  SIMD leave it 256 VGPRs), and writes m0, which its inline-asm LDS DMA reads
+  as the LDS destination, only in the instruction right before each DMA: the
+  compiler itself then never sees a stale m0.
+* No MFMA accumulates onto the result of an MFMA of another kind: gfx950
+  returns garbage when a 16x16x32 fp8 MFMA reads the result of a 16x16x128
+  f8f6f4 MFMA as its accumulator right behind it (or the other way round),
+  and the compiler does not keep them apart, so accumulator chains stay
+  within one instruction.
 * Packed-fp32 VALU instructions are disabled for device code by a build flag;
   none may appear in the output.
 """
@@ -17,15 +26,12 @@ import pytest
 
 from mla_latent_attention_amd import build
 
-SRC = os.path.join(build.CSRC, "mla_decode.hip")
 
-
-@pytest.fixture(scope="module")
-def compiled(tmp_path_factory):
-    out = tmp_path_factory.mktemp("asm") / "mla_decode.s"
+def _compile(tmp_path_factory, name):
+    out = tmp_path_factory.mktemp("asm") / (name + ".s")
     flags = [f for f in build.FLAGS if f not in ("-shared", "-fPIC")]
-    cmd = [build.hipcc(), *flags, "--cuda-device-only", "-S", SRC, "-o", str(out),
-           "-Rpass-analysis=kernel-resource-usage"]
+    cmd = [build.hipcc(), *flags, "--cuda-device-only", "-S", os.path.join(build.CSRC, name),
+           "-o", str(out), "-Rpass-analysis=kernel-resource-usage"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-3000:]
     usage, name = {}, None
@@ -37,6 +43,16 @@ def compiled(tmp_path_factory):
         if m and name:
             usage[name] = int(m.group(1))
     return out.read_text(), usage
+
+
+@pytest.fixture(scope="module")
+def compiled(tmp_path_factory):
+    return _compile(tmp_path_factory, "mla_decode.hip")
+
+
+@pytest.fixture(scope="module")
+def compiled_groups(tmp_path_factory):
+    return _compile(tmp_path_factory, "mla_decode_groups.hip")
 
 
 def _scratch(usage, needle):
@@ -55,6 +71,75 @@ def test_bf16_decode_kernel_scratch_is_small(compiled):
     assert _scratch(usage, "mla_decode_bf16_kernel") <= 64
 
 
-def test_no_packed_fp32_valu(compiled):
-    asm, _ = compiled
+def test_group_decode_kernel_uses_no_scratch(compiled_groups):
+    _, usage = compiled_groups
+    assert _scratch(usage, "mla_decode_groups_fp8_kernel") == 0
+
+
+def test_group_kernel_m0_written_only_for_its_dma(compiled_groups):
+    asm, _ = compiled_groups
+    lines = [l.strip() for l in asm.splitlines()]
+    code = [l for l in lines if l and not l.startswith((";", "."))]
+    writes = [i for i, l in enumerate(code) if re.match(r"s_\w+\s+m0\b", l)]
+    dmas = [i for i, l in enumerate(code) if l.startswith("global_load_lds_dwordx4")]
+    assert dmas and len(writes) == len(dmas)
+    assert all(code[i + 1].startswith("global_load_lds_dwordx4") for i in writes)
+    # nothing else names m0 (reads included)
+    others = [l for i, l in enumerate(code) if re.search(r"\bm0\b", l) and i not in writes]
+    assert not others, others[:5]
+
+
+def _regs(tok):
+    m = re.match(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+def mixed_mfma_chains(asm):
+    """(line, mfma, previous writer) wherever an MFMA's accumulator registers
+    were last written by an MFMA of another kind (straight-line order within a
+    function; any other write in between ends the chain)."""
+    last, bad = {}, []
+    for ln, line in enumerate(asm.splitlines(), 1):
+        t = line.strip()
+        if "-- Begin function" in t:
+            last = {}
+        if not t or t.startswith((";", ".")) or t.endswith(":"):
+            continue
+        parts = re.split(r"[\s,]+", t)
+        op = parts[0]
+        if op.startswith("v_mfma") and len(parts) > 4:
+            prev = {last.get(r) for r in _regs(parts[4])}
+            if any(p and p.startswith("v_mfma") and p != op for p in prev):
+                bad.append((ln, op, sorted(p for p in prev if p)))
+        if len(parts) > 1 and op.startswith(("v_", "ds_read", "global_load", "buffer_load",
+                                             "scratch_load", "flat_load")):
+            for r in _regs(parts[1]):
+                last[r] = op
+    return bad
+
+
+@pytest.mark.parametrize("which", ["compiled", "compiled_groups"])
+def test_mfma_accumulator_chains_do_not_mix_kinds(which, request):
+    asm, _ = request.getfixturevalue(which)
+    assert "v_mfma" in asm
+    bad = mixed_mfma_chains(asm)
+    assert not bad, bad[:5]
+
+
+def test_mixed_chain_detector_flags_a_mixed_chain():
+    asm = "\n".join([
+        "v_mfma_scale_f32_16x16x128_f8f6f4 v[0:3], v[4:11], v[12:19], 0, v1, v1",
+        "v_mfma_f32_16x16x32_fp8_fp8 v[0:3], v[20:21], v[22:23], v[0:3]",
+        "v_mov_b32 v0, 0",
+        "v_mfma_f32_16x16x32_fp8_fp8 v[30:33], v[20:21], v[22:23], v[30:33]",
+    ])
+    assert [b[0] for b in mixed_mfma_chains(asm)] == [2]
+
+
+@pytest.mark.parametrize("which", ["compiled", "compiled_groups"])
+def test_no_packed_fp32_valu(which, request):
+    asm, _ = request.getfixturevalue(which)
     assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", asm)

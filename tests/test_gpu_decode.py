@@ -119,6 +119,92 @@ def test_peaky_scores():
     assert_gate(m, "peaky", abs_tol=bf16_abs_tol(m["ref_absmax"]))
 
 
+# ------------------------------------------------------------------ group mode
+# fp8 calls with num_heads / 16 * max_seqlen_q >= 4 run the group-mode kernel:
+# one workgroup walks 4 row groups of one request over a shared KV range.
+
+
+def group_ragged():
+    lengths = [0, 1, 31, 32, 33, 100, 1000, 4097, 0, 2, 20000]
+    return workloads.build("group-ragged", lengths, num_heads=64, real_heads=60,
+                           pool_entries=1 << 15, kv_std=1.0, scale_range=(0.5, 2.0), seed=21,
+                           device=DEV)
+
+
+@pytest.mark.parametrize("nw", [0, 1, 3, 37, 512])
+def test_group_mode_ragged_any_worker_count(nw):
+    """64 heads, one token per request: a unit is the token's 4 head groups.
+    Requests of 1-2 entries return (scaled) V rows themselves, up to |o| ~ 4,
+    where bf16's own rounding exceeds 1e-2: the absolute bound is one bf16
+    unit in the last place at that magnitude (row-relative and lse gates as
+    everywhere)."""
+    o, lse, _ = check(group_ragged(), num_workers=nw, where=f"group ragged nw={nw}",
+                      bf16_ulp_abs=True)
+    for t in (0, 8):
+        assert torch.all(o[t] == 0) and torch.all(torch.isneginf(lse[t]))
+
+
+@pytest.mark.parametrize("nw", [0, 1, 5, 100])
+def test_group_mode_units_span_tokens(nw):
+    """16 heads, several query tokens: a unit holds 4 consecutive tokens, each
+    wave masking its own causal limit; early draft tokens see nothing."""
+    w = workloads.build("group-tokens", [5000, 10, 2, 3000, 1], num_heads=16, real_heads=12,
+                        qlens=[4, 1, 3, 4, 2], pool_entries=16384, kv_std=0.5,
+                        scale_range=(0.5, 2.0), seed=22, device=DEV)
+    o, lse, _ = check(w, num_workers=nw, where=f"group tokens nw={nw}")
+    qo = w.qo_indptr.cpu().tolist()
+    empty = [qo[2], qo[4]]  # (n=2, qlen=3) token 0; (n=1, qlen=2) token 0
+    for t in empty:
+        assert torch.all(o[t] == 0) and torch.all(torch.isneginf(lse[t]))
+
+
+def test_group_mode_pad_heads_bitwise_and_deterministic():
+    w = workloads.build("group-pad", [3000, 1234, 77], num_heads=64, real_heads=60,
+                        qlens=[2, 1, 2], pool_entries=8192, seed=23, device=DEV)
+    o_zero, lse_zero = run(w)
+    o_again, lse_again = run(w)
+    assert torch.equal(o_zero, o_again) and torch.equal(lse_zero, lse_again)
+    q_rand = w.q.clone()
+    g = torch.Generator(device=DEV).manual_seed(8)
+    noise = torch.randn(q_rand[:, 60:].shape, generator=g, device=DEV).clamp(-448, 448)
+    q_rand[:, 60:] = noise.to(torch.float8_e4m3fn)
+    o_r, lse_r = run(w, q=q_rand)
+    assert torch.equal(o_r[:, :60], o_zero[:, :60])
+    assert torch.equal(lse_r[:, :60], lse_zero[:, :60])
+
+
+def test_group_mode_graph_replay_matches_eager_bitwise():
+    w = workloads.build("group-graph", [2500, 900, 4000], num_heads=32, real_heads=32,
+                        qlens=[2, 2, 1], pool_entries=8192, seed=24, device=DEV)
+    o_eager, lse_eager = run(w)
+    o = torch.empty_like(o_eager)
+    lse = torch.empty_like(lse_eager)
+    ws = mla.new_workspace(mla.workspace_bytes(w.batch, w.num_tokens, w.num_heads, 2), DEV)
+
+    def call():
+        mla.decode(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_lens,
+                   w.sm_scale, w.q_scale, w.kv_scale, return_lse=True, o=o, lse=lse,
+                   max_seqlen_q=2, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        o.zero_()
+        lse.fill_(7.0)
+        run(group_ragged())  # unrelated eager work on the same device
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_eager), f"replay {rep}"
+        assert torch.equal(lse, lse_eager), f"replay {rep}"
+
+
 # ------------------------------------------------------------------ bf16 storage
 
 

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import workloads
-from mla_latent_attention_amd import plan_host
+from mla_latent_attention_amd import plan_groups_host, plan_host
 
 MIN_WORKER_ROWS = 512
 SNAP_ROWS = 64
@@ -30,6 +30,22 @@ def units(qo, kv, G):
             for g in range(G):
                 out.append((qo[b] + j, g, v, pos))
                 pos += v
+    return out, pos
+
+
+def group_units(qo, kv, G):
+    """Group mode: (request, unit, length, stream start) in stream order.  Unit u
+    of a request covers row groups 4u..4u+3 (row group = token * G + head
+    group) and is as long as its last row group sees."""
+    out, pos = [], 0
+    for b in range(len(qo) - 1):
+        n, ql = kv[b + 1] - kv[b], qo[b + 1] - qo[b]
+        R = ql * G
+        for u in range(-(-R // 4)):
+            last = min(4 * u + 3, R - 1)
+            v = visible(n, ql, last // G)
+            out.append((b, u, v, pos))
+            pos += v
     return out, pos
 
 
@@ -161,3 +177,95 @@ def test_empty_and_tiny_inputs():
 def test_rejects_bad_planner_input():
     with pytest.raises(ValueError):
         plan_host(indptr([1]), indptr([10]), 12, 4)
+
+
+# ---------------------------------------------------------------- group mode
+
+
+def check_group_plan(qo, kv, H, nw_req):
+    G = H // 16
+    us, W = group_units(qo, kv, G)
+    pieces = plan_groups_host(qo, kv, H, nw_req)
+    if W == 0:
+        assert len(pieces) == 0
+        return pieces
+    nw = min(nw_req, max(1, -(-W // MIN_WORKER_ROWS)))
+    S = snapped_bounds(us, W, nw)
+    assert all(a < b for a, b in zip(S, S[1:]))
+    cover = {}
+    for w, b, u, kb, ke, ul, slot, comp in pieces:
+        assert 0 <= kb < ke <= ul
+        cover.setdefault((b, u), []).append((kb, ke, w, slot, comp))
+    owner = lambda p: int(np.searchsorted(S, p, side="right")) - 1  # noqa: E731
+    for b, u, v, start in us:
+        if v == 0:
+            assert (b, u) not in cover
+            continue
+        segs = sorted(cover[(b, u)])
+        assert segs[0][0] == 0 and segs[-1][1] == v
+        for (a0, a1, *_), (b0, b1, *_) in zip(segs, segs[1:]):
+            assert a1 == b0
+        if len(segs) == 1:
+            assert segs[0][4] == 1 and segs[0][3] == -1
+            continue
+        assert all(s[4] == 0 for s in segs)
+        # The group combine reads, for the i-th worker after the first, slots
+        # 8 * (w0 + i) + wave: those workers must hold the unit as their first
+        # piece, in consecutive order; the first worker's slots start at
+        # 8 * w0, or 8 * w0 + 4 when the unit is not its first piece.
+        wlo, whi = owner(start), owner(start + v - 1)
+        assert [s[2] for s in segs] == list(range(wlo, whi + 1))
+        first = 8 * wlo + (4 if S[wlo] < start else 0)
+        assert segs[0][3] == first
+        assert [s[3] for s in segs[1:]] == [8 * w for w in range(wlo + 1, whi + 1)]
+    per_worker = np.zeros(nw, dtype=np.int64)
+    for w, b, u, kb, ke, *_ in pieces:
+        per_worker[w] += ke - kb
+    shares = np.array([S[w + 1] - S[w] for w in range(nw)])
+    assert np.array_equal(per_worker, shares)
+    assert np.all(np.abs(shares - W / nw) <= 2 * SNAP_ROWS + 1)
+    slots = [p[6] for p in pieces if p[6] >= 0]
+    assert len(slots) == len(set(slots))
+    for w in range(nw):
+        mine = pieces[pieces[:, 0] == w]
+        for i, p in enumerate(mine):
+            if p[7] == 0:
+                assert i in (0, len(mine) - 1)
+    return pieces
+
+
+def test_group_plan_dcp_share_workload():
+    """96 heads, 4 query tokens per request, 8 requests of 17,750 entries: 24
+    row groups per request, 6 units each, 512 workers."""
+    pieces = check_group_plan(indptr([4] * 8), indptr([17_750] * 8), 96, 512)
+    assert pieces[:, 2].max() == 5
+    # causal: unit lengths step up with the token of their last row group
+    lens = sorted(set(pieces[:, 5].tolist()))
+    assert lens == [17_747, 17_748, 17_749, 17_750]
+
+
+def test_group_units_mask_within_unit():
+    """With 16 heads and 4 tokens, one unit holds all four tokens; its length
+    is the last token's visible count, the others see fewer."""
+    us, W = group_units(indptr([4]), indptr([100]), 1)
+    assert [(u, v) for _, u, v, _ in us] == [(0, 100)]
+    us, W = group_units(indptr([3]), indptr([100]), 2)  # 6 row groups: units of 4 and 2
+    assert [(u, v) for _, u, v, _ in us] == [(0, 99), (1, 100)]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_group_random_ragged_plans(seed):
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 40))
+    lengths = rng.integers(0, 5000, size=B)
+    lengths[rng.random(B) < 0.2] = 0
+    qlens = rng.integers(1, 6, size=B)
+    H = 16 * int(rng.integers(1, 7))
+    check_group_plan(indptr(qlens), indptr(lengths), H, int(rng.integers(1, 600)))
+
+
+def test_group_empty_and_tiny_inputs():
+    check_group_plan(indptr([4, 4]), indptr([0, 0]), 16, 512)
+    p = check_group_plan(indptr([4]), indptr([200]), 16, 512)
+    assert len(p) == 1 and p[0, 7] == 1
+    check_group_plan(indptr([4, 3]), indptr([2, 1]), 32, 8)  # early draft tokens see nothing
