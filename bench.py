@@ -277,11 +277,13 @@ def measured_traffic(variant):
     try:
         with open(os.path.join(ROOT, "profiles", "traffic_c16.json")) as f:
             rec = json.load(f)
-        with open(os.path.join(ROOT, rec["kernel_source"]), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-    except (OSError, KeyError, ValueError):
+        for path, want in rec["kernel_sources_sha256"].items():
+            with open(os.path.join(ROOT, path), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != want:
+                    return None
+    except (OSError, KeyError, ValueError, AttributeError):
         return None
-    if sha != rec.get("kernel_source_sha256") or variant != rec.get("variant"):
+    if variant != rec.get("variant"):
         return None
     return int(rec["fetch_bytes_per_call"]) + int(rec["write_bytes_per_call"])
 
