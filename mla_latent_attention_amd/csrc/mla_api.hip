@@ -49,11 +49,11 @@ int slots_for(int num_heads, int max_seqlen_q) {
   return mla::slots_per_worker(mla::use_group_mode(num_heads / mla::kGroup, max_seqlen_q));
 }
 
-// Default worker count: one per CU, two per CU for the group-mode kernel
-// (which runs two workgroups per CU).  Sizing uses the larger count for every
-// group-mode shape, whatever the storage type.
+// Default worker count: one per CU (both kernels run one workgroup per CU).
 int workers_for(int num_heads, int max_seqlen_q, int cus) {
-  return mla::use_group_mode(num_heads / mla::kGroup, max_seqlen_q) ? 2 * cus : cus;
+  (void)num_heads;
+  (void)max_seqlen_q;
+  return cus;
 }
 
 }  // namespace
@@ -120,7 +120,7 @@ mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv
   if (num_workers == 0) {
     const int cus = current_cu_count();
     if (cus <= 0) return MLA_ERR_HIP;
-    num_workers = group_mode ? 2 * cus : cus;
+    num_workers = workers_for(num_heads, max_seqlen_q, cus);
     if (workspace_bytes < mla::workspace_bytes(num_workers, num_units, slots))
       return MLA_ERR_WORKSPACE_TOO_SMALL;
   }

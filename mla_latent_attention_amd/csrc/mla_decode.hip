@@ -703,7 +703,7 @@ void mla_decode_bf16_kernel(const DecodeParams p) {
 // The slots are the first worker's own and, for each later worker w', the
 // slot of its first piece: kSlots * w' + (position of the row group within
 // its piece), i.e. first_slot mod (kSlots / 2) (0 in the standard mode, with
-// kSlots = 2; the wave index in group mode, with kSlots = 8).
+// kSlots = 2; the row group within the unit in group mode, with kSlots = 16).
 constexpr int kCombineThreads = 64;
 
 template <int kSlots>
@@ -773,7 +773,7 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const Deco
 }
 
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_groups_kernel(const DecodeParams p) {
-  combine_unit<8>(p);
+  combine_unit<16>(p);
 }
 
 // ---------------------------------------------------------------- shard merge

@@ -8,27 +8,26 @@
 // (Sec. "1. Cache: keep conversation state available for reuse": all 96 heads
 // of 4 tokens over one rank's slice of the history) has 24 row groups per
 // request; with one unit per row group every cached row would be gathered 24
-// times.
+// times, and the attention arithmetic (not HBM) sets the time.
 //
 // Design (our own):
-//   * A unit is four consecutive row groups of one request (mla_plan.h, group
-//     mode); workers take equal, boundary-snapped shares of the unit stream as
-//     in the standard mode.
-//   * The four waves of a workgroup own the unit's four row groups and walk the
-//     same KV range.  Tiles of 32 rows are gathered once by all 256 threads
-//     with direct global->LDS loads (each lane 16 consecutive bytes of a row)
-//     into a three-tile LDS ring with a 592-byte row stride; two tiles are in
-//     flight while one is consumed.
-//   * Two workgroups share a CU (two waves per SIMD, 250 registers each), so one
-//     wave's softmax and LDS latency overlap the other wave's MFMAs.
-//   * Each wave computes its row group over the shared tile: S^T = K.Q^T on
-//     v_mfma_f32_16x16x32_fp8_fp8 with K read from LDS and q in registers, the
-//     online softmax (masking the entries its token may not see), and
-//     O^T += V^T.P^T on bf16 MFMA, with the V^T operand read from the
-//     row-major tile by the LDS transpose read (ds_read_b64_tr_b8) and widened
-//     exactly from fp8, and P in bf16: one MFMA per 16 dims and 32 rows
-//     instead of two fp8 ones (P as hi + lo).  Every wave writes its own o (or
-//     partial): there is no cross-wave merge.
+//   * A unit is eight row groups of one request (mla_plan.h, group mode);
+//     workers take equal, boundary-snapped shares of the unit stream as in
+//     the standard mode.  One workgroup (four waves, one per SIMD) per CU.
+//   * Wave wv owns the unit's row groups wv and wv + 4: 32 query rows, the N
+//     dimension of 32x32 MFMAs, so every K and V element read from LDS (and
+//     every fp8 -> bf16 widening of V) serves 32 rows.
+//   * Tiles of 32 KV rows are gathered once by all 256 threads with direct
+//     global->LDS loads (each lane 16 consecutive bytes of a row) into a
+//     six-tile LDS ring with a 592-byte row stride; up to four later tiles
+//     are in flight while one is consumed.
+//   * Per tile and wave: S^T = K.Q^T on v_mfma_scale_f32_32x32x64_f8f6f4
+//     (nine steps, K from LDS, q in registers), the online softmax (each
+//     lane masks the entries its row's token may not see), and
+//     O^T += V^T.P^T on v_mfma_f32_32x32x16_bf16, with the V^T operand read
+//     from the row-major tile by the LDS transpose read (ds_read_b64_tr_b8)
+//     and widened exactly from fp8, and P in bf16 from the lane's own scores.
+//     Every wave writes its own o (or partials): there is no cross-wave merge.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -37,54 +36,33 @@
 
 namespace mla {
 
-constexpr int kGTile = 32;                                    // KV rows per shared tile
-constexpr int kGBlocks = kGTile / 16;                         // 16-row S^T blocks per tile
-constexpr int kGHalves = kGTile / 32;                         // 32-row P.V steps per tile
-constexpr int kGIdxSeg = 2048;                                // kv_indices staged per segment
-constexpr int kGChunks = kRowDim / 16;                        // 16-byte chunks per row (36)
-constexpr int kGRowSlots = kGChunks + 1;                      // + one pad slot per staged row
-constexpr int kGStride = 16 * kGRowSlots;                     // LDS bytes per staged row (592)
-constexpr int kGLoads = 5;                                    // load instructions per wave per tile
-constexpr int kGTileBytes = kWaves * kGLoads * 64 * 16;       // 20,480 (>= 32 rows x 592)
-constexpr int kGRing = 3;                                     // tiles in the LDS ring
+constexpr int kGTile = 32;                               // KV rows per shared tile
+constexpr int kGIdxSeg = 4096;                           // kv_indices staged per segment
+constexpr int kGChunks = kRowDim / 16;                   // 16-byte chunks per row (36)
+constexpr int kGRowSlots = kGChunks + 1;                 // + one pad slot per staged row
+constexpr int kGStride = 16 * kGRowSlots;                // LDS bytes per staged row (592)
+constexpr int kGLoads = 5;                               // load instructions per wave per tile
+constexpr int kGTileBytes = kWaves * kGLoads * 64 * 16;  // 20,480 (>= 32 rows x 592)
+constexpr int kGRing = 6;                                // tiles in the LDS ring
 static_assert(kGTile * kGStride <= kGTileBytes, "a tile's rows must fit its ring slot");
-constexpr int kGSlotsPerPiece = kGroupsPerUnit;               // one partial slot per row group
+static_assert(kGroupsPerUnit == 2 * kWaves, "each wave owns two row groups of a unit");
+constexpr int kGSlotsPerPiece = kGroupsPerUnit;          // one partial slot per row group
+// P = 2^(s - m) with m a row's first visible score: P may grow to 2^kPBig
+// before the piece is redone with m = the row's true max (see wide_tile).
+constexpr float kPBig = 64.0f;
 
-// The ring's three tiles are separate LDS objects, always named statically:
-// the compiler then knows which tile a direct-to-LDS load writes and which one
-// an LDS read reads, and waits only for the loads of the tile being read
-// (through one array it must wait for every outstanding load before any read).
-__shared__ __attribute__((aligned(16))) uint8_t g_ring0[kGTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_ring1[kGTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_ring2[kGTileBytes];
-
-template <int kB>
-__device__ __forceinline__ uint8_t* ring() {
-  if constexpr (kB == 0) return g_ring0;
-  if constexpr (kB == 1) return g_ring1;
-  return g_ring2;
-}
+__shared__ __attribute__((aligned(16))) uint8_t g_ring[kGRing * kGTileBytes];
 
 struct alignas(16) GroupShared {
   int32_t idx[kGIdxSeg];  // kv_indices of the current segment of the piece
+  int flag[kWaves];       // per-wave "redo the piece" votes
   int64_t red[kWaves];
   int pb[2];
   int64_t pcum[2];
 };
 
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v8i_t __attribute__((ext_vector_type(8)));
-
-// q row lane%16 of the wave's row group, as the B operands of five
-// 16x16x128 MFMA steps.  Step c < 4 (latent dims 128c .. 128c + 127): the
-// lane holds dims 128c + 16gq + [0, 16) and 128c + 64 + 16gq + [0, 16)
-// (gq = lane/16), the same bytes it reads of each K row, so the contraction
-// pairs every q dim with the same K dim whatever order the instruction
-// assigns to a lane's 32 bytes.  Step 4: rope dims 512 + 16gq + [0, 16), then
-// 16 zero bytes (the K operand's matching half is any finite row data).
-struct GroupQ {
-  v8i_t part[5];
-};
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
@@ -94,8 +72,20 @@ typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8; all-ones leaves a counter unchecked).
 constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-constexpr int kVmcntOneTileOut = waitcnt_vm(kGLoads);  // all but the last tile's loads done
 constexpr int kVmcntNone = waitcnt_vm(0);
+
+// Waits until at most `tiles` tiles of this wave's ring loads are in flight
+// (kGLoads loads each; loads complete in order).
+__device__ __forceinline__ void wait_tiles_in_flight(int tiles) {
+  static_assert(kGRing - 2 == 4, "one case per possible count");
+  switch (tiles) {
+    case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(1 * kGLoads)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kGLoads)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kGLoads)); break;
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * kGLoads)); break;
+  }
+}
 
 __device__ __forceinline__ void uniformize(GCursor& c) {
   c.b = uniform(c.b);
@@ -128,25 +118,26 @@ __device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
 }
 
 // Gathers tile `tile` of the current segment (rows at positions tile*32 + r,
-// clamped to the segment's last row) straight into ring tile kB
-// with global_load_lds_dwordx4: instruction k of wave wv writes LDS bytes
-// [(5wv + k) * 1024, +1024), lane l the 16 bytes of slot s = 64(5wv + k) + l,
-// which is staged row s / 37, chunk s % 37.  Lanes on a pad slot (chunk 36) or
-// past the last row load a duplicate of a real chunk that is never read.
-// Every load is unconditional, so the outstanding-load count is static.
-template <int kB>
+// clamped to the segment's last row) straight into ring slot `slot` with
+// global_load_lds_dwordx4: instruction k of wave wv writes LDS bytes
+// [(5wv + k) * 1024, +1024) of the slot, lane l the 16 bytes of slot position
+// s = 64(5wv + k) + l, which is staged row s / 37, chunk s % 37.  Lanes on a
+// pad position (chunk 36) or past the last row load a duplicate of a real
+// chunk that is never read.  Every load is unconditional, so the
+// outstanding-load count is static.
 __device__ __forceinline__ void group_issue(const DecodeParams& p, const int32_t* sidx, int rows,
-                                            int tile, int wv, int lane) {
-  const uint32_t dst = lds_addr_of(ring<kB>()) + 1024u * (uint32_t)(uniform(wv) * kGLoads);
+                                            int tile, int slot, int wv, int lane) {
+  const uint32_t dst = lds_addr_of(g_ring) + (uint32_t)(uniform(slot) * kGTileBytes) +
+                       1024u * (uint32_t)(uniform(wv) * kGLoads);
   const uint32_t last_row = (uint32_t)lmin(p.pool_entries - 1, 0x7FFFFFFF);
   // All source addresses first (their index reads overlap), then the loads
   // (each asm statement orders the memory operations around it).
   const uint8_t* src[kGLoads];
 #pragma unroll
   for (int k = 0; k < kGLoads; ++k) {
-    const int slot = (wv * kGLoads + k) * 64 + lane;
-    const int row = imin(slot / kGRowSlots, kGTile - 1);
-    const int ch = imin(slot - (slot / kGRowSlots) * kGRowSlots, kGChunks - 1);
+    const int s = (wv * kGLoads + k) * 64 + lane;
+    const int row = imin(s / kGRowSlots, kGTile - 1);
+    const int ch = imin(s - (s / kGRowSlots) * kGRowSlots, kGChunks - 1);
     // Clamp to the pool without branches (a negative index becomes the last row).
     const uint32_t r = umin((uint32_t)sidx[imin(tile * kGTile + row, rows - 1)], last_row);
     src[k] = p.kv + (uint64_t)r * kRowDim + 16 * ch;
@@ -155,152 +146,198 @@ __device__ __forceinline__ void group_issue(const DecodeParams& p, const int32_t
   for (int k = 0; k < kGLoads; ++k) lds_dma_16(src[k], dst + 1024u * k);
 }
 
-// One shared 32-row tile for this wave's row group.  `base` is the piece
-// position of the tile's first row; positions >= rows_w are masked.
-template <int kB>
-__device__ __forceinline__ void group_tile(WaveState& st, const GroupQ& q, int base, int rows_w,
-                                           float cs, int n, int gq) {
-  const uint8_t* buf = ring<kB>();
-  // S^T for the tile's 16-row blocks, one independent MFMA chain each, all
-  // on v_mfma_scale_f32_16x16x128_f8f6f4 (fp8 operands, unit scales: E8M0
-  // 127 = 2^0).  The chain must not mix MFMA kinds: a 16x16x32 fp8 step that
-  // reads this 8-pass MFMA's result as its accumulator right behind it gets
-  // garbage, and the compiler does not separate the two.
-  v4f s[kGBlocks];
+// Per-wave state: O^T for the wave's 32 query rows (32x32 MFMA layout: lane l
+// holds row lane%32, dims 32*blk + 8*(v/4) + 4*(l/32) + v%4 in O[blk][v]);
+// for row lane%32 (equal in lanes l and l^32) the reference m of P = 2^(s - m),
+// the largest score seen and whether a score exceeded m + kPBig; this lane's
+// partial sum of P.
+struct WideState {
+  v16f O[16];
+  float m;
+  float mx;
+  float l;
+  bool big;
+};
+
+// Lane-specific LDS offsets within a ring slot.
+struct TileOffsets {
+  int k;     // K operand: row lane%32, bytes 32*(lane/32) of each 64-byte chunk
+  int v[2];  // V^T transpose-read source for the two 16-row P.V steps
+};
+
+// One shared 32-row tile for this wave's 32 query rows.  lim: the number of
+// the tile's rows that row lane%32 may see (<= 0: none); full: every row of
+// the wave sees every row of the tile (no masking).
+__device__ __forceinline__ void wide_tile(WideState& st, const v8i_t (&q)[9], const uint8_t* buf,
+                                          const TileOffsets& off, int lim, bool full, float cs,
+                                          int h) {
+  // S^T (32 KV rows x 32 query rows): nine 64-dim steps, one accumulator chain
+  // on a single MFMA kind.  The q bytes a lane holds for a step are the same
+  // dims it reads of each K row, so any order the instruction gives a lane's
+  // 32 bytes pairs equal dims.
+  v16f s;
 #pragma unroll
-  for (int b = 0; b < kGBlocks; ++b) s[b] = v4f{0.f, 0.f, 0.f, 0.f};
-  uint4 hi[kGBlocks];
+  for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-  for (int c = 0; c < 5; ++c) {
-    v8i_t kc[kGBlocks];
-#pragma unroll
-    for (int b = 0; b < kGBlocks; ++b) {
-      const uint8_t* row = buf + (16 * b + n) * kGStride + 128 * c + 16 * gq;
-      const uint4 a0 = *(const uint4*)row;
-      if (c < 4) hi[b] = *(const uint4*)(row + 64);  // step 4 reuses step 3's (q is zero there)
-      kc[b] = v8i_t{(int)a0.x,    (int)a0.y,    (int)a0.z,    (int)a0.w,
-                    (int)hi[b].x, (int)hi[b].y, (int)hi[b].z, (int)hi[b].w};
-    }
-#pragma unroll
-    for (int b = 0; b < kGBlocks; ++b)
-      s[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc[b], q.part[c], s[b], 0, 0, 0,
-                                                              127, 0, 127);
+  for (int c = 0; c < 9; ++c) {
+    const uint8_t* kp = buf + off.k + 64 * c;
+    const uint4 a0 = *(const uint4*)kp, a1 = *(const uint4*)(kp + 16);
+    const v8i_t ka = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, q[c], s, 0, 0, 0, 127, 0, 127);
   }
 
-  // Row lane%16; this lane holds kv rows 16b + 4gq + i of the tile.
-  float x[4 * kGBlocks];
+  // Value v of this lane is KV row 8*(v/4) + 4h + v%4 of the tile.
+  float x[16];
 #pragma unroll
-  for (int b = 0; b < kGBlocks; ++b)
+  for (int v = 0; v < 16; ++v) x[v] = s[v] * cs;
+  if (!full) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      x[4 * b + i] = (base + 16 * b + 4 * gq + i < rows_w) ? s[b][i] * cs : neg_inf();
-  softmax_update<4 * kGBlocks>(st, x);
+    for (int v = 0; v < 16; ++v)
+      x[v] = (8 * (v >> 2) + 4 * h + (v & 3) < lim) ? x[v] : neg_inf();
+  }
+  float tmax = x[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                                     false, false);
+    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max over lanes l, l^32
+  }
+  // The reference m is fixed at a row's first visible score maximum and never
+  // raised, so O is never rescaled inside the tile loop (O lives in the
+  // accumulator registers, where a rescale would cost a copy of all of it).
+  // P = 2^(s - m) may exceed 1; a row whose scores rise more than 2^kPBig
+  // above m sets `big` and the piece is redone with m = its true maximum.
+  // Before its first visible score m is -FLT_MAX (finite), which keeps
+  // P = 2^(-inf) = 0 for masked entries instead of NaN.
+  st.mx = fmaxf(st.mx, tmax);
+  st.m = (st.m == -__FLT_MAX__ && tmax > neg_inf()) ? tmax : st.m;
+  st.big = st.big || (tmax > st.m + kPBig);
+  float psum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    x[v] = fast_exp2(fminf(x[v] - st.m, kPBig));
+    psum += x[v];
+  }
+  st.l += psum;
 
-  // O^T += V^T . P^T over the tile's 32-row steps on v_mfma_f32_16x16x32_bf16.
-  // Within a step, operand element k = 8gq + j is kv row kappa(gq, j) =
-  // 4gq + j (j < 4), 16 + 4gq + j - 4: the rows this lane's S^T holds, so P^T
-  // is this lane's own probabilities in bf16 (about 16 significant bits).
-  // V^T comes from the row-major tile through the LDS transpose read: within
-  // each 16-lane group g, lane 2b + h addresses kv row kappa(g, b) at dims
-  // 16*blk + 8h, and lane i receives byte i of the 16 dims from each of the
-  // rows kappa(g, 0..7), i.e. its fp8 operand for dim 16*blk + i, widened
-  // exactly to bf16.
+  // P^T operands: step u takes this lane's values 8u .. 8u+7, i.e. KV rows
+  // kappa(h, j) = 16u + 8*(j/4) + 4h + j%4 for k index 8h + j.
+  v8bf_t pb[2];
 #pragma unroll
-  for (int h = 0; h < kGHalves; ++h) {
-    v8bf_t pb;
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pb[i] = (__bf16)x[8 * h + i];
-      pb[4 + i] = (__bf16)x[8 * h + 4 + i];
-    }
-    const int sl = n;  // lane within its 16-lane group
-    const int jr = sl >> 1;
-    const int krow = 32 * h + ((jr < 4) ? (4 * gq + jr) : (16 + 4 * gq + (jr - 4)));
-    const uint8_t* vbase = buf + krow * kGStride + 8 * (sl & 1);
+    for (int j = 0; j < 8; ++j) pb[u][j] = (__bf16)x[8 * u + j];
+
+  // O^T += V^T . P^T.  The transpose read gives lane l byte j = V[kappa(l/32,
+  // j)][32*blk + l%32]: its A operand row l%32, k index 8*(l/32) + j, widened
+  // exactly from fp8 to bf16.  The two steps of a block are 16 MFMAs apart.
 #pragma unroll
-    for (int blk = 0; blk < 32; ++blk) {
-      const v2i_t a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(vbase + 16 * blk));
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int blk = 0; blk < 16; ++blk) {
+      const v2i_t a =
+          __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(buf + off.v[u] + 32 * blk));
       const v2bf_t a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((u32)a.x, 1.0f, false);
       const v2bf_t a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((u32)a.x, 1.0f, true);
       const v2bf_t a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((u32)a.y, 1.0f, false);
       const v2bf_t a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((u32)a.y, 1.0f, true);
       const v8bf_t va = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-      st.O[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.O[blk], 0, 0, 0);
+      st.O[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], st.O[blk], 0, 0, 0);
     }
   }
 }
 
-// Consume tile tt from ring tile kB after issuing tile tt+2 into ring tile
-// (kB + 2) % 3 (the one every wave finished before this step's barrier).
-template <int kB>
-__device__ __forceinline__ void group_step(const DecodeParams& p, GroupShared& sh, WaveState& st,
-                                           const GroupQ& q, int seg0, int srows, int ntiles,
-                                           int tt, int rows_w, float cs, int wv, int lane, int n,
-                                           int gq) {
-  __builtin_amdgcn_s_waitcnt(kVmcntOneTileOut);
-  __syncthreads();  // tile tt is in LDS; every wave is done with tile tt-1
-  group_issue<(kB + 2) % kGRing>(p, sh.idx, srows, imin(tt + 2, ntiles - 1), wv, lane);
-  const int base = seg0 + tt * kGTile;
-  if (base < rows_w) group_tile<kB>(st, q, base, rows_w, cs, n, gq);
-}
-
 // One piece: positions [c.k, c.k + len) of unit c.u of request c.b (unit
-// length L).  slot_base < 0: the piece is the whole unit and every wave writes
-// o / lse; else wave wv writes partial slot slot_base + wv.
+// length L).  slot_base < 0: the piece is the whole unit and every row group
+// writes o / lse; else row group i of the unit writes partial slot
+// slot_base + i.
 __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& sh,
                                             const GCursor& c, int G, int L, int len,
                                             int slot_base, int w, float cs, float ks) {
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
+  const int tid = threadIdx.x, wv = uniform(tid >> 6), lane = tid & 63;
+  const int h = lane >> 5, hq = lane & 31, half = hq >> 4, n16 = hq & 15;
   const int R = c.r.qlen * G;
-  const int rg = kGroupsPerUnit * c.u + wv;
+  const bool complete = slot_base < 0;
+
+  // The wave's two row groups (uniform), then this lane's.
+  int rows_h[2], vis_h[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int rgk = kGroupsPerUnit * c.u + wv + kWaves * k;
+    const int jk = imin(rgk, R - 1) / G;
+    vis_h[k] = rgk < R ? visible(c.r.n, c.r.qlen, jk) : 0;
+    rows_h[k] = imax(0, imin(vis_h[k] - c.k, len));
+  }
+  const int wave_rows = imax(rows_h[0], rows_h[1]);
+  const int full_rows = imin(rows_h[0], rows_h[1]);
+  const int ulocal = wv + kWaves * half;  // this lane's row group within the unit
+  const int rg = kGroupsPerUnit * c.u + ulocal;
   const bool valid = rg < R;
   const int rgc = imin(rg, R - 1);
   const int j = rgc / G, g = rgc - j * G;
   const int t = c.r.q_base + j;
-  const int vw = valid ? visible(c.r.n, c.r.qlen, j) : 0;
-  const int rows_w = imax(0, imin(vw - c.k, len));  // positions this wave may see
-  const bool complete = slot_base < 0;
+  const int vw = half ? vis_h[1] : vis_h[0];
+  const int rows_w = half ? rows_h[1] : rows_h[0];
 
-  // Split-unit descriptor of this wave's row group (see mla_decode.hip):
-  // written by the workers holding the unit's first and last pieces.
-  if (lane == 0 && valid && vw > 0) {
+  // Split-unit descriptor of each row group (see mla_decode.hip): written by
+  // the workers holding the unit's first and last pieces.
+  if ((lane == 0 || lane == 16) && valid && vw > 0) {
     int* d = (int*)(p.desc + ((int64_t)t * G + g));
     if (c.k == 0) {
       d[0] = w;
-      d[2] = complete ? 0 : slot_base + wv;
+      d[2] = complete ? 0 : slot_base + ulocal;
       d[3] = complete ? 0 : 1;
     }
     if (!complete && c.k + len == L) d[1] = w;
   }
 
-  __syncthreads();  // the previous piece is done with the LDS tiles and indices
+  __syncthreads();  // the previous piece is done with the LDS ring and indices
 
-  // q of this wave's row group (registers) and the first index batch, in one
-  // round trip.
+  // q rows of this lane's row group (registers) and the first index batch, in
+  // one round trip.  Step c: head n16's bytes [64c + 32h, +32).
   const int kv_pos0 = c.r.kv_base + c.k;
-  GroupQ q;
+  v8i_t q[9];
   {
-    const uint8_t* qrow = p.q + ((int64_t)t * p.num_heads + g * kGroup + n) * kRowDim + 16 * gq;
-    uint4 xq[9];
+    const uint8_t* qrow =
+        p.q + ((int64_t)t * p.num_heads + g * kGroup + n16) * kRowDim + 32 * h;
+    uint4 xq[18];
 #pragma unroll
-    for (int cc = 0; cc < 9; ++cc) xq[cc] = *(const uint4*)(qrow + 64 * cc);
+    for (int i = 0; i < 18; ++i) xq[i] = *(const uint4*)(qrow + 64 * (i >> 1) + 16 * (i & 1));
     stage_first_indices(sh.idx, p.kv_indices + kv_pos0, imin(len, kGIdxSeg));
 #pragma unroll
-    for (int c = 0; c < 5; ++c) {
-      const uint4 a0 = xq[2 * c], a1 = (c < 4) ? xq[2 * c + 1] : make_uint4(0, 0, 0, 0);
-      q.part[c] = v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                        (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    for (int cc = 0; cc < 9; ++cc) {
+      const uint4 a0 = xq[2 * cc], a1 = xq[2 * cc + 1];
+      q[cc] = v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                    (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     }
     // Nothing the compiler tracks may be outstanding once the untracked tile
     // loads start: a later wait for q would also wait for those.
     __builtin_amdgcn_s_waitcnt(kVmcntNone);
   }
 
-  WaveState st;
+  TileOffsets off;
+  off.k = hq * kGStride + 32 * h;
 #pragma unroll
-  for (int b = 0; b < 32; ++b) st.O[b] = v4f{0.f, 0.f, 0.f, 0.f};
-  st.m = neg_inf();
+  for (int u = 0; u < 2; ++u) {
+    // Transpose-read source: 16-lane group gg = lane/16, position i = lane%16
+    // supplies KV row kappa(gg/2, i/2) at dims 16*(gg%2) + 8*(i%2) of the block.
+    const int gg = lane >> 4, i = lane & 15, b = i >> 1;
+    const int krow = 16 * u + 8 * (b >> 2) + 4 * (gg >> 1) + (b & 3);
+    off.v[u] = krow * kGStride + 16 * (gg & 1) + 8 * (i & 1);
+  }
+
+  WideState st;
+  st.m = -__FLT_MAX__;
+  st.mx = neg_inf();
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+  for (int b = 0; b < 16; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.O[b][i] = 0.f;
   st.l = 0.f;
+  st.big = false;
 
   for (int seg0 = 0; seg0 < len; seg0 += kGIdxSeg) {
     const int srows = imin(kGIdxSeg, len - seg0);
@@ -309,55 +346,80 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
                   srows);
     __syncthreads();
     const int ntiles = (srows + kGTile - 1) / kGTile;
-    // Ring of three tiles: while tile tt is consumed, tiles tt+1 and tt+2 are
-    // in flight.  Before the barrier that publishes tile tt, each wave waits
-    // until its own loads of tile tt have landed (the 5 loads of tile tt+1,
-    // issued later, may stay outstanding).  The loop is unrolled by the ring
-    // size so that every ring tile is named statically.
-    group_issue<0>(p, sh.idx, srows, 0, wv, lane);
-    group_issue<1>(p, sh.idx, srows, imin(1, ntiles - 1), wv, lane);
-    for (int tt = 0; tt < ntiles; tt += kGRing) {
-      group_step<0>(p, sh, st, q, seg0, srows, ntiles, tt, rows_w, cs, wv, lane, n, gq);
-      if (tt + 1 < ntiles)
-        group_step<1>(p, sh, st, q, seg0, srows, ntiles, tt + 1, rows_w, cs, wv, lane, n, gq);
-      if (tt + 2 < ntiles)
-        group_step<2>(p, sh, st, q, seg0, srows, ntiles, tt + 2, rows_w, cs, wv, lane, n, gq);
+    // Ring of six tiles: up to four later tiles are in flight while tile t is
+    // consumed; tile t+5 is issued into the slot of tile t-1 after the barrier
+    // that shows every wave done with it.  Before that barrier each wave waits
+    // until its own loads of tile t have landed.
+#pragma unroll
+    for (int i = 0; i < kGRing - 1; ++i)
+      if (i < ntiles) group_issue(p, sh.idx, srows, i, i, wv, lane);
+    int slot = 0;
+    for (int tt = 0; tt < ntiles; ++tt) {
+      wait_tiles_in_flight(imin(ntiles - 1, tt + kGRing - 2) - tt);
+      __syncthreads();  // tile tt is in LDS; every wave is done with tile tt-1
+      const int nslot = (slot == 0) ? kGRing - 1 : slot - 1;
+      if (tt + kGRing - 1 < ntiles)
+        group_issue(p, sh.idx, srows, tt + kGRing - 1, nslot, wv, lane);
+      const int base = seg0 + tt * kGTile;
+      if (base < wave_rows)
+        wide_tile(st, q, g_ring + slot * kGTileBytes, off, rows_w - base,
+                  base + kGTile <= full_rows, cs, h);
+      slot = (slot == kGRing - 1) ? 0 : slot + 1;
     }
-    __builtin_amdgcn_s_waitcnt(kVmcntNone);  // drain the tail loads before LDS is reused
+    __builtin_amdgcn_s_waitcnt(kVmcntNone);  // every ring load has landed
     __syncthreads();
   }
+  // Redo the piece (all waves: the tiles are gathered together) if any row's
+  // scores rose too far above its reference; then m is the row's maximum.
+  if (pass == 0) {
+    if ((tid & 63) == 0) sh.flag[wv] = __any(st.big) ? 1 : 0;
+    __syncthreads();
+    const int redo = sh.flag[0] | sh.flag[1] | sh.flag[2] | sh.flag[3];
+    __syncthreads();
+    if (!redo) break;
+    st.m = (st.mx == neg_inf()) ? -__FLT_MAX__ : st.mx;
+  }
+  }
 
-  if (!valid) return;
   float Lsum = st.l;
-  Lsum += __shfl_xor(Lsum, 16);
-  Lsum += __shfl_xor(Lsum, 32);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(Lsum), __float_as_uint(Lsum),
+                                                     false, false);
+    Lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  if (!valid) return;
   if (complete && vw == 0) return;  // the row group sees nothing: o / lse written elsewhere
 
-  // Lane (n, gq) holds dims 16*blk + 4gq + r of row n in O^T block blk,
-  // element r.
   const bool empty = rows_w == 0;  // only in a split piece: contributes weight 0
   const float oscale = empty ? 0.f : ks / Lsum;
   const float lse_val = empty ? neg_inf() : (st.m + fast_log2(Lsum)) * kLn2;
   if (complete) {
-    const int64_t orow = (int64_t)t * p.num_heads + g * kGroup + n;
-    uint16_t* dst = p.o + orow * kLatent + 4 * gq;
+    const int64_t orow = (int64_t)t * p.num_heads + g * kGroup + n16;
+    uint16_t* dst = p.o + orow * kLatent + 4 * h;
 #pragma unroll
-    for (int blk = 0; blk < 32; ++blk) {
-      uint2 pk;
-      pk.x = bf16_bits(st.O[blk][0] * oscale) | (bf16_bits(st.O[blk][1] * oscale) << 16);
-      pk.y = bf16_bits(st.O[blk][2] * oscale) | (bf16_bits(st.O[blk][3] * oscale) << 16);
-      *(uint2*)(dst + 16 * blk) = pk;
-    }
-    if (p.lse != nullptr && gq == 0) p.lse[orow] = lse_val;
+    for (int blk = 0; blk < 16; ++blk)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint2 pk;
+        pk.x = bf16_bits(st.O[blk][4 * q4 + 0] * oscale) |
+               (bf16_bits(st.O[blk][4 * q4 + 1] * oscale) << 16);
+        pk.y = bf16_bits(st.O[blk][4 * q4 + 2] * oscale) |
+               (bf16_bits(st.O[blk][4 * q4 + 3] * oscale) << 16);
+        *(uint2*)(dst + 32 * blk + 8 * q4) = pk;
+      }
+    if (p.lse != nullptr && h == 0) p.lse[orow] = lse_val;
     return;
   }
-  const int64_t slot = slot_base + wv;
-  float* dst = p.part_o + (slot * kGroup + n) * kLatent + 4 * gq;
+  const int64_t slot_id = slot_base + ulocal;
+  float* dst = p.part_o + (slot_id * kGroup + n16) * kLatent + 4 * h;
 #pragma unroll
-  for (int blk = 0; blk < 32; ++blk)
-    *(float4*)(dst + 16 * blk) = make_float4(st.O[blk][0] * oscale, st.O[blk][1] * oscale,
-                                             st.O[blk][2] * oscale, st.O[blk][3] * oscale);
-  if (gq == 0) p.part_lse[slot * kGroup + n] = lse_val;
+  for (int blk = 0; blk < 16; ++blk)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *(float4*)(dst + 32 * blk + 8 * q4) =
+          make_float4(st.O[blk][4 * q4 + 0] * oscale, st.O[blk][4 * q4 + 1] * oscale,
+                      st.O[blk][4 * q4 + 2] * oscale, st.O[blk][4 * q4 + 3] * oscale);
+  if (h == 0) p.part_lse[slot_id * kGroup + n16] = lse_val;
 }
 
 // One worker: locate its share of the group-mode stream and run its pieces.
@@ -433,9 +495,9 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
   }
 }
 
-// Two workgroups per CU (two waves per SIMD): one wave's softmax and LDS
-// latency overlap the other's MFMAs.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// One workgroup per CU: the four waves (one per SIMD) each hold 256 O^T
+// accumulators and use the whole register file.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_groups_fp8_kernel(const DecodeParams p) {
   __shared__ GroupShared sh;
   group_worker(p, sh);

@@ -30,8 +30,8 @@ struct DecodeParams {
 };
 
 // Partial-answer slots per worker: a worker holds at most two partial pieces,
-// each covering one row group, or kGroupsPerUnit (4) row groups in group mode.
-inline int slots_per_worker(bool group_mode) { return group_mode ? 8 : 2; }
+// each covering one row group, or kGroupsPerUnit (8) row groups in group mode.
+inline int slots_per_worker(bool group_mode) { return group_mode ? 16 : 2; }
 
 // Workspace layout for `num_workers` workers, `slots` partial slots per worker
 // and `num_units` = tokens * head groups (every byte the kernels read is
@@ -56,7 +56,7 @@ inline size_t workspace_bytes(int num_workers, int64_t num_units, int slots) {
 }
 
 // kv_dtype: 0 = fp8 e4m3fn, 1 = bf16.  group_mode selects the group-mode
-// kernels (fp8 only; the workspace then has 8 slots per worker).
+// kernels (fp8 only; the workspace then has 16 slots per worker).
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, bool group_mode, hipStream_t stream);
 // The group-mode decode kernel alone (mla_decode_groups.hip).
 hipError_t launch_decode_groups(const DecodeParams& p, hipStream_t stream);

@@ -156,16 +156,19 @@ MLA_HD bool cursor_next_unit(Cursor& c, const int32_t* qo, const int32_t* kvp, i
 }
 
 // ---- Group mode: a unit is kGroupsPerUnit consecutive row groups of one
-// request, processed by one workgroup over one shared KV range (each wave one
-// row group).  Row group rg = j * G + g (token j, head group g); unit u covers
-// row groups [4u, 4u + 4) of the request's qlen * G and is as long as the
+// request, processed by one workgroup over one shared KV range (each wave two
+// row groups).  Row group rg = j * G + g (token j, head group g); unit u covers
+// row groups [8u, 8u + 8) of the request's qlen * G and is as long as the
 // last of them sees (the others mask the entries they may not see).  Used when
-// a request has several row groups (many heads or several query tokens), where
-// a unit per row group would gather the same rows once per row group.
-constexpr int kGroupsPerUnit = 4;
+// a request may hold four or more row groups (many heads or several query
+// tokens), where a unit per row group would gather the same rows once per row
+// group; a unit with fewer than eight leaves some MFMA rows idle, which costs
+// less than the repeated gathers.
+constexpr int kGroupsPerUnit = 8;
+constexpr int kGroupModeMinRows = 4;
 
 MLA_HD bool use_group_mode(int G, int max_seqlen_q) {
-  return (int64_t)G * max_seqlen_q >= kGroupsPerUnit;
+  return (int64_t)G * max_seqlen_q >= kGroupModeMinRows;
 }
 
 MLA_HD int group_units(const Req& r, int G) {

@@ -14,6 +14,8 @@ from mla_latent_attention_amd import plan_groups_host, plan_host
 
 MIN_WORKER_ROWS = 512
 SNAP_ROWS = 64
+GROUPS_PER_UNIT = 8  # group mode: row groups per unit
+GROUP_SLOTS = 16  # group mode: partial slots per worker (two pieces x 8 row groups)
 
 
 def visible(n, qlen, j):
@@ -35,14 +37,15 @@ def units(qo, kv, G):
 
 def group_units(qo, kv, G):
     """Group mode: (request, unit, length, stream start) in stream order.  Unit u
-    of a request covers row groups 4u..4u+3 (row group = token * G + head
+    of a request covers row groups 8u..8u+7 (row group = token * G + head
     group) and is as long as its last row group sees."""
     out, pos = [], 0
+    U = GROUPS_PER_UNIT
     for b in range(len(qo) - 1):
         n, ql = kv[b + 1] - kv[b], qo[b + 1] - qo[b]
         R = ql * G
-        for u in range(-(-R // 4)):
-            last = min(4 * u + 3, R - 1)
+        for u in range(-(-R // U)):
+            last = min(U * u + U - 1, R - 1)
             v = visible(n, ql, last // G)
             out.append((b, u, v, pos))
             pos += v
@@ -210,14 +213,14 @@ def check_group_plan(qo, kv, H, nw_req):
             continue
         assert all(s[4] == 0 for s in segs)
         # The group combine reads, for the i-th worker after the first, slots
-        # 8 * (w0 + i) + wave: those workers must hold the unit as their first
-        # piece, in consecutive order; the first worker's slots start at
-        # 8 * w0, or 8 * w0 + 4 when the unit is not its first piece.
+        # 16 * (w0 + i) + row group: those workers must hold the unit as their
+        # first piece, in consecutive order; the first worker's slots start at
+        # 16 * w0, or 16 * w0 + 8 when the unit is not its first piece.
         wlo, whi = owner(start), owner(start + v - 1)
         assert [s[2] for s in segs] == list(range(wlo, whi + 1))
-        first = 8 * wlo + (4 if S[wlo] < start else 0)
+        first = GROUP_SLOTS * wlo + (GROUP_SLOTS // 2 if S[wlo] < start else 0)
         assert segs[0][3] == first
-        assert [s[3] for s in segs[1:]] == [8 * w for w in range(wlo + 1, whi + 1)]
+        assert [s[3] for s in segs[1:]] == [GROUP_SLOTS * w for w in range(wlo + 1, whi + 1)]
     per_worker = np.zeros(nw, dtype=np.int64)
     for w, b, u, kb, ke, *_ in pieces:
         per_worker[w] += ke - kb
@@ -236,12 +239,13 @@ def check_group_plan(qo, kv, H, nw_req):
 
 def test_group_plan_dcp_share_workload():
     """96 heads, 4 query tokens per request, 8 requests of 17,750 entries: 24
-    row groups per request, 6 units each, 512 workers."""
-    pieces = check_group_plan(indptr([4] * 8), indptr([17_750] * 8), 96, 512)
-    assert pieces[:, 2].max() == 5
-    # causal: unit lengths step up with the token of their last row group
+    row groups per request, 3 units each, 256 workers."""
+    pieces = check_group_plan(indptr([4] * 8), indptr([17_750] * 8), 96, 256)
+    assert pieces[:, 2].max() == 2
+    # causal: a unit is as long as the token of its last row group sees
+    # (row groups 0-7 end in token 1, 8-15 in token 2, 16-23 in token 3)
     lens = sorted(set(pieces[:, 5].tolist()))
-    assert lens == [17_747, 17_748, 17_749, 17_750]
+    assert lens == [17_748, 17_749, 17_750]
 
 
 def test_group_units_mask_within_unit():
@@ -249,7 +253,7 @@ def test_group_units_mask_within_unit():
     is the last token's visible count, the others see fewer."""
     us, W = group_units(indptr([4]), indptr([100]), 1)
     assert [(u, v) for _, u, v, _ in us] == [(0, 100)]
-    us, W = group_units(indptr([3]), indptr([100]), 2)  # 6 row groups: units of 4 and 2
+    us, W = group_units(indptr([5]), indptr([100]), 2)  # 10 row groups: units of 8 and 2
     assert [(u, v) for _, u, v, _ in us] == [(0, 99), (1, 100)]
 
 
