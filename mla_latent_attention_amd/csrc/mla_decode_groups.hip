@@ -65,8 +65,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef int v2i_t __attribute__((ext_vector_type(2)));
-typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
-typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+typedef float v2f_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
@@ -77,13 +76,12 @@ constexpr int kVmcntNone = waitcnt_vm(0);
 // Waits until at most `tiles` tiles of this wave's ring loads are in flight
 // (kGLoads loads each; loads complete in order).
 __device__ __forceinline__ void wait_tiles_in_flight(int tiles) {
-  static_assert(kGRing - 2 == 4, "one case per possible count");
+  static_assert(kGRing - 3 == 3, "one case per possible count");
   switch (tiles) {
     case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
     case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(1 * kGLoads)); break;
     case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kGLoads)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kGLoads)); break;
-    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * kGLoads)); break;
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kGLoads)); break;
   }
 }
 
@@ -159,33 +157,68 @@ struct WideState {
   bool big;
 };
 
+// P^T operands of one 64-row P.V step (two tiles), as fp8 hi + lo parts.
+// Byte 16*tau + v of a lane is the lane's value v of tile tau of the pair
+// (KV row 8*(v/4) + 4*(lane/32) + v%4 of that tile).  On the MFMA's k axis a
+// 32-value scale block is bytes 16b .. 16b+15 of lanes n and n+32, i.e. one
+// tile of one query row, with its E8M0 scale in lane n + 32b: e[tau] is the
+// row's exponent for tile tau.
+struct PairP {
+  v8i_t hi, lo;
+  int e[2];
+};
+
 // Lane-specific LDS offsets within a ring slot.
 struct TileOffsets {
   int k;     // K operand: row lane%32, bytes 32*(lane/32) of each 64-byte chunk
-  int v[2];  // V^T transpose-read source for the two 16-row P.V steps
+  int v[2];  // V^T transpose-read source for the two 16-row halves of a tile
 };
 
-// One shared 32-row tile for this wave's 32 query rows.  lim: the number of
-// the tile's rows that row lane%32 may see (<= 0: none); full: every row of
-// the wave sees every row of the tile (no masking).
-__device__ __forceinline__ void wide_tile(WideState& st, const v8i_t (&q)[9], const uint8_t* buf,
-                                          const TileOffsets& off, int lim, bool full, float cs,
-                                          int h) {
-  // S^T (32 KV rows x 32 query rows): nine 64-dim steps, one accumulator chain
-  // on a single MFMA kind.  The q bytes a lane holds for a step are the same
-  // dims it reads of each K row, so any order the instruction gives a lane's
-  // 32 bytes pairs equal dims.
+// S^T = K.Q^T as a chain of nine v_mfma_scale_f32_32x32x64_f8f6f4 steps
+// (unit E8M0 scales in `sc` = 127) with the accumulator in vector registers.
+// Written as inline assembly because the compiler puts an MFMA result in the
+// accumulator registers, which here all hold O^T: it would then move a block
+// of O^T out and back on every tile.  Same-kind steps may feed each other
+// back to back; the trailing 20 wait states cover the latency of the last
+// step's result before the vector ALU reads it (the compiler does not see the
+// MFMA inside the assembly).
+__device__ __forceinline__ v16f qk_chain(const v8i_t (&k)[9], const v8i_t (&q)[9], int sc) {
   v16f s;
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
+               : "=&v"(s)
+               : "v"(k[0]), "v"(q[0]), "v"(sc));
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] = 0.f;
+  for (int c = 1; c < 8; ++c)
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "+v"(s)
+                 : "v"(k[c]), "v"(q[c]), "v"(sc));
+  asm volatile(
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]\n\t"
+      "s_nop 15\n\ts_nop 3"
+      : "+v"(s)
+      : "v"(k[8]), "v"(q[8]), "v"(sc));
+  return s;
+}
+
+// Scores of one shared 32-row tile for this wave's 32 query rows and their
+// P operands (tile kTau of the current pair).  lim: the number of the tile's
+// rows that row lane%32 may see (<= 0: none); full: every row of the wave
+// sees every row of the tile (no masking).
+template <int kTau>
+__device__ __forceinline__ void tile_scores(WideState& st, PairP& pp, const v8i_t (&q)[9],
+                                            const uint8_t* buf, const TileOffsets& off, int lim,
+                                            bool full, float cs, int h, int sc) {
+  // All nine K operands are read before the first step, so the chain waits
+  // for one LDS round trip, not nine.
+  v8i_t ka[9];
 #pragma unroll
   for (int c = 0; c < 9; ++c) {
     const uint8_t* kp = buf + off.k + 64 * c;
     const uint4 a0 = *(const uint4*)kp, a1 = *(const uint4*)(kp + 16);
-    const v8i_t ka = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-    s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, q[c], s, 0, 0, 0, 127, 0, 127);
+    ka[c] = v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                  (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
   }
+  const v16f s = qk_chain(ka, q, sc);
 
   // Value v of this lane is KV row 8*(v/4) + 4h + v%4 of the tile.
   float x[16];
@@ -214,38 +247,54 @@ __device__ __forceinline__ void wide_tile(WideState& st, const v8i_t (&q)[9], co
   st.mx = fmaxf(st.mx, tmax);
   st.m = (st.m == -__FLT_MAX__ && tmax > neg_inf()) ? tmax : st.m;
   st.big = st.big || (tmax > st.m + kPBig);
+  // The tile's block exponent: P' = P * 2^-e <= 2^8 for the tile's row max,
+  // within fp8 range; entries far below it lose nothing that matters next to
+  // the block maximum (the hi + lo pair keeps about 8 significant bits).
+  const float rel = tmax - st.m;
+  int e = tmax > neg_inf() ? (int)__builtin_ceilf(fminf(fmaxf(rel, -200.f), 200.f)) - 8 : 0;
+  e = imin(imax(e, -127), 127);
+  const float mref = st.m + (float)e;
   float psum = 0.f;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    x[v] = fast_exp2(fminf(x[v] - st.m, kPBig));
+    x[v] = fast_exp2(x[v] - mref);
     psum += x[v];
   }
-  st.l += psum;
+  st.l += __builtin_ldexpf(psum, e);
+  pp.e[kTau] = e;
+  // fp8 hi part, then the residual as fp8 lo (same block scale).
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 0], x[4 * w + 1], 0, false);
+    hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 2], x[4 * w + 3], hw, true);
+    const v2f_t h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+    const v2f_t h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 0] - h01[0], x[4 * w + 1] - h01[1], 0, false);
+    lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 2] - h23[0], x[4 * w + 3] - h23[1], lw, true);
+    pp.hi[4 * kTau + w] = hw;
+    pp.lo[4 * kTau + w] = lw;
+  }
+}
 
-  // P^T operands: step u takes this lane's values 8u .. 8u+7, i.e. KV rows
-  // kappa(h, j) = 16u + 8*(j/4) + 4h + j%4 for k index 8h + j.
-  v8bf_t pb[2];
+// O^T += V^T . P^T over the pair's 64 rows on v_mfma_scale_f32_32x32x64_f8f6f4
+// (hi and lo parts of P, one step each per 32-dim block).  The A operand is
+// V^T straight from the row-major fp8 tiles by the LDS transpose read: read
+// (tile tau, half u) gives lane l byte j = V[kappa(l/32, j)][32*blk + l%32],
+// operand bytes 16*tau + 8*u + j, the same KV rows as the P bytes.
+__device__ __forceinline__ void pair_pv(WideState& st, const PairP& pp, const uint8_t* buf0,
+                                        const uint8_t* buf1, const TileOffsets& off, int h) {
+  const int sc = 127 + (h ? pp.e[1] : pp.e[0]);  // block tau's scale sits in lanes with l/32 = tau
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pb[u][j] = (__bf16)x[8 * u + j];
-
-  // O^T += V^T . P^T.  The transpose read gives lane l byte j = V[kappa(l/32,
-  // j)][32*blk + l%32]: its A operand row l%32, k index 8*(l/32) + j, widened
-  // exactly from fp8 to bf16.  The two steps of a block are 16 MFMAs apart.
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-#pragma unroll
-    for (int blk = 0; blk < 16; ++blk) {
-      const v2i_t a =
-          __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(buf + off.v[u] + 32 * blk));
-      const v2bf_t a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((u32)a.x, 1.0f, false);
-      const v2bf_t a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((u32)a.x, 1.0f, true);
-      const v2bf_t a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((u32)a.y, 1.0f, false);
-      const v2bf_t a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((u32)a.y, 1.0f, true);
-      const v8bf_t va = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-      st.O[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], st.O[blk], 0, 0, 0);
-    }
+  for (int blk = 0; blk < 16; ++blk) {
+    const v2i_t a0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(buf0 + off.v[0] + 32 * blk));
+    const v2i_t a1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(buf0 + off.v[1] + 32 * blk));
+    const v2i_t a2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(buf1 + off.v[0] + 32 * blk));
+    const v2i_t a3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(buf1 + off.v[1] + 32 * blk));
+    const v8i_t va = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+    st.O[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pp.hi, st.O[blk], 0, 0, 0, 127,
+                                                                0, sc);
+    st.O[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pp.lo, st.O[blk], 0, 0, 0, 127,
+                                                                0, sc);
   }
 }
 
@@ -328,6 +377,7 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
     off.v[u] = krow * kGStride + 16 * (gg & 1) + 8 * (i & 1);
   }
 
+  const int sc = uniform(127);  // E8M0 scale 2^0 for both MFMA operands
   WideState st;
   st.m = -__FLT_MAX__;
   st.mx = neg_inf();
@@ -346,25 +396,49 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
                   srows);
     __syncthreads();
     const int ntiles = (srows + kGTile - 1) / kGTile;
-    // Ring of six tiles: up to four later tiles are in flight while tile t is
-    // consumed; tile t+5 is issued into the slot of tile t-1 after the barrier
-    // that shows every wave done with it.  Before that barrier each wave waits
-    // until its own loads of tile t have landed.
+    // Ring of six tiles: P.V takes the tiles in pairs, so a tile's slot is
+    // reused two steps later.  At step t tile t+4 is issued into the slot of
+    // tile t-2 after the barrier that shows every wave done with it, so up to
+    // three later tiles are in flight while tile t is consumed.  Before that
+    // barrier each wave waits until its own loads of tile t have landed.
 #pragma unroll
-    for (int i = 0; i < kGRing - 1; ++i)
+    for (int i = 0; i < kGRing - 2; ++i)
       if (i < ntiles) group_issue(p, sh.idx, srows, i, i, wv, lane);
-    int slot = 0;
-    for (int tt = 0; tt < ntiles; ++tt) {
-      wait_tiles_in_flight(imin(ntiles - 1, tt + kGRing - 2) - tt);
-      __syncthreads();  // tile tt is in LDS; every wave is done with tile tt-1
-      const int nslot = (slot == 0) ? kGRing - 1 : slot - 1;
-      if (tt + kGRing - 1 < ntiles)
-        group_issue(p, sh.idx, srows, tt + kGRing - 1, nslot, wv, lane);
-      const int base = seg0 + tt * kGTile;
-      if (base < wave_rows)
-        wide_tile(st, q, g_ring + slot * kGTileBytes, off, rows_w - base,
-                  base + kGTile <= full_rows, cs, h);
-      slot = (slot == kGRing - 1) ? 0 : slot + 1;
+    auto publish = [&](int tt) {
+      wait_tiles_in_flight(imin(ntiles - 1, tt + kGRing - 3) - tt);
+      __syncthreads();  // tile tt is in LDS; every wave is done with tile tt-2
+      if (tt + kGRing - 2 < ntiles)
+        group_issue(p, sh.idx, srows, tt + kGRing - 2, (tt + kGRing - 2) % kGRing, wv, lane);
+    };
+    for (int tt = 0; tt < ntiles; tt += 2) {
+      PairP pp;
+      const uint8_t* buf0 = g_ring + (tt % kGRing) * kGTileBytes;
+      const int base0 = seg0 + tt * kGTile;
+      publish(tt);
+      if (base0 < wave_rows) {
+        tile_scores<0>(st, pp, q, buf0, off, rows_w - base0, base0 + kGTile <= full_rows, cs, h, sc);
+      } else {
+        pp.hi = v8i_t{};
+        pp.lo = v8i_t{};
+        pp.e[0] = 0;
+      }
+      const uint8_t* buf1 = buf0;  // an odd last tile pairs with itself at P = 0
+      const int base1 = base0 + kGTile;
+      if (tt + 1 < ntiles) {
+        buf1 = g_ring + ((tt + 1) % kGRing) * kGTileBytes;
+        publish(tt + 1);
+      }
+      if (tt + 1 < ntiles && base1 < wave_rows) {
+        tile_scores<1>(st, pp, q, buf1, off, rows_w - base1, base1 + kGTile <= full_rows, cs, h, sc);
+      } else {
+#pragma unroll
+        for (int w = 4; w < 8; ++w) {
+          pp.hi[w] = 0;
+          pp.lo[w] = 0;
+        }
+        pp.e[1] = 0;
+      }
+      if (base0 < wave_rows) pair_pv(st, pp, buf0, buf1, off, h);
     }
     __builtin_amdgcn_s_waitcnt(kVmcntNone);  // every ring load has landed
     __syncthreads();
