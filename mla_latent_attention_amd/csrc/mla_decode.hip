@@ -706,7 +706,7 @@ void mla_decode_bf16_kernel(const DecodeParams p) {
 // kSlots = 2; the row group within the unit in group mode, with kSlots = 16).
 constexpr int kCombineThreads = 64;
 
-template <int kSlots>
+template <int kSlots, bool kBf16Parts>
 __device__ __forceinline__ void combine_unit(const DecodeParams& p) {
   const int64_t u = blockIdx.x;
   const int4 d = p.desc[u];
@@ -732,7 +732,14 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p) {
     for (int j = 0; j < kBatch; ++j) {  // past-the-end slots reload the last one, weight 0
       const int64_t slot = slot_of(imin(i0 + j, S - 1));
       ls[j] = p.part_lse[slot * kGroup + n];
-      x[j] = *(const float4*)(p.part_o + (slot * kGroup + n) * kLatent + 256 * h + 4 * lane);
+      const int64_t e0 = (slot * kGroup + n) * kLatent + 256 * h + 4 * lane;
+      if constexpr (kBf16Parts) {
+        const uint2 b = *(const uint2*)((const uint16_t*)p.part_o + e0);
+        x[j] = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                           __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+      } else {
+        x[j] = *(const float4*)(p.part_o + e0);
+      }
     }
     // Keep the scheduler from interleaving these loads with their uses, which
     // would leave only a couple in flight at a time.
@@ -769,11 +776,11 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p) {
 }
 
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const DecodeParams p) {
-  combine_unit<2>(p);
+  combine_unit<2, false>(p);
 }
 
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_groups_kernel(const DecodeParams p) {
-  combine_unit<16>(p);
+  combine_unit<16, true>(p);
 }
 
 // ---------------------------------------------------------------- shard merge

@@ -484,15 +484,22 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
     if (p.lse != nullptr && h == 0) p.lse[orow] = lse_val;
     return;
   }
+  // Partials are stored in bf16 (round to nearest even): every worker writes
+  // eight row groups of them at the end of a split piece, and their bytes,
+  // written and read back by the combine, rival the attention arithmetic.
   const int64_t slot_id = slot_base + ulocal;
-  float* dst = p.part_o + (slot_id * kGroup + n16) * kLatent + 4 * h;
+  uint16_t* dst = (uint16_t*)p.part_o + (slot_id * kGroup + n16) * kLatent + 4 * h;
 #pragma unroll
   for (int blk = 0; blk < 16; ++blk)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *(float4*)(dst + 32 * blk + 8 * q4) =
-          make_float4(st.O[blk][4 * q4 + 0] * oscale, st.O[blk][4 * q4 + 1] * oscale,
-                      st.O[blk][4 * q4 + 2] * oscale, st.O[blk][4 * q4 + 3] * oscale);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      uint2 pk;
+      pk.x = bf16_bits(st.O[blk][4 * q4 + 0] * oscale) |
+             (bf16_bits(st.O[blk][4 * q4 + 1] * oscale) << 16);
+      pk.y = bf16_bits(st.O[blk][4 * q4 + 2] * oscale) |
+             (bf16_bits(st.O[blk][4 * q4 + 3] * oscale) << 16);
+      *(uint2*)(dst + 32 * blk + 8 * q4) = pk;
+    }
   if (h == 0) p.part_lse[slot_id * kGroup + n16] = lse_val;
 }
 

@@ -23,7 +23,7 @@ struct DecodeParams {
   const float* q_scale;     // device scalar or nullptr (1.0)
   const float* kv_scale;    // device scalar or nullptr (1.0)
   float* lse;               // (T, H) or nullptr
-  float* part_o;            // workspace: (slots*num_workers, 16, 512) fp32
+  float* part_o;            // workspace: (slots*num_workers, 16, 512) fp32 (bf16 in group mode)
   float* part_lse;          // workspace: (slots*num_workers, 16) fp32
   int4* desc;               // workspace: (tokens * head groups) split-unit descriptors
   int num_workers;
@@ -39,7 +39,9 @@ inline int slots_per_worker(bool group_mode) { return group_mode ? 16 : 2; }
 //   desc     (num_units) int4 per row group {first worker, last worker, slot
 //            of the first worker, 1} for a row group split over several
 //            workers, w = 0 else
-//   part_o   (slots * num_workers, 16, 512) fp32 partial outputs
+//   part_o   (slots * num_workers, 16, 512) fp32 partial outputs (group mode
+//            stores them as bf16 at the same element indices, in the first
+//            half of the region)
 //   part_lse (slots * num_workers, 16) fp32 partial lse
 constexpr int kMaxWorkers = 1 << 16;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
