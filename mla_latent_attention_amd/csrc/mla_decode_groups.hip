@@ -15,19 +15,20 @@
 //     workers take equal, boundary-snapped shares of the unit stream as in
 //     the standard mode.  One workgroup (four waves, one per SIMD) per CU.
 //   * Wave wv owns the unit's row groups wv and wv + 4: 32 query rows, the N
-//     dimension of 32x32 MFMAs, so every K and V element read from LDS (and
-//     every fp8 -> bf16 widening of V) serves 32 rows.
+//     dimension of 32x32 MFMAs, so every K and V element read from LDS
+//     serves 32 rows.
 //   * Tiles of 32 KV rows are gathered once by all 256 threads with direct
 //     global->LDS loads (each lane 16 consecutive bytes of a row) into a
-//     six-tile LDS ring with a 592-byte row stride; up to four later tiles
-//     are in flight while one is consumed.
+//     six-tile LDS ring with a 592-byte row stride; three later tiles are in
+//     flight while one is consumed.
 //   * Per tile and wave: S^T = K.Q^T on v_mfma_scale_f32_32x32x64_f8f6f4
 //     (nine steps, K from LDS, q in registers), the online softmax (each
-//     lane masks the entries its row's token may not see), and
-//     O^T += V^T.P^T on v_mfma_f32_32x32x16_bf16, with the V^T operand read
-//     from the row-major tile by the LDS transpose read (ds_read_b64_tr_b8)
-//     and widened exactly from fp8, and P in bf16 from the lane's own scores.
-//     Every wave writes its own o (or partials): there is no cross-wave merge.
+//     lane masks the entries its row's token may not see) and P packed as
+//     fp8 hi + lo under an E8M0 scale per (query row, tile).  Every two
+//     tiles, O^T += V^T.P^T on the same MFMA over 64 KV rows, with the V^T
+//     operand read straight from the fp8 tiles by the LDS transpose read
+//     (ds_read_b64_tr_b8).  Every wave writes its own o (or partials): there
+//     is no cross-wave merge.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

@@ -80,6 +80,8 @@ __device__ __forceinline__ void uniformize(Cursor& c) {
   c.r.qlen = uniform(c.r.qlen);
 }
 
+// Block-wide helpers for blocks of kT threads (red: kT/64 entries).
+template <int kT = kThreads>
 __device__ int64_t block_sum_i64(int64_t v, int64_t* red) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   const int wv = threadIdx.x >> 6;
@@ -87,11 +89,12 @@ __device__ int64_t block_sum_i64(int64_t v, int64_t* red) {
   if ((threadIdx.x & 63) == 0) red[wv] = v;
   __syncthreads();
   int64_t s = 0;
-  for (int i = 0; i < kWaves; ++i) s += red[i];
+  for (int i = 0; i < kT / 64; ++i) s += red[i];
   return s;
 }
 
-// Exclusive prefix sum over the block's 256 values; `total` gets the sum.
+// Exclusive prefix sum over the block's kT values; `total` gets the sum.
+template <int kT = kThreads>
 __device__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int64_t x = v;
@@ -104,7 +107,7 @@ __device__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) 
   __syncthreads();
   int64_t before = 0;
   total = 0;
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < kT / 64; ++i) {
     if (i < wv) before += red[i];
     total += red[i];
   }
@@ -115,19 +118,19 @@ __device__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) 
 // not looked up), where request r holds rows_of(r) stream rows: sb[i] =
 // request (-1 if not found, -2 if not looked up) and scum[i] = that request's
 // first stream position.
-template <class RowsOf>
+template <int kT = kThreads, class RowsOf>
 __device__ void plan_locate2(const DecodeParams& p, RowsOf rows_of, const int64_t (&x)[2],
                              int64_t* red, int* sb, int64_t* scum) {
   if (threadIdx.x < 2) sb[threadIdx.x] = x[threadIdx.x] < 0 ? -2 : -1;
   int64_t carry = 0;
-  for (int b0 = 0; b0 < p.batch; b0 += kThreads) {
+  for (int b0 = 0; b0 < p.batch; b0 += kT) {
     const int b = b0 + threadIdx.x;
     int64_t R = 0;
     if (b < p.batch) {
       R = rows_of(load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens));
     }
     int64_t total;
-    const int64_t cum = carry + block_excl_scan_i64(R, red, total);
+    const int64_t cum = carry + block_excl_scan_i64<kT>(R, red, total);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (R > 0 && x[i] >= cum && x[i] < cum + R) {
@@ -185,13 +188,14 @@ __device__ __forceinline__ void softmax_update(WaveState& st, float (&x)[N]) {
 // kv_indices loads issued per thread before the first store.
 constexpr int kIdxBatch = 8;
 
+template <int kT = kThreads>
 __device__ __forceinline__ void stage_first_indices(int32_t* idx_dst, const int32_t* idx_src,
                                                     int n) {
   int32_t iv[kIdxBatch];
 #pragma unroll
-  for (int j = 0; j < kIdxBatch; ++j) iv[j] = idx_src[imin(j * kThreads + (int)threadIdx.x, n - 1)];
+  for (int j = 0; j < kIdxBatch; ++j) iv[j] = idx_src[imin(j * kT + (int)threadIdx.x, n - 1)];
 #pragma unroll
-  for (int j = 0; j < kIdxBatch; ++j) idx_dst[imin(j * kThreads + (int)threadIdx.x, n - 1)] = iv[j];
+  for (int j = 0; j < kIdxBatch; ++j) idx_dst[imin(j * kT + (int)threadIdx.x, n - 1)] = iv[j];
 }
 
 __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&a)[8]) {
@@ -207,13 +211,14 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&a)[8])
 // Each thread issues kIdxBatch loads before its first store (past-the-end
 // positions reload the last index), so a segment costs one memory round trip
 // per 2048 indices instead of one per 256.
+template <int kT = kThreads>
 __device__ __forceinline__ void stage_indices(int32_t* dst, const int32_t* src, int from, int n) {
-  for (int i0 = from; i0 < n; i0 += kThreads * kIdxBatch) {
+  for (int i0 = from; i0 < n; i0 += kT * kIdxBatch) {
     int32_t v[kIdxBatch];
 #pragma unroll
-    for (int j = 0; j < kIdxBatch; ++j) v[j] = src[imin(i0 + j * kThreads + (int)threadIdx.x, n - 1)];
+    for (int j = 0; j < kIdxBatch; ++j) v[j] = src[imin(i0 + j * kT + (int)threadIdx.x, n - 1)];
 #pragma unroll
-    for (int j = 0; j < kIdxBatch; ++j) dst[imin(i0 + j * kThreads + (int)threadIdx.x, n - 1)] = v[j];
+    for (int j = 0; j < kIdxBatch; ++j) dst[imin(i0 + j * kT + (int)threadIdx.x, n - 1)] = v[j];
   }
 }
 
