@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode µs/call + HBM GB/s (% of 8 TB/s), bs16 kv≈68K fp8, 1 GPU"
 CONFIG_NAMES = ("c24_batch24_fp8", "mixed_batch64_fp8", "mixed_batch64_bf16",
-                "dcp_share_96heads_qlen4_fp8", "merge_8_shards_fp32", "merge_8_shards_bf16")
+                "dcp_share_96heads_qlen4_fp8", "c16_shared_prefix_cascade_fp8",
+                "merge_8_shards_fp32", "merge_8_shards_bf16")
 PEAK_GBS = 8000.0
 
 
@@ -158,6 +159,34 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
                      "algorithmic_bytes_per_call": nbytes, "kv_rows": base.total_kv,
                      "dtype": base.dtype, "calls": n}
         del layers, base, o, lse, ws
+        torch.cuda.empty_cache()
+    name = "c16_shared_prefix_cascade_fp8"
+    if only is None or only == name:
+        # The headline call through decode_cascade: the 63,911 shared entries
+        # given once, each request's own entries as its suffix.
+        base = workloads.c16(dev, "shared")
+        layers = extra_layers(base, n_layers, 0.5, 7000, dev)
+        pre, sptr, suf = workloads.split_prefix(base, workloads.SHARED_PREFIX)
+        T, H = base.num_tokens, base.num_heads
+        o = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+        ws = mla.new_workspace(mla.cascade_workspace_bytes(base.batch, T, H, 1), dev)
+
+        def cascade_for(w):
+            return lambda: mla.decode_cascade(w.q, w.kv_pool, w.qo_indptr, pre, sptr, suf,
+                                              w.sm_scale, w.q_scale, w.kv_scale, o=o,
+                                              max_seqlen_q=1, workspace=ws)
+
+        wall, ev, n = time_graph([cascade_for(w) for w in layers], steps, warmup)
+        nbytes = accounting.workload_bytes(base)
+        unique = accounting.cascade_bytes(base, workloads.SHARED_PREFIX)
+        out[name] = {"us_per_call": round(wall * 1e6, 2), "event_us": stats_us(ev),
+                     "GB_s_effective": round(nbytes / wall / 1e9, 2),
+                     "algorithmic_bytes_per_call": nbytes,
+                     "cascade_bytes_per_call": unique,
+                     "GB_s_cascade_bytes": round(unique / wall / 1e9, 2),
+                     "TFLOP_s": round(accounting.workload_flops(base) / wall / 1e12, 2),
+                     "kv_rows": base.total_kv, "dtype": "fp8", "calls": n}
+        del layers, base, o, ws, pre, sptr, suf
         torch.cuda.empty_cache()
     for parts_dtype in ("fp32", "bf16"):
         if only is not None and only != f"merge_8_shards_{parts_dtype}":

@@ -79,10 +79,11 @@ typedef enum {
  * workgroup a contiguous range of (token, head group) rows, at most two of
  * them partial (two 16x512 fp32 partial slots per worker), one worker per
  * compute unit.  When num_heads / 16 * max_seqlen_q >= 4 and the storage is
- * FP8, the group-mode kernel instead walks 4 row groups of one request over a
- * single shared KV range, so each gathered cache row feeds 64 query rows; it
- * runs two workers per compute unit with eight partial slots each.  The
- * workspace is sized for the larger layout whenever the shape qualifies.
+ * FP8, the group-mode kernel instead walks 8 row groups of one request over a
+ * single shared KV range, so each gathered cache row feeds 128 query rows; it
+ * also runs one worker per compute unit, with sixteen partial slots each (held
+ * in bf16).  The workspace is sized for the larger layout whenever the shape
+ * qualifies.
  */
 size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, int max_seqlen_q);
 
@@ -131,7 +132,7 @@ mla_status mla_decode(const void* q, int q_dtype, const void* kv_pool, int kv_dt
 
 /*
  * mla_decode with an explicit number of worker workgroups (0 = the library's
- * choice: one per compute unit, two in group mode).  The KV work is cut into
+ * choice: one per compute unit).  The KV work is cut into
  * `num_workers` equal contiguous ranges; results agree with mla_decode within
  * rounding.  The workspace must hold mla_decode_workspace_bytes_ex(...,
  * num_workers) bytes.
@@ -171,6 +172,37 @@ mla_status mla_merge_partials(const void* o_parts, int parts_dtype, const float*
 const char* mla_status_string(int status);
 
 /*
+ * Shared-prefix (cascade) decode, SURVEY-ranked next step of the pages' method
+ * ("[Kimi-K3 MLA TP8] MLA performance", ROCm/aiter issue 4541, Sec. 5.4 on
+ * shared-prefix reuse): the same result as mla_decode when request b's entry
+ * list is prefix_indices (shared by every request) followed by its own
+ * suffix_indices[suffix_indptr[b] .. suffix_indptr[b+1]).  The shared rows are
+ * gathered once for eight row groups (all tokens, all heads) instead of once
+ * per request and head group.
+ *
+ *  Arguments as for mla_decode, with kv_indptr / kv_indices replaced by
+ *  prefix_indices (prefix_len) int32 and suffix_indptr (batch+1) /
+ *  suffix_indices (suffix_indices_len) int32, all device memory.
+ *  Supported: FP8 q and KV only.  Causal draft tokens: every request's suffix
+ *  must hold at least qlen_b - 1 entries (a token's masked entries then all
+ *  lie in the suffix); this is the caller's contract, not checked.
+ *  workspace: at least mla_decode_cascade_workspace_bytes(...) bytes.
+ *  Runs three steps on `stream`: the prefix pass, the suffix pass (each with
+ *  its split combine) and an LSE merge of the two into o / lse.
+ */
+size_t mla_decode_cascade_workspace_bytes(int batch, int num_q_tokens, int num_heads,
+                                          int max_seqlen_q);
+
+mla_status mla_decode_cascade(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                              int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                              const int32_t* prefix_indices, int64_t prefix_len,
+                              const int32_t* suffix_indptr, const int32_t* suffix_indices,
+                              int64_t suffix_indices_len, int batch, int num_q_tokens,
+                              int num_heads, int max_seqlen_q, float sm_scale,
+                              const float* q_scale, const float* kv_scale, int return_lse,
+                              float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Host mirror of the work planner, for tests: given host copies of qo_indptr
  * and kv_indptr, fill `out` (capacity `out_cap` pieces, 8 int64 each:
  * worker, token, head_group, kv_begin, kv_end, unit_len, slot, is_complete)
@@ -183,15 +215,17 @@ int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int ba
 
 /*
  * Host mirror of the group-mode planner (the fp8 path when num_heads / 16 *
- * max_seqlen_q >= 4), for tests.  A unit is 4 consecutive row groups
+ * max_seqlen_q >= 4), for tests.  A unit is 8 consecutive row groups
  * rg = j * (num_heads / 16) + g of one request (token j, head group g), as
  * long as the last of them sees.  Records as for mla_plan_host but with
  * columns: worker, request, unit, kv_begin, kv_end, unit_len, slot_base,
- * is_complete; slot_base is the first of the piece's 4 partial slots (one per
- * row group), -1 for complete pieces.  Same return convention.
+ * is_complete; slot_base is the first of the piece's 8 partial slots (one per
+ * row group), -1 for complete pieces.  causal = 0 lets every token see all of
+ * its request's entries (the cascade's prefix pass).  Same return convention.
  */
 int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
-                             int num_heads, int num_workers, int64_t* out, int64_t out_cap);
+                             int num_heads, int num_workers, int causal, int64_t* out,
+                             int64_t out_cap);
 
 #ifdef __cplusplus
 }

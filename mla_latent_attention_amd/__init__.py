@@ -22,6 +22,8 @@ __all__ = [
     "workspace_bytes",
     "plan_host",
     "plan_groups_host",
+    "decode_cascade",
+    "cascade_workspace_bytes",
     "new_workspace",
     "MLAError",
     "library_path",
@@ -160,6 +162,80 @@ def decode(
     return (o, lse) if return_lse else o
 
 
+def cascade_workspace_bytes(batch: int, num_q_tokens: int, num_heads: int,
+                            max_seqlen_q: int = 1) -> int:
+    n = _lib.lib().mla_decode_cascade_workspace_bytes(batch, num_q_tokens, num_heads, max_seqlen_q)
+    if n == 0:
+        raise ValueError("invalid shape for the cascade workspace (or no HIP device)")
+    return int(n)
+
+
+def decode_cascade(
+    q: torch.Tensor,
+    kv_pool: torch.Tensor,
+    qo_indptr: torch.Tensor,
+    prefix_indices: torch.Tensor,
+    suffix_indptr: torch.Tensor,
+    suffix_indices: torch.Tensor,
+    sm_scale: float,
+    q_scale: torch.Tensor | None = None,
+    kv_scale: torch.Tensor | None = None,
+    return_lse: bool = False,
+    *,
+    o: torch.Tensor | None = None,
+    lse: torch.Tensor | None = None,
+    max_seqlen_q: int | None = None,
+    workspace: torch.Tensor | None = None,
+):
+    """Shared-prefix decode: the result of decode() when request b's entries
+    are prefix_indices followed by suffix_indices[suffix_indptr[b]:
+    suffix_indptr[b+1]].  fp8 only; every request's suffix must hold at least
+    qlen_b - 1 entries."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a device tensor")
+    if q.dim() != 3 or q.shape[2] != ROW_DIM:
+        raise ValueError(f"q must be (T, H, {ROW_DIM})")
+    T, H, _ = q.shape
+    if kv_pool.dim() == 4:
+        kv_pool = kv_pool.view(kv_pool.shape[0], ROW_DIM)
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_DIM:
+        raise ValueError(f"kv_pool must be (N, {ROW_DIM})")
+    _need(q, "q", dev)
+    _need(kv_pool, "kv_pool", dev)
+    B = qo_indptr.numel() - 1
+    _need(qo_indptr, "qo_indptr", dev, torch.int32, (B + 1,))
+    _need(suffix_indptr, "suffix_indptr", dev, torch.int32, (B + 1,))
+    _need(prefix_indices, "prefix_indices", dev, torch.int32)
+    _need(suffix_indices, "suffix_indices", dev, torch.int32)
+    for name, s in (("q_scale", q_scale), ("kv_scale", kv_scale)):
+        if s is not None:
+            _need(s, name, dev, torch.float32)
+    if o is None:
+        o = torch.empty((T, H, LATENT_DIM), dtype=torch.bfloat16, device=dev)
+    _need(o, "o", dev, torch.bfloat16, (T, H, LATENT_DIM))
+    if return_lse:
+        if lse is None:
+            lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        _need(lse, "lse", dev, torch.float32, (T, H))
+    if max_seqlen_q is None:
+        max_seqlen_q = int((qo_indptr[1:] - qo_indptr[:-1]).max().item()) if B > 0 else 1
+    need = cascade_workspace_bytes(B, T, H, max_seqlen_q)
+    if workspace is None:
+        workspace = new_workspace(need, dev)
+    _need(workspace, "workspace", dev)
+    status = _lib.lib().mla_decode_cascade(
+        _ptr(q), _storage_dtype(q), _ptr(kv_pool), _storage_dtype(kv_pool), kv_pool.shape[0],
+        _ptr(o), _ptr(qo_indptr), _ptr(prefix_indices), prefix_indices.numel(),
+        _ptr(suffix_indptr), _ptr(suffix_indices), suffix_indices.numel(), B, T, H, max_seqlen_q,
+        float(sm_scale), _ptr(q_scale), _ptr(kv_scale), 1 if return_lse else 0,
+        _ptr(lse) if return_lse else None, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev),
+    )
+    _lib.check(status, "mla_decode_cascade")
+    return (o, lse) if return_lse else o
+
+
 def merge_partials(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, o=None, lse=None,
                    return_lse: bool = True):
     """LSE merge of S shards: o_parts (S, T, H, 512) bf16|fp32, lse_parts (S, T, H) fp32."""
@@ -209,6 +285,11 @@ def plan_host(qo_indptr, kv_indptr, num_heads: int, num_workers: int) -> np.ndar
     return _plan(_lib.lib().mla_plan_host, qo_indptr, kv_indptr, num_heads, num_workers)
 
 
-def plan_groups_host(qo_indptr, kv_indptr, num_heads: int, num_workers: int) -> np.ndarray:
-    """The group-mode planner's pieces: int64 array (pieces, 8), columns GROUP_PLAN_FIELDS."""
-    return _plan(_lib.lib().mla_plan_groups_host, qo_indptr, kv_indptr, num_heads, num_workers)
+def plan_groups_host(qo_indptr, kv_indptr, num_heads: int, num_workers: int,
+                     causal: bool = True) -> np.ndarray:
+    """The group-mode planner's pieces: int64 array (pieces, 8), columns GROUP_PLAN_FIELDS.
+    causal=False: every token sees all of its request's entries."""
+    fn = _lib.lib().mla_plan_groups_host
+    c = 1 if causal else 0
+    return _plan(lambda q, k, B, H, nw, out, cap: fn(q, k, B, H, nw, c, out, cap),
+                 qo_indptr, kv_indptr, num_heads, num_workers)

@@ -33,8 +33,13 @@ SIGNATURES = {
     "mla_decode_workspace_bytes_ex": (C.c_size_t, [C.c_int] * 5),
     "mla_merge_partials": (C.c_int, [_vp, C.c_int, _vp, C.c_int, C.c_int, C.c_int, _vp, _vp, _vp]),
     "mla_status_string": (C.c_char_p, [C.c_int]),
+    "mla_decode_cascade": (C.c_int, [
+        _vp, C.c_int, _vp, C.c_int, C.c_int64, _vp, _vp, _vp, C.c_int64, _vp, _vp, C.c_int64,
+        C.c_int, C.c_int, C.c_int, C.c_int, C.c_float, _vp, _vp, C.c_int, _vp, _vp, C.c_size_t,
+        _vp]),
+    "mla_decode_cascade_workspace_bytes": (C.c_size_t, [C.c_int] * 4),
     "mla_plan_host": (C.c_int64, [_vp, _vp, C.c_int, C.c_int, C.c_int, _vp, C.c_int64]),
-    "mla_plan_groups_host": (C.c_int64, [_vp, _vp, C.c_int, C.c_int, C.c_int, _vp, C.c_int64]),
+    "mla_plan_groups_host": (C.c_int64, [_vp, _vp, C.c_int, C.c_int, C.c_int, C.c_int, _vp, C.c_int64]),
 }
 
 _lib = None

@@ -130,6 +130,7 @@ mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv
   p.kv = static_cast<const uint8_t*>(kv_pool);
   p.pool_entries = pool_entries;
   p.o = static_cast<uint16_t*>(o);
+  p.o32 = nullptr;
   p.qo_indptr = qo_indptr;
   p.kv_indptr = kv_indptr;
   p.kv_indices = kv_indices;
@@ -147,6 +148,7 @@ mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv
   p.part_lse = reinterpret_cast<float*>(ws + mla::desc_bytes(num_units) +
                                         mla::part_o_bytes(num_workers, slots));
   p.num_workers = num_workers;
+  p.causal = 1;
   if (mla::launch_decode(p, kdt, group_mode, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
@@ -163,6 +165,125 @@ mla_status mla_decode(const void* q, int q_dtype, const void* kv_pool, int kv_dt
                        kv_indices, kv_indices_len, kv_last_page_lens, batch, num_q_tokens,
                        num_heads, max_seqlen_q, sm_scale, q_scale, kv_scale, return_lse, lse,
                        workspace, workspace_bytes, 0, stream);
+}
+
+namespace {
+
+// Cascade workspace: one decode workspace (either pass, one after the other
+// on the stream) followed by the two passes' outputs, fp32 o and lse (fp32 o
+// keeps the merge from adding a third bf16 rounding to the result).
+struct CascadeLayout {
+  size_t decode_bytes, parts_off, lse_off, total;
+};
+
+CascadeLayout cascade_layout(int batch, int num_q_tokens, int num_heads, int max_seqlen_q,
+                             int cus) {
+  const int G = num_heads / mla::kGroup;
+  const int64_t units = (int64_t)num_q_tokens * G;
+  const size_t prefix = mla::workspace_bytes(cus, units, mla::slots_per_worker(true));
+  const size_t suffix = mla::workspace_bytes(cus, units, slots_for(num_heads, max_seqlen_q));
+  CascadeLayout l;
+  l.decode_bytes = mla::align256(prefix > suffix ? prefix : suffix);
+  l.parts_off = l.decode_bytes;
+  l.lse_off = l.parts_off + mla::align256((size_t)2 * num_q_tokens * num_heads * mla::kLatent * 4);
+  l.total = l.lse_off + mla::align256((size_t)2 * num_q_tokens * num_heads * 4);
+  (void)batch;
+  return l;
+}
+
+void set_workspace(mla::DecodeParams& p, char* ws, int64_t units, int slots) {
+  p.desc = reinterpret_cast<int4*>(ws);
+  p.part_o = reinterpret_cast<float*>(ws + mla::desc_bytes(units));
+  p.part_lse = reinterpret_cast<float*>(ws + mla::desc_bytes(units) +
+                                        mla::part_o_bytes(p.num_workers, slots));
+}
+
+}  // namespace
+
+size_t mla_decode_cascade_workspace_bytes(int batch, int num_q_tokens, int num_heads,
+                                          int max_seqlen_q) {
+  if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
+  if (num_heads % mla::kGroup) return 0;
+  const int cus = current_cu_count();
+  if (cus <= 0) return 0;
+  return cascade_layout(batch, num_q_tokens, num_heads, max_seqlen_q, cus).total;
+}
+
+mla_status mla_decode_cascade(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                              int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                              const int32_t* prefix_indices, int64_t prefix_len,
+                              const int32_t* suffix_indptr, const int32_t* suffix_indices,
+                              int64_t suffix_indices_len, int batch, int num_q_tokens,
+                              int num_heads, int max_seqlen_q, float sm_scale,
+                              const float* q_scale, const float* kv_scale, int return_lse,
+                              float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !kv_pool || !o || !qo_indptr || !suffix_indptr || !workspace)
+    return MLA_ERR_NULL_POINTER;
+  if (prefix_len > 0 && !prefix_indices) return MLA_ERR_NULL_POINTER;
+  if (suffix_indices_len > 0 && !suffix_indices) return MLA_ERR_NULL_POINTER;
+  if (return_lse && !lse) return MLA_ERR_NULL_POINTER;
+  if (q_dtype != MLA_DTYPE_FP8_E4M3FN || kv_dtype != MLA_DTYPE_FP8_E4M3FN) return MLA_ERR_BAD_DTYPE;
+  if (num_heads <= 0 || num_heads % mla::kGroup != 0) return MLA_ERR_UNSUPPORTED;
+  const int T = num_q_tokens;
+  if (!shape_ok(batch, T, num_heads, max_seqlen_q)) return MLA_ERR_BAD_SHAPE;
+  if (pool_entries < 1 || prefix_len < 0 || prefix_len > 0x7FFFFFFF || suffix_indices_len < 0 ||
+      suffix_indices_len > 0x7FFFFFFF)
+    return MLA_ERR_BAD_SHAPE;
+  const int cus = current_cu_count();
+  if (cus <= 0) return MLA_ERR_HIP;
+  const CascadeLayout lay = cascade_layout(batch, T, num_heads, max_seqlen_q, cus);
+  if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  const int G = num_heads / mla::kGroup;
+  const int64_t units = (int64_t)T * G;
+  char* ws = static_cast<char*>(workspace);
+  float* parts = reinterpret_cast<float*>(ws + lay.parts_off);
+  float* lse_parts = reinterpret_cast<float*>(ws + lay.lse_off);
+  const int64_t rows = (int64_t)T * num_heads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  mla::DecodeParams p;
+  p.q = static_cast<const uint8_t*>(q);
+  p.kv = static_cast<const uint8_t*>(kv_pool);
+  p.pool_entries = pool_entries;
+  p.num_tokens = T;
+  p.num_heads = num_heads;
+  p.sm_scale = sm_scale;
+  p.q_scale = q_scale;
+  p.kv_scale = kv_scale;
+  p.num_workers = cus;
+
+  // Pass 1: every token against the shared prefix, as one request whose
+  // tokens all see every entry (group mode: eight row groups per gather).
+  p.o = nullptr;
+  p.o32 = parts;  // both passes keep fp32 outputs for the merge
+  p.lse = lse_parts;
+  p.qo_indptr = nullptr;
+  p.kv_indptr = nullptr;
+  p.kv_indices = prefix_indices;
+  p.kv_indices_len = (int)prefix_len;
+  p.batch = 1;
+  p.causal = 0;
+  set_workspace(p, ws, units, mla::slots_per_worker(true));
+  if (mla::launch_decode(p, 0, true, st) != hipSuccess) return MLA_ERR_HIP;
+
+  // Pass 2: each request's own entries, causal (the usual kernels).
+  const bool group = mla::use_group_mode(G, max_seqlen_q);
+  p.o32 = parts + rows * mla::kLatent;
+  p.lse = lse_parts + rows;
+  p.qo_indptr = qo_indptr;
+  p.kv_indptr = suffix_indptr;
+  p.kv_indices = suffix_indices;
+  p.kv_indices_len = (int)suffix_indices_len;
+  p.batch = batch;
+  p.causal = 1;
+  set_workspace(p, ws, units, slots_for(num_heads, max_seqlen_q));
+  if (mla::launch_decode(p, 0, group, st) != hipSuccess) return MLA_ERR_HIP;
+
+  // LSE merge of the two passes (a pass that saw nothing has lse = -inf).
+  if (mla::launch_merge(parts, 1, lse_parts, 2, rows, static_cast<uint16_t*>(o),
+                        return_lse ? lse : nullptr, st) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
 }
 
 mla_status mla_merge_partials(const void* o_parts, int parts_dtype, const float* lse_parts,
@@ -252,7 +373,8 @@ int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int ba
 }
 
 int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
-                             int num_heads, int num_workers, int64_t* out, int64_t out_cap) {
+                             int num_heads, int num_workers, int causal, int64_t* out,
+                             int64_t out_cap) {
   using namespace mla;
   if (!qo_indptr || !kv_indptr || batch < 1 || num_heads < kGroup || num_heads % kGroup ||
       num_workers < 1 || (out_cap > 0 && !out))
@@ -263,7 +385,7 @@ int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   if (T < 0 || kv_cap < 0) return -1;
   std::vector<int64_t> cum(batch + 1, 0);
   for (int b = 0; b < batch; ++b)
-    cum[b + 1] = cum[b] + group_request_rows(load_req(qo_indptr, kv_indptr, b, kv_cap, T), G);
+    cum[b + 1] = cum[b] + group_request_rows(load_req(qo_indptr, kv_indptr, b, kv_cap, T, causal), G);
   const int64_t W = cum[batch];
   if (W == 0) return 0;
   const int nw = effective_workers(W, num_workers);
@@ -272,7 +394,7 @@ int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   auto locate = [&](int64_t x, GCursor& c) {
     int b = 0;
     while (!(cum[b] <= x && x < cum[b + 1])) ++b;
-    gcursor_in_request(c, b, load_req(qo_indptr, kv_indptr, b, kv_cap, T), x - cum[b], G);
+    gcursor_in_request(c, b, load_req(qo_indptr, kv_indptr, b, kv_cap, T, causal), x - cum[b], G);
   };
   for (int w = 0; w < nw; ++w) {
     const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
@@ -288,7 +410,7 @@ int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     if (p0 < x0) {
       c.k = 0;
     } else if (p0 > x0) {
-      if (!gcursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G)) continue;
+      if (!gcursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G, causal)) continue;
     }
     int64_t pos = p0;
     int piece = 0;
@@ -313,7 +435,7 @@ int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
       pos += len;
       c.k += len;
       ++piece;
-      if (pos < p1 && c.k == L && !gcursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G))
+      if (pos < p1 && c.k == L && !gcursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G, causal))
         return -1;
     }
   }

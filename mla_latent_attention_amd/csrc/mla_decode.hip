@@ -575,9 +575,19 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
   const float lse_val = (M + fast_log2(L)) * kLn2;
   if (slot < 0) {
     const int64_t orow = (int64_t)u.t * p.num_heads + u.g * kGroup + n;
-    uint16_t* dst = p.o + orow * kLatent + dim0;
+    if (p.o32 != nullptr) {
+      float* d32 = p.o32 + orow * kLatent + dim0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) store_bf16x8(dst + Path::kDimStride * i, acc[i]);
+      for (int i = 0; i < 4; ++i) {
+        float* d = d32 + Path::kDimStride * i;
+        *(float4*)d = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+        *(float4*)(d + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+      }
+    } else {
+      uint16_t* dst = p.o + orow * kLatent + dim0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_bf16x8(dst + Path::kDimStride * i, acc[i]);
+    }
     if (p.lse != nullptr && wv == 0 && gq == 0) p.lse[orow] = lse_val;
     return;
   }
@@ -768,10 +778,15 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p) {
   const float inv = 1.0f / sum;
   const int64_t t = u / G, g = u % G;
   const int64_t orow = t * p.num_heads + g * kGroup + n;
-  uint2 pk;
-  pk.x = bf16_bits(acc.x * inv) | (bf16_bits(acc.y * inv) << 16);
-  pk.y = bf16_bits(acc.z * inv) | (bf16_bits(acc.w * inv) << 16);
-  *(uint2*)(p.o + orow * kLatent + 256 * h + 4 * lane) = pk;
+  if (p.o32 != nullptr) {
+    *(float4*)(p.o32 + orow * kLatent + 256 * h + 4 * lane) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  } else {
+    uint2 pk;
+    pk.x = bf16_bits(acc.x * inv) | (bf16_bits(acc.y * inv) << 16);
+    pk.y = bf16_bits(acc.z * inv) | (bf16_bits(acc.w * inv) << 16);
+    *(uint2*)(p.o + orow * kLatent + 256 * h + 4 * lane) = pk;
+  }
   if (p.lse != nullptr && h == 0 && lane == 0) p.lse[orow] = M + fast_log2(sum) * kLn2;
 }
 

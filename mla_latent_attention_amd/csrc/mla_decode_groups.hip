@@ -317,7 +317,7 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   for (int k = 0; k < 2; ++k) {
     const int rgk = kGroupsPerUnit * c.u + wv + kWaves * k;
     const int jk = imin(rgk, R - 1) / G;
-    vis_h[k] = rgk < R ? visible(c.r.n, c.r.qlen, jk) : 0;
+    vis_h[k] = rgk < R ? req_visible(c.r, jk) : 0;
     rows_h[k] = imax(0, imin(vis_h[k] - c.k, len));
   }
   const int wave_rows = imax(rows_h[0], rows_h[1]);
@@ -470,6 +470,18 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   const float lse_val = empty ? neg_inf() : (st.m + fast_log2(Lsum)) * kLn2;
   if (complete) {
     const int64_t orow = (int64_t)t * p.num_heads + g * kGroup + n16;
+    if (p.o32 != nullptr) {
+      float* d32 = p.o32 + orow * kLatent + 4 * h;
+#pragma unroll
+      for (int blk = 0; blk < 16; ++blk)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(float4*)(d32 + 32 * blk + 8 * q4) =
+              make_float4(st.O[blk][4 * q4 + 0] * oscale, st.O[blk][4 * q4 + 1] * oscale,
+                          st.O[blk][4 * q4 + 2] * oscale, st.O[blk][4 * q4 + 3] * oscale);
+      if (p.lse != nullptr && h == 0) p.lse[orow] = lse_val;
+      return;
+    }
     uint16_t* dst = p.o + orow * kLatent + 4 * h;
 #pragma unroll
     for (int blk = 0; blk < 16; ++blk)
@@ -511,9 +523,9 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
   // Pass 1 over requests: stream length W; zero this block's empty tokens.
   int64_t acc = 0;
   for (int b = threadIdx.x; b < p.batch; b += kThreads) {
-    const Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
+    const Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens, p.causal);
     acc += group_request_rows(r, G);
-    const int nempty = imin(r.qlen, imax(0, r.qlen - r.n));
+    const int nempty = req_empty_tokens(r);
     for (int jj = 0; jj < nempty; ++jj)
       if ((r.q_base + jj) % (int)gridDim.x == (int)blockIdx.x) zero_token(p, r.q_base + jj);
   }
@@ -525,18 +537,20 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
   const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
   const int64_t xs[2] = {x0, x1 < W ? x1 : -1};
   plan_locate2(p, [G](const Req& r) { return group_request_rows(r, G); }, xs, sh.red, sh.pb,
-               sh.pcum);
+               sh.pcum, p.causal);
   const int b0 = uniform(sh.pb[0]), b1 = uniform(sh.pb[1]);
   if (b0 < 0 || b1 == -1) return;  // not reached with consistent indptr
   GCursor c;
-  gcursor_in_request(c, b0, load_req(p.qo_indptr, p.kv_indptr, b0, p.kv_indices_len, p.num_tokens),
-                     x0 - uniform(sh.pcum[0]), G);
+  gcursor_in_request(
+      c, b0, load_req(p.qo_indptr, p.kv_indptr, b0, p.kv_indices_len, p.num_tokens, p.causal),
+      x0 - uniform(sh.pcum[0]), G);
   uniformize(c);
   int64_t p1 = W;
   if (x1 < W) {
     GCursor c1;
     gcursor_in_request(c1, b1,
-                       load_req(p.qo_indptr, p.kv_indptr, b1, p.kv_indices_len, p.num_tokens),
+                       load_req(p.qo_indptr, p.kv_indptr, b1, p.kv_indices_len, p.num_tokens,
+                                p.causal),
                        x1 - uniform(sh.pcum[1]), G);
     uniformize(c1);
     p1 = gsnap_at(x1, c1, G);
@@ -547,7 +561,7 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
     c.k = 0;
   } else if (p0 > x0) {
     if (!gcursor_next_unit(c, p.qo_indptr, p.kv_indptr, p.batch, p.kv_indices_len, p.num_tokens,
-                           G))
+                           G, p.causal))
       return;
     uniformize(c);
   }
@@ -570,7 +584,7 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
     ++piece;
     if (pos < p1 && c.k == L) {
       if (!gcursor_next_unit(c, p.qo_indptr, p.kv_indptr, p.batch, p.kv_indices_len,
-                             p.num_tokens, G))
+                             p.num_tokens, G, p.causal))
         break;
       uniformize(c);
     }

@@ -120,14 +120,14 @@ __device__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) 
 // first stream position.
 template <int kT = kThreads, class RowsOf>
 __device__ void plan_locate2(const DecodeParams& p, RowsOf rows_of, const int64_t (&x)[2],
-                             int64_t* red, int* sb, int64_t* scum) {
+                             int64_t* red, int* sb, int64_t* scum, int causal = 1) {
   if (threadIdx.x < 2) sb[threadIdx.x] = x[threadIdx.x] < 0 ? -2 : -1;
   int64_t carry = 0;
   for (int b0 = 0; b0 < p.batch; b0 += kT) {
     const int b = b0 + threadIdx.x;
     int64_t R = 0;
     if (b < p.batch) {
-      R = rows_of(load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens));
+      R = rows_of(load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens, causal));
     }
     int64_t total;
     const int64_t cum = carry + block_excl_scan_i64<kT>(R, red, total);
@@ -229,8 +229,13 @@ __device__ void zero_token(const DecodeParams& p, int t) {
   for (int g = 0; g < G; ++g) p.desc[(int64_t)t * G + g] = make_int4(0, 0, 0, 0);
   for (int h = 0; h < p.num_heads; ++h) {
     const int64_t orow = (int64_t)t * p.num_heads + h;
-    uint4* dst = (uint4*)(p.o + orow * kLatent);
-    for (int k = 0; k < kLatent / 8; ++k) dst[k] = make_uint4(0, 0, 0, 0);
+    if (p.o32 != nullptr) {
+      float4* d32 = (float4*)(p.o32 + orow * kLatent);
+      for (int k = 0; k < kLatent / 4; ++k) d32[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      uint4* dst = (uint4*)(p.o + orow * kLatent);
+      for (int k = 0; k < kLatent / 8; ++k) dst[k] = make_uint4(0, 0, 0, 0);
+    }
     if (p.lse != nullptr) p.lse[orow] = neg_inf();
   }
 }

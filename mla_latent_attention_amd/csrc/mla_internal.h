@@ -12,6 +12,7 @@ struct DecodeParams {
   const uint8_t* kv;        // (pool_entries, 576)
   int64_t pool_entries;
   uint16_t* o;              // (T, H, 512) bf16
+  float* o32;               // if set, o is written here in fp32 instead (cascade passes)
   const int32_t* qo_indptr;  // (B+1)
   const int32_t* kv_indptr;  // (B+1)
   const int32_t* kv_indices;
@@ -27,6 +28,8 @@ struct DecodeParams {
   float* part_lse;          // workspace: (slots*num_workers, 16) fp32
   int4* desc;               // workspace: (tokens * head groups) split-unit descriptors
   int num_workers;
+  int causal;               // 1: bottom-right causal; 0 (group mode only): every token of a
+                            // request sees all of its entries
 };
 
 // Partial-answer slots per worker: a worker holds at most two partial pieces,

@@ -84,11 +84,15 @@ struct Req {
   int n;        // KV length
   int q_base;   // its first query token
   int qlen;     // query tokens
+  int causal;   // 1: token j sees visible(n, qlen, j) entries; 0: every token sees all n
 };
 
-MLA_HD Req load_req(const int32_t* qo, const int32_t* kvp, int b, int kv_cap, int T) {
-  int k0 = kvp[b], k1 = kvp[b + 1];
-  int q0 = qo[b], q1 = qo[b + 1];
+// Request b's bounds.  A null qo (kvp) stands for the single range [0, T)
+// ([0, kv_cap)): one request holding every token (entry).
+MLA_HD Req load_req(const int32_t* qo, const int32_t* kvp, int b, int kv_cap, int T,
+                    int causal = 1) {
+  int k0 = kvp ? kvp[b] : 0, k1 = kvp ? kvp[b + 1] : kv_cap;
+  int q0 = qo ? qo[b] : 0, q1 = qo ? qo[b + 1] : T;
   k0 = imin(imax(k0, 0), kv_cap);
   k1 = imin(imax(k1, k0), kv_cap);
   q0 = imin(imax(q0, 0), T);
@@ -98,7 +102,16 @@ MLA_HD Req load_req(const int32_t* qo, const int32_t* kvp, int b, int kv_cap, in
   r.n = k1 - k0;
   r.q_base = q0;
   r.qlen = q1 - q0;
+  r.causal = causal;
   return r;
+}
+
+// Entries visible to token j of request r.
+MLA_HD int req_visible(const Req& r, int j) { return r.causal ? visible(r.n, r.qlen, j) : r.n; }
+
+// Tokens of r that see no entry.
+MLA_HD int req_empty_tokens(const Req& r) {
+  return r.causal ? imin(r.qlen, imax(0, r.qlen - r.n)) : (r.n == 0 ? r.qlen : 0);
 }
 
 // Position in the unit stream: request b, its token j, head group g, offset k.
@@ -177,7 +190,7 @@ MLA_HD int group_units(const Req& r, int G) {
 
 MLA_HD int group_unit_len(const Req& r, int G, int u) {
   const int last = imin(kGroupsPerUnit * u + kGroupsPerUnit - 1, r.qlen * G - 1);
-  return visible(r.n, r.qlen, last / G);
+  return req_visible(r, last / G);
 }
 
 // Stream rows of request r in group mode.
@@ -214,11 +227,11 @@ MLA_HD void gcursor_in_request(GCursor& c, int b, const Req& r, int64_t off, int
 // Move to the start of the next non-empty unit (unit lengths never shrink
 // within a request).  Returns false past the end.
 MLA_HD bool gcursor_next_unit(GCursor& c, const int32_t* qo, const int32_t* kvp, int B, int kv_cap,
-                              int T, int G) {
+                              int T, int G, int causal) {
   c.k = 0;
   if (++c.u < group_units(c.r, G)) return true;
   for (int b = c.b + 1; b < B; ++b) {
-    Req r = load_req(qo, kvp, b, kv_cap, T);
+    Req r = load_req(qo, kvp, b, kv_cap, T, causal);
     if (group_request_rows(r, G) > 0) {
       c.b = b;
       c.r = r;

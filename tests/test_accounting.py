@@ -58,3 +58,19 @@ def test_c24_lengths_stay_in_captured_range(golden):
     lo = min(r[0] for r in g["kv_len_min_max_sum_late"])
     hi = max(r[1] for r in g["kv_len_min_max_sum_late"])
     assert lo - 500 <= min(lengths) and max(lengths) <= hi
+
+
+def test_cascade_bytes_count_the_shared_prefix_once():
+    """Distinct slots of the batch-16 call: the 63,911-slot prefix once plus
+    16 unique tails (the pages' "~137k distinct slots", 8.04x fewer)."""
+    w = workloads.Workload(name="c16-lengths", dtype="fp8", q=None, kv_pool=None, qo_indptr=None,
+                           kv_indptr=None, kv_indices=None, kv_last_page_lens=None, q_scale=None,
+                           kv_scale=None, sm_scale=0.0, num_heads=16, real_heads=12,
+                           max_seqlen_q=1, return_lse=False, lengths=workloads.c16_lengths(),
+                           qlens=[1] * 16)
+    P = workloads.SHARED_PREFIX
+    distinct = P + sum(n - P for n in w.lengths)
+    assert distinct == 63_911 + 16 * 4_519 + sum(b % 5 for b in range(16))
+    assert acc.cascade_bytes(w, P) == distinct * 580 + 16 * 16 * (576 + 1024)
+    assert abs(acc.workload_bytes(w) / acc.cascade_bytes(w, P) - 8.0) < 0.1
+    assert acc.cascade_bytes(w, 0) == acc.workload_bytes(w)

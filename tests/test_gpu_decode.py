@@ -205,6 +205,91 @@ def test_group_mode_graph_replay_matches_eager_bitwise():
         assert torch.equal(lse, lse_eager), f"replay {rep}"
 
 
+# ------------------------------------------------------------------ cascade
+# decode_cascade(q, prefix + per-request suffixes) must equal decode() over the
+# concatenated lists.
+
+
+def run_cascade(w, prefix, return_lse=True):
+    pre, sptr, suf = workloads.split_prefix(w, prefix)
+    torch.cuda.synchronize()
+    out = mla.decode_cascade(w.q, w.kv_pool, w.qo_indptr, pre, sptr, suf, w.sm_scale, w.q_scale,
+                             w.kv_scale, return_lse=return_lse, max_seqlen_q=w.max_seqlen_q)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_cascade(w, prefix, requests=None, where="", bf16_ulp_abs=False):
+    say(f"[cascade] {w.name} prefix={prefix} requests={requests}")
+    o, lse = run_cascade(w, prefix)
+    toks, o_ref, lse_ref = oracle(w, requests)
+    m = metrics(o[toks], o_ref, lse[toks], lse_ref)
+    say(f"[cascade] {w.name}: {m}")
+    tol = {"abs_tol": bf16_abs_tol(m["ref_absmax"])} if bf16_ulp_abs else {}
+    assert_gate(m, where or f"cascade {w.name}", **tol)
+    return o, lse
+
+
+def test_cascade_small_matches_oracle_and_plain_call():
+    w = small_shared(11)
+    o, lse = check_cascade(w, 2000)
+    o2, lse2 = run(w)
+    m = metrics(o, o2.float().cpu().numpy().astype(np.float64), lse, lse2.cpu().numpy())
+    assert_gate(m, "cascade vs plain decode")
+
+
+def test_cascade_edge_cases():
+    """No prefix; empty suffixes; a request that is prefix only."""
+    w = workloads.build("casc-edge", [1500, 1200, 1200, 2900], num_heads=32, real_heads=32,
+                        pool_entries=8192, kv_std=0.5, scale_range=(0.5, 2.0), shared_prefix=1200,
+                        seed=31, device=DEV)
+    check_cascade(w, 1200, where="cascade: suffixes 300, 0, 0, 1700")
+    check_cascade(w, 0, where="cascade: no prefix")
+    v = workloads.build("casc-pre-only", [900, 900], num_heads=16, real_heads=12, pool_entries=4096,
+                        shared_prefix=900, seed=32, device=DEV)
+    check_cascade(v, 900, where="cascade: every suffix empty")
+
+
+def test_cascade_multi_token_many_heads():
+    """Draft tokens with 64 heads: the suffix pass runs in group mode, and every
+    suffix holds at least qlen - 1 entries."""
+    w = workloads.build("casc-mt", [2500, 2003, 2600], num_heads=64, real_heads=64,
+                        qlens=[2, 4, 1], pool_entries=8192, kv_std=0.5, scale_range=(0.5, 2.0),
+                        shared_prefix=2000, seed=33, device=DEV)
+    check_cascade(w, 2000)
+
+
+def test_cascade_graph_replay_matches_eager_bitwise():
+    w = small_shared(12)
+    pre, sptr, suf = workloads.split_prefix(w, 2000)
+    o_e, lse_e = run_cascade(w, 2000)
+    o = torch.empty_like(o_e)
+    lse = torch.empty_like(lse_e)
+    ws = mla.new_workspace(mla.cascade_workspace_bytes(w.batch, w.num_tokens, w.num_heads, 1), DEV)
+
+    def call():
+        mla.decode_cascade(w.q, w.kv_pool, w.qo_indptr, pre, sptr, suf, w.sm_scale, w.q_scale,
+                           w.kv_scale, return_lse=True, o=o, lse=lse, max_seqlen_q=1, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        o.zero_()
+        lse.fill_(7.0)
+        run(small_shared(8))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_e), f"replay {rep}"
+        assert torch.equal(lse, lse_e), f"replay {rep}"
+
+
 # ------------------------------------------------------------------ bf16 storage
 
 
@@ -456,6 +541,12 @@ def test_mixed_lengths_bf16_sampled():
 def test_dcp_share_sampled():
     w = workloads.dcp_share(DEV)
     check(w, requests=[0, 5])
+
+
+def test_headline_batch16_cascade_sampled():
+    w = workloads.c16(DEV, "shared", return_lse=True)
+    check_cascade(w, workloads.SHARED_PREFIX, requests=[0, 7, 15])
+    del w
 
 
 def test_captured_argument_layout_is_accepted():

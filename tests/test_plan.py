@@ -35,7 +35,7 @@ def units(qo, kv, G):
     return out, pos
 
 
-def group_units(qo, kv, G):
+def group_units(qo, kv, G, causal=True):
     """Group mode: (request, unit, length, stream start) in stream order.  Unit u
     of a request covers row groups 8u..8u+7 (row group = token * G + head
     group) and is as long as its last row group sees."""
@@ -46,7 +46,7 @@ def group_units(qo, kv, G):
         R = ql * G
         for u in range(-(-R // U)):
             last = min(U * u + U - 1, R - 1)
-            v = visible(n, ql, last // G)
+            v = visible(n, ql, last // G) if causal else n
             out.append((b, u, v, pos))
             pos += v
     return out, pos
@@ -185,10 +185,10 @@ def test_rejects_bad_planner_input():
 # ---------------------------------------------------------------- group mode
 
 
-def check_group_plan(qo, kv, H, nw_req):
+def check_group_plan(qo, kv, H, nw_req, causal=True):
     G = H // 16
-    us, W = group_units(qo, kv, G)
-    pieces = plan_groups_host(qo, kv, H, nw_req)
+    us, W = group_units(qo, kv, G, causal)
+    pieces = plan_groups_host(qo, kv, H, nw_req, causal)
     if W == 0:
         assert len(pieces) == 0
         return pieces
@@ -273,3 +273,14 @@ def test_group_empty_and_tiny_inputs():
     p = check_group_plan(indptr([4]), indptr([200]), 16, 512)
     assert len(p) == 1 and p[0, 7] == 1
     check_group_plan(indptr([4, 3]), indptr([2, 1]), 32, 8)  # early draft tokens see nothing
+
+
+def test_group_plan_without_causal_mask():
+    """The cascade's prefix pass: one request holding every token, all of which
+    see every entry; units are as long as the request."""
+    pieces = check_group_plan(indptr([16]), indptr([63_911]), 16, 256, causal=False)
+    assert set(pieces[:, 5].tolist()) == {63_911}
+    check_group_plan(indptr([7]), indptr([5000]), 64, 37, causal=False)
+    check_group_plan(indptr([3]), indptr([0]), 32, 8, causal=False)
+    us, _ = group_units(indptr([4]), indptr([100]), 1, causal=False)
+    assert [(u, v) for _, u, v, _ in us] == [(0, 100)]

@@ -316,3 +316,21 @@ def merge_shards(
         lse[s, s % num_tokens, (7 * s) % num_heads] = -math.inf
     lse[:, num_tokens - 1, num_heads - 1] = -math.inf
     return o.to(tdtype), lse.to(torch.float32)
+
+def split_prefix(w: Workload, prefix: int):
+    """The same call as a shared prefix plus per-request suffixes (the layout
+    decode_cascade takes): the first `prefix` entries of every request must be
+    the same pool slots (build(..., shared_prefix >= prefix) makes them so).
+    Returns (prefix_indices, suffix_indptr, suffix_indices) on w's device."""
+    kvp = w.kv_indptr.cpu().tolist()
+    idx = w.kv_indices
+    pre = idx[kvp[0]: kvp[0] + prefix].clone()
+    for b in range(w.batch):
+        if kvp[b + 1] - kvp[b] < prefix or not torch.equal(idx[kvp[b]: kvp[b] + prefix], pre):
+            raise ValueError(f"request {b} does not start with the shared prefix")
+    parts = [idx[kvp[b] + prefix: kvp[b + 1]] for b in range(w.batch)]
+    lens = [int(t.numel()) for t in parts]
+    suf_indptr = torch.tensor([0] + list(__import__("itertools").accumulate(lens)), dtype=torch.int32,
+                              device=idx.device)
+    suf = torch.cat(parts) if sum(lens) else torch.zeros(1, dtype=torch.int32, device=idx.device)
+    return pre, suf_indptr, suf

@@ -52,3 +52,12 @@ def workload_bytes(w) -> int:
 
 def workload_flops(w) -> int:
     return decode_flops(w.lengths, w.qlens, w.num_heads)
+
+
+def cascade_bytes(w, prefix: int) -> int:
+    """Bytes a shared-prefix (cascade) call must move: the prefix rows and
+    indices once, each request's own rows and indices, q read and o written."""
+    rows = prefix + sum(max(0, n - prefix) for n in w.lengths)
+    T = sum(w.qlens)
+    return (rows * (row_bytes(w.dtype) + INDEX_BYTES) + T * w.num_heads * ROW_DIM * _ELEM[w.dtype]
+            + T * w.num_heads * LATENT_DIM * 2 + (T * w.num_heads * 4 if w.return_lse else 0))
