@@ -172,9 +172,9 @@ mla_status mla_merge_partials(const void* o_parts, int parts_dtype, const float*
 const char* mla_status_string(int status);
 
 /*
- * Shared-prefix (cascade) decode, SURVEY-ranked next step of the pages' method
- * ("[Kimi-K3 MLA TP8] MLA performance", ROCm/aiter issue 4541, Sec. 5.4 on
- * shared-prefix reuse): the same result as mla_decode when request b's entry
+ * Shared-prefix (cascade) decode ("[Kimi-K3 MLA TP8] MLA performance",
+ * ROCm/aiter issue 4541, Sec. 5.4 on reuse of the prefix shared by the
+ * batch's requests): the same result as mla_decode when request b's entry
  * list is prefix_indices (shared by every request) followed by its own
  * suffix_indices[suffix_indptr[b] .. suffix_indptr[b+1]).  The shared rows are
  * gathered once for eight row groups (all tokens, all heads) instead of once

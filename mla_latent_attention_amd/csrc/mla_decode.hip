@@ -707,39 +707,54 @@ void mla_decode_bf16_kernel(const DecodeParams p) {
 
 // ---------------------------------------------------------------- split combine
 
-// grid (units, 32) of single waves: block (u, 2n + h) merges row n, dims
+// grid (units, 32) of four-wave blocks: block (u, 2n + h) merges row n, dims
 // [256h, 256h + 256) of unit u = t * G + g if it was split, 4 dims per lane:
 // M = max lse_s, o = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
 // The slots are the first worker's own and, for each later worker w', the
 // slot of its first piece: kSlots * w' + (position of the row group within
 // its piece), i.e. first_slot mod (kSlots / 2) (0 in the standard mode, with
 // kSlots = 2; the row group within the unit in group mode, with kSlots = 16).
-constexpr int kCombineThreads = 64;
+// Up to 16 slots are merged by the first wave alone; beyond that wave wv takes
+// batches wv, wv + 4, ... of 16 slots and the four partial merges are merged
+// once more through LDS, so a unit split over many workers costs a quarter of
+// the dependent load rounds.
+constexpr int kCombineWaves = 4;
+constexpr int kCombineThreads = 64 * kCombineWaves;
+constexpr int kCombineBatch = 16;
+
+struct CombineShared {
+  float4 acc[kCombineWaves][64];
+  float m[kCombineWaves];
+  float sum[kCombineWaves];
+};
 
 template <int kSlots, bool kBf16Parts>
-__device__ __forceinline__ void combine_unit(const DecodeParams& p) {
+__device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShared& sh) {
   const int64_t u = blockIdx.x;
   const int4 d = p.desc[u];
   if (d.w == 0) return;
   const int G = p.num_heads / kGroup;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = blockIdx.y >> 1, h = blockIdx.y & 1;
   const int w0 = d.x, S = d.y - d.x + 1;
+  const bool many = S > kCombineBatch;  // uniform over the block
+  if (!many && wv != 0) return;
   const int pos = d.z % (kSlots / 2);
   auto slot_of = [&](int i) -> int64_t {
     return i == 0 ? (int64_t)d.z : (int64_t)kSlots * (w0 + i) + pos;
   };
 
-  // Slots in batches of 16: every load of a batch is issued before any is
-  // used, with an online rescale across batches.
+  // Slots in batches: every load of a batch is issued before any is used,
+  // with an online rescale across batches.  A slot whose lse is -inf (its
+  // piece held none of the row's visible entries) gets weight 0.
   float M = neg_inf(), sum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  constexpr int kBatch = 16;
-  for (int i0 = 0; i0 < S; i0 += kBatch) {
-    float4 x[kBatch];
-    float ls[kBatch];
+  const int step = many ? kCombineWaves * kCombineBatch : kCombineBatch;
+  for (int i0 = wv * kCombineBatch; i0 < S; i0 += step) {
+    float4 x[kCombineBatch];
+    float ls[kCombineBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {  // past-the-end slots reload the last one, weight 0
+    for (int j = 0; j < kCombineBatch; ++j) {  // past-the-end slots reload the last one, weight 0
       const int64_t slot = slot_of(imin(i0 + j, S - 1));
       ls[j] = p.part_lse[slot * kGroup + n];
       const int64_t e0 = (slot * kGroup + n) * kLatent + 256 * h + 4 * lane;
@@ -756,8 +771,9 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p) {
     __builtin_amdgcn_sched_barrier(0);
     float bm = M;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j)
+    for (int j = 0; j < kCombineBatch; ++j)
       if (i0 + j < S) bm = fmaxf(bm, ls[j]);
+    if (bm == neg_inf()) continue;  // nothing visible yet: acc and sum stay 0
     const float alpha = (M == neg_inf()) ? 0.f : fast_exp2((M - bm) * kLog2e);
     sum *= alpha;
     acc.x *= alpha;
@@ -766,7 +782,7 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p) {
     acc.w *= alpha;
     M = bm;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
+    for (int j = 0; j < kCombineBatch; ++j) {
       const float wt = (i0 + j < S) ? fast_exp2((ls[j] - M) * kLog2e) : 0.f;
       sum += wt;
       acc.x += wt * x[j].x;
@@ -775,7 +791,31 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p) {
       acc.w += wt * x[j].w;
     }
   }
-  const float inv = 1.0f / sum;
+  if (many) {
+    sh.acc[wv][lane] = acc;
+    if (lane == 0) {
+      sh.m[wv] = M;
+      sh.sum[wv] = sum;
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    M = neg_inf();
+#pragma unroll
+    for (int i = 0; i < kCombineWaves; ++i) M = fmaxf(M, sh.m[i]);
+    sum = 0.f;
+    acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < kCombineWaves; ++i) {
+      const float wt = (sh.m[i] == neg_inf()) ? 0.f : fast_exp2((sh.m[i] - M) * kLog2e);
+      const float4 a = sh.acc[i][lane];
+      sum += wt * sh.sum[i];
+      acc.x += wt * a.x;
+      acc.y += wt * a.y;
+      acc.z += wt * a.z;
+      acc.w += wt * a.w;
+    }
+  }
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;  // a row that sees nothing: o = 0, lse = -inf
   const int64_t t = u / G, g = u % G;
   const int64_t orow = t * p.num_heads + g * kGroup + n;
   if (p.o32 != nullptr) {
@@ -787,15 +827,18 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p) {
     pk.y = bf16_bits(acc.z * inv) | (bf16_bits(acc.w * inv) << 16);
     *(uint2*)(p.o + orow * kLatent + 256 * h + 4 * lane) = pk;
   }
-  if (p.lse != nullptr && h == 0 && lane == 0) p.lse[orow] = M + fast_log2(sum) * kLn2;
+  if (p.lse != nullptr && h == 0 && lane == 0)
+    p.lse[orow] = sum > 0.f ? M + fast_log2(sum) * kLn2 : neg_inf();
 }
 
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const DecodeParams p) {
-  combine_unit<2, false>(p);
+  __shared__ CombineShared sh;
+  combine_unit<2, false>(p, sh);
 }
 
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_groups_kernel(const DecodeParams p) {
-  combine_unit<16, true>(p);
+  __shared__ CombineShared sh;
+  combine_unit<16, true>(p, sh);
 }
 
 // ---------------------------------------------------------------- shard merge

@@ -19,7 +19,8 @@
 //   * A worker boundary that falls within kSnapRows rows of a unit boundary
 //     is moved onto it, so no worker pays the fixed cost of a piece of a few
 //     rows (with equal shares, unit boundaries drift a few rows past worker
-//     boundaries).  Boundaries stay >= 256 rows apart, so they never cross.
+//     boundaries).  Unsnapped boundaries are >= kMinWorkerRows - 1 rows apart
+//     and each moves at most kSnapRows, so they never meet.
 //   * Only a worker's first and last piece can be partial: a partial first
 //     piece writes its (o, lse) to workspace slot 2w, a partial last piece to
 //     slot 2w+1.  Complete pieces write o (and lse) directly.
@@ -42,7 +43,7 @@ namespace mla {
 constexpr int kRowDim = 576;     // latent 512 + rope 64
 constexpr int kLatent = 512;
 constexpr int kGroup = 16;       // heads per row group (one MFMA tile of rows)
-constexpr int kMinWorkerRows = 512;
+constexpr int kMinWorkerRows = 256;
 
 MLA_HD int imin(int a, int b) { return a < b ? a : b; }
 MLA_HD int imax(int a, int b) { return a > b ? a : b; }
@@ -59,7 +60,7 @@ MLA_HD int64_t request_rows(int n, int qlen) {
 }
 
 MLA_HD int effective_workers(int64_t W, int nw) {
-  int64_t need = (W + kMinWorkerRows - 1) / kMinWorkerRows;
+  int64_t need = W / kMinWorkerRows;  // rounded down: every worker gets >= kMinWorkerRows
   if (need < 1) need = 1;
   return (int)lmin(need, (int64_t)nw);
 }

@@ -88,6 +88,17 @@ def test_small_shared_prefix_any_worker_count(nw):
     check(small_shared(), num_workers=nw, where=f"small nw={nw}")
 
 
+@pytest.mark.parametrize("heads", [16, 96])
+def test_one_long_request_split_over_many_workers(heads):
+    """One request split over ~100-150 workers: the combine merges more than 16
+    partials per row, which takes its four-wave path (standard and group mode)."""
+    n = 40_000 if heads == 16 else 30_000
+    w = workloads.build(f"long-{heads}", [n], num_heads=heads, real_heads=heads,
+                        pool_entries=1 << 16, kv_std=0.5, scale_range=(0.5, 2.0), seed=61,
+                        device=DEV)
+    check(w, num_workers=256, where=f"one long request, {heads} heads")
+
+
 def test_ragged_lengths_and_empty_requests():
     lengths = [0, 1, 31, 32, 33, 100, 1000, 4097, 0, 2]
     qlens = [1, 1, 1, 1, 1, 1, 1, 1, 1, 1]

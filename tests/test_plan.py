@@ -12,7 +12,7 @@ import pytest
 import workloads
 from mla_latent_attention_amd import plan_groups_host, plan_host
 
-MIN_WORKER_ROWS = 512
+MIN_WORKER_ROWS = 256
 SNAP_ROWS = 64
 GROUPS_PER_UNIT = 8  # group mode: row groups per unit
 GROUP_SLOTS = 16  # group mode: partial slots per worker (two pieces x 8 row groups)
@@ -81,7 +81,7 @@ def check_plan(qo, kv, H, nw_req):
     if W == 0:
         assert len(pieces) == 0
         return pieces
-    nw = min(nw_req, max(1, -(-W // MIN_WORKER_ROWS)))
+    nw = min(nw_req, max(1, W // MIN_WORKER_ROWS))
     S = snapped_bounds(us, W, nw)
     assert all(a < b for a, b in zip(S, S[1:]))
     cover = {}
@@ -192,7 +192,7 @@ def check_group_plan(qo, kv, H, nw_req, causal=True):
     if W == 0:
         assert len(pieces) == 0
         return pieces
-    nw = min(nw_req, max(1, -(-W // MIN_WORKER_ROWS)))
+    nw = min(nw_req, max(1, W // MIN_WORKER_ROWS))
     S = snapped_bounds(us, W, nw)
     assert all(a < b for a, b in zip(S, S[1:]))
     cover = {}
