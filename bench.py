@@ -144,6 +144,12 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
         ws = mla.new_workspace(mla.workspace_bytes(base.batch, T, H, base.max_seqlen_q), dev)
 
         def call_for(w):
+            if w.g_kv_indptr is not None:  # one DCP shard
+                return lambda: mla.decode_dcp(
+                    w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_lens,
+                    w.sm_scale, w.q_scale, w.kv_scale, return_lse=w.return_lse,
+                    g_kv_indptr=w.g_kv_indptr, cp_world_size=w.cp_size, cp_rank=w.cp_rank, o=o,
+                    lse=lse, max_seqlen_q=w.max_seqlen_q, workspace=ws)
             return lambda: mla.decode(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
                                       w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale,
                                       return_lse=w.return_lse, o=o, lse=lse,

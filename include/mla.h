@@ -150,6 +150,45 @@ size_t mla_decode_workspace_bytes_ex(int batch, int num_q_tokens, int num_heads,
                                      int max_seqlen_q, int num_workers);
 
 /*
+ * One shard of decode context parallelism (DCP): "Kimi K3 on AMD Instinct
+ * MI355X ...", Sec. "1. Cache: keep conversation state available for reuse"
+ * (each of the GPUs keeps one eighth of the cached positions, runs the
+ * exchanged queries of all heads against them, and the partial answers are
+ * merged with softmax weights; multi-token verification under DCP), with the
+ * shard arguments of the entry point in "[Kimi-K3 MLA TP8] MLA performance",
+ * Sec. 3 (g_kv_indptr, cp_world_size, cp_rank).
+ *
+ * Arguments as for mla_decode, where kv_indptr / kv_indices describe this
+ * shard's entries, plus:
+ *  g_kv_indptr    (batch+1) int32 device offsets of the requests' full
+ *                 (all-shard) lists: N_b = g_kv_indptr[b+1] - g_kv_indptr[b]
+ *                 positions in total.
+ *  cp_world_size  shards the positions are dealt over, 1..1024.
+ *  cp_rank        this shard, 0 <= cp_rank < cp_world_size.
+ * Layout (caller's contract): positions are dealt round-robin, so this
+ * shard's i-th entry of request b is the entry at full-list position
+ * cp_rank + i * cp_world_size; it holds ceil((N_b - cp_rank) /
+ * cp_world_size) entries.  Query token j of a request with qlen tokens sees
+ * the local entries whose full-list position is <= N_b - qlen + j (the
+ * bottom-right causal rule of mla_decode applied to full-list positions); a
+ * row that sees nothing gets o = 0 and lse = -inf, which
+ * mla_merge_partials gives weight 0.  With return_lse set, merging the
+ * cp_world_size shards' (o, lse) with mla_merge_partials gives the result of
+ * mla_decode over the full lists.  Same workspace as mla_decode; same
+ * supported types and shapes.  A NULL g_kv_indptr returns
+ * MLA_ERR_NULL_POINTER, a cp_world_size or cp_rank out of range
+ * MLA_ERR_BAD_SHAPE.
+ */
+mla_status mla_decode_dcp(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                          int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                          const int32_t* kv_indptr, const int32_t* kv_indices,
+                          int64_t kv_indices_len, const int32_t* kv_last_page_lens, int batch,
+                          int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
+                          const float* q_scale, const float* kv_scale, int return_lse,
+                          float* lse, const int32_t* g_kv_indptr, int cp_world_size,
+                          int cp_rank, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * LSE-weighted merge of partial answers over disjoint KV shards (the DCP
  * merge of the blog's Sec. 1; the same math combines the decode's own splits).
  *
@@ -207,11 +246,14 @@ mla_status mla_decode_cascade(const void* q, int q_dtype, const void* kv_pool, i
  * and kv_indptr, fill `out` (capacity `out_cap` pieces, 8 int64 each:
  * worker, token, head_group, kv_begin, kv_end, unit_len, slot, is_complete)
  * with the pieces every worker processes, in worker order.  slot is the
- * partial-answer slot (-1 for complete pieces).  Returns the number of pieces
+ * partial-answer slot (-1 for complete pieces).  g_kv_indptr (host, may be
+ * NULL), cp_world_size and cp_rank describe a DCP shard as for
+ * mla_decode_dcp (NULL, 1, 0 without DCP).  Returns the number of pieces
  * (which may exceed out_cap; only out_cap are written), or -1 on bad input.
  */
-int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
-                      int num_heads, int num_workers, int64_t* out, int64_t out_cap);
+int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                      const int32_t* g_kv_indptr, int batch, int num_heads, int num_workers,
+                      int cp_world_size, int cp_rank, int64_t* out, int64_t out_cap);
 
 /*
  * Host mirror of the group-mode planner (the fp8 path when num_heads / 16 *
@@ -221,11 +263,13 @@ int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int ba
  * columns: worker, request, unit, kv_begin, kv_end, unit_len, slot_base,
  * is_complete; slot_base is the first of the piece's 8 partial slots (one per
  * row group), -1 for complete pieces.  causal = 0 lets every token see all of
- * its request's entries (the cascade's prefix pass).  Same return convention.
+ * its request's entries (the cascade's prefix pass).  DCP arguments and
+ * return convention as for mla_plan_host.
  */
-int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
-                             int num_heads, int num_workers, int causal, int64_t* out,
-                             int64_t out_cap);
+int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                             const int32_t* g_kv_indptr, int batch, int num_heads,
+                             int num_workers, int causal, int cp_world_size, int cp_rank,
+                             int64_t* out, int64_t out_cap);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,7 @@ __all__ = [
     "plan_host",
     "plan_groups_host",
     "decode_cascade",
+    "decode_dcp",
     "cascade_workspace_bytes",
     "new_workspace",
     "MLAError",
@@ -102,6 +103,7 @@ def decode(
     max_seqlen_q: int | None = None,
     workspace: torch.Tensor | None = None,
     num_workers: int = 0,
+    _dcp=None,
 ):
     """Latent MLA decode; returns o (T, H, 512) bf16, or (o, lse) if return_lse.
 
@@ -151,15 +153,51 @@ def decode(
     ws_len = workspace.numel() * workspace.element_size()
     L = _lib.lib()
     qdt, kdt = _storage_dtype(q), _storage_dtype(kv_pool)
-    status = L.mla_decode_ex(
+    head = (
         _ptr(q), qdt, _ptr(kv_pool), kdt, kv_pool.shape[0], _ptr(o), _ptr(qo_indptr),
         _ptr(kv_indptr), _ptr(kv_indices), kv_indices.numel(), _ptr(kv_last_page_lens),
         B, T, H, max_seqlen_q, float(sm_scale), _ptr(q_scale), _ptr(kv_scale),
-        1 if return_lse else 0, _ptr(lse) if return_lse else None, _ptr(workspace), ws_len,
-        int(num_workers), _stream(dev),
+        1 if return_lse else 0, _ptr(lse) if return_lse else None,
     )
-    _lib.check(status, "mla_decode")
+    if _dcp is None:
+        status = L.mla_decode_ex(*head, _ptr(workspace), ws_len, int(num_workers), _stream(dev))
+        _lib.check(status, "mla_decode")
+    else:
+        g_kv_indptr, cp_world_size, cp_rank = _dcp
+        _need(g_kv_indptr, "g_kv_indptr", dev, torch.int32, (B + 1,))
+        status = L.mla_decode_dcp(*head, _ptr(g_kv_indptr), int(cp_world_size), int(cp_rank),
+                                  _ptr(workspace), ws_len, _stream(dev))
+        _lib.check(status, "mla_decode_dcp")
     return (o, lse) if return_lse else o
+
+
+def decode_dcp(
+    q: torch.Tensor,
+    kv_pool: torch.Tensor,
+    qo_indptr: torch.Tensor,
+    kv_indptr: torch.Tensor,
+    kv_indices: torch.Tensor,
+    kv_last_page_lens: torch.Tensor | None,
+    sm_scale: float,
+    q_scale: torch.Tensor | None = None,
+    kv_scale: torch.Tensor | None = None,
+    return_lse: bool = False,
+    *,
+    g_kv_indptr: torch.Tensor,
+    cp_world_size: int,
+    cp_rank: int,
+    o: torch.Tensor | None = None,
+    lse: torch.Tensor | None = None,
+    max_seqlen_q: int | None = None,
+    workspace: torch.Tensor | None = None,
+):
+    """One DCP shard's decode (mla_decode_dcp): kv_indptr / kv_indices hold this
+    shard's entries, the full-list positions cp_rank, cp_rank + cp_world_size, ...
+    of each request; g_kv_indptr (B+1) int32 on the device gives the full lists'
+    offsets.  Returns what decode() returns."""
+    return decode(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_lens, sm_scale,
+                  q_scale, kv_scale, return_lse, o=o, lse=lse, max_seqlen_q=max_seqlen_q,
+                  workspace=workspace, _dcp=(g_kv_indptr, cp_world_size, cp_rank))
 
 
 def cascade_workspace_bytes(batch: int, num_q_tokens: int, num_heads: int,
@@ -267,29 +305,39 @@ GROUP_PLAN_FIELDS = ("worker", "request", "unit", "kv_begin", "kv_end", "unit_le
                      "complete")
 
 
-def _plan(fn, qo_indptr, kv_indptr, num_heads, num_workers):
+def _plan(fn, qo_indptr, kv_indptr, num_heads, num_workers, g_kv_indptr=None):
     qo = np.ascontiguousarray(np.asarray(qo_indptr, dtype=np.int32))
     kv = np.ascontiguousarray(np.asarray(kv_indptr, dtype=np.int32))
+    gkv = None if g_kv_indptr is None else np.ascontiguousarray(np.asarray(g_kv_indptr, np.int32))
+    gp = None if gkv is None else gkv.ctypes.data
     B = len(qo) - 1
-    n = fn(qo.ctypes.data, kv.ctypes.data, B, num_heads, num_workers, None, 0)
+    n = fn(qo.ctypes.data, kv.ctypes.data, gp, B, num_heads, num_workers, None, 0)
     if n < 0:
         raise ValueError("invalid planner input")
     out = np.zeros((max(n, 1), 8), dtype=np.int64)
-    n2 = fn(qo.ctypes.data, kv.ctypes.data, B, num_heads, num_workers, out.ctypes.data, n)
+    n2 = fn(qo.ctypes.data, kv.ctypes.data, gp, B, num_heads, num_workers, out.ctypes.data, n)
     assert n2 == n
     return out[:n]
 
 
-def plan_host(qo_indptr, kv_indptr, num_heads: int, num_workers: int) -> np.ndarray:
-    """The planner's pieces for host indptr arrays: int64 array (pieces, 8), columns PLAN_FIELDS."""
-    return _plan(_lib.lib().mla_plan_host, qo_indptr, kv_indptr, num_heads, num_workers)
+def plan_host(qo_indptr, kv_indptr, num_heads: int, num_workers: int, *, g_kv_indptr=None,
+              cp_world_size: int = 1, cp_rank: int = 0) -> np.ndarray:
+    """The planner's pieces for host indptr arrays: int64 array (pieces, 8), columns
+    PLAN_FIELDS.  g_kv_indptr / cp_world_size / cp_rank: a DCP shard (mla_decode_dcp)."""
+    fn = _lib.lib().mla_plan_host
+    return _plan(lambda q, k, g, B, H, nw, out, cap: fn(q, k, g, B, H, nw, cp_world_size, cp_rank,
+                                                         out, cap),
+                 qo_indptr, kv_indptr, num_heads, num_workers, g_kv_indptr)
 
 
 def plan_groups_host(qo_indptr, kv_indptr, num_heads: int, num_workers: int,
-                     causal: bool = True) -> np.ndarray:
+                     causal: bool = True, *, g_kv_indptr=None, cp_world_size: int = 1,
+                     cp_rank: int = 0) -> np.ndarray:
     """The group-mode planner's pieces: int64 array (pieces, 8), columns GROUP_PLAN_FIELDS.
-    causal=False: every token sees all of its request's entries."""
+    causal=False: every token sees all of its request's entries.  DCP arguments as for
+    plan_host."""
     fn = _lib.lib().mla_plan_groups_host
     c = 1 if causal else 0
-    return _plan(lambda q, k, B, H, nw, out, cap: fn(q, k, B, H, nw, c, out, cap),
-                 qo_indptr, kv_indptr, num_heads, num_workers)
+    return _plan(lambda q, k, g, B, H, nw, out, cap: fn(q, k, g, B, H, nw, c, cp_world_size,
+                                                         cp_rank, out, cap),
+                 qo_indptr, kv_indptr, num_heads, num_workers, g_kv_indptr)

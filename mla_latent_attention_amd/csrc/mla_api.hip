@@ -42,6 +42,7 @@ bool shape_ok(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
 }
 
 using mla::kMaxWorkers;
+constexpr int kMaxCpSize = 1024;  // DCP shards accepted by mla_decode_dcp
 
 // Partial slots per worker for a call shape (group mode applies to the fp8
 // kernels; the layout is sized the same for both storage types).
@@ -56,49 +57,14 @@ int workers_for(int num_heads, int max_seqlen_q, int cus) {
   return cus;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* mla_status_string(int status) {
-  switch (status) {
-    case MLA_OK: return "MLA_OK";
-    case MLA_ERR_NULL_POINTER: return "MLA_ERR_NULL_POINTER: a required pointer is NULL";
-    case MLA_ERR_BAD_SHAPE: return "MLA_ERR_BAD_SHAPE: a size argument is out of range";
-    case MLA_ERR_BAD_DTYPE: return "MLA_ERR_BAD_DTYPE: unsupported storage type combination";
-    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: num_heads must be a multiple of 16";
-    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: workspace missing or too small";
-    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
-    default: return "MLA_ERR_UNKNOWN";
-  }
-}
-
-size_t mla_decode_workspace_bytes_ex(int batch, int num_q_tokens, int num_heads,
-                                     int max_seqlen_q, int num_workers) {
-  if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
-  if (num_workers < 1 || num_workers > kMaxWorkers) return 0;
-  return mla::workspace_bytes(num_workers, (int64_t)num_q_tokens * (num_heads / mla::kGroup),
-                              slots_for(num_heads, max_seqlen_q));
-}
-
-size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
-  if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
-  const int cus = current_cu_count();
-  if (cus <= 0) return 0;
-  return mla::workspace_bytes(workers_for(num_heads, max_seqlen_q, cus),
-                              (int64_t)num_q_tokens * (num_heads / mla::kGroup),
-                              slots_for(num_heads, max_seqlen_q));
-}
-
-mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
-                         int64_t pool_entries, void* o, const int32_t* qo_indptr,
-                         const int32_t* kv_indptr, const int32_t* kv_indices,
-                         int64_t kv_indices_len, const int32_t* kv_last_page_lens, int batch,
-                         int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
-                         const float* q_scale, const float* kv_scale, int return_lse,
-                         float* lse, void* workspace, size_t workspace_bytes, int num_workers,
-                         void* stream) {
-  (void)kv_last_page_lens;  // page_size 1: all ones by contract, never read
+mla_status decode_impl(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                       int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                       const int32_t* kv_indptr, const int32_t* kv_indices, int64_t kv_indices_len,
+                       int batch, int num_q_tokens, int num_heads, int max_seqlen_q,
+                       float sm_scale, const float* q_scale, const float* kv_scale,
+                       int return_lse, float* lse, const int32_t* g_kv_indptr, int cp_size,
+                       int cp_rank, void* workspace, size_t workspace_bytes, int num_workers,
+                       void* stream) {
   if (!q || !kv_pool || !o || !qo_indptr || !kv_indptr || !kv_indices)
     return MLA_ERR_NULL_POINTER;
   if (return_lse && !lse) return MLA_ERR_NULL_POINTER;
@@ -149,9 +115,79 @@ mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv
                                         mla::part_o_bytes(num_workers, slots));
   p.num_workers = num_workers;
   p.causal = 1;
+  p.g_kv_indptr = g_kv_indptr;
+  p.cp_size = cp_size;
+  p.cp_rank = cp_rank;
   if (mla::launch_decode(p, kdt, group_mode, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL_POINTER: return "MLA_ERR_NULL_POINTER: a required pointer is NULL";
+    case MLA_ERR_BAD_SHAPE: return "MLA_ERR_BAD_SHAPE: a size argument is out of range";
+    case MLA_ERR_BAD_DTYPE: return "MLA_ERR_BAD_DTYPE: unsupported storage type combination";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: num_heads must be a multiple of 16";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+size_t mla_decode_workspace_bytes_ex(int batch, int num_q_tokens, int num_heads,
+                                     int max_seqlen_q, int num_workers) {
+  if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
+  if (num_workers < 1 || num_workers > kMaxWorkers) return 0;
+  return mla::workspace_bytes(num_workers, (int64_t)num_q_tokens * (num_heads / mla::kGroup),
+                              slots_for(num_heads, max_seqlen_q));
+}
+
+size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
+  if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
+  const int cus = current_cu_count();
+  if (cus <= 0) return 0;
+  return mla::workspace_bytes(workers_for(num_heads, max_seqlen_q, cus),
+                              (int64_t)num_q_tokens * (num_heads / mla::kGroup),
+                              slots_for(num_heads, max_seqlen_q));
+}
+
+mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                         int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                         const int32_t* kv_indptr, const int32_t* kv_indices,
+                         int64_t kv_indices_len, const int32_t* kv_last_page_lens, int batch,
+                         int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
+                         const float* q_scale, const float* kv_scale, int return_lse,
+                         float* lse, void* workspace, size_t workspace_bytes, int num_workers,
+                         void* stream) {
+  (void)kv_last_page_lens;  // page_size 1: all ones by contract, never read
+  return decode_impl(q, q_dtype, kv_pool, kv_dtype, pool_entries, o, qo_indptr, kv_indptr,
+                     kv_indices, kv_indices_len, batch, num_q_tokens, num_heads, max_seqlen_q,
+                     sm_scale, q_scale, kv_scale, return_lse, lse, nullptr, 1, 0, workspace,
+                     workspace_bytes, num_workers, stream);
+}
+
+mla_status mla_decode_dcp(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                          int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                          const int32_t* kv_indptr, const int32_t* kv_indices,
+                          int64_t kv_indices_len, const int32_t* kv_last_page_lens, int batch,
+                          int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
+                          const float* q_scale, const float* kv_scale, int return_lse,
+                          float* lse, const int32_t* g_kv_indptr, int cp_world_size,
+                          int cp_rank, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)kv_last_page_lens;
+  if (!g_kv_indptr) return MLA_ERR_NULL_POINTER;
+  if (cp_world_size < 1 || cp_world_size > kMaxCpSize || cp_rank < 0 || cp_rank >= cp_world_size)
+    return MLA_ERR_BAD_SHAPE;
+  return decode_impl(q, q_dtype, kv_pool, kv_dtype, pool_entries, o, qo_indptr, kv_indptr,
+                     kv_indices, kv_indices_len, batch, num_q_tokens, num_heads, max_seqlen_q,
+                     sm_scale, q_scale, kv_scale, return_lse, lse, g_kv_indptr, cp_world_size,
+                     cp_rank, workspace, workspace_bytes, 0, stream);
 }
 
 mla_status mla_decode(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
@@ -301,21 +337,21 @@ mla_status mla_merge_partials(const void* o_parts, int parts_dtype, const float*
   return MLA_OK;
 }
 
-int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
-                      int num_heads, int num_workers, int64_t* out, int64_t out_cap) {
+int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                      const int32_t* g_kv_indptr, int batch, int num_heads, int num_workers,
+                      int cp_world_size, int cp_rank, int64_t* out, int64_t out_cap) {
   using namespace mla;
   if (!qo_indptr || !kv_indptr || batch < 1 || num_heads < kGroup || num_heads % kGroup ||
       num_workers < 1 || (out_cap > 0 && !out))
     return -1;
+  if (cp_world_size < 1 || cp_rank < 0 || cp_rank >= cp_world_size) return -1;
   const int G = num_heads / kGroup;
   const int T = qo_indptr[batch];
   const int kv_cap = kv_indptr[batch];
   if (T < 0 || kv_cap < 0) return -1;
+  const ReqSource src{qo_indptr, kv_indptr, g_kv_indptr, kv_cap, T, 1, cp_world_size, cp_rank};
   std::vector<int64_t> cum(batch + 1, 0);
-  for (int b = 0; b < batch; ++b) {
-    const Req r = load_req(qo_indptr, kv_indptr, b, kv_cap, T);
-    cum[b + 1] = cum[b] + (int64_t)G * request_rows(r.n, r.qlen);
-  }
+  for (int b = 0; b < batch; ++b) cum[b + 1] = cum[b] + (int64_t)G * request_rows(load_req(src, b));
   const int64_t W = cum[batch];
   if (W == 0) return 0;
   const int nw = effective_workers(W, num_workers);
@@ -324,7 +360,7 @@ int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int ba
   auto locate = [&](int64_t x, Cursor& c) {
     int b = 0;
     while (!(cum[b] <= x && x < cum[b + 1])) ++b;
-    cursor_in_request(c, b, load_req(qo_indptr, kv_indptr, b, kv_cap, T), x - cum[b], G);
+    cursor_in_request(c, b, load_req(src, b), x - cum[b], G);
   };
   for (int w = 0; w < nw; ++w) {
     const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
@@ -340,12 +376,12 @@ int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int ba
     if (p0 < x0) {
       c.k = 0;
     } else if (p0 > x0) {
-      if (!cursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G)) continue;
+      if (!cursor_next_unit(c, src, batch, G)) continue;
     }
     int64_t pos = p0;
     int piece = 0;
     while (pos < p1) {
-      const int v = visible(c.r.n, c.r.qlen, c.j);
+      const int v = req_visible(c.r, c.j);
       const int len = (int)lmin((int64_t)(v - c.k), p1 - pos);
       if (len <= 0) return -1;
       const bool complete = (c.k == 0 && len == v);
@@ -365,27 +401,30 @@ int64_t mla_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int ba
       pos += len;
       c.k += len;
       ++piece;
-      if (pos < p1 && c.k == v && !cursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G))
+      if (pos < p1 && c.k == v && !cursor_next_unit(c, src, batch, G))
         return -1;
     }
   }
   return count;
 }
 
-int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr, int batch,
-                             int num_heads, int num_workers, int causal, int64_t* out,
-                             int64_t out_cap) {
+int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                             const int32_t* g_kv_indptr, int batch, int num_heads,
+                             int num_workers, int causal, int cp_world_size, int cp_rank,
+                             int64_t* out, int64_t out_cap) {
   using namespace mla;
   if (!qo_indptr || !kv_indptr || batch < 1 || num_heads < kGroup || num_heads % kGroup ||
       num_workers < 1 || (out_cap > 0 && !out))
     return -1;
+  if (cp_world_size < 1 || cp_rank < 0 || cp_rank >= cp_world_size) return -1;
   const int G = num_heads / kGroup;
   const int T = qo_indptr[batch];
   const int kv_cap = kv_indptr[batch];
   if (T < 0 || kv_cap < 0) return -1;
+  const ReqSource src{qo_indptr, kv_indptr, g_kv_indptr, kv_cap, T, causal ? 1 : 0, cp_world_size,
+                      cp_rank};
   std::vector<int64_t> cum(batch + 1, 0);
-  for (int b = 0; b < batch; ++b)
-    cum[b + 1] = cum[b] + group_request_rows(load_req(qo_indptr, kv_indptr, b, kv_cap, T, causal), G);
+  for (int b = 0; b < batch; ++b) cum[b + 1] = cum[b] + group_request_rows(load_req(src, b), G);
   const int64_t W = cum[batch];
   if (W == 0) return 0;
   const int nw = effective_workers(W, num_workers);
@@ -394,7 +433,7 @@ int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   auto locate = [&](int64_t x, GCursor& c) {
     int b = 0;
     while (!(cum[b] <= x && x < cum[b + 1])) ++b;
-    gcursor_in_request(c, b, load_req(qo_indptr, kv_indptr, b, kv_cap, T, causal), x - cum[b], G);
+    gcursor_in_request(c, b, load_req(src, b), x - cum[b], G);
   };
   for (int w = 0; w < nw; ++w) {
     const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
@@ -410,7 +449,7 @@ int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     if (p0 < x0) {
       c.k = 0;
     } else if (p0 > x0) {
-      if (!gcursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G, causal)) continue;
+      if (!gcursor_next_unit(c, src, batch, G)) continue;
     }
     int64_t pos = p0;
     int piece = 0;
@@ -435,7 +474,7 @@ int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
       pos += len;
       c.k += len;
       ++piece;
-      if (pos < p1 && c.k == L && !gcursor_next_unit(c, qo_indptr, kv_indptr, batch, kv_cap, T, G, causal))
+      if (pos < p1 && c.k == L && !gcursor_next_unit(c, src, batch, G))
         return -1;
     }
   }

@@ -607,11 +607,12 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
   const int G = p.num_heads / kGroup;
 
   // Pass 1 over requests: stream length W; zero this block's empty tokens.
+  const ReqSource src = source_of(p);
   int64_t acc = 0;
   for (int b = threadIdx.x; b < p.batch; b += kThreads) {
-    const Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens);
-    acc += (int64_t)G * request_rows(r.n, r.qlen);
-    const int nempty = imin(r.qlen, imax(0, r.qlen - r.n));
+    const Req r = load_req(src, b);
+    acc += (int64_t)G * request_rows(r);
+    const int nempty = req_empty_tokens(r);
     for (int j = 0; j < nempty; ++j)
       if ((r.q_base + j) % (int)gridDim.x == (int)blockIdx.x) zero_token(p, r.q_base + j);
   }
@@ -624,19 +625,17 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
   // a unit boundary within kSnapRows (0 and W are boundaries already).
   const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
   const int64_t xs[2] = {x0, x1 < W ? x1 : -1};
-  plan_locate2(p, [G](const Req& r) { return (int64_t)G * request_rows(r.n, r.qlen); }, xs, sh.red,
-               sh.pb, sh.pcum);
+  plan_locate2(p, [G](const Req& r) { return (int64_t)G * request_rows(r); }, xs, sh.red, sh.pb,
+               sh.pcum);
   const int b0 = uniform(sh.pb[0]), b1 = uniform(sh.pb[1]);
   if (b0 < 0 || b1 == -1) return;  // not reached with consistent indptr
   Cursor c;
-  cursor_in_request(c, b0, load_req(p.qo_indptr, p.kv_indptr, b0, p.kv_indices_len, p.num_tokens),
-                    x0 - uniform(sh.pcum[0]), G);
+  cursor_in_request(c, b0, load_req(src, b0), x0 - uniform(sh.pcum[0]), G);
   uniformize(c);
   int64_t p1 = W;
   if (x1 < W) {
     Cursor c1;
-    cursor_in_request(c1, b1, load_req(p.qo_indptr, p.kv_indptr, b1, p.kv_indices_len, p.num_tokens),
-                      x1 - uniform(sh.pcum[1]), G);
+    cursor_in_request(c1, b1, load_req(src, b1), x1 - uniform(sh.pcum[1]), G);
     uniformize(c1);
     p1 = snap_at(x1, c1);
   }
@@ -645,9 +644,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
   if (p0 < x0) {
     c.k = 0;  // moved back to the start of its unit
   } else if (p0 > x0) {  // moved forward past the end of its unit
-    if (!cursor_next_unit(c, p.qo_indptr, p.kv_indptr, p.batch, p.kv_indices_len, p.num_tokens,
-                          G))
-      return;
+    if (!cursor_next_unit(c, src, p.batch, G)) return;
     uniformize(c);
   }
   const float qs = p.q_scale ? *p.q_scale : 1.0f;
@@ -657,7 +654,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
   int64_t pos = p0;
   int piece = 0;
   while (pos < p1) {
-    const int v = visible(c.r.n, c.r.qlen, c.j);
+    const int v = req_visible(c.r, c.j);
     const int len = (int)lmin((int64_t)(v - c.k), p1 - pos);
     if (len <= 0) break;  // not reached with a consistent plan
     const bool complete = (c.k == 0 && len == v);
@@ -685,9 +682,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
     c.k += len;
     ++piece;
     if (pos < p1 && c.k == v) {
-      if (!cursor_next_unit(c, p.qo_indptr, p.kv_indptr, p.batch, p.kv_indices_len, p.num_tokens,
-                            G))
-        break;
+      if (!cursor_next_unit(c, src, p.batch, G)) break;
       uniformize(c);
     }
   }

@@ -90,10 +90,7 @@ __device__ __forceinline__ void uniformize(GCursor& c) {
   c.b = uniform(c.b);
   c.u = uniform(c.u);
   c.k = uniform(c.k);
-  c.r.kv_base = uniform(c.r.kv_base);
-  c.r.n = uniform(c.r.n);
-  c.r.q_base = uniform(c.r.q_base);
-  c.r.qlen = uniform(c.r.qlen);
+  uniformize(c.r);
 }
 
 __device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
@@ -521,9 +518,10 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
   const int G = p.num_heads / kGroup;
 
   // Pass 1 over requests: stream length W; zero this block's empty tokens.
+  const ReqSource src = source_of(p);
   int64_t acc = 0;
   for (int b = threadIdx.x; b < p.batch; b += kThreads) {
-    const Req r = load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens, p.causal);
+    const Req r = load_req(src, b);
     acc += group_request_rows(r, G);
     const int nempty = req_empty_tokens(r);
     for (int jj = 0; jj < nempty; ++jj)
@@ -537,21 +535,16 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
   const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
   const int64_t xs[2] = {x0, x1 < W ? x1 : -1};
   plan_locate2(p, [G](const Req& r) { return group_request_rows(r, G); }, xs, sh.red, sh.pb,
-               sh.pcum, p.causal);
+               sh.pcum);
   const int b0 = uniform(sh.pb[0]), b1 = uniform(sh.pb[1]);
   if (b0 < 0 || b1 == -1) return;  // not reached with consistent indptr
   GCursor c;
-  gcursor_in_request(
-      c, b0, load_req(p.qo_indptr, p.kv_indptr, b0, p.kv_indices_len, p.num_tokens, p.causal),
-      x0 - uniform(sh.pcum[0]), G);
+  gcursor_in_request(c, b0, load_req(src, b0), x0 - uniform(sh.pcum[0]), G);
   uniformize(c);
   int64_t p1 = W;
   if (x1 < W) {
     GCursor c1;
-    gcursor_in_request(c1, b1,
-                       load_req(p.qo_indptr, p.kv_indptr, b1, p.kv_indices_len, p.num_tokens,
-                                p.causal),
-                       x1 - uniform(sh.pcum[1]), G);
+    gcursor_in_request(c1, b1, load_req(src, b1), x1 - uniform(sh.pcum[1]), G);
     uniformize(c1);
     p1 = gsnap_at(x1, c1, G);
   }
@@ -560,9 +553,7 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
   if (p0 < x0) {
     c.k = 0;
   } else if (p0 > x0) {
-    if (!gcursor_next_unit(c, p.qo_indptr, p.kv_indptr, p.batch, p.kv_indices_len, p.num_tokens,
-                           G, p.causal))
-      return;
+    if (!gcursor_next_unit(c, src, p.batch, G)) return;
     uniformize(c);
   }
   const float qs = p.q_scale ? *p.q_scale : 1.0f;
@@ -583,9 +574,7 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
     c.k += len;
     ++piece;
     if (pos < p1 && c.k == L) {
-      if (!gcursor_next_unit(c, p.qo_indptr, p.kv_indptr, p.batch, p.kv_indices_len,
-                             p.num_tokens, G, p.causal))
-        break;
+      if (!gcursor_next_unit(c, src, p.batch, G)) break;
       uniformize(c);
     }
   }

@@ -69,15 +69,22 @@ __device__ __forceinline__ int64_t uniform(int64_t x) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
+__device__ __forceinline__ void uniformize(Req& r) {
+  r.kv_base = uniform(r.kv_base);
+  r.n = uniform(r.n);
+  r.q_base = uniform(r.q_base);
+  r.qlen = uniform(r.qlen);
+  r.causal = uniform(r.causal);
+  r.vbase = uniform(r.vbase);
+  r.vstep = uniform(r.vstep);
+}
+
 __device__ __forceinline__ void uniformize(Cursor& c) {
   c.b = uniform(c.b);
   c.j = uniform(c.j);
   c.g = uniform(c.g);
   c.k = uniform(c.k);
-  c.r.kv_base = uniform(c.r.kv_base);
-  c.r.n = uniform(c.r.n);
-  c.r.q_base = uniform(c.r.q_base);
-  c.r.qlen = uniform(c.r.qlen);
+  uniformize(c.r);
 }
 
 // Block-wide helpers for blocks of kT threads (red: kT/64 entries).
@@ -120,14 +127,15 @@ __device__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) 
 // first stream position.
 template <int kT = kThreads, class RowsOf>
 __device__ void plan_locate2(const DecodeParams& p, RowsOf rows_of, const int64_t (&x)[2],
-                             int64_t* red, int* sb, int64_t* scum, int causal = 1) {
+                             int64_t* red, int* sb, int64_t* scum) {
   if (threadIdx.x < 2) sb[threadIdx.x] = x[threadIdx.x] < 0 ? -2 : -1;
+  const ReqSource src = source_of(p);
   int64_t carry = 0;
   for (int b0 = 0; b0 < p.batch; b0 += kT) {
     const int b = b0 + threadIdx.x;
     int64_t R = 0;
     if (b < p.batch) {
-      R = rows_of(load_req(p.qo_indptr, p.kv_indptr, b, p.kv_indices_len, p.num_tokens, causal));
+      R = rows_of(load_req(src, b));
     }
     int64_t total;
     const int64_t cum = carry + block_excl_scan_i64<kT>(R, red, total);

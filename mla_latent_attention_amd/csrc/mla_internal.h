@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "mla_plan.h"
+
 namespace mla {
 
 struct DecodeParams {
@@ -28,9 +30,26 @@ struct DecodeParams {
   float* part_lse;          // workspace: (slots*num_workers, 16) fp32
   int4* desc;               // workspace: (tokens * head groups) split-unit descriptors
   int num_workers;
-  int causal;               // 1: bottom-right causal; 0 (group mode only): every token of a
-                            // request sees all of its entries
+  int causal;               // 1: bottom-right causal; 0: every token of a request sees all
+                            // of its entries
+  const int32_t* g_kv_indptr = nullptr;  // (B+1) full-list offsets under DCP, or nullptr
+  int cp_size = 1;                        // DCP shards (1 without DCP)
+  int cp_rank = 0;                        // this shard
 };
+
+// The planner's view of the call's requests.
+__host__ __device__ inline ReqSource source_of(const DecodeParams& p) {
+  ReqSource s;
+  s.qo = p.qo_indptr;
+  s.kvp = p.kv_indptr;
+  s.gkvp = p.g_kv_indptr;
+  s.kv_cap = p.kv_indices_len;
+  s.T = p.num_tokens;
+  s.causal = p.causal;
+  s.cp_size = p.cp_size;
+  s.cp_rank = p.cp_rank;
+  return s;
+}
 
 // Partial-answer slots per worker: a worker holds at most two partial pieces,
 // each covering one row group, or kGroupsPerUnit (8) row groups in group mode.

@@ -49,16 +49,6 @@ MLA_HD int imin(int a, int b) { return a < b ? a : b; }
 MLA_HD int imax(int a, int b) { return a > b ? a : b; }
 MLA_HD int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
 
-// Entries visible to query token j of a request with qlen tokens and n entries.
-MLA_HD int visible(int n, int qlen, int j) { return imax(0, n - (qlen - 1 - j)); }
-
-// Sum over the request's query tokens of their visible entries.
-MLA_HD int64_t request_rows(int n, int qlen) {
-  int m = imin(qlen, n);
-  if (m <= 0) return 0;
-  return (int64_t)m * n - (int64_t)m * (m - 1) / 2;
-}
-
 MLA_HD int effective_workers(int64_t W, int nw) {
   int64_t need = W / kMinWorkerRows;  // rounded down: every worker gets >= kMinWorkerRows
   if (need < 1) need = 1;
@@ -79,40 +69,89 @@ MLA_HD int64_t snap_position(int64_t x, int k, int v) {
   return x;
 }
 
-// One request's bounds, clamped so that no later read can leave its buffer.
-struct Req {
-  int kv_base;  // offset of its first entry in kv_indices
-  int n;        // KV length
-  int q_base;   // its first query token
-  int qlen;     // query tokens
-  int causal;   // 1: token j sees visible(n, qlen, j) entries; 0: every token sees all n
+// Where the requests' tokens and entries are, and which entries each token
+// sees.  A null qo (kvp) stands for the single range [0, T) ([0, kv_cap)): one
+// request holding every token (entry).
+//
+// Causal draft tokens see a prefix of their request's entry list: token j of
+// qlen sees the entries at global positions <= N - qlen + j, N being the
+// request's total entry count.  Without context parallelism (gkvp null) the
+// list holds every position in order, so token j sees n - (qlen - 1 - j) of
+// its n entries.  Under DCP the positions are dealt round-robin over cp_size
+// shards: this shard (cp_rank) holds positions cp_rank + i * cp_size, i = 0..,
+// gkvp gives N per request, and token j sees the local entries i with
+// cp_rank + i * cp_size <= N - qlen + j ("Kimi K3 on AMD Instinct MI355X ...",
+// Sec. 1: each GPU keeps an eighth of the positions; multi-token verification
+// under DCP).
+struct ReqSource {
+  const int32_t* qo;    // (B+1) query-token offsets, or null
+  const int32_t* kvp;   // (B+1) local entry offsets, or null
+  const int32_t* gkvp;  // (B+1) offsets of the requests' full (all-shard) lists, or null
+  int kv_cap;           // entries in kv_indices
+  int T;                // query tokens
+  int causal;           // 0: every token sees all of its request's local entries
+  int cp_size;          // shards the positions are dealt over (1 without DCP)
+  int cp_rank;          // this shard
 };
 
-// Request b's bounds.  A null qo (kvp) stands for the single range [0, T)
-// ([0, kv_cap)): one request holding every token (entry).
-MLA_HD Req load_req(const int32_t* qo, const int32_t* kvp, int b, int kv_cap, int T,
-                    int causal = 1) {
-  int k0 = kvp ? kvp[b] : 0, k1 = kvp ? kvp[b + 1] : kv_cap;
-  int q0 = qo ? qo[b] : 0, q1 = qo ? qo[b + 1] : T;
-  k0 = imin(imax(k0, 0), kv_cap);
-  k1 = imin(imax(k1, k0), kv_cap);
-  q0 = imin(imax(q0, 0), T);
-  q1 = imin(imax(q1, q0), T);
+// One request's bounds, clamped so that no later read can leave its buffer,
+// and its visibility rule: token j sees min(n, (vbase + j) / vstep + 1)
+// entries when vbase + j >= 0, none otherwise.
+struct Req {
+  int kv_base;  // offset of its first entry in kv_indices
+  int n;        // local entry count
+  int q_base;   // its first query token
+  int qlen;     // query tokens
+  int causal;   // 0: every token sees all n
+  int vbase;    // N - qlen - cp_rank
+  int vstep;    // cp_size
+};
+
+MLA_HD Req load_req(const ReqSource& s, int b) {
+  int k0 = s.kvp ? s.kvp[b] : 0, k1 = s.kvp ? s.kvp[b + 1] : s.kv_cap;
+  int q0 = s.qo ? s.qo[b] : 0, q1 = s.qo ? s.qo[b + 1] : s.T;
+  k0 = imin(imax(k0, 0), s.kv_cap);
+  k1 = imin(imax(k1, k0), s.kv_cap);
+  q0 = imin(imax(q0, 0), s.T);
+  q1 = imin(imax(q1, q0), s.T);
   Req r;
   r.kv_base = k0;
   r.n = k1 - k0;
   r.q_base = q0;
   r.qlen = q1 - q0;
-  r.causal = causal;
+  r.causal = s.causal;
+  if (s.gkvp) {
+    const int N = imax(s.gkvp[b + 1] - s.gkvp[b], 0);
+    r.vbase = N - r.qlen - s.cp_rank;
+    r.vstep = imax(s.cp_size, 1);
+  } else {
+    r.vbase = r.n - r.qlen;
+    r.vstep = 1;
+  }
   return r;
 }
 
-// Entries visible to token j of request r.
-MLA_HD int req_visible(const Req& r, int j) { return r.causal ? visible(r.n, r.qlen, j) : r.n; }
+// Entries visible to token j of request r (never decreasing in j).
+MLA_HD int req_visible(const Req& r, int j) {
+  if (!r.causal) return r.n;
+  const int x = r.vbase + j;
+  return x < 0 ? 0 : imin(r.n, x / r.vstep + 1);
+}
 
-// Tokens of r that see no entry.
-MLA_HD int req_empty_tokens(const Req& r) {
-  return r.causal ? imin(r.qlen, imax(0, r.qlen - r.n)) : (r.n == 0 ? r.qlen : 0);
+// First token of r with a non-empty visible set (qlen if none): the number of
+// tokens of r that see nothing.
+MLA_HD int first_visible_token(const Req& r) {
+  if (r.n == 0) return r.qlen;
+  return r.causal ? imin(r.qlen, imax(0, -r.vbase)) : 0;
+}
+
+MLA_HD int req_empty_tokens(const Req& r) { return first_visible_token(r); }
+
+// Sum over the request's query tokens of their visible entries.
+MLA_HD int64_t request_rows(const Req& r) {
+  int64_t s = 0;
+  for (int j = first_visible_token(r); j < r.qlen; ++j) s += req_visible(r, j);
+  return s;
 }
 
 // Position in the unit stream: request b, its token j, head group g, offset k.
@@ -121,15 +160,12 @@ struct Cursor {
   Req r;
 };
 
-// First token of r with a non-empty visible set.
-MLA_HD int first_visible_token(const Req& r) { return imax(0, r.qlen - r.n); }
-
 // Place the cursor at offset `off` (< G * request_rows) inside request b.
 MLA_HD void cursor_in_request(Cursor& c, int b, const Req& r, int64_t off, int G) {
   c.b = b;
   c.r = r;
   for (int j = first_visible_token(r); j < r.qlen; ++j) {
-    int v = visible(r.n, r.qlen, j);
+    const int v = req_visible(r, j);
     int64_t rows = (int64_t)G * v;
     if (off < rows) {
       c.j = j;
@@ -146,20 +182,19 @@ MLA_HD void cursor_in_request(Cursor& c, int b, const Req& r, int64_t off, int G
 
 // Snap stream position x whose cursor is c (set by cursor_in_request).
 MLA_HD int64_t snap_at(int64_t x, const Cursor& c) {
-  return snap_position(x, c.k, visible(c.r.n, c.r.qlen, c.j));
+  return snap_position(x, c.k, req_visible(c.r, c.j));
 }
 
 // Move to the start of the next non-empty unit.  Returns false past the end.
-MLA_HD bool cursor_next_unit(Cursor& c, const int32_t* qo, const int32_t* kvp, int B, int kv_cap,
-                             int T, int G) {
+MLA_HD bool cursor_next_unit(Cursor& c, const ReqSource& src, int B, int G) {
   c.k = 0;
   if (++c.g < G) return true;
   c.g = 0;
   ++c.j;
-  if (c.j < c.r.qlen) return true;  // visible counts only grow with j
+  if (c.j < c.r.qlen) return true;  // visible counts never decrease with j
   for (int b = c.b + 1; b < B; ++b) {
-    Req r = load_req(qo, kvp, b, kv_cap, T);
-    if (request_rows(r.n, r.qlen) > 0) {
+    const Req r = load_req(src, b);
+    if (request_rows(r) > 0) {
       c.b = b;
       c.r = r;
       c.j = first_visible_token(r);
@@ -227,12 +262,11 @@ MLA_HD void gcursor_in_request(GCursor& c, int b, const Req& r, int64_t off, int
 
 // Move to the start of the next non-empty unit (unit lengths never shrink
 // within a request).  Returns false past the end.
-MLA_HD bool gcursor_next_unit(GCursor& c, const int32_t* qo, const int32_t* kvp, int B, int kv_cap,
-                              int T, int G, int causal) {
+MLA_HD bool gcursor_next_unit(GCursor& c, const ReqSource& src, int B, int G) {
   c.k = 0;
   if (++c.u < group_units(c.r, G)) return true;
   for (int b = c.b + 1; b < B; ++b) {
-    Req r = load_req(qo, kvp, b, kv_cap, T, causal);
+    const Req r = load_req(src, b);
     if (group_request_rows(r, G) > 0) {
       c.b = b;
       c.r = r;

@@ -47,6 +47,12 @@ def workload_args(w, requests=None) -> dict:
     lens = np.array([e - a for a, e in kv_lists], dtype=np.int64)
     qlens = np.array([qo[b + 1] - qo[b] for b in reqs], dtype=np.int64)
     tok_t = torch.tensor(toks, dtype=torch.int64, device=w.q.device)
+    dcp = {}
+    if getattr(w, "g_kv_indptr", None) is not None:
+        g = w.g_kv_indptr.cpu().numpy().astype(np.int64)
+        glens = np.array([g[b + 1] - g[b] for b in reqs], dtype=np.int64)
+        dcp = dict(g_kv_indptr=np.concatenate([[0], np.cumsum(glens)]), cp_size=int(w.cp_size),
+                   cp_rank=int(w.cp_rank))
     return dict(
         q=codes(w.q.index_select(0, tok_t)) if toks else codes(w.q[:0]),
         kv_pool=codes(pool_rows),
@@ -58,6 +64,7 @@ def workload_args(w, requests=None) -> dict:
         kv_scale=float(w.kv_scale.item()),
         dtype=w.dtype,
         tokens=np.array(toks, dtype=np.int64),
+        **dcp,
     )
 
 

@@ -32,6 +32,12 @@ Readings taken where the pages are silent (each is listed in the design notes):
 5. A query row that sees no entry gets o = 0 and lse = -inf; a shard with
    lse = -inf has weight 0 in the merge, and an all -inf merge gives o = 0,
    lse = -inf.
+6. Under decode context parallelism ([Blog] Sec. 1: each of the GPUs keeps an
+   eighth of the cached positions; multi-token verification under DCP; the
+   entry point's g_kv_indptr / cp_world_size / cp_rank arguments, [Issue]
+   Sec. 3) a request's positions are dealt round-robin: shard r of W holds
+   full-list positions r, r + W, r + 2W, ... in that order, and reading 4
+   applies to full-list positions (``dcp_visible_length``).
 """
 
 from __future__ import annotations
@@ -55,6 +61,20 @@ def visible_length(n: int, qlen: int, j: int) -> int:
     return max(0, n - (qlen - 1 - j))
 
 
+def dcp_visible_length(n_full: int, n_local: int, qlen: int, j: int, cp_size: int,
+                      cp_rank: int) -> int:
+    """Entries of one DCP shard's list visible to query token ``j`` of ``qlen``.
+
+    Reading 6: local entry i is position cp_rank + i * cp_size of the request's
+    full list of ``n_full`` positions, and token j sees the full-list positions
+    0 .. n_full - qlen + j (reading 4).  The visible entries are a prefix of
+    the local list because positions grow with i.
+    """
+    last = n_full - qlen + j
+    positions = cp_rank + cp_size * np.arange(n_local, dtype=np.int64)
+    return int(np.count_nonzero(positions <= last))
+
+
 def mla_decode(
     q: np.ndarray,
     kv_pool: np.ndarray,
@@ -65,6 +85,9 @@ def mla_decode(
     q_scale: float = 1.0,
     kv_scale: float = 1.0,
     dtype: str = "fp8",
+    g_kv_indptr: np.ndarray | None = None,
+    cp_size: int = 1,
+    cp_rank: int = 0,
 ) -> tuple[np.ndarray, np.ndarray]:
     """Reference MLA decode.
 
@@ -76,6 +99,9 @@ def mla_decode(
       kv_indices: pool entry of every cached token, request by request.
       sm_scale, q_scale, kv_scale: the scalars exactly as the device sees them.
       dtype:      'fp8' or 'bf16' storage type of q and kv_pool.
+      g_kv_indptr, cp_size, cp_rank: one DCP shard (reading 6): kv_indptr /
+                  kv_indices are the shard's lists and g_kv_indptr's deltas the
+                  full lists' lengths.  None: no DCP.
 
     Returns (o, lse): o (T, H, 512) float64 and lse (T, H) float64.
     """
@@ -107,7 +133,11 @@ def mla_decode(
         V = K[:, :LATENT_DIM]  # (n, 512)
         for j in range(qlen):
             t = t0 + j
-            vis = visible_length(n, qlen, j)
+            if g_kv_indptr is None:
+                vis = visible_length(n, qlen, j)
+            else:
+                n_full = int(g_kv_indptr[b + 1] - g_kv_indptr[b])
+                vis = dcp_visible_length(n_full, n, qlen, j, cp_size, cp_rank)
             if vis == 0:
                 continue  # reading 5: o = 0, lse = -inf
             Q = q_scale * codecs.decode(q[t], dtype)  # (H, 576)

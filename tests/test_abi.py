@@ -102,3 +102,31 @@ def test_decode_rejects_bad_arguments_before_any_launch(over, status):
 )
 def test_merge_rejects_bad_arguments(args, status):
     assert _lib.lib().mla_merge_partials(*args) == status
+
+
+def _decode_dcp(**over):
+    args = dict(
+        q=FAKE, q_dtype=0, kv=FAKE, kv_dtype=0, pool=256, o=FAKE, qo=FAKE, kvp=FAKE, idx=FAKE,
+        idx_len=164, lpl=None, batch=2, T=2, H=16, qmax=1, sm=0.072, qs=None, ks=None, rl=0,
+        lse=None, gkv=FAKE, cps=8, cpr=3, ws=FAKE, ws_len=1 << 30, stream=None,
+    )
+    args.update(over)
+    return _lib.lib().mla_decode_dcp(*args.values())
+
+
+@pytest.mark.parametrize(
+    "over,status",
+    [
+        (dict(gkv=None), 1),
+        (dict(cps=0), 2),
+        (dict(cps=1025), 2),
+        (dict(cpr=8), 2),
+        (dict(cpr=-1), 2),
+        (dict(q=None), 1),
+        (dict(H=24), 4),
+        (dict(qmax=65), 2),
+        (dict(ws=None), 5),
+    ],
+)
+def test_decode_dcp_rejects_bad_arguments_before_any_launch(over, status):
+    assert _decode_dcp(**over) == status

@@ -33,12 +33,18 @@ def say(*a):
 
 
 def run(w, num_workers=0, return_lse=True, q=None):
+    """decode() on w's inputs, or decode_dcp() when w is one DCP shard."""
     torch.cuda.synchronize()
-    out = mla.decode(
-        w.q if q is None else q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
-        w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale, return_lse=return_lse,
-        max_seqlen_q=w.max_seqlen_q, num_workers=num_workers,
-    )
+    args = (w.q if q is None else q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
+            w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale)
+    if w.g_kv_indptr is not None:
+        assert num_workers == 0
+        out = mla.decode_dcp(*args, return_lse=return_lse, g_kv_indptr=w.g_kv_indptr,
+                             cp_world_size=w.cp_size, cp_rank=w.cp_rank,
+                             max_seqlen_q=w.max_seqlen_q)
+    else:
+        out = mla.decode(*args, return_lse=return_lse, max_seqlen_q=w.max_seqlen_q,
+                         num_workers=num_workers)
     torch.cuda.synchronize()
     return out
 
@@ -479,6 +485,52 @@ def test_dcp_shards_plus_merge_equal_the_full_call():
     assert_gate(metrics(o_full, o_ref, lse_full, lse_ref), "dcp full vs oracle")
 
 
+# ------------------------------------------------------------------ DCP shards
+# Positions dealt round-robin over the shards (mla_decode_dcp): every shard
+# against the oracle's shard rule, and the merged shards against the full call.
+
+DCP_CASES = {
+    "fp8-16heads-standard": dict(num_heads=16, real_heads=12, qlens=[1, 3, 2, 3, 1, 3, 2],
+                                 dtype="fp8"),
+    "fp8-96heads-group": dict(num_heads=96, real_heads=96, qlens=[4, 1, 3, 4, 2, 4, 4],
+                              dtype="fp8"),
+    "bf16-16heads": dict(num_heads=16, real_heads=12, qlens=[4, 1, 3, 4, 2, 4, 4], dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DCP_CASES))
+def test_dcp_interleaved_shards_and_merge(case):
+    kw = DCP_CASES[case]
+    full = workloads.build(f"dcp-{case}", [0, 3, 9, 700, 2501, 4096, 5003], pool_entries=1 << 14,
+                           kv_std=0.5, scale_range=(0.5, 2.0), seed=71, device=DEV, **kw)
+    W = 8
+    parts_o, parts_l = [], []
+    for r in range(W):
+        shard = workloads.dcp_shard(full, W, r)
+        o, lse, _ = check(shard, where=f"dcp {case} rank {r}")
+        parts_o.append(o)
+        parts_l.append(lse)
+    o_m, lse_m = mla.merge_partials(torch.stack(parts_o), torch.stack(parts_l))
+    toks, o_ref, lse_ref = oracle(full)
+    m = metrics(o_m, o_ref, lse_m, lse_ref)
+    say(f"[dcp] {case} merged: {m}")
+    # The merged answer carries two bf16 roundings (each shard's o, then the
+    # merge's), and the 3- and 9-position requests leave shards of one or two
+    # entries, so |o| reaches ~2.5, where one bf16 ulp (2^-6) exceeds 1e-2:
+    # the absolute bound is one ulp at the largest |o| (row-normwise and lse
+    # bounds unchanged).
+    assert_gate(m, f"dcp {case}: 8 shards merged vs the full call",
+                abs_tol=bf16_abs_tol(m["ref_absmax"]))
+
+
+def test_dcp_bad_arguments_are_rejected():
+    w = workloads.dcp_shard(workloads.tiny(DEV), 2, 1)
+    for cps, cpr in ((2, 2), (0, 0), (2, -1)):
+        with pytest.raises(mla.MLAError):
+            mla.decode_dcp(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices, None,
+                           w.sm_scale, g_kv_indptr=w.g_kv_indptr, cp_world_size=cps, cp_rank=cpr)
+
+
 # ------------------------------------------------------------------ merge
 
 
@@ -550,6 +602,7 @@ def test_mixed_lengths_bf16_sampled():
 
 
 def test_dcp_share_sampled():
+    """One DCP8 rank at full size (rank 7 of 142,000 positions per request)."""
     w = workloads.dcp_share(DEV)
     check(w, requests=[0, 5])
 

@@ -22,20 +22,29 @@ def visible(n, qlen, j):
     return max(0, n - (qlen - 1 - j))
 
 
-def units(qo, kv, G):
+def dcp_rule(gkv, cps, cpr):
+    """Visible count on a DCP shard, by enumeration: local entry i is full-list
+    position cpr + i * cps; token j of qlen sees positions <= N - qlen + j."""
+    def vis(b, n, qlen, j):
+        N = gkv[b + 1] - gkv[b]
+        return sum(1 for i in range(n) if cpr + i * cps <= N - qlen + j)
+    return vis
+
+
+def units(qo, kv, G, rule=None):
     """(token, group, length, stream start) in stream order, skipping nothing."""
     out, pos = [], 0
     for b in range(len(qo) - 1):
         n, ql = kv[b + 1] - kv[b], qo[b + 1] - qo[b]
         for j in range(ql):
-            v = visible(n, ql, j)
+            v = visible(n, ql, j) if rule is None else rule(b, n, ql, j)
             for g in range(G):
                 out.append((qo[b] + j, g, v, pos))
                 pos += v
     return out, pos
 
 
-def group_units(qo, kv, G, causal=True):
+def group_units(qo, kv, G, causal=True, rule=None):
     """Group mode: (request, unit, length, stream start) in stream order.  Unit u
     of a request covers row groups 8u..8u+7 (row group = token * G + head
     group) and is as long as its last row group sees."""
@@ -46,7 +55,12 @@ def group_units(qo, kv, G, causal=True):
         R = ql * G
         for u in range(-(-R // U)):
             last = min(U * u + U - 1, R - 1)
-            v = visible(n, ql, last // G) if causal else n
+            if not causal:
+                v = n
+            elif rule is None:
+                v = visible(n, ql, last // G)
+            else:
+                v = rule(b, n, ql, last // G)
             out.append((b, u, v, pos))
             pos += v
     return out, pos
@@ -74,10 +88,13 @@ def snapped_bounds(us, W, nw):
     return bounds
 
 
-def check_plan(qo, kv, H, nw_req):
+def check_plan(qo, kv, H, nw_req, dcp=None):
+    """dcp = (g_kv_indptr, cp_world_size, cp_rank) for a DCP shard's call."""
     G = H // 16
-    us, W = units(qo, kv, G)
-    pieces = plan_host(qo, kv, H, nw_req)
+    rule = None if dcp is None else dcp_rule(*dcp)
+    us, W = units(qo, kv, G, rule)
+    kw = {} if dcp is None else dict(g_kv_indptr=dcp[0], cp_world_size=dcp[1], cp_rank=dcp[2])
+    pieces = plan_host(qo, kv, H, nw_req, **kw)
     if W == 0:
         assert len(pieces) == 0
         return pieces
@@ -185,10 +202,12 @@ def test_rejects_bad_planner_input():
 # ---------------------------------------------------------------- group mode
 
 
-def check_group_plan(qo, kv, H, nw_req, causal=True):
+def check_group_plan(qo, kv, H, nw_req, causal=True, dcp=None):
     G = H // 16
-    us, W = group_units(qo, kv, G, causal)
-    pieces = plan_groups_host(qo, kv, H, nw_req, causal)
+    rule = None if dcp is None else dcp_rule(*dcp)
+    us, W = group_units(qo, kv, G, causal, rule)
+    kw = {} if dcp is None else dict(g_kv_indptr=dcp[0], cp_world_size=dcp[1], cp_rank=dcp[2])
+    pieces = plan_groups_host(qo, kv, H, nw_req, causal, **kw)
     if W == 0:
         assert len(pieces) == 0
         return pieces
@@ -284,3 +303,47 @@ def test_group_plan_without_causal_mask():
     check_group_plan(indptr([3]), indptr([0]), 32, 8, causal=False)
     us, _ = group_units(indptr([4]), indptr([100]), 1, causal=False)
     assert [(u, v) for _, u, v, _ in us] == [(0, 100)]
+
+
+# ---------------------------------------------------------------- DCP shards
+
+
+def shard_lengths(full, cps, cpr):
+    return [max(0, -(-(N - cpr) // cps)) for N in full]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_dcp_shard_plans(seed):
+    """Positions dealt round-robin over cps shards; the planner's unit lengths
+    follow the shard's visibility rule (standard and group mode)."""
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 20))
+    full = rng.integers(0, 4000, size=B)
+    full[rng.random(B) < 0.2] = int(rng.integers(0, 9))
+    qlens = rng.integers(1, 5, size=B)
+    cps = int(rng.integers(1, 9))
+    cpr = int(rng.integers(0, cps))
+    kv = indptr(shard_lengths(full, cps, cpr))
+    dcp = (indptr(full), cps, cpr)
+    check_plan(indptr(qlens), kv, 16, int(rng.integers(1, 300)), dcp=dcp)
+    check_group_plan(indptr(qlens), kv, 16 * int(rng.integers(1, 7)), int(rng.integers(1, 300)),
+                     dcp=dcp)
+
+
+def test_group_plan_dcp_share_interleaved():
+    """The benchmark's DCP share: 142,000 positions per request dealt over 8
+    shards, rank 7 (17,750 each).  Row groups 0-7 end in token 1, 8-15 in token
+    2, 16-23 in token 3, which see positions up to 141,997, 141,998, 141,999."""
+    full = [142_000] * 8
+    kv = indptr(shard_lengths(full, 8, 7))
+    pieces = check_group_plan(indptr([4] * 8), kv, 96, 256, dcp=(indptr(full), 8, 7))
+    assert sorted(set(pieces[:, 5].tolist())) == [17_749, 17_750]
+    pieces = check_group_plan(indptr([4] * 8), indptr(shard_lengths(full, 8, 0)), 96, 256,
+                              dcp=(indptr(full), 8, 0))
+    assert sorted(set(pieces[:, 5].tolist())) == [17_750]
+
+
+def test_dcp_rejects_bad_rank():
+    with pytest.raises(ValueError):
+        plan_host(indptr([1]), indptr([10]), 16, 4, g_kv_indptr=indptr([80]), cp_world_size=8,
+                  cp_rank=8)

@@ -61,6 +61,11 @@ class Workload:
     lengths: list[int]
     qlens: list[int]
     recipe: dict = field(default_factory=dict)
+    # One DCP shard of a larger call (dcp_shard): offsets of the full lists,
+    # the number of shards the positions are dealt over, and this shard.
+    g_kv_indptr: torch.Tensor | None = None
+    cp_size: int = 1
+    cp_rank: int = 0
 
     @property
     def batch(self) -> int:
@@ -288,13 +293,49 @@ def mixed(device="cpu", dtype: str = "fp8", return_lse: bool = False) -> Workloa
 DCP_LOCAL = 142_000 // 8  # 17,750 positions per request on one DCP8 rank
 
 
-def dcp_share(device="cpu") -> Workload:
-    """One DCP8 rank: batch 8, 96 heads, 4 query tokens (causal), kv 17,750."""
-    return build(
-        "dcp-share", [DCP_LOCAL] * 8, num_heads=96, real_heads=96, qlens=[4] * 8,
+def dcp_shard(w: Workload, cp_size: int, cp_rank: int) -> Workload:
+    """Shard `cp_rank` of call `w` under DCP with positions dealt round-robin over
+    `cp_size` shards: the shard's list for request b holds positions cp_rank,
+    cp_rank + cp_size, ... of b's list in `w`.  Everything else (q, pool,
+    scales) is shared.  The result carries g_kv_indptr = w.kv_indptr."""
+    kvp = w.kv_indptr.cpu().tolist()
+    parts = [w.kv_indices[kvp[b] + cp_rank: kvp[b + 1]: cp_size] for b in range(w.batch)]
+    lens = [int(t.numel()) for t in parts]
+    dev = w.kv_indices.device
+    kv_indptr = torch.zeros(w.batch + 1, dtype=torch.int32)
+    kv_indptr[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    idx = torch.cat(parts) if sum(lens) else torch.zeros(1, dtype=torch.int32, device=dev)
+    return Workload(**{
+        **w.__dict__,
+        "name": f"{w.name}-cp{cp_rank}of{cp_size}",
+        "kv_indptr": kv_indptr.to(dev),
+        "kv_indices": idx.contiguous(),
+        "lengths": lens,
+        "recipe": {**w.recipe, "cp_size": cp_size, "cp_rank": cp_rank},
+        "g_kv_indptr": w.kv_indptr,
+        "cp_size": cp_size,
+        "cp_rank": cp_rank,
+    })
+
+
+DCP_FULL = 142_000  # [Blog] Sec. 1: a 142,000-token conversation
+DCP_SIZE = 8
+
+
+def dcp_share(device="cpu", cp_rank: int = DCP_SIZE - 1) -> Workload:
+    """One DCP8 rank's share: batch 8, 96 heads (12 per GPU x 8 after the query
+    exchange), 4 draft tokens (causal over full-list positions), each request's
+    142,000 positions dealt round-robin over 8 shards (17,750 here).  Rank 7
+    holds the last position of every request, so its draft tokens mask
+    entries."""
+    full = build(
+        "dcp-full", [DCP_FULL] * 8, num_heads=96, real_heads=96, qlens=[4] * 8,
         pool_entries=POOL_ENTRIES, dtype="fp8", kv_std=0.5, q_std=1.0,
         scale_range=(0.5, 2.0), return_lse=True, seed=5000, device=device,
     )
+    w = dcp_shard(full, DCP_SIZE, cp_rank)
+    w.name = "dcp-share"
+    return w
 
 
 def merge_shards(

@@ -35,9 +35,22 @@ def decode_bytes(lengths, qlens, num_heads, dtype="fp8", return_lse=False) -> in
     return kv + q + o + lse
 
 
-def decode_flops(lengths, qlens, num_heads) -> int:
-    """2 * heads * sum over query tokens of visible entries * (576 + 512)."""
-    vis = sum(visible(n, ql, j) for n, ql in zip(lengths, qlens) for j in range(ql))
+def shard_visible(n: int, full: int, qlen: int, j: int, cp_size: int, cp_rank: int) -> int:
+    """Visible entries of draft token j on a DCP shard whose i-th entry is
+    full-list position cp_rank + i * cp_size (token j sees positions <= full - qlen + j)."""
+    last = full - qlen + j
+    return 0 if last < cp_rank else min(n, (last - cp_rank) // cp_size + 1)
+
+
+def decode_flops(lengths, qlens, num_heads, shard=None) -> int:
+    """2 * heads * sum over query tokens of visible entries * (576 + 512).
+    shard = (full_lengths, cp_size, cp_rank) for one DCP shard's call."""
+    if shard is None:
+        vis = sum(visible(n, ql, j) for n, ql in zip(lengths, qlens) for j in range(ql))
+    else:
+        full, cs, cr = shard
+        vis = sum(shard_visible(n, N, ql, j, cs, cr)
+                  for n, N, ql in zip(lengths, full, qlens) for j in range(ql))
     return 2 * num_heads * vis * (ROW_DIM + LATENT_DIM)
 
 
@@ -51,7 +64,11 @@ def workload_bytes(w) -> int:
 
 
 def workload_flops(w) -> int:
-    return decode_flops(w.lengths, w.qlens, w.num_heads)
+    shard = None
+    if getattr(w, "g_kv_indptr", None) is not None:
+        g = [int(x) for x in w.g_kv_indptr.cpu().tolist()]
+        shard = ([g[b + 1] - g[b] for b in range(len(g) - 1)], w.cp_size, w.cp_rank)
+    return decode_flops(w.lengths, w.qlens, w.num_heads, shard)
 
 
 def cascade_bytes(w, prefix: int) -> int:
