@@ -99,6 +99,19 @@ def with_indices(layers, variant, dev):
     return [workloads.Workload(**{**w.__dict__, "kv_indices": idx}) for w in layers]
 
 
+def with_pages(layers, page_size, dev):
+    """The same layers as a paged call: a page table of page_size-slot pages
+    (the prefix's whole pages shared, the rest of each request in its own)."""
+    import workloads
+
+    kvp, idx, last = workloads.make_paged_indices(layers[0].lengths, page_size,
+                                                  workloads.SHARED_PREFIX,
+                                                  layers[0].kv_pool.shape[0], 2000 + 3, dev)
+    return [workloads.Workload(**{**w.__dict__, "kv_indptr": kvp, "kv_indices": idx,
+                                  "kv_last_page_lens": last, "page_size": page_size})
+            for w in layers]
+
+
 def extra_layers(base, n_layers, kv_std, seed0, dev):
     """base plus n_layers - 1 copies with separate pools and q (same indices)."""
     import torch
@@ -216,6 +229,11 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
 
 def make_calls(mla, layers, o, ws):
     def call_for(w):
+        if w.page_size > 1:
+            return lambda: mla.decode_paged(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                            w.kv_last_page_lens, w.sm_scale, w.q_scale,
+                                            w.kv_scale, page_size=w.page_size, o=o,
+                                            max_seqlen_q=1, workspace=ws)
         return lambda: mla.decode(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
                                   w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale,
                                   o=o, max_seqlen_q=1, workspace=ws)
@@ -422,6 +440,16 @@ def main():
             variants[f"{var}_prefix"] = {"us_per_call": round(wv * 1e6, 2),
                                          "GB_s": round(nbytes / wv / 1e9, 2),
                                          "pct_of_8TBs": round(100 * nbytes / wv / 1e9 / PEAK_GBS, 2)}
+        # The same call through mla_decode_paged with 128-slot pages (one index
+        # per page instead of one per entry).
+        paged = with_pages(layers, 128, dev)
+        pbytes = accounting.workload_bytes(paged[0])
+        wp, evp, _ = timer(make_calls(mla, paged, o, ws), max(16, a.steps // 4), a.warmup)
+        variants["paged128"] = {"us_per_call": round(wp * 1e6, 2),
+                                "algorithmic_bytes_per_call": pbytes,
+                                "GB_s": round(pbytes / wp / 1e9, 2),
+                                "pct_of_8TBs": round(100 * pbytes / wp / 1e9 / PEAK_GBS, 2)}
+        del paged
         out["variants"] = variants
     if not a.no_configs:
         del calls, layers

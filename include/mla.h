@@ -150,6 +150,40 @@ size_t mla_decode_workspace_bytes_ex(int batch, int num_q_tokens, int num_heads,
                                      int max_seqlen_q, int num_workers);
 
 /*
+ * mla_decode over a paged cache with pages of page_size entries ("[Kimi-K3
+ * MLA TP8] MLA performance", Sec. 3: the entry point's page_size and
+ * kv_last_page_lens arguments; Sec. 5.2: the captured call runs with
+ * page_size 1, and the allocator hands out blocks of 128 slots).
+ *
+ * Arguments as for mla_decode, except:
+ *  kv_pool        (pool_entries, 576) rows, i.e. (pool_entries / page_size)
+ *                 pages of page_size consecutive rows; page k holds rows
+ *                 [k * page_size, (k + 1) * page_size).
+ *  kv_indptr      (batch+1) int32 offsets into kv_indices, in pages.
+ *  kv_indices     (kv_indices_len) int32 page numbers, request by request.
+ *  kv_last_page_lens (batch) int32 device array: slots used in each request's
+ *                 last page, 1..page_size.
+ *  page_size      a power of two, 1..4096; for 1 the call is mla_decode and
+ *                 kv_last_page_lens is not read.
+ * Request b holds (pages_b - 1) * page_size + kv_last_page_lens[b] entries
+ * (none if it has no pages); entry i is pool row
+ * kv_indices[kv_indptr[b] + i / page_size] * page_size + i % page_size.  A
+ * last-page length outside 1..page_size is clamped to it.  For
+ * page_size > 1, pool_entries must be a multiple of page_size and at most
+ * 2^31 - 1 (MLA_ERR_BAD_SHAPE), and kv_last_page_lens must not be NULL
+ * (MLA_ERR_NULL_POINTER).  Same workspace, types, shapes and masking as
+ * mla_decode.
+ */
+mla_status mla_decode_paged(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                            int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                            const int32_t* kv_indptr, const int32_t* kv_indices,
+                            int64_t kv_indices_len, const int32_t* kv_last_page_lens,
+                            int page_size, int batch, int num_q_tokens, int num_heads,
+                            int max_seqlen_q, float sm_scale, const float* q_scale,
+                            const float* kv_scale, int return_lse, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * One shard of decode context parallelism (DCP): "Kimi K3 on AMD Instinct
  * MI355X ...", Sec. "1. Cache: keep conversation state available for reuse"
  * (each of the GPUs keeps one eighth of the cached positions, runs the

@@ -24,6 +24,7 @@ __all__ = [
     "plan_groups_host",
     "decode_cascade",
     "decode_dcp",
+    "decode_paged",
     "cascade_workspace_bytes",
     "new_workspace",
     "MLAError",
@@ -104,6 +105,7 @@ def decode(
     workspace: torch.Tensor | None = None,
     num_workers: int = 0,
     _dcp=None,
+    _page_size: int = 1,
 ):
     """Latent MLA decode; returns o (T, H, 512) bf16, or (o, lse) if return_lse.
 
@@ -119,9 +121,9 @@ def decode(
         raise ValueError(f"q must be (T, H, {ROW_DIM})")
     T, H, _ = q.shape
     if kv_pool.dim() == 4:
-        if tuple(kv_pool.shape[1:]) != (1, 1, ROW_DIM):
-            raise ValueError("a 4-d kv_pool must be (N, 1, 1, 576)")
-        kv_pool = kv_pool.view(kv_pool.shape[0], ROW_DIM)
+        if tuple(kv_pool.shape[1:]) not in ((1, 1, ROW_DIM), (_page_size, 1, ROW_DIM)):
+            raise ValueError("a 4-d kv_pool must be (N, 1, 1, 576) or (pages, page_size, 1, 576)")
+        kv_pool = kv_pool.view(-1, ROW_DIM)
     if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_DIM:
         raise ValueError(f"kv_pool must be (N, {ROW_DIM})")
     _need(q, "q", dev)
@@ -159,7 +161,13 @@ def decode(
         B, T, H, max_seqlen_q, float(sm_scale), _ptr(q_scale), _ptr(kv_scale),
         1 if return_lse else 0, _ptr(lse) if return_lse else None,
     )
-    if _dcp is None:
+    if _page_size != 1:
+        if kv_last_page_lens is None:
+            raise ValueError("a paged call needs kv_last_page_lens")
+        status = L.mla_decode_paged(*head[:11], int(_page_size), *head[11:], _ptr(workspace),
+                                    ws_len, _stream(dev))
+        _lib.check(status, "mla_decode_paged")
+    elif _dcp is None:
         status = L.mla_decode_ex(*head, _ptr(workspace), ws_len, int(num_workers), _stream(dev))
         _lib.check(status, "mla_decode")
     else:
@@ -169,6 +177,35 @@ def decode(
                                   _ptr(workspace), ws_len, _stream(dev))
         _lib.check(status, "mla_decode_dcp")
     return (o, lse) if return_lse else o
+
+
+def decode_paged(
+    q: torch.Tensor,
+    kv_pool: torch.Tensor,
+    qo_indptr: torch.Tensor,
+    kv_indptr: torch.Tensor,
+    kv_indices: torch.Tensor,
+    kv_last_page_lens: torch.Tensor,
+    sm_scale: float,
+    q_scale: torch.Tensor | None = None,
+    kv_scale: torch.Tensor | None = None,
+    return_lse: bool = False,
+    *,
+    page_size: int,
+    o: torch.Tensor | None = None,
+    lse: torch.Tensor | None = None,
+    max_seqlen_q: int | None = None,
+    workspace: torch.Tensor | None = None,
+):
+    """decode() over a paged cache (mla_decode_paged): kv_pool (rows, 576) or
+    (pages, page_size, 1, 576); kv_indptr counts pages, kv_indices holds page
+    numbers and kv_last_page_lens (B,) int32 the slots used in each request's
+    last page.  Returns what decode() returns."""
+    if page_size == 1:
+        raise ValueError("page_size 1 is decode()")
+    return decode(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_lens, sm_scale,
+                  q_scale, kv_scale, return_lse, o=o, lse=lse, max_seqlen_q=max_seqlen_q,
+                  workspace=workspace, _page_size=page_size)
 
 
 def decode_dcp(

@@ -43,6 +43,7 @@ bool shape_ok(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
 
 using mla::kMaxWorkers;
 constexpr int kMaxCpSize = 1024;  // DCP shards accepted by mla_decode_dcp
+constexpr int kMaxPageShift = 12;  // page sizes accepted by mla_decode_paged: 1 .. 4096
 
 // Partial slots per worker for a call shape (group mode applies to the fp8
 // kernels; the layout is sized the same for both storage types).
@@ -63,8 +64,8 @@ mla_status decode_impl(const void* q, int q_dtype, const void* kv_pool, int kv_d
                        int batch, int num_q_tokens, int num_heads, int max_seqlen_q,
                        float sm_scale, const float* q_scale, const float* kv_scale,
                        int return_lse, float* lse, const int32_t* g_kv_indptr, int cp_size,
-                       int cp_rank, void* workspace, size_t workspace_bytes, int num_workers,
-                       void* stream) {
+                       int cp_rank, const int32_t* last_page_lens, int page_shift, void* workspace,
+                       size_t workspace_bytes, int num_workers, void* stream) {
   if (!q || !kv_pool || !o || !qo_indptr || !kv_indptr || !kv_indices)
     return MLA_ERR_NULL_POINTER;
   if (return_lse && !lse) return MLA_ERR_NULL_POINTER;
@@ -118,6 +119,8 @@ mla_status decode_impl(const void* q, int q_dtype, const void* kv_pool, int kv_d
   p.g_kv_indptr = g_kv_indptr;
   p.cp_size = cp_size;
   p.cp_rank = cp_rank;
+  p.last_page_lens = page_shift > 0 ? last_page_lens : nullptr;
+  p.page_shift = page_shift;
   if (mla::launch_decode(p, kdt, group_mode, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
@@ -168,8 +171,30 @@ mla_status mla_decode_ex(const void* q, int q_dtype, const void* kv_pool, int kv
   (void)kv_last_page_lens;  // page_size 1: all ones by contract, never read
   return decode_impl(q, q_dtype, kv_pool, kv_dtype, pool_entries, o, qo_indptr, kv_indptr,
                      kv_indices, kv_indices_len, batch, num_q_tokens, num_heads, max_seqlen_q,
-                     sm_scale, q_scale, kv_scale, return_lse, lse, nullptr, 1, 0, workspace,
-                     workspace_bytes, num_workers, stream);
+                     sm_scale, q_scale, kv_scale, return_lse, lse, nullptr, 1, 0, nullptr, 0,
+                     workspace, workspace_bytes, num_workers, stream);
+}
+
+mla_status mla_decode_paged(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                            int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                            const int32_t* kv_indptr, const int32_t* kv_indices,
+                            int64_t kv_indices_len, const int32_t* kv_last_page_lens,
+                            int page_size, int batch, int num_q_tokens, int num_heads,
+                            int max_seqlen_q, float sm_scale, const float* q_scale,
+                            const float* kv_scale, int return_lse, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int shift = 0;
+  while (shift <= kMaxPageShift && (1 << shift) != page_size) ++shift;
+  if (page_size < 1 || shift > kMaxPageShift) return MLA_ERR_BAD_SHAPE;
+  if (shift > 0 && !kv_last_page_lens) return MLA_ERR_NULL_POINTER;
+  // Rows are page * page_size + slot: every page number must name whole rows
+  // of the pool, and the largest row must stay a valid int32.
+  if (shift > 0 && (pool_entries % page_size != 0 || pool_entries > 0x7FFFFFFF))
+    return MLA_ERR_BAD_SHAPE;
+  return decode_impl(q, q_dtype, kv_pool, kv_dtype, pool_entries, o, qo_indptr, kv_indptr,
+                     kv_indices, kv_indices_len, batch, num_q_tokens, num_heads, max_seqlen_q,
+                     sm_scale, q_scale, kv_scale, return_lse, lse, nullptr, 1, 0,
+                     kv_last_page_lens, shift, workspace, workspace_bytes, 0, stream);
 }
 
 mla_status mla_decode_dcp(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
@@ -187,7 +212,7 @@ mla_status mla_decode_dcp(const void* q, int q_dtype, const void* kv_pool, int k
   return decode_impl(q, q_dtype, kv_pool, kv_dtype, pool_entries, o, qo_indptr, kv_indptr,
                      kv_indices, kv_indices_len, batch, num_q_tokens, num_heads, max_seqlen_q,
                      sm_scale, q_scale, kv_scale, return_lse, lse, g_kv_indptr, cp_world_size,
-                     cp_rank, workspace, workspace_bytes, 0, stream);
+                     cp_rank, nullptr, 0, workspace, workspace_bytes, 0, stream);
 }
 
 mla_status mla_decode(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,

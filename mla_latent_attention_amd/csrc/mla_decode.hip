@@ -81,9 +81,10 @@ __device__ __forceinline__ const uint8_t* row_ptr(const uint8_t* kv, int64_t poo
 // The first kIdxBatch * kThreads kv_indices of the piece (n of them, n >= 1)
 // are copied to idx_dst in the same pass, so the piece's start costs one
 // memory round trip; the caller copies the rest.
-template <int kLoads, int kRowBytes>
+template <int kLoads, int kRowBytes, bool kPaged>
 __device__ __forceinline__ const uint4* stage_q(uint8_t* dst_bytes, const uint8_t* q0,
-                                                int32_t* idx_dst, const int32_t* idx_src, int n) {
+                                                int32_t* idx_dst, const DecodeParams& p,
+                                                RowSrc idx_src, int n) {
   // Thread (wave wv, lane l) copies entries 64c + l for c = wv, wv + 4, ...:
   // one per-lane base address plus a wave-uniform offset per load.  Waves
   // past the last c repeat it (the same value to the same entry).
@@ -95,8 +96,16 @@ __device__ __forceinline__ const uint4* stage_q(uint8_t* dst_bytes, const uint8_
   int32_t iv[kIdxBatch];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) v[k] = *(const uint4*)(src + 64 * imin(kWaves * k + wv, kLoads - 1));
+  const int32_t* ibase = p.kv_indices + idx_src.ib;
+  if constexpr (!kPaged) {
 #pragma unroll
-  for (int j = 0; j < kIdxBatch; ++j) iv[j] = idx_src[imin(j * kThreads + (int)threadIdx.x, n - 1)];
+    for (int j = 0; j < kIdxBatch; ++j) iv[j] = ibase[imin(j * kThreads + (int)threadIdx.x, n - 1)];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kIdxBatch; ++j)
+      iv[j] = paged_row(ibase, p.page_shift,
+                        idx_src.k0 + imin(j * kThreads + (int)threadIdx.x, n - 1));
+  }
   // Stores are unconditional too (past-the-end lanes rewrite the last entry
   // with the value its owner writes): a conditional store would let the
   // compiler sink each load into its branch and serialise the round trips.
@@ -251,8 +260,9 @@ struct Fp8Path {
   using Q = Fp8Q;
   // Q stays in registers (lane l: row l%16 of the unit's head group); its
   // loads go out with the piece's first index batch.
+  template <bool kPaged>
   static __device__ __forceinline__ void load_q(Q& q, const DecodeParams& p, DecodeShared& sh,
-                                                const UnitRef& u, const int32_t* idx, int n) {
+                                                const UnitRef& u, RowSrc idx, int n) {
     const int lane = threadIdx.x & 63;
     const uint8_t* qrow = p.q +
                           ((int64_t)u.t * p.num_heads + u.g * kGroup + (lane & 15)) * kRowBytes +
@@ -260,7 +270,7 @@ struct Fp8Path {
     uint4 x[9];
 #pragma unroll
     for (int c = 0; c < 9; ++c) x[c] = *(const uint4*)(qrow + 64 * c);
-    stage_first_indices(sh.idx, idx, n);
+    stage_first_indices<kPaged>(sh.idx, p, idx, n);
 #pragma unroll
     for (int c = 0; c < 9; ++c) {
       q.lo[c] = as_long(x[c].x, x[c].y);
@@ -425,11 +435,12 @@ struct Bf16Path {
   using Q = Bf16Q;
   // Cooperative copy of the unit's 16 q rows into LDS; the caller synchronises
   // the block before the first tile reads it.
+  template <bool kPaged>
   static __device__ __forceinline__ void load_q(Q& q, const DecodeParams& p, DecodeShared& sh,
-                                                const UnitRef& u, const int32_t* idx, int n) {
-    q.lds = stage_q<18, kRowBytes>(sh.buf + kBf16QOffset,
+                                                const UnitRef& u, RowSrc idx, int n) {
+    q.lds = stage_q<18, kRowBytes, kPaged>(sh.buf + kBf16QOffset,
                                    p.q + ((int64_t)u.t * p.num_heads + u.g * kGroup) * kRowBytes,
-                                   sh.idx, idx, n);
+                                   sh.idx, p, idx, n);
   }
   static __device__ __forceinline__ TileIdx fetch_idx(const int32_t* sidx, int rows, int tile,
                                                       int n) {
@@ -457,8 +468,8 @@ static_assert(kBf16QOffset + 18 * 64 * 16 <= kCombBytes, "bf16 V staging and Q m
 
 // ---------------------------------------------------------------- pieces
 
-// One piece: KV positions [kv_pos0, kv_pos0 + rows) of unit u.  slot < 0 means
-// the piece is the whole unit and o / lse are written directly.
+// One piece: the `rows` entries of unit u whose pool rows `src` gives.  slot < 0
+// means the piece is the whole unit and o / lse are written directly.
 //
 // The 4 waves take interleaved tiles (wave wv: tiles wv, wv + 4, ...) and run
 // independent online softmaxes over them, merged through LDS at the end.  A
@@ -467,15 +478,15 @@ static_assert(kBf16QOffset + 18 * 64 * 16 <= kCombBytes, "bf16 V staging and Q m
 // (positions past the segment repeat its last index and are masked), so the
 // outstanding-load count stays static and the prefetch survives compilation.
 // Indices are staged in LDS per segment, off the vector-memory counter.
-template <class Path>
+template <class Path, bool kPaged>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared& sh,
-                                             const UnitRef& u, int kv_pos0, int rows, int slot,
+                                             const UnitRef& u, RowSrc src, int rows, int slot,
                                              float cs, float ks) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
   __syncthreads();  // the previous piece is done with the LDS buffer
 
   typename Path::Q q;
-  Path::load_q(q, p, sh, u, p.kv_indices + kv_pos0, imin(rows, kIdxSeg));
+  Path::template load_q<kPaged>(q, p, sh, u, src, imin(rows, kIdxSeg));
 
   WaveState st;
 #pragma unroll
@@ -488,8 +499,8 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
     const int srows = imin(kIdxSeg, rows - seg0);
     if (seg0 > 0) __syncthreads();  // the previous segment's index reads are done
     // The first kIdxBatch * kThreads indices of segment 0 came with Q.
-    stage_indices(sh.idx, p.kv_indices + kv_pos0 + seg0, seg0 == 0 ? kIdxBatch * kThreads : 0,
-                  srows);
+    stage_indices<kPaged>(sh.idx, p, src.template at<kPaged>(seg0),
+                          seg0 == 0 ? kIdxBatch * kThreads : 0, srows);
     __syncthreads();
     const int32_t* sidx = sh.idx;
     const int ntiles = (srows + Path::kTile - 1) / Path::kTile;
@@ -602,12 +613,12 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
 }
 
 // One worker: locate its share of the KV stream and run its pieces.
-template <class Path>
+template <class Path, bool kPaged>
 __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShared& sh) {
   const int G = p.num_heads / kGroup;
 
   // Pass 1 over requests: stream length W; zero this block's empty tokens.
-  const ReqSource src = source_of(p);
+  const ReqSource src = source_of<kPaged>(p);
   int64_t acc = 0;
   for (int b = threadIdx.x; b < p.batch; b += kThreads) {
     const Req r = load_req(src, b);
@@ -625,7 +636,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
   // a unit boundary within kSnapRows (0 and W are boundaries already).
   const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
   const int64_t xs[2] = {x0, x1 < W ? x1 : -1};
-  plan_locate2(p, [G](const Req& r) { return (int64_t)G * request_rows(r); }, xs, sh.red, sh.pb,
+  plan_locate2<kPaged>(p, [G](const Req& r) { return (int64_t)G * request_rows(r); }, xs, sh.red, sh.pb,
                sh.pcum);
   const int b0 = uniform(sh.pb[0]), b1 = uniform(sh.pb[1]);
   if (b0 < 0 || b1 == -1) return;  // not reached with consistent indptr
@@ -677,7 +688,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
       }
       if (!complete && c.k + len == v) d[1] = w;
     }
-    decode_piece<Path>(p, sh, u, c.r.kv_base + c.k, len, slot, cs, ks);
+    decode_piece<Path, kPaged>(p, sh, u, row_src<kPaged>(c.r, c.k), len, slot, cs, ks);
     pos += len;
     c.k += len;
     ++piece;
@@ -691,13 +702,26 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_fp8_kernel(const DecodeParams p) {
   __shared__ DecodeShared sh;
-  decode_worker<Fp8Path>(p, sh);
+  decode_worker<Fp8Path, false>(p, sh);
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_bf16_kernel(const DecodeParams p) {
   __shared__ DecodeShared sh;
-  decode_worker<Bf16Path>(p, sh);
+  decode_worker<Bf16Path, false>(p, sh);
+}
+
+// Paged-cache builds (page_size > 1).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_fp8_paged_kernel(const DecodeParams p) {
+  __shared__ DecodeShared sh;
+  decode_worker<Fp8Path, true>(p, sh);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_bf16_paged_kernel(const DecodeParams p) {
+  __shared__ DecodeShared sh;
+  decode_worker<Bf16Path, true>(p, sh);
 }
 
 // ---------------------------------------------------------------- split combine
@@ -926,10 +950,17 @@ hipError_t launch_decode(const DecodeParams& p, int kv_dtype, bool group_mode, h
   if (group_mode && kv_dtype == 0)
     e = launch_decode_groups(p, stream);
   else if (kv_dtype == 0 || kv_dtype == 1) {
-    if (kv_dtype == 0)
+    const bool paged = p.page_shift > 0;
+    if (kv_dtype == 0 && !paged)
       hipLaunchKernelGGL(mla_decode_fp8_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream, p);
-    else
+    else if (kv_dtype == 0)
+      hipLaunchKernelGGL(mla_decode_fp8_paged_kernel, dim3(p.num_workers), dim3(kThreads), 0,
+                         stream, p);
+    else if (!paged)
       hipLaunchKernelGGL(mla_decode_bf16_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL(mla_decode_bf16_paged_kernel, dim3(p.num_workers), dim3(kThreads), 0,
+                         stream, p);
     e = hipGetLastError();
   } else {
     return hipErrorNotSupported;

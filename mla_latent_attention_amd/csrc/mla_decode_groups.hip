@@ -300,6 +300,7 @@ __device__ __forceinline__ void pair_pv(WideState& st, const PairP& pp, const ui
 // length L).  slot_base < 0: the piece is the whole unit and every row group
 // writes o / lse; else row group i of the unit writes partial slot
 // slot_base + i.
+template <bool kPaged>
 __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& sh,
                                             const GCursor& c, int G, int L, int len,
                                             int slot_base, int w, float cs, float ks) {
@@ -344,7 +345,7 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
 
   // q rows of this lane's row group (registers) and the first index batch, in
   // one round trip.  Step c: head n16's bytes [64c + 32h, +32).
-  const int kv_pos0 = c.r.kv_base + c.k;
+  const RowSrc src = row_src<kPaged>(c.r, c.k);
   v8i_t q[9];
   {
     const uint8_t* qrow =
@@ -352,7 +353,7 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
     uint4 xq[18];
 #pragma unroll
     for (int i = 0; i < 18; ++i) xq[i] = *(const uint4*)(qrow + 64 * (i >> 1) + 16 * (i & 1));
-    stage_first_indices(sh.idx, p.kv_indices + kv_pos0, imin(len, kGIdxSeg));
+    stage_first_indices<kPaged>(sh.idx, p, src, imin(len, kGIdxSeg));
 #pragma unroll
     for (int cc = 0; cc < 9; ++cc) {
       const uint4 a0 = xq[2 * cc], a1 = xq[2 * cc + 1];
@@ -390,8 +391,8 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   for (int seg0 = 0; seg0 < len; seg0 += kGIdxSeg) {
     const int srows = imin(kGIdxSeg, len - seg0);
     if (seg0 > 0) __syncthreads();  // the previous segment is done with the indices
-    stage_indices(sh.idx, p.kv_indices + kv_pos0 + seg0, seg0 == 0 ? kIdxBatch * kThreads : 0,
-                  srows);
+    stage_indices<kPaged>(sh.idx, p, src.template at<kPaged>(seg0),
+                          seg0 == 0 ? kIdxBatch * kThreads : 0, srows);
     __syncthreads();
     const int ntiles = (srows + kGTile - 1) / kGTile;
     // Ring of six tiles: P.V takes the tiles in pairs, so a tile's slot is
@@ -514,11 +515,12 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
 }
 
 // One worker: locate its share of the group-mode stream and run its pieces.
+template <bool kPaged>
 __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared& sh) {
   const int G = p.num_heads / kGroup;
 
   // Pass 1 over requests: stream length W; zero this block's empty tokens.
-  const ReqSource src = source_of(p);
+  const ReqSource src = source_of<kPaged>(p);
   int64_t acc = 0;
   for (int b = threadIdx.x; b < p.batch; b += kThreads) {
     const Req r = load_req(src, b);
@@ -534,7 +536,7 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
   if (w >= nw) return;
   const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
   const int64_t xs[2] = {x0, x1 < W ? x1 : -1};
-  plan_locate2(p, [G](const Req& r) { return group_request_rows(r, G); }, xs, sh.red, sh.pb,
+  plan_locate2<kPaged>(p, [G](const Req& r) { return group_request_rows(r, G); }, xs, sh.red, sh.pb,
                sh.pcum);
   const int b0 = uniform(sh.pb[0]), b1 = uniform(sh.pb[1]);
   if (b0 < 0 || b1 == -1) return;  // not reached with consistent indptr
@@ -569,7 +571,7 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
     const bool complete = (c.k == 0 && len == L);
     const int slot_base =
         complete ? -1 : kGSlotsPerPiece * (2 * w + (piece == 0 ? 0 : 1));
-    group_piece(p, sh, c, G, L, len, slot_base, w, cs, ks);
+    group_piece<kPaged>(p, sh, c, G, L, len, slot_base, w, cs, ks);
     pos += len;
     c.k += len;
     ++piece;
@@ -585,12 +587,23 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_groups_fp8_kernel(const DecodeParams p) {
   __shared__ GroupShared sh;
-  group_worker(p, sh);
+  group_worker<false>(p, sh);
+}
+
+// The paged-cache build (page_size > 1).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_groups_fp8_paged_kernel(const DecodeParams p) {
+  __shared__ GroupShared sh;
+  group_worker<true>(p, sh);
 }
 
 hipError_t launch_decode_groups(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(mla_decode_groups_fp8_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream,
-                     p);
+  if (p.page_shift > 0)
+    hipLaunchKernelGGL(mla_decode_groups_fp8_paged_kernel, dim3(p.num_workers), dim3(kThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL(mla_decode_groups_fp8_kernel, dim3(p.num_workers), dim3(kThreads), 0,
+                       stream, p);
   return hipGetLastError();
 }
 

@@ -125,11 +125,11 @@ __device__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) 
 // not looked up), where request r holds rows_of(r) stream rows: sb[i] =
 // request (-1 if not found, -2 if not looked up) and scum[i] = that request's
 // first stream position.
-template <int kT = kThreads, class RowsOf>
+template <bool kPaged, int kT = kThreads, class RowsOf>
 __device__ void plan_locate2(const DecodeParams& p, RowsOf rows_of, const int64_t (&x)[2],
                              int64_t* red, int* sb, int64_t* scum) {
   if (threadIdx.x < 2) sb[threadIdx.x] = x[threadIdx.x] < 0 ? -2 : -1;
-  const ReqSource src = source_of(p);
+  const ReqSource src = source_of<kPaged>(p);
   int64_t carry = 0;
   for (int b0 = 0; b0 < p.batch; b0 += kT) {
     const int b = b0 + threadIdx.x;
@@ -196,12 +196,58 @@ __device__ __forceinline__ void softmax_update(WaveState& st, float (&x)[N]) {
 // kv_indices loads issued per thread before the first store.
 constexpr int kIdxBatch = 8;
 
-template <int kT = kThreads>
-__device__ __forceinline__ void stage_first_indices(int32_t* idx_dst, const int32_t* idx_src,
-                                                    int n) {
+// Pool rows of a piece's entries.  Entry i of the piece is entry k0 + i of its
+// request.  One entry per index (page_shift 0): the row is kv_indices[ib + i],
+// ib being the piece's first index.  Paged cache (page_size 2^page_shift): ib
+// is the request's first page number's index and the row is page * page_size
+// + slot of entry k0 + i.  Consecutive entries share a page number, so a
+// page's index is fetched from memory once and served from cache to the
+// others.  (Two integers, so the pieces' long loops keep little extra state.)
+struct RowSrc {
+  int ib;
+  int k0;
+
+  template <bool kPaged>
+  __device__ __forceinline__ RowSrc at(int i) const {  // the same source from entry i on
+    RowSrc r = *this;
+    if constexpr (kPaged)
+      r.k0 += i;
+    else
+      r.ib += i;
+    return r;
+  }
+};
+
+// Kernels come in two builds: kPaged = false (one entry per index) and true
+// (paged cache), so the common build carries none of the paging state.
+template <bool kPaged>
+__device__ __forceinline__ RowSrc row_src(const Req& r, int k) {
+  RowSrc s;
+  s.ib = r.kv_base + (kPaged ? 0 : k);
+  s.k0 = k;
+  return s;
+}
+
+// Pool row of entry e of a request whose page numbers start at `pages` (a
+// page number out of range gives a row that the row loads clamp).
+__device__ __forceinline__ int32_t paged_row(const int32_t* pages, int shift, int e) {
+  return (int32_t)(((uint32_t)pages[e >> shift] << shift) | (uint32_t)(e & ((1 << shift) - 1)));
+}
+
+// Rows of entries [0, n) of src (first kIdxBatch * kT of them) to idx_dst.
+template <bool kPaged, int kT = kThreads>
+__device__ __forceinline__ void stage_first_indices(int32_t* idx_dst, const DecodeParams& p,
+                                                    RowSrc src, int n) {
   int32_t iv[kIdxBatch];
+  const int32_t* base = p.kv_indices + src.ib;
+  if constexpr (!kPaged) {
 #pragma unroll
-  for (int j = 0; j < kIdxBatch; ++j) iv[j] = idx_src[imin(j * kT + (int)threadIdx.x, n - 1)];
+    for (int j = 0; j < kIdxBatch; ++j) iv[j] = base[imin(j * kT + (int)threadIdx.x, n - 1)];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kIdxBatch; ++j)
+      iv[j] = paged_row(base, p.page_shift, src.k0 + imin(j * kT + (int)threadIdx.x, n - 1));
+  }
 #pragma unroll
   for (int j = 0; j < kIdxBatch; ++j) idx_dst[imin(j * kT + (int)threadIdx.x, n - 1)] = iv[j];
 }
@@ -215,16 +261,24 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&a)[8])
   *(uint4*)dst = pk;
 }
 
-// Copies indices [from, n) of src (n >= 1) to the same positions of dst.
-// Each thread issues kIdxBatch loads before its first store (past-the-end
-// positions reload the last index), so a segment costs one memory round trip
-// per 2048 indices instead of one per 256.
-template <int kT = kThreads>
-__device__ __forceinline__ void stage_indices(int32_t* dst, const int32_t* src, int from, int n) {
+// Copies the rows of entries [from, n) of src (n >= 1) to the same positions
+// of dst.  Each thread issues kIdxBatch loads before its first store
+// (past-the-end positions reload the last index), so a segment costs one
+// memory round trip per 2048 indices instead of one per 256.
+template <bool kPaged, int kT = kThreads>
+__device__ __forceinline__ void stage_indices(int32_t* dst, const DecodeParams& p, RowSrc src,
+                                              int from, int n) {
+  const int32_t* base = p.kv_indices + src.ib;
   for (int i0 = from; i0 < n; i0 += kT * kIdxBatch) {
     int32_t v[kIdxBatch];
+    if constexpr (!kPaged) {
 #pragma unroll
-    for (int j = 0; j < kIdxBatch; ++j) v[j] = src[imin(i0 + j * kT + (int)threadIdx.x, n - 1)];
+      for (int j = 0; j < kIdxBatch; ++j) v[j] = base[imin(i0 + j * kT + (int)threadIdx.x, n - 1)];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kIdxBatch; ++j)
+        v[j] = paged_row(base, p.page_shift, src.k0 + imin(i0 + j * kT + (int)threadIdx.x, n - 1));
+    }
 #pragma unroll
     for (int j = 0; j < kIdxBatch; ++j) dst[imin(i0 + j * kT + (int)threadIdx.x, n - 1)] = v[j];
   }

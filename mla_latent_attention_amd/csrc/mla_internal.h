@@ -35,9 +35,13 @@ struct DecodeParams {
   const int32_t* g_kv_indptr = nullptr;  // (B+1) full-list offsets under DCP, or nullptr
   int cp_size = 1;                        // DCP shards (1 without DCP)
   int cp_rank = 0;                        // this shard
+  const int32_t* last_page_lens = nullptr;  // (B) paged caches: used slots of the last page
+  int page_shift = 0;                     // log2(page_size); 0: kv_indices name entries
 };
 
-// The planner's view of the call's requests.
+// The planner's view of the call's requests.  kPaged = false builds drop the
+// paging fields as constants (page_size 1).
+template <bool kPaged>
 __host__ __device__ inline ReqSource source_of(const DecodeParams& p) {
   ReqSource s;
   s.qo = p.qo_indptr;
@@ -48,6 +52,8 @@ __host__ __device__ inline ReqSource source_of(const DecodeParams& p) {
   s.causal = p.causal;
   s.cp_size = p.cp_size;
   s.cp_rank = p.cp_rank;
+  s.lpl = kPaged ? p.last_page_lens : nullptr;
+  s.page_shift = kPaged ? p.page_shift : 0;
   return s;
 }
 

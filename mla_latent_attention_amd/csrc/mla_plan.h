@@ -83,22 +83,28 @@ MLA_HD int64_t snap_position(int64_t x, int k, int v) {
 // cp_rank + i * cp_size <= N - qlen + j ("Kimi K3 on AMD Instinct MI355X ...",
 // Sec. 1: each GPU keeps an eighth of the positions; multi-token verification
 // under DCP).
+//
+// Paged caches (page_size = 2^page_shift > 1): kvp counts pages, kv_indices
+// holds page (block) numbers, and request b's last page holds lpl[b] of its
+// page_size slots, so it has (pages - 1) * page_size + lpl[b] entries.
 struct ReqSource {
   const int32_t* qo;    // (B+1) query-token offsets, or null
-  const int32_t* kvp;   // (B+1) local entry offsets, or null
+  const int32_t* kvp;   // (B+1) local entry (page) offsets, or null
   const int32_t* gkvp;  // (B+1) offsets of the requests' full (all-shard) lists, or null
-  int kv_cap;           // entries in kv_indices
+  int kv_cap;           // entries (pages) in kv_indices
   int T;                // query tokens
   int causal;           // 0: every token sees all of its request's local entries
   int cp_size;          // shards the positions are dealt over (1 without DCP)
   int cp_rank;          // this shard
+  const int32_t* lpl;   // (B) used slots of each request's last page (paged caches)
+  int page_shift;       // log2(page_size); 0: one entry per index
 };
 
 // One request's bounds, clamped so that no later read can leave its buffer,
 // and its visibility rule: token j sees min(n, (vbase + j) / vstep + 1)
 // entries when vbase + j >= 0, none otherwise.
 struct Req {
-  int kv_base;  // offset of its first entry in kv_indices
+  int kv_base;  // offset of its first entry (page) in kv_indices
   int n;        // local entry count
   int q_base;   // its first query token
   int qlen;     // query tokens
@@ -117,6 +123,10 @@ MLA_HD Req load_req(const ReqSource& s, int b) {
   Req r;
   r.kv_base = k0;
   r.n = k1 - k0;
+  if (s.page_shift > 0 && r.n > 0) {
+    const int P = 1 << s.page_shift;
+    r.n = ((r.n - 1) << s.page_shift) + imin(imax(s.lpl[b], 1), P);
+  }
   r.q_base = q0;
   r.qlen = q1 - q0;
   r.causal = s.causal;

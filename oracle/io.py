@@ -34,17 +34,24 @@ def workload_args(w, requests=None) -> dict:
     kvp = w.kv_indptr.cpu().numpy().astype(np.int64)
     B = len(qo) - 1
     reqs = list(range(B)) if requests is None else [int(b) for b in requests]
-    toks, kv_lists = [], []
+    dev = w.kv_indices.device
+    page_size = int(getattr(w, "page_size", 1))
+    toks, req_rows = [], []
     for b in reqs:
         toks.extend(range(qo[b], qo[b + 1]))
-        kv_lists.append((kvp[b], kvp[b + 1]))
-    idx_dev = torch.cat(
-        [w.kv_indices[a:e].to(torch.int64) for a, e in kv_lists]
-        or [torch.empty(0, dtype=torch.int64, device=w.kv_indices.device)]
-    )
+        if page_size == 1:
+            req_rows.append(w.kv_indices[kvp[b]: kvp[b + 1]].to(torch.int64))
+        else:  # expand the request's page list to one pool row per entry
+            from .mla import paged_entry_rows
+
+            pages = w.kv_indices[kvp[b]: kvp[b + 1]].cpu().numpy()
+            last = w.kv_last_page_lens[b: b + 1].cpu().numpy()
+            _, rows = paged_entry_rows(np.array([0, len(pages)]), pages, last, page_size)
+            req_rows.append(torch.from_numpy(rows).to(dev))
+    idx_dev = torch.cat(req_rows or [torch.empty(0, dtype=torch.int64, device=dev)])
     uniq, inverse = torch.unique(idx_dev, return_inverse=True)
     pool_rows = w.kv_pool.index_select(0, uniq) if uniq.numel() else w.kv_pool[:1]
-    lens = np.array([e - a for a, e in kv_lists], dtype=np.int64)
+    lens = np.array([int(r.numel()) for r in req_rows], dtype=np.int64)
     qlens = np.array([qo[b + 1] - qo[b] for b in reqs], dtype=np.int64)
     tok_t = torch.tensor(toks, dtype=torch.int64, device=w.q.device)
     dcp = {}

@@ -38,6 +38,12 @@ Readings taken where the pages are silent (each is listed in the design notes):
    Sec. 3) a request's positions are dealt round-robin: shard r of W holds
    full-list positions r, r + W, r + 2W, ... in that order, and reading 4
    applies to full-list positions (``dcp_visible_length``).
+7. Paged caches ([Issue] Sec. 3: the entry point's page_size and
+   kv_last_page_lens arguments; Sec. 5.2: the capture uses page_size 1 while
+   the allocator's blocks hold 128 slots): kv_indptr counts pages, kv_indices
+   holds page numbers, page k holds pool rows k*P .. k*P + P - 1, and a
+   request's last page holds kv_last_page_lens[b] of its P slots
+   (``paged_entry_rows``).
 """
 
 from __future__ import annotations
@@ -59,6 +65,30 @@ def visible_length(n: int, qlen: int, j: int) -> int:
     draft token sees one entry fewer.  Equals ``n`` when qlen = 1.
     """
     return max(0, n - (qlen - 1 - j))
+
+
+def paged_entry_rows(kv_indptr, kv_indices, last_page_lens, page_size: int):
+    """Per-entry pool rows of a paged call (reading 7).
+
+    Request b owns pages kv_indices[kv_indptr[b]:kv_indptr[b+1]]; its entry i
+    lives in its page number i // P at slot i % P, i.e. pool row
+    page * P + i % P, and it has (pages - 1) * P + last_page_lens[b] entries
+    (none without pages).  Returns (entry_indptr, rows) in the one-row-per-
+    entry form ``mla_decode`` takes.
+    """
+    P = int(page_size)
+    kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
+    kv_indices = np.asarray(kv_indices, dtype=np.int64)
+    last = np.asarray(last_page_lens, dtype=np.int64)
+    rows, counts = [], []
+    for b in range(len(kv_indptr) - 1):
+        pages = kv_indices[kv_indptr[b]: kv_indptr[b + 1]]
+        n = 0 if len(pages) == 0 else (len(pages) - 1) * P + int(last[b])
+        i = np.arange(n, dtype=np.int64)
+        rows.append(pages[i // P] * P + i % P)
+        counts.append(n)
+    entry_indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return entry_indptr, (np.concatenate(rows) if rows else np.zeros(0, np.int64))
 
 
 def dcp_visible_length(n_full: int, n_local: int, qlen: int, j: int, cp_size: int,

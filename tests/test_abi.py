@@ -130,3 +130,31 @@ def _decode_dcp(**over):
 )
 def test_decode_dcp_rejects_bad_arguments_before_any_launch(over, status):
     assert _decode_dcp(**over) == status
+
+
+def _decode_paged(**over):
+    args = dict(
+        q=FAKE, q_dtype=0, kv=FAKE, kv_dtype=0, pool=1024, o=FAKE, qo=FAKE, kvp=FAKE, idx=FAKE,
+        idx_len=8, lpl=FAKE, page=128, batch=2, T=2, H=16, qmax=1, sm=0.072, qs=None, ks=None,
+        rl=0, lse=None, ws=FAKE, ws_len=1 << 30, stream=None,
+    )
+    args.update(over)
+    return _lib.lib().mla_decode_paged(*args.values())
+
+
+@pytest.mark.parametrize(
+    "over,status",
+    [
+        (dict(page=0), 2),
+        (dict(page=3), 2),
+        (dict(page=8192), 2),
+        (dict(lpl=None), 1),
+        (dict(pool=1000), 2),
+        (dict(pool=1 << 31), 2),
+        (dict(q=None), 1),
+        (dict(H=24), 4),
+        (dict(ws=None), 5),
+    ],
+)
+def test_decode_paged_rejects_bad_arguments_before_any_launch(over, status):
+    assert _decode_paged(**over) == status

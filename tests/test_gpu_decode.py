@@ -33,11 +33,16 @@ def say(*a):
 
 
 def run(w, num_workers=0, return_lse=True, q=None):
-    """decode() on w's inputs, or decode_dcp() when w is one DCP shard."""
+    """decode() on w's inputs; decode_paged() for a paged cache, decode_dcp()
+    for one DCP shard."""
     torch.cuda.synchronize()
     args = (w.q if q is None else q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
             w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale)
-    if w.g_kv_indptr is not None:
+    if w.page_size > 1:
+        assert num_workers == 0
+        out = mla.decode_paged(*args, return_lse=return_lse, page_size=w.page_size,
+                               max_seqlen_q=w.max_seqlen_q)
+    elif w.g_kv_indptr is not None:
         assert num_workers == 0
         out = mla.decode_dcp(*args, return_lse=return_lse, g_kv_indptr=w.g_kv_indptr,
                              cp_world_size=w.cp_size, cp_rank=w.cp_rank,
@@ -531,6 +536,44 @@ def test_dcp_bad_arguments_are_rejected():
                            w.sm_scale, g_kv_indptr=w.g_kv_indptr, cp_world_size=cps, cp_rank=cpr)
 
 
+# ------------------------------------------------------------------ paged cache
+# mla_decode_paged: kv_indices hold page numbers; ragged last pages, empty
+# requests, draft tokens, both storage types and both kernels.
+
+PAGED_CASES = {
+    "fp8-p128-16heads": dict(page_size=128, num_heads=16, real_heads=12, qlens=None, dtype="fp8"),
+    "fp8-p2-16heads-draft": dict(page_size=2, num_heads=16, real_heads=12,
+                                 qlens=[1, 3, 2, 1, 3, 2, 3], dtype="fp8"),
+    "fp8-p16-96heads-group": dict(page_size=16, num_heads=96, real_heads=96,
+                                  qlens=[4, 1, 3, 4, 2, 4, 4], dtype="fp8"),
+    "bf16-p128-draft": dict(page_size=128, num_heads=16, real_heads=12,
+                            qlens=[4, 1, 3, 4, 2, 4, 4], dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(PAGED_CASES))
+def test_paged_cache_matches_oracle(case):
+    kw = dict(PAGED_CASES[case])
+    P = kw["page_size"]
+    w = workloads.build(f"paged-{case}", [0, 1, 127, 128, 129, 1000, 5003],
+                        pool_entries=P * max(64, (1 << 15) // P), kv_std=0.5,
+                        scale_range=(0.5, 2.0), shared_prefix=300, seed=81, device=DEV, **kw)
+    o, lse, _ = check(w, where=f"paged {case}")
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_paged_bad_arguments_are_rejected():
+    w = workloads.build("paged-bad", [200], num_heads=16, pool_entries=1024, seed=82, device=DEV,
+                        page_size=128)
+    for P in (3, 8192, 0):
+        with pytest.raises(mla.MLAError):
+            mla.decode_paged(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                             w.kv_last_page_lens, w.sm_scale, page_size=P)
+    with pytest.raises(mla.MLAError):  # the pool is not a whole number of pages
+        mla.decode_paged(w.q, w.kv_pool[:1000], w.qo_indptr, w.kv_indptr, w.kv_indices,
+                         w.kv_last_page_lens, w.sm_scale, page_size=128)
+
+
 # ------------------------------------------------------------------ merge
 
 
@@ -605,6 +648,13 @@ def test_dcp_share_sampled():
     """One DCP8 rank at full size (rank 7 of 142,000 positions per request)."""
     w = workloads.dcp_share(DEV)
     check(w, requests=[0, 5])
+
+
+def test_headline_batch16_paged128_sampled():
+    """The headline call as a page table of 128-slot pages (mla_decode_paged)."""
+    w = workloads.c16(DEV, "paged128", return_lse=True)
+    check(w, requests=[0, 9])
+    del w
 
 
 def test_headline_batch16_cascade_sampled():

@@ -66,6 +66,9 @@ class Workload:
     g_kv_indptr: torch.Tensor | None = None
     cp_size: int = 1
     cp_rank: int = 0
+    # Paged cache (page_size > 1): kv_indptr counts pages, kv_indices holds page
+    # numbers and kv_last_page_lens the slots used in each last page.
+    page_size: int = 1
 
     @property
     def batch(self) -> int:
@@ -141,6 +144,37 @@ def make_indices(lengths, shared_prefix, pool_entries, layout, seed, device, ind
     return kv_indices
 
 
+def make_paged_indices(lengths, page_size, shared_prefix, pool_entries, seed, device):
+    """Page tables for `lengths` over a pool of pool_entries / page_size pages,
+    handed out in a seeded random order.  The first shared_prefix // page_size
+    pages of every request are the same pages (only whole pages are shared, as
+    in prefix caching); the rest are disjoint.  Returns (kv_indptr in pages,
+    kv_indices = page numbers, kv_last_page_lens), int32 on `device`."""
+    P = page_size
+    npages = pool_entries // P
+    gi = _gen(seed, device)
+    perm = torch.randperm(npages, generator=gi, device=device, dtype=torch.int64)
+    shared = shared_prefix // P
+    off = shared
+    parts, counts, last = [], [], []
+    for n in lengths:
+        pages = -(-n // P)
+        s = min(pages, shared) if n >= shared * P else 0
+        parts.append(perm[:s])
+        parts.append(perm[off: off + pages - s])
+        off += pages - s
+        counts.append(pages)
+        last.append(n - (pages - 1) * P if pages else 1)
+    if off > npages:
+        raise ValueError(f"paged workload needs {off} pages, pool has {npages}")
+    kv_indptr = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    kv_indptr[1:] = torch.cumsum(torch.tensor(counts, dtype=torch.int64), 0).to(torch.int32)
+    used = torch.cat(parts) if parts else torch.empty(0, dtype=torch.int64, device=device)
+    idx = torch.zeros(max(int(used.numel()), 1), dtype=torch.int32, device=device)
+    idx[: used.numel()] = used.to(torch.int32)
+    return (kv_indptr.to(device), idx, torch.tensor(last, dtype=torch.int32, device=device))
+
+
 def build(
     name: str,
     lengths: list[int],
@@ -159,6 +193,7 @@ def build(
     return_lse: bool = True,
     seed: int = 0,
     device="cpu",
+    page_size: int = 1,
 ) -> Workload:
     """Assemble a decode call.
 
@@ -169,6 +204,8 @@ def build(
     layout:        'random' scatters slots by a seeded permutation of the pool;
                    'blocked' hands out runs of 128 consecutive slots (the
                    allocator's block size) in a seeded random block order.
+    page_size:     > 1 builds a paged call (make_paged_indices; layout and
+                   index_buffer do not apply).
     Seeds: lengths are the caller's; KV uses seed+1, q seed+2, indices seed+3,
     scales seed+4 (q_scale) and seed+5 (kv_scale).
     """
@@ -182,12 +219,16 @@ def build(
     if need > pool_entries:
         raise ValueError(f"workload needs {need} distinct slots, pool has {pool_entries}")
 
-    kv_indices = make_indices(lengths, shared_prefix, pool_entries, layout, seed + 3, device,
-                              index_buffer)
+    if page_size > 1:
+        kv_indptr, kv_indices, last_page_lens = make_paged_indices(
+            lengths, page_size, shared_prefix, pool_entries, seed + 3, device)
+    else:
+        kv_indices = make_indices(lengths, shared_prefix, pool_entries, layout, seed + 3, device,
+                                  index_buffer)
+        kv_indptr = torch.zeros(B + 1, dtype=torch.int32)
+        kv_indptr[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+        last_page_lens = torch.ones(B, dtype=torch.int32, device=device)
     buf_len = int(kv_indices.numel())
-
-    kv_indptr = torch.zeros(B + 1, dtype=torch.int32)
-    kv_indptr[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
     qo_indptr = torch.zeros(B + 1, dtype=torch.int32)
     qo_indptr[1:] = torch.cumsum(torch.tensor(qlens, dtype=torch.int64), 0).to(torch.int32)
 
@@ -204,7 +245,7 @@ def build(
         qo_indptr=qo_indptr.to(device),
         kv_indptr=kv_indptr.to(device),
         kv_indices=kv_indices,
-        kv_last_page_lens=torch.ones(B, dtype=torch.int32, device=device),
+        kv_last_page_lens=last_page_lens,
         q_scale=_scale(scale_range, seed + 4, device),
         kv_scale=_scale(scale_range, seed + 5, device),
         sm_scale=SM_SCALE,
@@ -217,8 +258,9 @@ def build(
         recipe=dict(
             seed=seed, pool_entries=pool_entries, kv_std=kv_std, q_std=q_std,
             scale_range=scale_range, shared_prefix=shared_prefix, layout=layout,
-            index_buffer=buf_len, dtype=dtype,
+            index_buffer=buf_len, dtype=dtype, page_size=page_size,
         ),
+        page_size=page_size,
     )
 
 
@@ -245,7 +287,9 @@ def c16(device="cpu", variant: str = "shared", return_lse: bool = False) -> Work
 
     variant: 'shared' (prefix slots shared by all requests, as captured),
              'unshared' (every request's prefix uses its own slots),
-             'blocked' (shared prefix, slots handed out in 128-slot runs).
+             'blocked' (shared prefix, slots handed out in 128-slot runs),
+             'paged128' (a page table of 128-slot pages: the 499 whole pages
+             of the prefix shared, the rest of each request in its own pages).
     """
     lengths = c16_lengths()
     shared = 0 if variant == "unshared" else SHARED_PREFIX
@@ -254,7 +298,7 @@ def c16(device="cpu", variant: str = "shared", return_lse: bool = False) -> Work
         f"c16-{variant}", lengths, num_heads=16, real_heads=12, pool_entries=POOL_ENTRIES,
         dtype="fp8", kv_std=0.5, q_std=1.0, scale_range=(0.5, 2.0), shared_prefix=shared,
         layout=layout, index_buffer=INDEX_BUFFER, return_lse=return_lse, seed=2000,
-        device=device,
+        device=device, page_size=128 if variant == "paged128" else 1,
     )
 
 

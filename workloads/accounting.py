@@ -25,10 +25,16 @@ def visible(n: int, qlen: int, j: int) -> int:
     return max(0, n - (qlen - 1 - j))
 
 
-def decode_bytes(lengths, qlens, num_heads, dtype="fp8", return_lse=False) -> int:
-    """HBM bytes the method must move for one call."""
+def decode_bytes(lengths, qlens, num_heads, dtype="fp8", return_lse=False, page_size=1) -> int:
+    """HBM bytes the method must move for one call.  A paged cache reads one
+    index per page plus each request's last-page length instead of one index
+    per entry."""
     T = sum(qlens)
-    kv = sum(lengths) * (row_bytes(dtype) + INDEX_BYTES)
+    if page_size == 1:
+        kv = sum(lengths) * (row_bytes(dtype) + INDEX_BYTES)
+    else:
+        pages = sum(-(-n // page_size) for n in lengths)
+        kv = sum(lengths) * row_bytes(dtype) + (pages + len(lengths)) * INDEX_BYTES
     q = T * num_heads * ROW_DIM * _ELEM[dtype]
     o = T * num_heads * LATENT_DIM * 2
     lse = T * num_heads * 4 if return_lse else 0
@@ -60,7 +66,8 @@ def merge_bytes(num_parts, num_tokens, num_heads, parts_dtype="fp32", with_lse_o
 
 
 def workload_bytes(w) -> int:
-    return decode_bytes(w.lengths, w.qlens, w.num_heads, w.dtype, w.return_lse)
+    return decode_bytes(w.lengths, w.qlens, w.num_heads, w.dtype, w.return_lse,
+                        getattr(w, "page_size", 1))
 
 
 def workload_flops(w) -> int:
