@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode µs/call + HBM GB/s (% of 8 TB/s), bs16 kv≈68K fp8, 1 GPU"
 CONFIG_NAMES = ("c24_batch24_fp8", "mixed_batch64_fp8", "mixed_batch64_bf16",
                 "dcp_share_96heads_qlen4_fp8", "c16_shared_prefix_cascade_fp8",
-                "merge_8_shards_fp32", "merge_8_shards_bf16")
+                "merge_8_shards_fp32", "merge_8_shards_bf16", "c16_layer_step_rope_decode_v")
 PEAK_GBS = 8000.0
 
 
@@ -224,7 +224,68 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
             "pct_of_8TBs": round(100 * nbytes / wall / 1e9 / PEAK_GBS, 2),
             "algorithmic_bytes_per_call": nbytes, "calls": n}
         del sets
+    if only is None or only == "c16_layer_step_rope_decode_v":
+        out["c16_layer_step_rope_decode_v"] = layer_step_line(mla, dev, steps, warmup)
     return out
+
+
+def layer_step_line(mla, dev, steps, warmup, n_layers=4):
+    """The batch-16 call with the steps either side: the fused rope / fp8 /
+    cache-write step, the decode, and the latent -> v_head_dim GEMM, per
+    layer (n_layers caches and weights cycled); each step also alone."""
+    import torch
+
+    import workloads
+    from workloads import accounting
+
+    layers = make_layers(n_layers, "shared", dev)
+    w0 = layers[0]
+    T, Hp, H = w0.num_tokens, w0.num_heads, w0.real_heads
+    sur = [workloads.surround(T, H, 73_728, w0.kv_pool.shape[0], seed=8000 + k, device=dev)
+           for k in range(n_layers)]
+    kvp = w0.kv_indptr.cpu().tolist()
+    # each request's new entry goes to the last slot of its list
+    slots = torch.stack([w0.kv_indices[kvp[b + 1] - 1] for b in range(w0.batch)]).to(torch.int32)
+    q = torch.empty((T, Hp, 576), dtype=torch.float8_e4m3fn, device=dev)
+    o = torch.empty((T, Hp, 512), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    ws = mla.new_workspace(mla.workspace_bytes(w0.batch, T, Hp, 1), dev)
+
+    def rope(w, s):
+        return lambda: mla.rope_quant_cache(s.q_latent, s.q_pe, s.k_latent, s.k_pe, s.positions,
+                                            s.cos_sin, w.kv_pool, slots, num_heads_pad=Hp,
+                                            q_scale=w.q_scale, kv_scale=w.kv_scale, q_out=q)
+
+    def dec(w):
+        return lambda: mla.decode(q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                  w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale, o=o,
+                                  max_seqlen_q=1, workspace=ws)
+
+    def bmm(s):
+        return lambda: mla.latent_to_v(o, s.w_uv, out=v)
+
+    def step(w, s):
+        r, d, b = rope(w, s), dec(w), bmm(s)
+        return lambda: (r(), d(), b())
+
+    res = {}
+    for name, calls in (("rope_quant_cache", [rope(w, s) for w, s in zip(layers, sur)]),
+                        ("latent_to_v", [bmm(s) for s in sur]),
+                        ("layer_step", [step(w, s) for w, s in zip(layers, sur)])):
+        wall, ev, n = time_graph(calls, steps, warmup)
+        res[name] = {"us_per_call": round(wall * 1e6, 2), "event_us": stats_us(ev), "calls": n}
+    rope_bytes = (T * H * (512 + 64) * 2 + T * 576 * 2 + T * 8 + T * 256
+                  + T * Hp * 576 + T * 576)
+    bmm_bytes = T * H * 512 * 2 + H * 128 * 512 * 2 + T * H * 128 * 2
+    res["rope_quant_cache"]["algorithmic_bytes_per_call"] = rope_bytes
+    res["latent_to_v"]["algorithmic_bytes_per_call"] = bmm_bytes
+    res["latent_to_v"]["GB_s"] = round(bmm_bytes / (res["latent_to_v"]["us_per_call"] * 1e-6) / 1e9, 2)
+    res["layer_step"]["decode_bytes_per_call"] = accounting.workload_bytes(w0)
+    res["workload"] = (f"c16 (T={T}, {H} heads padded to {Hp}): rope + fp8 + cache write of the new "
+                       f"entries, the decode, then o (T,{H},512) x W_uv ({H},128,512)")
+    del layers, sur
+    torch.cuda.empty_cache()
+    return res
 
 
 def make_calls(mla, layers, o, ws):

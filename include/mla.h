@@ -276,6 +276,60 @@ mla_status mla_decode_cascade(const void* q, int q_dtype, const void* kv_pool, i
                               float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The step before the decode ("[Kimi-K3 MLA TP8] MLA performance", Sec. 3:
+ * the decode's q is produced by one fused op that also writes the step's new
+ * cache entry into the pool the decode reads; Sec. 2 geometry: 512 latent +
+ * 64 rope dims).  For every token t:
+ *   q_out[t, h]  = fp8((q_latent[t, h] ++ rope(q_pe[t, h], positions[t])) / q_scale)
+ *                  for h < num_heads, all-zero codes for the pad heads
+ *                  num_heads <= h < num_heads_pad;
+ *   kv_pool[slot_mapping[t]] = fp8((k_latent[t] ++ rope(k_pe[t], positions[t])) / kv_scale)
+ *                  unless slot_mapping[t] is negative or >= pool_entries (no write).
+ *
+ *  q_latent      (num_q_tokens, num_heads, 512) bf16: the absorbed q.
+ *  q_pe          (num_q_tokens, num_heads, 64) bf16: q's rope dims before rotation.
+ *  k_latent      (num_q_tokens, 512) bf16, k_pe (num_q_tokens, 64) bf16: the
+ *                tokens' new cache entries before rotation and quantisation.
+ *  positions     (num_q_tokens) int32, clamped to [0, max_pos).
+ *  cos_sin       (max_pos, 64) fp32: cos of the 32 rotation angles of a
+ *                position, then their sin.
+ *  rope_style    0: dims (2j, 2j+1) rotate by angle j; 1: dims (j, j+32) do.
+ *                A rotated dim is x_a cos - x_b sin or x_b cos + x_a sin with
+ *                every product and sum rounded to fp32 (no fused multiply-add).
+ *  q_out         (num_q_tokens, num_heads_pad, 576) fp8 e4m3fn, written.
+ *  kv_pool       (pool_entries, 576) fp8 e4m3fn; only the slots named are written.
+ *  q_scale, kv_scale  device fp32 scalars (NULL = 1.0); stored = real / scale,
+ *                divided in fp32 (correctly rounded).
+ * fp8 is round-to-nearest-even with finite values beyond 448 saturating to
+ * +-448 (NaN stays NaN).  Tokens writing the same slot race.  Errors: NULL
+ * pointers; num_q_tokens, num_heads or max_pos < 1, num_heads_pad <
+ * num_heads, rope_style not 0 or 1 (MLA_ERR_BAD_SHAPE).
+ */
+mla_status mla_rope_quant_cache(const void* q_latent, const void* q_pe, const void* k_latent,
+                                const void* k_pe, const int32_t* positions, const float* cos_sin,
+                                int max_pos, int rope_style, void* q_out, int num_q_tokens,
+                                int num_heads, int num_heads_pad, void* kv_pool,
+                                int64_t pool_entries, const int32_t* slot_mapping,
+                                const float* q_scale, const float* kv_scale, void* stream);
+
+/*
+ * The step after the decode ("[Kimi-K3 MLA TP8] MLA performance", Sec. 3: a
+ * separate batched GEMM maps the 512-dim latent output back to v_head_dim;
+ * Sec. 2: v_head_dim = 128):
+ *   out[t, h, :] = o_latent[t, h, :] . w_uv[h]^T   for h < num_heads
+ * with fp32 accumulation, rounded to bf16 (nearest even).
+ *
+ *  o_latent  (num_q_tokens, num_heads_pad, 512) bf16: mla_decode's o (the
+ *            pad heads are not read).
+ *  w_uv      (num_heads, 128, 512) bf16: each head's (out, in) weight.
+ *  out       (num_q_tokens, num_heads, 128) bf16, written.
+ * Errors: NULL pointers; num_q_tokens < 1, num_heads outside 1..65535 or
+ * num_heads_pad < num_heads (MLA_ERR_BAD_SHAPE).
+ */
+mla_status mla_latent_to_v(const void* o_latent, const void* w_uv, void* out, int num_q_tokens,
+                           int num_heads, int num_heads_pad, void* stream);
+
+/*
  * Host mirror of the work planner, for tests: given host copies of qo_indptr
  * and kv_indptr, fill `out` (capacity `out_cap` pieces, 8 int64 each:
  * worker, token, head_group, kv_begin, kv_end, unit_len, slot, is_complete)

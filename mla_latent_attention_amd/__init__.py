@@ -25,6 +25,8 @@ __all__ = [
     "decode_cascade",
     "decode_dcp",
     "decode_paged",
+    "rope_quant_cache",
+    "latent_to_v",
     "cascade_workspace_bytes",
     "new_workspace",
     "MLAError",
@@ -378,3 +380,68 @@ def plan_groups_host(qo_indptr, kv_indptr, num_heads: int, num_workers: int,
     return _plan(lambda q, k, g, B, H, nw, out, cap: fn(q, k, g, B, H, nw, c, cp_world_size,
                                                          cp_rank, out, cap),
                  qo_indptr, kv_indptr, num_heads, num_workers, g_kv_indptr)
+
+
+def rope_quant_cache(q_latent, q_pe, k_latent, k_pe, positions, cos_sin, kv_pool, slot_mapping,
+                     *, rope_style: int = 0, num_heads_pad: int | None = None, q_scale=None,
+                     kv_scale=None, q_out=None):
+    """The step before the decode (mla_rope_quant_cache): returns q_out
+    (T, num_heads_pad, 576) float8_e4m3fn and writes each token's new entry
+    to kv_pool[slot_mapping[t]] (negative slots are skipped).
+
+    q_latent (T, H, 512), q_pe (T, H, 64), k_latent (T, 512), k_pe (T, 64)
+    bf16; positions / slot_mapping (T,) int32; cos_sin (max_pos, 64) fp32;
+    kv_pool (N, 576) float8_e4m3fn; scales 0-d fp32 device tensors or None."""
+    dev = q_latent.device
+    if q_latent.dim() != 3 or q_latent.shape[2] != LATENT_DIM:
+        raise ValueError("q_latent must be (T, H, 512)")
+    T, H, _ = q_latent.shape
+    Hp = H if num_heads_pad is None else int(num_heads_pad)
+    _need(q_latent, "q_latent", dev, torch.bfloat16)
+    _need(q_pe, "q_pe", dev, torch.bfloat16, (T, H, 64))
+    _need(k_latent, "k_latent", dev, torch.bfloat16, (T, LATENT_DIM))
+    _need(k_pe, "k_pe", dev, torch.bfloat16, (T, 64))
+    _need(positions, "positions", dev, torch.int32, (T,))
+    _need(slot_mapping, "slot_mapping", dev, torch.int32, (T,))
+    _need(cos_sin, "cos_sin", dev, torch.float32)
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != 64:
+        raise ValueError("cos_sin must be (max_pos, 64)")
+    if kv_pool.dim() == 4:
+        kv_pool = kv_pool.view(-1, ROW_DIM)
+    _need(kv_pool, "kv_pool", dev, torch.float8_e4m3fn)
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_DIM:
+        raise ValueError("kv_pool must be (N, 576)")
+    for name, s in (("q_scale", q_scale), ("kv_scale", kv_scale)):
+        if s is not None:
+            _need(s, name, dev, torch.float32)
+    if q_out is None:
+        q_out = torch.empty((T, Hp, ROW_DIM), dtype=torch.float8_e4m3fn, device=dev)
+    _need(q_out, "q_out", dev, torch.float8_e4m3fn, (T, Hp, ROW_DIM))
+    status = _lib.lib().mla_rope_quant_cache(
+        _ptr(q_latent), _ptr(q_pe), _ptr(k_latent), _ptr(k_pe), _ptr(positions), _ptr(cos_sin),
+        cos_sin.shape[0], int(rope_style), _ptr(q_out), T, H, Hp, _ptr(kv_pool), kv_pool.shape[0],
+        _ptr(slot_mapping), _ptr(q_scale), _ptr(kv_scale), _stream(dev))
+    _lib.check(status, "mla_rope_quant_cache")
+    return q_out
+
+
+def latent_to_v(o_latent, w_uv, *, out=None):
+    """The step after the decode (mla_latent_to_v): out (T, H, 128) bf16 with
+    out[t, h] = o_latent[t, h] . w_uv[h]^T; o_latent (T, H_pad, 512) bf16 (the
+    decode's o, pad heads unread), w_uv (H, 128, 512) bf16."""
+    dev = o_latent.device
+    if o_latent.dim() != 3 or o_latent.shape[2] != LATENT_DIM:
+        raise ValueError("o_latent must be (T, H_pad, 512)")
+    T, Hp, _ = o_latent.shape
+    if w_uv.dim() != 3 or tuple(w_uv.shape[1:]) != (128, LATENT_DIM):
+        raise ValueError("w_uv must be (H, 128, 512)")
+    H = w_uv.shape[0]
+    _need(o_latent, "o_latent", dev, torch.bfloat16)
+    _need(w_uv, "w_uv", dev, torch.bfloat16)
+    if out is None:
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", dev, torch.bfloat16, (T, H, 128))
+    status = _lib.lib().mla_latent_to_v(_ptr(o_latent), _ptr(w_uv), _ptr(out), T, H, Hp,
+                                        _stream(dev))
+    _lib.check(status, "mla_latent_to_v")
+    return out

@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["mla_decode.hip", "mla_decode_groups.hip", "mla_api.hip"]
+SOURCES = ["mla_decode.hip", "mla_decode_groups.hip", "mla_surround.hip", "mla_api.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

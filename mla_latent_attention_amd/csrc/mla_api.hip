@@ -506,4 +506,40 @@ int64_t mla_plan_groups_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   return count;
 }
 
+mla_status mla_rope_quant_cache(const void* q_latent, const void* q_pe, const void* k_latent,
+                                const void* k_pe, const int32_t* positions, const float* cos_sin,
+                                int max_pos, int rope_style, void* q_out, int num_q_tokens,
+                                int num_heads, int num_heads_pad, void* kv_pool,
+                                int64_t pool_entries, const int32_t* slot_mapping,
+                                const float* q_scale, const float* kv_scale, void* stream) {
+  if (!q_latent || !q_pe || !k_latent || !k_pe || !positions || !cos_sin || !q_out || !kv_pool ||
+      !slot_mapping)
+    return MLA_ERR_NULL_POINTER;
+  if (num_q_tokens < 1 || num_heads < 1 || num_heads_pad < num_heads || max_pos < 1 ||
+      pool_entries < 1 || (rope_style != 0 && rope_style != 1))
+    return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)(num_heads_pad + 1) * 72 > 0x7FFFFFFF) return MLA_ERR_BAD_SHAPE;
+  if (mla::launch_rope_quant_cache(
+          static_cast<const uint16_t*>(q_latent), static_cast<const uint16_t*>(q_pe),
+          static_cast<const uint16_t*>(k_latent), static_cast<const uint16_t*>(k_pe), positions,
+          cos_sin, max_pos, rope_style, static_cast<uint8_t*>(q_out), num_q_tokens, num_heads,
+          num_heads_pad, static_cast<uint8_t*>(kv_pool), pool_entries, slot_mapping, q_scale,
+          kv_scale, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+mla_status mla_latent_to_v(const void* o_latent, const void* w_uv, void* out, int num_q_tokens,
+                           int num_heads, int num_heads_pad, void* stream) {
+  if (!o_latent || !w_uv || !out) return MLA_ERR_NULL_POINTER;
+  if (num_q_tokens < 1 || num_heads < 1 || num_heads > 65535 || num_heads_pad < num_heads)
+    return MLA_ERR_BAD_SHAPE;
+  if (mla::launch_latent_to_v(static_cast<const uint16_t*>(o_latent),
+                              static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out),
+                              num_q_tokens, num_heads, num_heads_pad,
+                              static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 }  // extern "C"

@@ -94,4 +94,15 @@ hipError_t launch_decode_groups(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_merge(const void* o_parts, int parts_fp32, const float* lse_parts, int num_parts,
                         int64_t rows, uint16_t* o, float* lse, hipStream_t stream);
 
+// Steps either side of the decode (mla_surround.hip).
+hipError_t launch_rope_quant_cache(const uint16_t* q_latent, const uint16_t* q_pe,
+                                   const uint16_t* k_latent, const uint16_t* k_pe,
+                                   const int32_t* positions, const float* cos_sin, int max_pos,
+                                   int rope_style, uint8_t* q_out, int T, int num_heads,
+                                   int num_heads_pad, uint8_t* kv_pool, int64_t pool_entries,
+                                   const int32_t* slot_mapping, const float* q_scale,
+                                   const float* kv_scale, hipStream_t stream);
+hipError_t launch_latent_to_v(const uint16_t* o_latent, const uint16_t* w_uv, uint16_t* out, int T,
+                              int H, int H_pad, hipStream_t stream);
+
 }  // namespace mla

@@ -158,3 +158,30 @@ def _decode_paged(**over):
 )
 def test_decode_paged_rejects_bad_arguments_before_any_launch(over, status):
     assert _decode_paged(**over) == status
+
+
+def _rope(**over):
+    args = dict(ql=FAKE, qp=FAKE, kl=FAKE, kp=FAKE, pos=FAKE, cs=FAKE, max_pos=100, style=0,
+                q_out=FAKE, T=16, H=12, Hp=16, pool=FAKE, n=1024, slots=FAKE, qs=None, ks=None,
+                stream=None)
+    args.update(over)
+    return _lib.lib().mla_rope_quant_cache(*args.values())
+
+
+@pytest.mark.parametrize(
+    "over,status",
+    [(dict(ql=None), 1), (dict(slots=None), 1), (dict(pool=None), 1), (dict(style=2), 2),
+     (dict(Hp=8), 2), (dict(T=0), 2), (dict(max_pos=0), 2), (dict(n=0), 2)],
+)
+def test_rope_quant_cache_rejects_bad_arguments(over, status):
+    assert _rope(**over) == status
+
+
+@pytest.mark.parametrize(
+    "args,status",
+    [((None, FAKE, FAKE, 16, 12, 16, None), 1), ((FAKE, FAKE, None, 16, 12, 16, None), 1),
+     ((FAKE, FAKE, FAKE, 16, 12, 8, None), 2), ((FAKE, FAKE, FAKE, 0, 12, 16, None), 2),
+     ((FAKE, FAKE, FAKE, 16, 70000, 70000, None), 2)],
+)
+def test_latent_to_v_rejects_bad_arguments(args, status):
+    assert _lib.lib().mla_latent_to_v(*args) == status

@@ -419,3 +419,57 @@ def split_prefix(w: Workload, prefix: int):
                               device=idx.device)
     suf = torch.cat(parts) if sum(lens) else torch.zeros(1, dtype=torch.int32, device=idx.device)
     return pre, suf_indptr, suf
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the steps either side of the decode: the fused rope / fp8 /
+# cache-write step before it and the latent -> v_head_dim GEMM after it.
+# ---------------------------------------------------------------------------
+
+V_HEAD_DIM = 128  # [Issue] Sec. 2
+ROPE_DIM = 64  # [Issue] Sec. 2
+
+
+@dataclass
+class SurroundInputs:
+    q_latent: torch.Tensor  # (T, H, 512) bf16
+    q_pe: torch.Tensor  # (T, H, 64) bf16
+    k_latent: torch.Tensor  # (T, 512) bf16
+    k_pe: torch.Tensor  # (T, 64) bf16
+    positions: torch.Tensor  # (T,) int32
+    cos_sin: torch.Tensor  # (max_pos, 64) fp32: cos of 32 angles, then sin
+    slot_mapping: torch.Tensor  # (T,) int32, distinct pool slots
+    w_uv: torch.Tensor  # (H, 128, 512) bf16
+    q_scale: torch.Tensor  # 0-d fp32
+    kv_scale: torch.Tensor  # 0-d fp32
+
+
+def rope_table(max_pos: int, base: float = 10000.0, device="cpu") -> torch.Tensor:
+    """cos / sin table of the usual rotary frequencies base^(-2j/64), j < 32,
+    at positions 0 .. max_pos-1: (max_pos, 64) fp32 (angles in float64)."""
+    j = torch.arange(ROPE_DIM // 2, dtype=torch.float64)
+    inv = base ** (-2.0 * j / ROPE_DIM)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * inv[None, :]
+    return torch.cat([ang.cos(), ang.sin()], dim=1).to(torch.float32).to(device)
+
+
+def surround(num_tokens: int, num_heads: int, max_pos: int, pool_entries: int, seed: int,
+             device="cpu", scale_range=(0.5, 2.0)) -> SurroundInputs:
+    """Seeded inputs: q parts N(0,1), new cache entries N(0,0.5), positions
+    U{0..max_pos-1}, distinct random slots, W N(0, 1/512) (bf16)."""
+    g = _gen(seed, device)
+    T, H = num_tokens, num_heads
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(shape, generator=g, device=device) * std).to(torch.bfloat16)
+
+    q_latent = randn(T, H, LATENT_DIM)
+    q_pe = randn(T, H, ROPE_DIM)
+    k_latent = randn(T, LATENT_DIM, std=0.5)
+    k_pe = randn(T, ROPE_DIM, std=0.5)
+    positions = torch.randint(0, max_pos, (T,), generator=g, device=device, dtype=torch.int32)
+    slots = torch.randperm(pool_entries, generator=g, device=device)[:T].to(torch.int32)
+    w_uv = randn(H, V_HEAD_DIM, LATENT_DIM, std=LATENT_DIM ** -0.5)
+    return SurroundInputs(q_latent, q_pe, k_latent, k_pe, positions,
+                          rope_table(max_pos, device=device), slots, w_uv,
+                          _scale(scale_range, seed + 4, device), _scale(scale_range, seed + 5, device))
