@@ -49,6 +49,11 @@ def parse():
     ap.add_argument("--only", default=None, choices=sorted(CONFIG_NAMES),
                     help="time just this other configuration and print its line (for profiling)")
     ap.add_argument("--cpu-requests", type=int, default=2, help="requests in the oracle sample")
+    ap.add_argument("--no-cpu-runs", action="store_true",
+                    help="skip the oracle runs at 1 thread / all threads on the tiny, batch-16 and "
+                         "DCP-share samples")
+    ap.add_argument("--oracle-timing", default=None, metavar="NPZ",
+                    help="(child mode) time the float64 oracle on saved arguments and print JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain fp32 copy-like kernel (out = -in) over BYTES, "
                          "to calibrate HBM byte counters, and exit")
@@ -383,6 +388,81 @@ def cpu_baseline(w, n_req):
     return per_call, cores, sample
 
 
+def oracle_timing_child(path):
+    """Child-process mode: the oracle on saved arguments, with the BLAS thread
+    count its environment sets (numpy is imported here, after that is set)."""
+    import numpy as np
+
+    from oracle import mla as omla
+
+    with np.load(path, allow_pickle=False) as d:
+        args = {k: (d[k].item() if d[k].ndim == 0 else d[k]) for k in d.files}
+    try:
+        from threadpoolctl import threadpool_info
+
+        info = threadpool_info()
+        threads = max([int(i.get("num_threads", 1)) for i in info] or [1])
+        blas = ",".join(sorted({f"{i.get('internal_api')}" for i in info})) or "none"
+    except Exception:  # pragma: no cover
+        threads, blas = -1, "unknown"
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        omla.mla_decode(**args)
+        reps += 1
+        if time.perf_counter() - t0 > 5.0 or reps >= 5:
+            break
+    print(json.dumps({"s_per_call": (time.perf_counter() - t0) / reps, "reps": reps,
+                      "threads": threads, "blas": blas}), flush=True)
+
+
+def cpu_baseline_runs(dev, w16, n_req):
+    """The oracle at 1 thread and at all the host's threads, in child processes
+    (the thread count must be set before numpy loads), on the tiny call, a
+    sample of the batch-16 call and a sample of the DCP share."""
+    import subprocess
+    import tempfile
+
+    import numpy as np
+
+    import workloads
+    from oracle import io as oio
+    from workloads import accounting
+
+    cores = len(os.sched_getaffinity(0))
+    cases = []
+    w = workloads.tiny(dev)
+    cases.append(("tiny", w, None, 1.0, accounting.workload_bytes(w), "the whole call"))
+    cases.append(("c16_batch16", w16, list(range(n_req)), w16.batch / n_req,
+                  accounting.workload_bytes(w16),
+                  f"{n_req} of {w16.batch} requests, scaled x{w16.batch / n_req:g}"))
+    w5 = workloads.dcp_share(dev)
+    cases.append(("dcp_share", w5, [0], float(w5.batch), accounting.workload_bytes(w5),
+                  f"1 of {w5.batch} requests, scaled x{w5.batch}"))
+    runs = []
+    with tempfile.TemporaryDirectory() as tmp:
+        for name, w, reqs, scale, nbytes, sample in cases:
+            args = oio.workload_args(w, reqs)
+            args.pop("tokens")
+            path = os.path.join(tmp, f"{name}.npz")
+            np.savez(path, **{k: np.asarray(v) for k, v in args.items()})
+            for threads in (1, cores):
+                env = dict(os.environ, OMP_NUM_THREADS=str(threads),
+                           OPENBLAS_NUM_THREADS=str(threads), MKL_NUM_THREADS=str(threads))
+                r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-timing",
+                                    path], env=env, capture_output=True, text=True, timeout=600)
+                if r.returncode != 0:
+                    raise RuntimeError(f"oracle timing child failed: {r.stderr[-2000:]}")
+                res = json.loads(r.stdout.strip().splitlines()[-1])
+                per_call = res["s_per_call"] * scale
+                runs.append({"config": name, "threads": res["threads"], "blas": res["blas"],
+                             "us_per_call": round(per_call * 1e6, 1),
+                             "GB_s": round(nbytes / per_call / 1e9, 5), "sample": sample,
+                             "reps": res["reps"]})
+    del w5
+    return runs, cores
+
+
 def measured_traffic(variant):
     """HBM bytes per call from the committed counter runs, if they were taken on
     this exact kernel source and workload variant; else None."""
@@ -413,6 +493,9 @@ def stats_us(ev):
 
 def main():
     a = parse()
+    if a.oracle_timing:
+        oracle_timing_child(a.oracle_timing)
+        return
     if a.calibrate_copy:
         calibrate_copy(a.calibrate_copy, max(1, a.steps))
         return
@@ -521,6 +604,10 @@ def main():
         out["cpu_baseline"] = {"value": round(nbytes / per_call / 1e9, 4), "unit": "GB/s",
                                "us_per_call": round(per_call * 1e6, 1), "cores": cores,
                                "kind": "oracle", "sample": sample}
+        if not a.no_cpu_runs:
+            runs, host_cores = cpu_baseline_runs(dev, w0, a.cpu_requests)
+            out["cpu_baseline"]["runs"] = runs
+            out["cpu_baseline"]["host_cores"] = host_cores
     print(json.dumps(out), flush=True)
 
 

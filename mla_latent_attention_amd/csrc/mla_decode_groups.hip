@@ -395,25 +395,28 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
                           seg0 == 0 ? kIdxBatch * kThreads : 0, srows);
     __syncthreads();
     const int ntiles = (srows + kGTile - 1) / kGTile;
-    // Ring of six tiles: P.V takes the tiles in pairs, so a tile's slot is
-    // reused two steps later.  At step t tile t+4 is issued into the slot of
-    // tile t-2 after the barrier that shows every wave done with it, so up to
-    // three later tiles are in flight while tile t is consumed.  Before that
-    // barrier each wave waits until its own loads of tile t have landed.
+    // Ring of six tiles, consumed in pairs (P.V takes two tiles per step).
+    // At the step of pair (t, t+1) one barrier publishes both tiles and shows
+    // every wave done with pair (t-2, t-1), whose slots then take tiles t+4
+    // and t+5, so two later tiles are always in flight and two more are
+    // issued while the pair is consumed.  Before that barrier each wave waits
+    // until its own loads of tiles t and t+1 have landed.
 #pragma unroll
     for (int i = 0; i < kGRing - 2; ++i)
       if (i < ntiles) group_issue(p, sh.idx, srows, i, i, wv, lane);
-    auto publish = [&](int tt) {
-      wait_tiles_in_flight(imin(ntiles - 1, tt + kGRing - 3) - tt);
-      __syncthreads();  // tile tt is in LDS; every wave is done with tile tt-2
-      if (tt + kGRing - 2 < ntiles)
-        group_issue(p, sh.idx, srows, tt + kGRing - 2, (tt + kGRing - 2) % kGRing, wv, lane);
+    auto publish_pair = [&](int tt) {
+      const int last_issued = imin(ntiles - 1, tt + kGRing - 3);
+      wait_tiles_in_flight(last_issued - imin(tt + 1, ntiles - 1));
+      __syncthreads();  // tiles tt, tt+1 are in LDS; every wave is done with tt-2, tt-1
+#pragma unroll
+      for (int k = kGRing - 2; k < kGRing; ++k)
+        if (tt + k < ntiles) group_issue(p, sh.idx, srows, tt + k, (tt + k) % kGRing, wv, lane);
     };
     for (int tt = 0; tt < ntiles; tt += 2) {
       PairP pp;
       const uint8_t* buf0 = g_ring + (tt % kGRing) * kGTileBytes;
       const int base0 = seg0 + tt * kGTile;
-      publish(tt);
+      publish_pair(tt);
       if (base0 < wave_rows) {
         tile_scores<0>(st, pp, q, buf0, off, rows_w - base0, base0 + kGTile <= full_rows, cs, h, sc);
       } else {
@@ -423,10 +426,7 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
       }
       const uint8_t* buf1 = buf0;  // an odd last tile pairs with itself at P = 0
       const int base1 = base0 + kGTile;
-      if (tt + 1 < ntiles) {
-        buf1 = g_ring + ((tt + 1) % kGRing) * kGTileBytes;
-        publish(tt + 1);
-      }
+      if (tt + 1 < ntiles) buf1 = g_ring + ((tt + 1) % kGRing) * kGTileBytes;
       if (tt + 1 < ntiles && base1 < wave_rows) {
         tile_scores<1>(st, pp, q, buf1, off, rows_w - base1, base1 + kGTile <= full_rows, cs, h, sc);
       } else {
