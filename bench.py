@@ -362,8 +362,13 @@ def time_eager(calls, steps, warmup):
     return wall, ev, steps
 
 
-def cpu_baseline(w, n_req):
-    """The float64 oracle on `n_req` full-length requests of the same call."""
+def cpu_baseline(w, n_req, gpu_out=None):
+    """The float64 oracle on `n_req` full-length requests of the same call.
+    gpu_out = (o, lse) of the same call on the GPU: its error against the
+    oracle on those requests is returned too (max abs and row-relative on o,
+    max abs on lse)."""
+    import numpy as np
+
     from oracle import io as oio
 
     try:
@@ -376,7 +381,7 @@ def cpu_baseline(w, n_req):
     t0 = time.perf_counter()
     reps = 0
     while True:
-        oio.call_decode(args)
+        ref = oio.call_decode(args)
         reps += 1
         if time.perf_counter() - t0 > 10.0 or reps >= 3:
             break
@@ -385,7 +390,20 @@ def cpu_baseline(w, n_req):
     rows = sum(w.lengths[:n_req])
     sample = (f"{n_req} of {w.batch} requests ({rows} KV rows x 16 heads), {reps} reps; "
               f"scaled x{w.batch / n_req:g} to one call")
-    return per_call, cores, sample
+    parity = None
+    if gpu_out is not None:
+        o_ref, lse_ref = ref
+        toks = args["tokens"]
+        o = gpu_out[0][toks].float().cpu().numpy().astype(np.float64)
+        lse = gpu_out[1][toks].cpu().numpy().astype(np.float64)
+        err = np.abs(o - o_ref)
+        ref_row = np.abs(o_ref).max(axis=-1)
+        live = ref_row > 0
+        parity = {"tokens": int(len(toks)), "max_abs": float(err.max()),
+                  "row_rel": float((err.max(axis=-1)[live] / ref_row[live]).max()),
+                  "lse_abs": float(np.abs(lse - lse_ref).max()),
+                  "gate": "max_abs <= 1e-2, row_rel <= 2^-7, lse_abs <= 1e-3"}
+    return per_call, cores, sample, parity
 
 
 def oracle_timing_child(path):
@@ -600,10 +618,15 @@ def main():
         torch.cuda.empty_cache()
         out["configs"] = config_lines(mla, dev, max(64, a.steps // 4), 8)
     if not a.no_cpu_baseline:
-        per_call, cores, sample = cpu_baseline(w0, a.cpu_requests)
+        o_chk, lse_chk = mla.decode(w0.q, w0.kv_pool, w0.qo_indptr, w0.kv_indptr, w0.kv_indices,
+                                    w0.kv_last_page_lens, w0.sm_scale, w0.q_scale, w0.kv_scale,
+                                    return_lse=True, max_seqlen_q=1)
+        torch.cuda.synchronize()
+        per_call, cores, sample, parity = cpu_baseline(w0, a.cpu_requests, (o_chk, lse_chk))
         out["cpu_baseline"] = {"value": round(nbytes / per_call / 1e9, 4), "unit": "GB/s",
                                "us_per_call": round(per_call * 1e6, 1), "cores": cores,
                                "kind": "oracle", "sample": sample}
+        out["parity_vs_oracle"] = parity
         if not a.no_cpu_runs:
             runs, host_cores = cpu_baseline_runs(dev, w0, a.cpu_requests)
             out["cpu_baseline"]["runs"] = runs

@@ -57,9 +57,6 @@ __host__ __device__ inline ReqSource source_of(const DecodeParams& p) {
   return s;
 }
 
-// Partial-answer slots per worker: a worker holds at most two partial pieces,
-// each covering one row group, or kGroupsPerUnit (8) row groups in group mode.
-inline int slots_per_worker(bool group_mode) { return group_mode ? 16 : 2; }
 
 // Workspace layout for `num_workers` workers, `slots` partial slots per worker
 // and `num_units` = tokens * head groups (every byte the kernels read is

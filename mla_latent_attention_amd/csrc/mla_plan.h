@@ -226,6 +226,10 @@ MLA_HD bool cursor_next_unit(Cursor& c, const ReqSource& src, int B, int G) {
 constexpr int kGroupsPerUnit = 8;
 constexpr int kGroupModeMinRows = 4;
 
+// Partial-answer slots per worker: a worker holds at most two partial pieces,
+// each covering one row group, or kGroupsPerUnit row groups in group mode.
+MLA_HD int slots_per_worker(bool group_mode) { return group_mode ? 2 * kGroupsPerUnit : 2; }
+
 MLA_HD bool use_group_mode(int G, int max_seqlen_q) {
   return (int64_t)G * max_seqlen_q >= kGroupModeMinRows;
 }

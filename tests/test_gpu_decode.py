@@ -128,6 +128,39 @@ def test_multi_token_causal_many_heads():
         check(w, num_workers=nw, where=f"mt-96 nw={nw}")
 
 
+@pytest.mark.parametrize("dtype,heads", [("fp8", 16), ("fp8", 96), ("bf16", 16)])
+def test_multi_token_call_equals_truncated_single_token_calls(dtype, heads):
+    """Draft token j of qlen sees the first n - (qlen - 1 - j) entries: the
+    multi-token call and single-token calls over those prefixes (different
+    kernels: group mode vs the standard one for fp8) must both match the
+    oracle's row for that token.  (Each is compared with the oracle, not with
+    the other: two bf16 results can differ by twice the gate.)"""
+    w = workloads.build(f"trunc-{dtype}-{heads}", [1500, 2999], num_heads=heads,
+                        real_heads=heads, qlens=[4, 3], pool_entries=8192, kv_std=0.5,
+                        scale_range=(0.5, 2.0), dtype=dtype, seed=17, device=DEV)
+    o, lse = run(w)
+    toks, o_ref, lse_ref = oracle(w)
+    assert list(toks) == list(range(w.num_tokens))
+    assert_gate(metrics(o, o_ref, lse, lse_ref), f"{dtype} {heads} heads: multi-token call")
+    kvp = w.kv_indptr.cpu().tolist()
+    qo = w.qo_indptr.cpu().tolist()
+    for b in range(2):
+        n, ql = kvp[b + 1] - kvp[b], qo[b + 1] - qo[b]
+        for j in range(ql):
+            vis = n - (ql - 1 - j)
+            t = qo[b] + j
+            one = workloads.Workload(**{
+                **w.__dict__, "q": w.q[t:t + 1].contiguous(),
+                "qo_indptr": torch.tensor([0, 1], dtype=torch.int32, device=DEV),
+                "kv_indptr": torch.tensor([0, vis], dtype=torch.int32, device=DEV),
+                "kv_indices": w.kv_indices[kvp[b]: kvp[b] + vis].contiguous(),
+                "kv_last_page_lens": w.kv_last_page_lens[:1], "lengths": [vis], "qlens": [1],
+                "max_seqlen_q": 1})
+            o1, l1 = run(one)
+            m = metrics(o1, o_ref[t:t + 1], l1, lse_ref[t:t + 1])
+            assert_gate(m, f"{dtype} {heads} heads: request {b} token {j} as a single-token call")
+
+
 def test_peaky_scores():
     """Stress case outside the benchmark distributions: |o| reaches ~5, where a
     bf16 unit in the last place (2^-5) exceeds 1e-2, so the absolute bound is
