@@ -231,9 +231,10 @@ mla_status mla_decode(const void* q, int q_dtype, const void* kv_pool, int kv_dt
 
 namespace {
 
-// Cascade workspace: one decode workspace (either pass, one after the other
-// on the stream) followed by the two passes' outputs, fp32 o and lse (fp32 o
-// keeps the merge from adding a third bf16 rounding to the result).
+// Cascade workspace: the group-mode decode workspace for the one-launch call
+// (2T virtual tokens), followed by its fp32 outputs, parts (2, T, H, 512) and
+// lse_parts (2, T, H): prefix first, suffix second (fp32 keeps the merge from
+// adding a third bf16 rounding to the result).
 struct CascadeLayout {
   size_t decode_bytes, parts_off, lse_off, total;
 };
@@ -241,15 +242,14 @@ struct CascadeLayout {
 CascadeLayout cascade_layout(int batch, int num_q_tokens, int num_heads, int max_seqlen_q,
                              int cus) {
   const int G = num_heads / mla::kGroup;
-  const int64_t units = (int64_t)num_q_tokens * G;
-  const size_t prefix = mla::workspace_bytes(cus, units, mla::slots_per_worker(true));
-  const size_t suffix = mla::workspace_bytes(cus, units, slots_for(num_heads, max_seqlen_q));
+  const int64_t units = 2 * (int64_t)num_q_tokens * G;
   CascadeLayout l;
-  l.decode_bytes = mla::align256(prefix > suffix ? prefix : suffix);
+  l.decode_bytes = mla::align256(mla::workspace_bytes(cus, units, mla::slots_per_worker(true)));
   l.parts_off = l.decode_bytes;
   l.lse_off = l.parts_off + mla::align256((size_t)2 * num_q_tokens * num_heads * mla::kLatent * 4);
   l.total = l.lse_off + mla::align256((size_t)2 * num_q_tokens * num_heads * 4);
   (void)batch;
+  (void)max_seqlen_q;
   return l;
 }
 
@@ -288,8 +288,8 @@ mla_status mla_decode_cascade(const void* q, int q_dtype, const void* kv_pool, i
   if (num_heads <= 0 || num_heads % mla::kGroup != 0) return MLA_ERR_UNSUPPORTED;
   const int T = num_q_tokens;
   if (!shape_ok(batch, T, num_heads, max_seqlen_q)) return MLA_ERR_BAD_SHAPE;
-  if (pool_entries < 1 || prefix_len < 0 || prefix_len > 0x7FFFFFFF || suffix_indices_len < 0 ||
-      suffix_indices_len > 0x7FFFFFFF)
+  if (pool_entries < 1 || prefix_len < 0 || suffix_indices_len < 0 ||
+      prefix_len + suffix_indices_len > 0x7FFFFFFF || T > (1 << 29) || batch > (1 << 29))
     return MLA_ERR_BAD_SHAPE;
   const int cus = current_cu_count();
   if (cus <= 0) return MLA_ERR_HIP;
@@ -314,32 +314,27 @@ mla_status mla_decode_cascade(const void* q, int q_dtype, const void* kv_pool, i
   p.kv_scale = kv_scale;
   p.num_workers = cus;
 
-  // Pass 1: every token against the shared prefix, as one request whose
-  // tokens all see every entry (group mode: eight row groups per gather).
+  // One group-mode launch over the cascade view (see ReqSource): request 0
+  // is every token (virtual tokens 0 .. T-1) against the prefix, all entries
+  // visible, so each prefix row is gathered once per eight row groups of the
+  // whole batch; requests 1 .. B are the caller's requests again (virtual
+  // tokens T .. 2T-1) against their suffixes, causal.  The two passes share
+  // one balanced work stream and one split combine, and their fp32 outputs
+  // land in parts[0] and parts[1].
   p.o = nullptr;
-  p.o32 = parts;  // both passes keep fp32 outputs for the merge
+  p.o32 = parts;
   p.lse = lse_parts;
-  p.qo_indptr = nullptr;
-  p.kv_indptr = nullptr;
-  p.kv_indices = prefix_indices;
-  p.kv_indices_len = (int)prefix_len;
-  p.batch = 1;
-  p.causal = 0;
-  set_workspace(p, ws, units, mla::slots_per_worker(true));
-  if (mla::launch_decode(p, 0, true, st) != hipSuccess) return MLA_ERR_HIP;
-
-  // Pass 2: each request's own entries, causal (the usual kernels).
-  const bool group = mla::use_group_mode(G, max_seqlen_q);
-  p.o32 = parts + rows * mla::kLatent;
-  p.lse = lse_parts + rows;
   p.qo_indptr = qo_indptr;
   p.kv_indptr = suffix_indptr;
-  p.kv_indices = suffix_indices;
-  p.kv_indices_len = (int)suffix_indices_len;
-  p.batch = batch;
+  p.kv_indices = prefix_indices;
+  p.kv_indices2 = suffix_indices;
+  p.cascade_prefix = (int)prefix_len;
+  p.kv_indices_len = (int)(prefix_len + suffix_indices_len);
+  p.batch = batch + 1;
+  p.num_tokens = 2 * T;
   p.causal = 1;
-  set_workspace(p, ws, units, slots_for(num_heads, max_seqlen_q));
-  if (mla::launch_decode(p, 0, group, st) != hipSuccess) return MLA_ERR_HIP;
+  set_workspace(p, ws, 2 * units, mla::slots_per_worker(true));
+  if (mla::launch_decode(p, 0, true, st) != hipSuccess) return MLA_ERR_HIP;
 
   // LSE merge of the two passes (a pass that saw nothing has lse = -inf).
   if (mla::launch_merge(parts, 1, lse_parts, 2, rows, static_cast<uint16_t*>(o),

@@ -300,7 +300,7 @@ __device__ __forceinline__ void pair_pv(WideState& st, const PairP& pp, const ui
 // length L).  slot_base < 0: the piece is the whole unit and every row group
 // writes o / lse; else row group i of the unit writes partial slot
 // slot_base + i.
-template <bool kPaged>
+template <bool kPaged, bool kCascade>
 __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& sh,
                                             const GCursor& c, int G, int L, int len,
                                             int slot_base, int w, float cs, float ks) {
@@ -326,6 +326,9 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   const int rgc = imin(rg, R - 1);
   const int j = rgc / G, g = rgc - j * G;
   const int t = c.r.q_base + j;
+  // The q row: in a one-launch cascade call tokens T .. 2T-1 (the suffix
+  // requests) are the caller's tokens 0 .. T-1 again.
+  const int qtok = (kCascade && t >= (p.num_tokens >> 1)) ? t - (p.num_tokens >> 1) : t;
   const int vw = half ? vis_h[1] : vis_h[0];
   const int rows_w = half ? rows_h[1] : rows_h[0];
 
@@ -349,11 +352,11 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   v8i_t q[9];
   {
     const uint8_t* qrow =
-        p.q + ((int64_t)t * p.num_heads + g * kGroup + n16) * kRowDim + 32 * h;
+        p.q + ((int64_t)qtok * p.num_heads + g * kGroup + n16) * kRowDim + 32 * h;
     uint4 xq[18];
 #pragma unroll
     for (int i = 0; i < 18; ++i) xq[i] = *(const uint4*)(qrow + 64 * (i >> 1) + 16 * (i & 1));
-    stage_first_indices<kPaged>(sh.idx, p, src, imin(len, kGIdxSeg));
+    stage_first_indices<kPaged, kThreads, kCascade>(sh.idx, p, src, imin(len, kGIdxSeg));
 #pragma unroll
     for (int cc = 0; cc < 9; ++cc) {
       const uint4 a0 = xq[2 * cc], a1 = xq[2 * cc + 1];
@@ -391,8 +394,8 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   for (int seg0 = 0; seg0 < len; seg0 += kGIdxSeg) {
     const int srows = imin(kGIdxSeg, len - seg0);
     if (seg0 > 0) __syncthreads();  // the previous segment is done with the indices
-    stage_indices<kPaged>(sh.idx, p, src.template at<kPaged>(seg0),
-                          seg0 == 0 ? kIdxBatch * kThreads : 0, srows);
+    stage_indices<kPaged, kThreads, kCascade>(sh.idx, p, src.template at<kPaged>(seg0),
+                                              seg0 == 0 ? kIdxBatch * kThreads : 0, srows);
     __syncthreads();
     const int ntiles = (srows + kGTile - 1) / kGTile;
     // Ring of six tiles, consumed in pairs (P.V takes two tiles per step).
@@ -515,12 +518,12 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
 }
 
 // One worker: locate its share of the group-mode stream and run its pieces.
-template <bool kPaged>
+template <bool kPaged, bool kCascade>
 __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared& sh) {
   const int G = p.num_heads / kGroup;
 
   // Pass 1 over requests: stream length W; zero this block's empty tokens.
-  const ReqSource src = source_of<kPaged>(p);
+  const ReqSource src = source_of<kPaged, kCascade>(p);
   int64_t acc = 0;
   for (int b = threadIdx.x; b < p.batch; b += kThreads) {
     const Req r = load_req(src, b);
@@ -536,8 +539,8 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
   if (w >= nw) return;
   const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
   const int64_t xs[2] = {x0, x1 < W ? x1 : -1};
-  plan_locate2<kPaged>(p, [G](const Req& r) { return group_request_rows(r, G); }, xs, sh.red, sh.pb,
-               sh.pcum);
+  plan_locate2<kPaged, kThreads, kCascade>(p, [G](const Req& r) { return group_request_rows(r, G); },
+                                           xs, sh.red, sh.pb, sh.pcum);
   const int b0 = uniform(sh.pb[0]), b1 = uniform(sh.pb[1]);
   if (b0 < 0 || b1 == -1) return;  // not reached with consistent indptr
   GCursor c;
@@ -571,7 +574,7 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
     const bool complete = (c.k == 0 && len == L);
     const int slot_base =
         complete ? -1 : kGSlotsPerPiece * (2 * w + (piece == 0 ? 0 : 1));
-    group_piece<kPaged>(p, sh, c, G, L, len, slot_base, w, cs, ks);
+    group_piece<kPaged, kCascade>(p, sh, c, G, L, len, slot_base, w, cs, ks);
     pos += len;
     c.k += len;
     ++piece;
@@ -587,18 +590,28 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_groups_fp8_kernel(const DecodeParams p) {
   __shared__ GroupShared sh;
-  group_worker<false>(p, sh);
+  group_worker<false, false>(p, sh);
 }
 
 // The paged-cache build (page_size > 1).
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_groups_fp8_paged_kernel(const DecodeParams p) {
   __shared__ GroupShared sh;
-  group_worker<true>(p, sh);
+  group_worker<true, false>(p, sh);
+}
+
+// The one-launch shared-prefix (cascade) build.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_groups_fp8_cascade_kernel(const DecodeParams p) {
+  __shared__ GroupShared sh;
+  group_worker<false, true>(p, sh);
 }
 
 hipError_t launch_decode_groups(const DecodeParams& p, hipStream_t stream) {
-  if (p.page_shift > 0)
+  if (p.cascade_prefix >= 0)
+    hipLaunchKernelGGL(mla_decode_groups_fp8_cascade_kernel, dim3(p.num_workers), dim3(kThreads), 0,
+                       stream, p);
+  else if (p.page_shift > 0)
     hipLaunchKernelGGL(mla_decode_groups_fp8_paged_kernel, dim3(p.num_workers), dim3(kThreads), 0,
                        stream, p);
   else

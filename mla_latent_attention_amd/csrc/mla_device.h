@@ -125,11 +125,11 @@ __device__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) 
 // not looked up), where request r holds rows_of(r) stream rows: sb[i] =
 // request (-1 if not found, -2 if not looked up) and scum[i] = that request's
 // first stream position.
-template <bool kPaged, int kT = kThreads, class RowsOf>
+template <bool kPaged, int kT = kThreads, bool kCascade = false, class RowsOf>
 __device__ void plan_locate2(const DecodeParams& p, RowsOf rows_of, const int64_t (&x)[2],
                              int64_t* red, int* sb, int64_t* scum) {
   if (threadIdx.x < 2) sb[threadIdx.x] = x[threadIdx.x] < 0 ? -2 : -1;
-  const ReqSource src = source_of<kPaged>(p);
+  const ReqSource src = source_of<kPaged, kCascade>(p);
   int64_t carry = 0;
   for (int b0 = 0; b0 < p.batch; b0 += kT) {
     const int b = b0 + threadIdx.x;
@@ -234,12 +234,21 @@ __device__ __forceinline__ int32_t paged_row(const int32_t* pages, int shift, in
   return (int32_t)(((uint32_t)pages[e >> shift] << shift) | (uint32_t)(e & ((1 << shift) - 1)));
 }
 
+// Where index ib lives: kv_indices, or in a one-launch cascade call the
+// suffixes' buffer past the prefix (a piece never straddles the two).
+template <bool kCascade>
+__device__ __forceinline__ const int32_t* index_base(const DecodeParams& p, int ib) {
+  if constexpr (kCascade)
+    return ib < p.cascade_prefix ? p.kv_indices + ib : p.kv_indices2 + (ib - p.cascade_prefix);
+  return p.kv_indices + ib;
+}
+
 // Rows of entries [0, n) of src (first kIdxBatch * kT of them) to idx_dst.
-template <bool kPaged, int kT = kThreads>
+template <bool kPaged, int kT = kThreads, bool kCascade = false>
 __device__ __forceinline__ void stage_first_indices(int32_t* idx_dst, const DecodeParams& p,
                                                     RowSrc src, int n) {
   int32_t iv[kIdxBatch];
-  const int32_t* base = p.kv_indices + src.ib;
+  const int32_t* base = index_base<kCascade>(p, src.ib);
   if constexpr (!kPaged) {
 #pragma unroll
     for (int j = 0; j < kIdxBatch; ++j) iv[j] = base[imin(j * kT + (int)threadIdx.x, n - 1)];
@@ -265,10 +274,10 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&a)[8])
 // of dst.  Each thread issues kIdxBatch loads before its first store
 // (past-the-end positions reload the last index), so a segment costs one
 // memory round trip per 2048 indices instead of one per 256.
-template <bool kPaged, int kT = kThreads>
+template <bool kPaged, int kT = kThreads, bool kCascade = false>
 __device__ __forceinline__ void stage_indices(int32_t* dst, const DecodeParams& p, RowSrc src,
                                               int from, int n) {
-  const int32_t* base = p.kv_indices + src.ib;
+  const int32_t* base = index_base<kCascade>(p, src.ib);
   for (int i0 = from; i0 < n; i0 += kT * kIdxBatch) {
     int32_t v[kIdxBatch];
     if constexpr (!kPaged) {

@@ -37,23 +37,29 @@ struct DecodeParams {
   int cp_rank = 0;                        // this shard
   const int32_t* last_page_lens = nullptr;  // (B) paged caches: used slots of the last page
   int page_shift = 0;                     // log2(page_size); 0: kv_indices name entries
+  // Shared-prefix (cascade) call in one group-mode launch (the ReqSource
+  // cascade view): entries [0, cascade_prefix) come from kv_indices (the
+  // prefix), the rest from kv_indices2 (the suffixes); -1: off.
+  int cascade_prefix = -1;
+  const int32_t* kv_indices2 = nullptr;
 };
 
-// The planner's view of the call's requests.  kPaged = false builds drop the
-// paging fields as constants (page_size 1).
-template <bool kPaged>
+// The planner's view of the call's requests.  Builds without kPaged /
+// kCascade drop those fields as constants.
+template <bool kPaged, bool kCascade = false>
 __host__ __device__ inline ReqSource source_of(const DecodeParams& p) {
   ReqSource s;
   s.qo = p.qo_indptr;
   s.kvp = p.kv_indptr;
-  s.gkvp = p.g_kv_indptr;
+  s.gkvp = kCascade ? nullptr : p.g_kv_indptr;  // a cascade call is never a DCP shard
   s.kv_cap = p.kv_indices_len;
   s.T = p.num_tokens;
   s.causal = p.causal;
-  s.cp_size = p.cp_size;
-  s.cp_rank = p.cp_rank;
+  s.cp_size = kCascade ? 1 : p.cp_size;
+  s.cp_rank = kCascade ? 0 : p.cp_rank;
   s.lpl = kPaged ? p.last_page_lens : nullptr;
   s.page_shift = kPaged ? p.page_shift : 0;
+  s.prefix_len = kCascade ? p.cascade_prefix : -1;
   return s;
 }
 

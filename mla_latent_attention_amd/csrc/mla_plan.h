@@ -98,6 +98,13 @@ struct ReqSource {
   int cp_rank;          // this shard
   const int32_t* lpl;   // (B) used slots of each request's last page (paged caches)
   int page_shift;       // log2(page_size); 0: one entry per index
+  // Shared-prefix (cascade) view, on when prefix_len >= 0: the caller's B
+  // requests become B + 1 over 2T tokens.  Request 0 is every token (tokens
+  // 0 .. T-1) against entries [0, prefix_len), all visible; request b + 1 is
+  // request b's tokens (T + qo[b] ..) against its own entries prefix_len +
+  // kvp[b] .., under `causal`.  qo / kvp are then the caller's qo_indptr and
+  // suffix offsets, and T above is the ReqSource's T / 2.
+  int prefix_len;
 };
 
 // One request's bounds, clamped so that no later read can leave its buffer,
@@ -114,8 +121,27 @@ struct Req {
 };
 
 MLA_HD Req load_req(const ReqSource& s, int b) {
-  int k0 = s.kvp ? s.kvp[b] : 0, k1 = s.kvp ? s.kvp[b + 1] : s.kv_cap;
-  int q0 = s.qo ? s.qo[b] : 0, q1 = s.qo ? s.qo[b + 1] : s.T;
+  int k0, k1, q0, q1, causal = s.causal;
+  if (s.prefix_len >= 0) {  // cascade view
+    const int T = s.T / 2, P = imin(s.prefix_len, s.kv_cap);
+    if (b == 0) {
+      k0 = 0;
+      k1 = P;
+      q0 = 0;
+      q1 = T;
+      causal = 0;
+    } else {
+      k0 = imax(P + s.kvp[b - 1], P);
+      k1 = P + s.kvp[b];
+      q0 = imax(T + s.qo[b - 1], T);
+      q1 = T + s.qo[b];
+    }
+  } else {
+    k0 = s.kvp ? s.kvp[b] : 0;
+    k1 = s.kvp ? s.kvp[b + 1] : s.kv_cap;
+    q0 = s.qo ? s.qo[b] : 0;
+    q1 = s.qo ? s.qo[b + 1] : s.T;
+  }
   k0 = imin(imax(k0, 0), s.kv_cap);
   k1 = imin(imax(k1, k0), s.kv_cap);
   q0 = imin(imax(q0, 0), s.T);
@@ -129,7 +155,7 @@ MLA_HD Req load_req(const ReqSource& s, int b) {
   }
   r.q_base = q0;
   r.qlen = q1 - q0;
-  r.causal = s.causal;
+  r.causal = causal;
   if (s.gkvp) {
     const int N = imax(s.gkvp[b + 1] - s.gkvp[b], 0);
     r.vbase = N - r.qlen - s.cp_rank;

@@ -26,7 +26,8 @@ inline int64_t plan_pieces_host(const int32_t* qo_indptr, const int32_t* kv_indp
   const int T = qo_indptr[batch];
   const int kv_cap = kv_indptr[batch];
   if (T < 0 || kv_cap < 0) return -1;
-  const ReqSource src{qo_indptr, kv_indptr, g_kv_indptr, kv_cap, T, 1, cp_world_size, cp_rank};
+  const ReqSource src{qo_indptr, kv_indptr, g_kv_indptr, kv_cap, T, 1, cp_world_size, cp_rank,
+                      nullptr, 0, -1};
   std::vector<int64_t> cum(batch + 1, 0);
   for (int b = 0; b < batch; ++b) cum[b + 1] = cum[b] + (int64_t)G * request_rows(load_req(src, b));
   const int64_t W = cum[batch];
@@ -98,7 +99,7 @@ inline int64_t plan_group_pieces_host(const int32_t* qo_indptr, const int32_t* k
   const int kv_cap = kv_indptr[batch];
   if (T < 0 || kv_cap < 0) return -1;
   const ReqSource src{qo_indptr, kv_indptr, g_kv_indptr, kv_cap, T, causal ? 1 : 0, cp_world_size,
-                      cp_rank};
+                      cp_rank, nullptr, 0, -1};
   std::vector<int64_t> cum(batch + 1, 0);
   for (int b = 0; b < batch; ++b) cum[b + 1] = cum[b] + group_request_rows(load_req(src, b), G);
   const int64_t W = cum[batch];

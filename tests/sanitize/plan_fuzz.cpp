@@ -72,7 +72,7 @@ int main() {
     const int32_t* g = dcp ? gkv.data() : nullptr;
     const int w_cp = dcp ? cps : 1, r_cp = dcp ? cpr : 0;
     // Expected stream lengths from the planner's own request view.
-    mla::ReqSource src{qo.data(), kv.data(), g, kv[B], qo[B], 1, w_cp, r_cp, nullptr, 0};
+    mla::ReqSource src{qo.data(), kv.data(), g, kv[B], qo[B], 1, w_cp, r_cp, nullptr, 0, -1};
     int64_t W = 0, Wg = 0;
     for (int b = 0; b < B; ++b) W += (int64_t)G * mla::request_rows(mla::load_req(src, b));
     src.causal = causal;

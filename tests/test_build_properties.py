@@ -17,6 +17,11 @@
   within one instruction.
 * Packed-fp32 VALU instructions are disabled for device code by a build flag;
   none may appear in the output.
+* No register spill is stored while a divergent branch's narrowed exec mask
+  is still in force at the branch's join (a scratch store right before the
+  exec restore): only the branch's lanes would save the value, and the other
+  lanes would reload stale data.  One kernel build showed exactly that (its
+  partial-slot index was saved for one lane), so every build is scanned.
 """
 
 import os
@@ -144,3 +149,26 @@ def test_mixed_chain_detector_flags_a_mixed_chain():
 def test_no_packed_fp32_valu(which, request):
     asm, _ = request.getfixturevalue(which)
     assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", asm)
+
+
+def _spill_before_exec_restore(asm):
+    """(line, text) of scratch stores directly followed by an exec restore."""
+    hits, prev = [], None
+    for n, line in enumerate(asm.splitlines()):
+        t = line.strip()
+        if prev is not None and t.startswith("s_or_b64 exec, exec"):
+            hits.append(prev)
+        prev = (n, t) if t.startswith("scratch_store") else None
+    return hits
+
+
+def test_no_spill_store_under_a_narrowed_exec_mask(compiled, compiled_groups):
+    for asm, _ in (compiled, compiled_groups):
+        assert _spill_before_exec_restore(asm) == []
+
+
+def test_spill_scanner_flags_the_pattern():
+    asm = "\n".join(["  v_add_u32_e32 v10, s4, v3", "  s_and_saveexec_b64 s[12:13], s[16:17]",
+                      ".LBB0_1:", "  scratch_store_dword off, v10, off", "  s_or_b64 exec, exec, s[12:13]"])
+    assert len(_spill_before_exec_restore(asm)) == 1
+    assert _spill_before_exec_restore(asm.replace("scratch_store_dword", "v_mov_b32")) == []

@@ -213,6 +213,16 @@ def test_group_mode_units_span_tokens(nw):
         assert torch.all(o[t] == 0) and torch.all(torch.isneginf(lse[t]))
 
 
+@pytest.mark.parametrize("nw", [0, 3])
+def test_group_mode_single_row_group_requests(nw):
+    """16 heads with one 4-token request forces group mode; the single-token
+    requests then form units of one row group (seven of eight idle)."""
+    w = workloads.build("group-r1", [900, 2100, 5, 0, 3001, 1], num_heads=16, real_heads=12,
+                        qlens=[1, 4, 1, 1, 1, 1], pool_entries=8192, kv_std=0.5,
+                        scale_range=(0.5, 2.0), seed=19, device=DEV)
+    check(w, num_workers=nw, where=f"group mode, one-row-group units, nw={nw}")
+
+
 def test_group_mode_pad_heads_bitwise_and_deterministic():
     w = workloads.build("group-pad", [3000, 1234, 77], num_heads=64, real_heads=60,
                         qlens=[2, 1, 2], pool_entries=8192, seed=23, device=DEV)
