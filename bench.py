@@ -104,13 +104,14 @@ def with_indices(layers, variant, dev):
     return [workloads.Workload(**{**w.__dict__, "kv_indices": idx}) for w in layers]
 
 
-def with_pages(layers, page_size, dev):
+def with_pages(layers, page_size, dev, shared=True):
     """The same layers as a paged call: a page table of page_size-slot pages
-    (the prefix's whole pages shared, the rest of each request in its own)."""
+    (the prefix's whole pages shared, or none with shared=False; the rest of
+    each request in its own pages)."""
     import workloads
 
     kvp, idx, last = workloads.make_paged_indices(layers[0].lengths, page_size,
-                                                  workloads.SHARED_PREFIX,
+                                                  workloads.SHARED_PREFIX if shared else 0,
                                                   layers[0].kv_pool.shape[0], 2000 + 3, dev)
     return [workloads.Workload(**{**w.__dict__, "kv_indptr": kvp, "kv_indices": idx,
                                   "kv_last_page_lens": last, "page_size": page_size})
@@ -604,14 +605,15 @@ def main():
                                          "pct_of_8TBs": round(100 * nbytes / wv / 1e9 / PEAK_GBS, 2)}
         # The same call through mla_decode_paged with 128-slot pages (one index
         # per page instead of one per entry).
-        paged = with_pages(layers, 128, dev)
-        pbytes = accounting.workload_bytes(paged[0])
-        wp, evp, _ = timer(make_calls(mla, paged, o, ws), max(16, a.steps // 4), a.warmup)
-        variants["paged128"] = {"us_per_call": round(wp * 1e6, 2),
-                                "algorithmic_bytes_per_call": pbytes,
-                                "GB_s": round(pbytes / wp / 1e9, 2),
-                                "pct_of_8TBs": round(100 * pbytes / wp / 1e9 / PEAK_GBS, 2)}
-        del paged
+        for name, shared in (("paged128", True), ("paged128_unshared_prefix", False)):
+            paged = with_pages(layers, 128, dev, shared)
+            pbytes = accounting.workload_bytes(paged[0])
+            wp, evp, _ = timer(make_calls(mla, paged, o, ws), max(16, a.steps // 4), a.warmup)
+            variants[name] = {"us_per_call": round(wp * 1e6, 2),
+                              "algorithmic_bytes_per_call": pbytes,
+                              "GB_s": round(pbytes / wp / 1e9, 2),
+                              "pct_of_8TBs": round(100 * pbytes / wp / 1e9 / PEAK_GBS, 2)}
+            del paged
         out["variants"] = variants
     if not a.no_configs:
         del calls, layers
