@@ -161,6 +161,33 @@ def test_multi_token_call_equals_truncated_single_token_calls(dtype, heads):
             assert_gate(m, f"{dtype} {heads} heads: request {b} token {j} as a single-token call")
 
 
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_largest_draft_length_and_head_count(dtype):
+    """max_seqlen_q = 64 (the largest accepted) with 128 heads: early draft
+    tokens of short requests see nothing; fp8 runs in group mode (64 row
+    groups of 8 head groups), bf16 in the standard kernel."""
+    w = workloads.build(f"max-{dtype}", [5000, 70, 40, 0], num_heads=128, real_heads=128,
+                        qlens=[64, 1, 33, 2], pool_entries=8192, kv_std=0.5,
+                        scale_range=(0.5, 2.0), dtype=dtype, seed=27, device=DEV)
+    o, lse, _ = check(w, where=f"qlen 64, 128 heads, {dtype}")
+    T0 = 64 + 1  # request 2's first token
+    assert torch.all(torch.isfinite(lse[T0 + 32]))  # its last token sees all 40 entries
+    assert torch.all(lse[-2:] == -float("inf"))  # request 3 has no entries
+
+
+def test_many_requests_span_several_planner_chunks():
+    """700 requests (the planner scans requests 256 at a time per workgroup)
+    with ragged lengths, some empty."""
+    rng = np.random.default_rng(29)
+    lengths = [int(x) for x in rng.integers(0, 400, size=700)]
+    for i in range(0, 700, 37):
+        lengths[i] = 0
+    w = workloads.build("many-requests", lengths, num_heads=16, real_heads=12,
+                        pool_entries=1 << 18, kv_std=0.5, scale_range=(0.5, 2.0), seed=28,
+                        device=DEV)
+    check(w, requests=[0, 1, 255, 256, 257, 511, 512, 699], where="700 requests")
+
+
 def test_peaky_scores():
     """Stress case outside the benchmark distributions: |o| reaches ~5, where a
     bf16 unit in the last place (2^-5) exceeds 1e-2, so the absolute bound is
