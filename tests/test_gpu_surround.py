@@ -117,3 +117,64 @@ def test_layer_chain_matches_the_oracle_chain():
     rel = float((np.abs(got - v_ref).max(axis=-1) / np.abs(v_ref).max(axis=-1)).max())
     say(f"[chain] latent_to_v row rel {rel:.3e}")
     assert rel <= 2.0 ** -7
+
+
+def test_layer_step_graph_replay_matches_eager_bitwise():
+    """rope -> paged decode -> latent_to_v, and a DCP-shard decode, captured in
+    one HIP graph and replayed (with eager work in between): every replay
+    gives the eager results bit for bit."""
+    T, H, Hp = 4, 12, 16
+    w = workloads.build("graph-paged", [700, 900, 300, 1200], num_heads=Hp, real_heads=H,
+                        pool_entries=1 << 14, kv_std=0.5, scale_range=(0.5, 2.0), seed=120,
+                        device=DEV, page_size=128)
+    s = workloads.surround(T, H, 4096, 1 << 14, seed=121, device=DEV)
+    kvp = w.kv_indptr.cpu().tolist()
+    last = w.kv_last_page_lens.cpu().tolist()
+    # each request's new entry is the last slot of its last page
+    slots = torch.tensor([int(w.kv_indices[kvp[b + 1] - 1]) * 128 + last[b] - 1 for b in range(T)],
+                         dtype=torch.int32, device=DEV)
+    full = workloads.build("graph-dcp", [801, 77], num_heads=16, real_heads=12, qlens=[3, 1],
+                           pool_entries=4096, kv_std=0.5, seed=122, device=DEV)
+    sh = workloads.dcp_shard(full, 4, 2)
+    q = torch.empty((T, Hp, 576), dtype=torch.float8_e4m3fn, device=DEV)
+    o = torch.empty((T, Hp, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((T, Hp), dtype=torch.float32, device=DEV)
+    v = torch.empty((T, H, 128), dtype=torch.bfloat16, device=DEV)
+    o2 = torch.empty((sh.num_tokens, 16, 512), dtype=torch.bfloat16, device=DEV)
+    lse2 = torch.empty((sh.num_tokens, 16), dtype=torch.float32, device=DEV)
+    ws = mla.new_workspace(mla.workspace_bytes(T, T, Hp, 1), DEV)
+    ws2 = mla.new_workspace(mla.workspace_bytes(2, sh.num_tokens, 16, 3), DEV)
+
+    def step():
+        mla.rope_quant_cache(s.q_latent, s.q_pe, s.k_latent, s.k_pe, s.positions, s.cos_sin,
+                             w.kv_pool, slots, num_heads_pad=Hp, q_scale=w.q_scale,
+                             kv_scale=w.kv_scale, q_out=q)
+        mla.decode_paged(q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                         w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale,
+                         return_lse=True, page_size=128, o=o, lse=lse, max_seqlen_q=1,
+                         workspace=ws)
+        mla.latent_to_v(o, s.w_uv, out=v)
+        mla.decode_dcp(sh.q, sh.kv_pool, sh.qo_indptr, sh.kv_indptr, sh.kv_indices, None,
+                       sh.sm_scale, sh.q_scale, sh.kv_scale, return_lse=True,
+                       g_kv_indptr=sh.g_kv_indptr, cp_world_size=4, cp_rank=2, o=o2, lse=lse2,
+                       max_seqlen_q=3, workspace=ws2)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (q, o, lse, v, o2, lse2)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (q, o, lse, v, o2, lse2):
+            t.zero_()
+        mla.latent_to_v(torch.randn((8, 16, 512), device=DEV).to(torch.bfloat16), s.w_uv)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((q, o, lse, v, o2, lse2), eager):
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.float8_e4m3fn else a,
+                               b.view(torch.uint8) if b.dtype == torch.float8_e4m3fn else b), rep
