@@ -388,14 +388,11 @@ __device__ __forceinline__ void bf16_tile(WaveState& st, uint4 (&B)[18], TileIdx
   softmax_update<4>(st, x);
 
   // P = hi + lo, both bf16; element j of the operand is kv row 4gq + j.
-  u32 hb[4], lb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hb[i] = bf16_bits(x[i]);
-    lb[i] = bf16_bits(x[i] - __uint_as_float(hb[i] << 16));
-  }
-  const v4s phi = as_v4s(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-  const v4s plo = as_v4s(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+  const u32 h01 = pack_bf16x2(x[0], x[1]), h23 = pack_bf16x2(x[2], x[3]);
+  const u32 l01 = pack_bf16x2(x[0] - __uint_as_float(h01 << 16), x[1] - __uint_as_float(h01 & 0xFFFF0000u));
+  const u32 l23 = pack_bf16x2(x[2] - __uint_as_float(h23 << 16), x[3] - __uint_as_float(h23 & 0xFFFF0000u));
+  const v4s phi = as_v4s(h01, h23);
+  const v4s plo = as_v4s(l01, l23);
 
   // O^T += V^T . P^T.  For c = 0..3 the lane reads dims [8m, 8m + 8) with
   // m = n + 16c of kv rows 4gq + j; word w of those 16 bytes holds dims 8m + 2w
@@ -842,8 +839,8 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShare
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   } else {
     uint2 pk;
-    pk.x = bf16_bits(acc.x * inv) | (bf16_bits(acc.y * inv) << 16);
-    pk.y = bf16_bits(acc.z * inv) | (bf16_bits(acc.w * inv) << 16);
+    pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+    pk.y = pack_bf16x2(acc.z * inv, acc.w * inv);
     *(uint2*)(p.o + orow * kLatent + 256 * h + 4 * lane) = pk;
   }
   if (p.lse != nullptr && h == 0 && lane == 0)
@@ -935,10 +932,10 @@ __global__ __launch_bounds__(kThreads) void mla_merge_kernel(const void* o_parts
   }
   const float inv = 1.0f / sum;
   uint4 pk;
-  pk.x = bf16_bits(acc[0] * inv) | (bf16_bits(acc[1] * inv) << 16);
-  pk.y = bf16_bits(acc[2] * inv) | (bf16_bits(acc[3] * inv) << 16);
-  pk.z = bf16_bits(acc[4] * inv) | (bf16_bits(acc[5] * inv) << 16);
-  pk.w = bf16_bits(acc[6] * inv) | (bf16_bits(acc[7] * inv) << 16);
+  pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  pk.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  pk.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
   *(uint4*)dst = pk;
   if (lse != nullptr && lane == 0) lse[row] = M + fast_log2(sum) * kLn2;
 }

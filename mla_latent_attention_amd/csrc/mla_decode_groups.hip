@@ -172,69 +172,97 @@ struct TileOffsets {
   int v[2];  // V^T transpose-read source for the two 16-row halves of a tile
 };
 
-// S^T = K.Q^T as a chain of nine v_mfma_scale_f32_32x32x64_f8f6f4 steps
-// (unit E8M0 scales in `sc` = 127) with the accumulator in vector registers.
-// Written as inline assembly because the compiler puts an MFMA result in the
+// S^T = bias + K.Q^T as a chain of nine v_mfma_scale_f32_32x32x64_f8f6f4
+// steps (unit E8M0 scales in `sc` = 127) with the accumulator in vector
+// registers; bias is 0, or -inf for the entries a row may not see.  Written
+// as inline assembly because the compiler puts an MFMA result in the
 // accumulator registers, which here all hold O^T: it would then move a block
 // of O^T out and back on every tile.  Same-kind steps may feed each other
-// back to back; the trailing 20 wait states cover the latency of the last
-// step's result before the vector ALU reads it (the compiler does not see the
-// MFMA inside the assembly).
-__device__ __forceinline__ v16f qk_chain(const v8i_t (&k)[9], const v8i_t (&q)[9], int sc) {
-  v16f s;
-  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
-               : "=&v"(s)
-               : "v"(k[0]), "v"(q[0]), "v"(sc));
-#pragma unroll
-  for (int c = 1; c < 8; ++c)
+// back to back.  Steps [kC0, kC0 + 3) here, K operands of those steps in k.
+template <int kC0>
+__device__ __forceinline__ void qk_steps(v16f& s, const v8i_t (&k)[3], const v8i_t (&q)[9], int sc,
+                                         const v16f& bias) {
+  if (kC0 == 0) {
+    // The leading wait states separate the vector ALU's last writes of the
+    // bias registers from the MFMA's read of them (the compiler inserts no
+    // wait for an MFMA it cannot see).
+    asm volatile("s_nop 4\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %4, %3, %3 op_sel_hi:[0,0,0]"
+                 : "=&v"(s)
+                 : "v"(k[0]), "v"(q[0]), "v"(sc), "v"(bias));
+  } else {
+    // bias is an (unused) input of the next steps so that its registers stay
+    // untouched while the first step may still read it (an MFMA reads its
+    // accumulator input late in its passes).
     asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
                  : "+v"(s)
-                 : "v"(k[c]), "v"(q[c]), "v"(sc));
-  asm volatile(
-      "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]\n\t"
-      "s_nop 15\n\ts_nop 3"
-      : "+v"(s)
-      : "v"(k[8]), "v"(q[8]), "v"(sc));
+                 : "v"(k[0]), "v"(q[kC0]), "v"(sc), "v"(bias));
+  }
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+               : "+v"(s)
+               : "v"(k[1]), "v"(q[kC0 + 1]), "v"(sc));
+  if (kC0 < 6) {
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "+v"(s)
+                 : "v"(k[2]), "v"(q[kC0 + 2]), "v"(sc));
+  } else {
+    // The trailing 20 wait states cover the latency of the last step's result
+    // before the vector ALU reads it.
+    asm volatile(
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]\n\t"
+        "s_nop 15\n\ts_nop 3"
+        : "+v"(s)
+        : "v"(k[2]), "v"(q[kC0 + 2]), "v"(sc));
+  }
+}
+
+// K operands of steps [kC0, kC0 + 3) of a tile (row lane%32, bytes
+// 64c + 32*(lane/32) .. +32 of the 576-byte row).
+template <int kC0>
+__device__ __forceinline__ void read_k3(v8i_t (&k)[3], const uint8_t* buf, const TileOffsets& off) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const uint8_t* kp = buf + off.k + 64 * (kC0 + i);
+    const uint4 a0 = *(const uint4*)kp, a1 = *(const uint4*)(kp + 16);
+    k[i] = v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                 (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  }
+}
+
+// S^T of one shared 32-row tile for this wave's 32 query rows.  The K
+// operands are read three steps at a time (24 registers live, not 72).
+__device__ __forceinline__ v16f tile_qk(const v8i_t (&q)[9], const uint8_t* buf,
+                                        const TileOffsets& off, int sc, const v16f& bias) {
+  v16f s;
+  v8i_t k[3];
+  read_k3<0>(k, buf, off);
+  qk_steps<0>(s, k, q, sc, bias);
+  read_k3<3>(k, buf, off);
+  qk_steps<3>(s, k, q, sc, bias);
+  read_k3<6>(k, buf, off);
+  qk_steps<6>(s, k, q, sc, bias);
   return s;
 }
 
-// Scores of one shared 32-row tile for this wave's 32 query rows and their
-// P operands (tile kTau of the current pair).  lim: the number of the tile's
-// rows that row lane%32 may see (<= 0: none); full: every row of the wave
-// sees every row of the tile (no masking).
+// The online-softmax step of one tile from its raw scores s (masked entries
+// already -inf) and the tile's P operand.  Value v of this lane is KV row
+// 8*(v/4) + 4h + v%4 of the tile.  cs > 0 is the base-2 score scale, so a
+// tile's scaled maximum is its raw maximum scaled, and each exponent is one
+// fused multiply-add.  Straight-line code: no branch splits it from the P.V
+// steps it is interleaved with.
 template <int kTau>
-__device__ __forceinline__ void tile_scores(WideState& st, PairP& pp, const v8i_t (&q)[9],
-                                            const uint8_t* buf, const TileOffsets& off, int lim,
-                                            bool full, float cs, int h, int sc) {
-  // All nine K operands are read before the first step, so the chain waits
-  // for one LDS round trip, not nine.
-  v8i_t ka[9];
+__device__ __forceinline__ void tile_softmax(WideState& st, PairP& pp, const v16f& s, float cs) {
+  float r[16];
 #pragma unroll
-  for (int c = 0; c < 9; ++c) {
-    const uint8_t* kp = buf + off.k + 64 * c;
-    const uint4 a0 = *(const uint4*)kp, a1 = *(const uint4*)(kp + 16);
-    ka[c] = v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                  (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-  }
-  const v16f s = qk_chain(ka, q, sc);
-
-  // Value v of this lane is KV row 8*(v/4) + 4h + v%4 of the tile.
-  float x[16];
+  for (int v = 0; v < 16; ++v) r[v] = s[v];
+  float tr = r[0];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) x[v] = s[v] * cs;
-  if (!full) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      x[v] = (8 * (v >> 2) + 4 * h + (v & 3) < lim) ? x[v] : neg_inf();
-  }
-  float tmax = x[0];
-#pragma unroll
-  for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
+  for (int v = 1; v < 16; ++v) tr = fmaxf(tr, r[v]);
   {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tr), __float_as_uint(tr),
                                                      false, false);
-    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max over lanes l, l^32
+    tr = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max over lanes l, l^32
   }
+  const float tmax = tr * cs;
   // The reference m is fixed at a row's first visible score maximum and never
   // raised, so O is never rescaled inside the tile loop (O lives in the
   // accumulator registers, where a rescale would cost a copy of all of it).
@@ -248,42 +276,50 @@ __device__ __forceinline__ void tile_scores(WideState& st, PairP& pp, const v8i_
   // The tile's block exponent: P' = P * 2^-e <= 2^8 for the tile's row max,
   // within fp8 range; entries far below it lose nothing that matters next to
   // the block maximum (the hi + lo pair keeps about 8 significant bits).
+  // A row that sees none of the tile (tmax = -inf) gets e = -127 and P = 0.
   const float rel = tmax - st.m;
-  int e = tmax > neg_inf() ? (int)__builtin_ceilf(fminf(fmaxf(rel, -200.f), 200.f)) - 8 : 0;
+  int e = (int)__builtin_ceilf(fminf(fmaxf(rel, -200.f), 200.f)) - 8;
   e = imin(imax(e, -127), 127);
-  const float mref = st.m + (float)e;
-  float psum = 0.f;
+  const float nref = -(st.m + (float)e);
+  float x[16], ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    x[v] = fast_exp2(x[v] - mref);
-    psum += x[v];
+    x[v] = fast_exp2(__builtin_fmaf(r[v], cs, nref));
+    ps[v & 3] += x[v];
   }
-  st.l += __builtin_ldexpf(psum, e);
+  st.l += __builtin_ldexpf((ps[0] + ps[1]) + (ps[2] + ps[3]), e);
   pp.e[kTau] = e;
-  // fp8 hi part, then the residual as fp8 lo (same block scale).
+  // fp8 hi part, then the residual as fp8 lo (same block scale).  Each
+  // packing's first write keeps the upper half of its destination, given a
+  // register that is dead by then, so no zeroing move is needed.
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 0], x[4 * w + 1], 0, false);
+    int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 0], x[4 * w + 1], __float_as_int(r[4 * w]),
+                                             false);
     hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 2], x[4 * w + 3], hw, true);
     const v2f_t h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
     const v2f_t h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 0] - h01[0], x[4 * w + 1] - h01[1], 0, false);
-    lw = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 2] - h23[0], x[4 * w + 3] - h23[1], lw, true);
+    const float d0 = x[4 * w + 0] - h01[0], d1 = x[4 * w + 1] - h01[1];
+    const float d2 = x[4 * w + 2] - h23[0], d3 = x[4 * w + 3] - h23[1];
+    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, __float_as_int(d0), false);
+    lw = __builtin_amdgcn_cvt_pk_fp8_f32(d2, d3, lw, true);
     pp.hi[4 * kTau + w] = hw;
     pp.lo[4 * kTau + w] = lw;
   }
 }
 
-// O^T += V^T . P^T over the pair's 64 rows on v_mfma_scale_f32_32x32x64_f8f6f4
-// (hi and lo parts of P, one step each per 32-dim block).  The A operand is
-// V^T straight from the row-major fp8 tiles by the LDS transpose read: read
-// (tile tau, half u) gives lane l byte j = V[kappa(l/32, j)][32*blk + l%32],
-// operand bytes 16*tau + 8*u + j, the same KV rows as the P bytes.
+// O^T += V^T . P^T over the pair's 64 rows for dim blocks [kB0, kB0 + 8) on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (hi and lo parts of P, one step each per
+// 32-dim block).  The A operand is V^T straight from the row-major fp8 tiles
+// by the LDS transpose read: read (tile tau, half u) gives lane l byte j =
+// V[kappa(l/32, 8u + j)][32*blk + l%32], operand bytes 16*tau + 8*u + j, the
+// same KV rows as the P bytes.
+template <int kB0>
 __device__ __forceinline__ void pair_pv(WideState& st, const PairP& pp, const uint8_t* buf0,
                                         const uint8_t* buf1, const TileOffsets& off, int h) {
   const int sc = 127 + (h ? pp.e[1] : pp.e[0]);  // block tau's scale sits in lanes with l/32 = tau
 #pragma unroll
-  for (int blk = 0; blk < 16; ++blk) {
+  for (int blk = kB0; blk < kB0 + 8; ++blk) {
     const v2i_t a0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(buf0 + off.v[0] + 32 * blk));
     const v2i_t a1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(buf0 + off.v[1] + 32 * blk));
     const v2i_t a2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(buf1 + off.v[0] + 32 * blk));
@@ -293,16 +329,90 @@ __device__ __forceinline__ void pair_pv(WideState& st, const PairP& pp, const ui
                                                                 0, sc);
     st.O[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pp.lo, st.O[blk], 0, 0, 0, 127,
                                                                 0, sc);
+    // Only vector and scalar ALU work may cross (the softmax it runs beside):
+    // hoisting later blocks' V reads would hold their registers early.
+    __builtin_amdgcn_sched_barrier(0x0406);
   }
 }
 
-// One piece: positions [c.k, c.k + len) of unit c.u of request c.b (unit
+// Score bias of one tile for row lane%32: 0 for the first lim rows, -inf for
+// the rest.  Value v of this lane is KV row 8*(v/4) + 4h + v%4.
+__device__ __forceinline__ v16f mask_bias(int lim, int h) {
+  v16f c;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) c[v] = (8 * (v >> 2) + 4 * h + (v & 3) < lim) ? 0.f : neg_inf();
+  return c;
+}
+
+// One step of the tile loop: S^T of the two tiles of a new pair, their
+// softmax and P operands (cur), and the previous pair's P.V (prev, still in
+// its ring slots p0 / p1), half of it after each tile's scores.  Row lane%32
+// sees the first lim0 / lim1 rows of the two tiles; full: all rows of both.
+__device__ __forceinline__ void pair_step(WideState& st, PairP& cur, const PairP& prev,
+                                          const v8i_t (&q)[9], const uint8_t* b0,
+                                          const uint8_t* b1, const uint8_t* p0, const uint8_t* p1,
+                                          const TileOffsets& off, int sc, int lim0, int lim1,
+                                          bool full, float cs, int h) {
+  // Each half is one basic block (the mask's branch comes before it).
+  v16f c0 = {};
+  if (!full) c0 = mask_bias(lim0, h);
+  const v16f s0 = tile_qk(q, b0, off, sc, c0);
+  tile_softmax<0>(st, cur, s0, cs);
+  pair_pv<0>(st, prev, p0, p1, off, h);
+  v16f c1 = {};
+  if (!full) c1 = mask_bias(lim1, h);
+  const v16f s1 = tile_qk(q, b1, off, sc, c1);
+  tile_softmax<1>(st, cur, s1, cs);
+  pair_pv<8>(st, prev, p0, p1, off, h);
+}
+
+// The 32 partial rows of a wave (bf16 of O^T * oscale) go to global memory
+// through LDS: a lane holds 8-byte pieces of its row scattered over 16 blocks,
+// so storing them directly makes every store instruction touch 32 rows 1 KB
+// apart, which issues slowly; staged, each store writes two whole 512-byte
+// half rows.  Row r = lane%32 of the wave is head r%16 of row group
+// wv + 4*(r/16), whose partial slot is slot_base + wv + 4*(r/16).  Uses ring
+// bytes [wv * kStageBytes, +kStageBytes): no wave reads the ring after its
+// tile loop, and the next piece waits for every wave before refilling it.
+constexpr int kStageStride = 528;                 // 512 bytes of a half row + 16 (bank spread)
+constexpr int kStageBytes = 32 * kStageStride;  // one wave's 32 rows
+static_assert(kWaves * kStageBytes <= kGRing * kGTileBytes, "staging fits in the ring");
+
+__device__ __forceinline__ void store_partials(const WideState& st, float oscale, uint16_t* part,
+                                               int64_t slot_base, int wv, int lane) {
+  uint8_t* stage = g_ring + wv * kStageBytes;
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {  // dims [256 half, +256)
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int blk = 8 * half + b;
+        uint2 pk;
+        pk.x = pack_bf16x2(st.O[blk][4 * q4 + 0] * oscale, st.O[blk][4 * q4 + 1] * oscale);
+        pk.y = pack_bf16x2(st.O[blk][4 * q4 + 2] * oscale, st.O[blk][4 * q4 + 3] * oscale);
+        *(uint2*)(stage + r * kStageStride + 2 * (32 * b + 8 * q4 + 4 * h)) = pk;
+      }
+    wave_lds_sync();  // the wave's writes are in LDS before any lane reads another's
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {  // two rows per instruction, 32 lanes x 16 bytes each
+      const int rr = 2 * it + (lane >> 5), c = lane & 31;
+      const uint4 v = *(const uint4*)(stage + rr * kStageStride + 16 * c);
+      const int64_t slot = slot_base + wv + kWaves * (rr >> 4);
+      *(uint4*)(part + (slot * kGroup + (rr & 15)) * kLatent + 256 * half + 8 * c) = v;
+    }
+    wave_lds_sync();  // reads done before the next half overwrites the rows
+  }
+}
+
+// One piece: entries [k0, k0 + len) of unit c.u of request c.b (unit
 // length L).  slot_base < 0: the piece is the whole unit and every row group
 // writes o / lse; else row group i of the unit writes partial slot
 // slot_base + i.
 template <bool kPaged, bool kCascade>
 __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& sh,
-                                            const GCursor& c, int G, int L, int len,
+                                            const GCursor& c, int k0, int G, int L, int len,
                                             int slot_base, int w, float cs, float ks) {
   const int tid = threadIdx.x, wv = uniform(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, hq = lane & 31, half = hq >> 4, n16 = hq & 15;
@@ -316,7 +426,7 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
     const int rgk = kGroupsPerUnit * c.u + wv + kWaves * k;
     const int jk = imin(rgk, R - 1) / G;
     vis_h[k] = rgk < R ? req_visible(c.r, jk) : 0;
-    rows_h[k] = imax(0, imin(vis_h[k] - c.k, len));
+    rows_h[k] = imax(0, imin(vis_h[k] - k0, len));
   }
   const int wave_rows = imax(rows_h[0], rows_h[1]);
   const int full_rows = imin(rows_h[0], rows_h[1]);
@@ -333,22 +443,27 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   const int rows_w = half ? rows_h[1] : rows_h[0];
 
   // Split-unit descriptor of each row group (see mla_decode.hip): written by
-  // the workers holding the unit's first and last pieces.
-  if ((lane == 0 || lane == 16) && valid && vw > 0) {
-    int* d = (int*)(p.desc + ((int64_t)t * G + g));
-    if (c.k == 0) {
+  // the workers holding the unit's first and last pieces.  Every lane stores
+  // (the conditions are uniform); lanes that hold no row group's descriptor
+  // store to the spare entry after the last, so that no divergent branch
+  // exists here: the compiler has placed a register spill under such a
+  // branch's narrowed exec mask, saving only the branch's lanes.
+  {
+    const bool mine = (lane == 0 || lane == 16) && valid && vw > 0;
+    int* d = (int*)(p.desc + (mine ? (int64_t)t * G + g : (int64_t)p.num_tokens * G));
+    if (k0 == 0) {
       d[0] = w;
       d[2] = complete ? 0 : slot_base + ulocal;
       d[3] = complete ? 0 : 1;
     }
-    if (!complete && c.k + len == L) d[1] = w;
+    if (!complete && k0 + len == L) d[1] = w;
   }
 
   __syncthreads();  // the previous piece is done with the LDS ring and indices
 
   // q rows of this lane's row group (registers) and the first index batch, in
   // one round trip.  Step c: head n16's bytes [64c + 32h, +32).
-  const RowSrc src = row_src<kPaged>(c.r, c.k);
+  const RowSrc src = row_src<kPaged>(c.r, k0);
   v8i_t q[9];
   {
     const uint8_t* qrow =
@@ -363,10 +478,19 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
       q[cc] = v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                     (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     }
+    // The softmax scales raw scores by a positive factor: a negative scale
+    // moves onto q, whose fp8 sign bits flip exactly.
+    if (cs < 0.f) {
+#pragma unroll
+      for (int cc = 0; cc < 9; ++cc) q[cc] ^= (int)0x80808080u;
+    }
     // Nothing the compiler tracks may be outstanding once the untracked tile
     // loads start: a later wait for q would also wait for those.
     __builtin_amdgcn_s_waitcnt(kVmcntNone);
   }
+  // |cs|, kept >= the smallest normal so that a masked score (-inf) still
+  // scales to -inf (a NaN scale stays NaN).
+  const float csa = fabsf(cs) < __FLT_MIN__ ? __FLT_MIN__ : fabsf(cs);
 
   TileOffsets off;
   off.k = hq * kGStride + 32 * h;
@@ -398,49 +522,47 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
                                               seg0 == 0 ? kIdxBatch * kThreads : 0, srows);
     __syncthreads();
     const int ntiles = (srows + kGTile - 1) / kGTile;
-    // Ring of six tiles, consumed in pairs (P.V takes two tiles per step).
-    // At the step of pair (t, t+1) one barrier publishes both tiles and shows
-    // every wave done with pair (t-2, t-1), whose slots then take tiles t+4
-    // and t+5, so two later tiles are always in flight and two more are
-    // issued while the pair is consumed.  Before that barrier each wave waits
-    // until its own loads of tiles t and t+1 have landed.
+    // Ring of six tiles, consumed in pairs (P.V takes two tiles per step).  At
+    // the step of pair (t, t+1) one barrier publishes both tiles and shows
+    // every wave done with pair (t-4, t-3) (its P.V ran at the previous step),
+    // whose slots then take pair (t+2, t+3): the pair is scored and pair
+    // (t-2, t-1) goes through P.V while the next pair is in flight.  Before
+    // the barrier each wave waits until its own loads of tiles t and t+1 have
+    // landed.  An odd last tile pairs with itself at P = 0.
 #pragma unroll
-    for (int i = 0; i < kGRing - 2; ++i)
+    for (int i = 0; i < 2; ++i)
       if (i < ntiles) group_issue(p, sh.idx, srows, i, i, wv, lane);
-    auto publish_pair = [&](int tt) {
-      const int last_issued = imin(ntiles - 1, tt + kGRing - 3);
-      wait_tiles_in_flight(last_issued - imin(tt + 1, ntiles - 1));
-      __syncthreads();  // tiles tt, tt+1 are in LDS; every wave is done with tt-2, tt-1
+    // One straight-line step per pair, so that its softmax (vector ALU) and
+    // the previous pair's P.V (matrix cores), which are independent, can issue
+    // interleaved.  A tile past this wave's rows is scored fully masked (P = 0
+    // changes no state), and the first step's P.V runs with P = 0.
+    PairP prev;
+    prev.hi = v8i_t{};
+    prev.lo = v8i_t{};
+    prev.e[0] = prev.e[1] = 0;
+    const uint8_t* pb0 = g_ring;
+    const uint8_t* pb1 = g_ring;
+    for (int t = 0; t < ntiles; t += 2) {
+      wait_tiles_in_flight(0);  // this wave's loads of tiles t, t+1 (the last it issued)
+      __syncthreads();  // tiles t, t+1 are in LDS; every wave is done with t-4, t-3
 #pragma unroll
-      for (int k = kGRing - 2; k < kGRing; ++k)
-        if (tt + k < ntiles) group_issue(p, sh.idx, srows, tt + k, (tt + k) % kGRing, wv, lane);
-    };
-    for (int tt = 0; tt < ntiles; tt += 2) {
-      PairP pp;
-      const uint8_t* buf0 = g_ring + (tt % kGRing) * kGTileBytes;
-      const int base0 = seg0 + tt * kGTile;
-      publish_pair(tt);
-      if (base0 < wave_rows) {
-        tile_scores<0>(st, pp, q, buf0, off, rows_w - base0, base0 + kGTile <= full_rows, cs, h, sc);
-      } else {
-        pp.hi = v8i_t{};
-        pp.lo = v8i_t{};
-        pp.e[0] = 0;
-      }
-      const uint8_t* buf1 = buf0;  // an odd last tile pairs with itself at P = 0
-      const int base1 = base0 + kGTile;
-      if (tt + 1 < ntiles) buf1 = g_ring + ((tt + 1) % kGRing) * kGTileBytes;
-      if (tt + 1 < ntiles && base1 < wave_rows) {
-        tile_scores<1>(st, pp, q, buf1, off, rows_w - base1, base1 + kGTile <= full_rows, cs, h, sc);
-      } else {
-#pragma unroll
-        for (int w = 4; w < 8; ++w) {
-          pp.hi[w] = 0;
-          pp.lo[w] = 0;
-        }
-        pp.e[1] = 0;
-      }
-      if (base0 < wave_rows) pair_pv(st, pp, buf0, buf1, off, h);
+      for (int k = 2; k < 4; ++k)
+        if (t + k < ntiles) group_issue(p, sh.idx, srows, t + k, (t + k) % kGRing, wv, lane);
+      const uint8_t* b0 = g_ring + (t % kGRing) * kGTileBytes;
+      const uint8_t* b1 = t + 1 < ntiles ? g_ring + ((t + 1) % kGRing) * kGTileBytes : b0;
+      const int base0 = seg0 + t * kGTile, base1 = base0 + kGTile;
+      // lim1 <= 0 also masks a missing odd tile: its rows lie past the piece.
+      const int lim1 = t + 1 < ntiles ? rows_w - base1 : 0;
+      PairP cur;
+      pair_step(st, cur, prev, q, b0, b1, pb0, pb1, off, sc, rows_w - base0, lim1,
+                t + 1 < ntiles && base1 + kGTile <= full_rows, csa, h);
+      prev = cur;
+      pb0 = b0;
+      pb1 = b1;
+    }
+    if (seg0 + (((ntiles - 1) >> 1) << 1) * kGTile < wave_rows) {  // the last pair
+      pair_pv<0>(st, prev, pb0, pb1, off, h);
+      pair_pv<8>(st, prev, pb0, pb1, off, h);
     }
     __builtin_amdgcn_s_waitcnt(kVmcntNone);  // every ring load has landed
     __syncthreads();
@@ -463,13 +585,23 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
                                                      false, false);
     Lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  if (!valid) return;
-  if (complete && vw == 0) return;  // the row group sees nothing: o / lse written elsewhere
-
-  const bool empty = rows_w == 0;  // only in a split piece: contributes weight 0
+  const bool empty = rows_w == 0;  // in a split piece: contributes weight 0
   const float oscale = empty ? 0.f : ks / Lsum;
   const float lse_val = empty ? neg_inf() : (st.m + fast_log2(Lsum)) * kLn2;
-  if (complete) {
+  if (!complete) {
+    // Partials are stored in bf16 (round to nearest even): every worker
+    // writes eight row groups of them at the end of a split piece, and their
+    // bytes, written and read back by the combine, rival the attention
+    // arithmetic.  Every lane takes part: the rows of a row group past the
+    // request's last (empty, weight 0) land in that row group's own slot,
+    // which the combine never reads.  Lanes l and l+32 store the same lse.
+    store_partials(st, oscale, (uint16_t*)p.part_o, slot_base, wv, lane);
+    p.part_lse[(slot_base + ulocal) * kGroup + n16] = lse_val;
+    return;
+  }
+  if (!valid) return;
+  if (vw == 0) return;  // the row group sees nothing: o / lse written elsewhere
+  {
     const int64_t orow = (int64_t)t * p.num_heads + g * kGroup + n16;
     if (p.o32 != nullptr) {
       float* d32 = p.o32 + orow * kLatent + 4 * h;
@@ -489,32 +621,13 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         uint2 pk;
-        pk.x = bf16_bits(st.O[blk][4 * q4 + 0] * oscale) |
-               (bf16_bits(st.O[blk][4 * q4 + 1] * oscale) << 16);
-        pk.y = bf16_bits(st.O[blk][4 * q4 + 2] * oscale) |
-               (bf16_bits(st.O[blk][4 * q4 + 3] * oscale) << 16);
+        pk.x = pack_bf16x2(st.O[blk][4 * q4 + 0] * oscale, st.O[blk][4 * q4 + 1] * oscale);
+        pk.y = pack_bf16x2(st.O[blk][4 * q4 + 2] * oscale, st.O[blk][4 * q4 + 3] * oscale);
         *(uint2*)(dst + 32 * blk + 8 * q4) = pk;
       }
     if (p.lse != nullptr && h == 0) p.lse[orow] = lse_val;
     return;
   }
-  // Partials are stored in bf16 (round to nearest even): every worker writes
-  // eight row groups of them at the end of a split piece, and their bytes,
-  // written and read back by the combine, rival the attention arithmetic.
-  const int64_t slot_id = slot_base + ulocal;
-  uint16_t* dst = (uint16_t*)p.part_o + (slot_id * kGroup + n16) * kLatent + 4 * h;
-#pragma unroll
-  for (int blk = 0; blk < 16; ++blk)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      uint2 pk;
-      pk.x = bf16_bits(st.O[blk][4 * q4 + 0] * oscale) |
-             (bf16_bits(st.O[blk][4 * q4 + 1] * oscale) << 16);
-      pk.y = bf16_bits(st.O[blk][4 * q4 + 2] * oscale) |
-             (bf16_bits(st.O[blk][4 * q4 + 3] * oscale) << 16);
-      *(uint2*)(dst + 32 * blk + 8 * q4) = pk;
-    }
-  if (h == 0) p.part_lse[slot_id * kGroup + n16] = lse_val;
 }
 
 // One worker: locate its share of the group-mode stream and run its pieces.
@@ -565,20 +678,29 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
   const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
   const float cs = p.sm_scale * kLog2e * qs * ks;
 
+  // Walk the share in stream rows (unit spans); each span's leading
+  // kGroupPieceRows rows hold no entries, so a share may end with rows that
+  // only charge a unit's start: no piece there.
   int64_t pos = p0;
   int piece = 0;
   while (pos < p1) {
     const int L = group_unit_len(c.r, G, c.u);
-    const int len = (int)lmin((int64_t)(L - c.k), p1 - pos);
-    if (len <= 0) break;  // not reached with a consistent plan
-    const bool complete = (c.k == 0 && len == L);
-    const int slot_base =
-        complete ? -1 : kGSlotsPerPiece * (2 * w + (piece == 0 ? 0 : 1));
-    group_piece<kPaged, kCascade>(p, sh, c, G, L, len, slot_base, w, cs, ks);
-    pos += len;
-    c.k += len;
-    ++piece;
-    if (pos < p1 && c.k == L) {
+    const int span = L + kGroupPieceRows;
+    const int n = (int)lmin((int64_t)(span - c.k), p1 - pos);
+    if (n <= 0) break;  // not reached with a consistent plan
+    int k0, len;
+    group_piece_entries(c.k, n, k0, len);
+    if (len > 0) {
+      const bool complete = (k0 == 0 && len == L);
+      const int slot_base =
+          complete ? -1 : kGSlotsPerPiece * (2 * w + (piece == 0 ? 0 : 1));
+      group_piece<kPaged, kCascade>(p, sh, c, uniform(k0), G, L, uniform(len), slot_base, w, cs,
+                                    ks);
+      ++piece;
+    }
+    pos += n;
+    c.k += n;
+    if (pos < p1 && c.k == span) {
       if (!gcursor_next_unit(c, src, p.batch, G)) break;
       uniformize(c);
     }

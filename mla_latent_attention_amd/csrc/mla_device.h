@@ -28,11 +28,21 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite).
-__device__ __forceinline__ u32 bf16_bits(float f) {
+typedef float v2f32_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16_t __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> bf16 bits with integer operations (finite
+// inputs).
+__device__ __forceinline__ u32 bf16_rne_bits(float f) {
   u32 u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// Two floats as packed bf16 bits (a in the low half), rounded to nearest even
+// by one hardware conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ u32 pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(u32, __builtin_convertvector(v2f32_t{a, b}, v2bf16_t));
 }
 
 __device__ __forceinline__ long as_long(u32 lo, u32 hi) {
@@ -263,10 +273,13 @@ __device__ __forceinline__ void stage_first_indices(int32_t* idx_dst, const Deco
 
 __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&a)[8]) {
   uint4 pk;
-  pk.x = bf16_bits(a[0]) | (bf16_bits(a[1]) << 16);
-  pk.y = bf16_bits(a[2]) | (bf16_bits(a[3]) << 16);
-  pk.z = bf16_bits(a[4]) | (bf16_bits(a[5]) << 16);
-  pk.w = bf16_bits(a[6]) | (bf16_bits(a[7]) << 16);
+  // Integer rounding here, not pack_bf16x2: with the conversion instruction
+  // the standard fp8 kernel's register allocation spills (same results: both
+  // round to nearest even).
+  pk.x = bf16_rne_bits(a[0]) | (bf16_rne_bits(a[1]) << 16);
+  pk.y = bf16_rne_bits(a[2]) | (bf16_rne_bits(a[3]) << 16);
+  pk.z = bf16_rne_bits(a[4]) | (bf16_rne_bits(a[5]) << 16);
+  pk.w = bf16_rne_bits(a[6]) | (bf16_rne_bits(a[7]) << 16);
   *(uint4*)dst = pk;
 }
 

@@ -69,14 +69,16 @@ __host__ __device__ inline ReqSource source_of(const DecodeParams& p) {
 // written earlier in the same call, so no clearing is ever needed):
 //   desc     (num_units) int4 per row group {first worker, last worker, slot
 //            of the first worker, 1} for a row group split over several
-//            workers, w = 0 else
+//            workers, w = 0 else; then one spare entry (index num_units) that
+//            takes the stores of lanes holding no descriptor, so that the
+//            group kernel writes descriptors without a divergent branch
 //   part_o   (slots * num_workers, 16, 512) fp32 partial outputs (group mode
 //            stores them as bf16 at the same element indices, in the first
 //            half of the region)
 //   part_lse (slots * num_workers, 16) fp32 partial lse
 constexpr int kMaxWorkers = 1 << 16;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-inline size_t desc_bytes(int64_t num_units) { return align256(size_t(num_units) * 16); }
+inline size_t desc_bytes(int64_t num_units) { return align256(size_t(num_units + 1) * 16); }
 inline size_t part_o_bytes(int num_workers, int slots) {
   return align256(size_t(slots) * num_workers * 16 * 512 * 4);
 }

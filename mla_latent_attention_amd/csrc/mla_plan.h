@@ -269,15 +269,31 @@ MLA_HD int group_unit_len(const Req& r, int G, int u) {
   return req_visible(r, last / G);
 }
 
-// Stream rows of request r in group mode.
+// A group-mode piece has fixed work worth about kGroupPieceRows rows of its
+// tile loop (q and index staging, the first tile loads, eight row groups of
+// partial stores), so in the work stream every non-empty unit is that many
+// rows longer than its entries: its span.  The extra rows come first, so the
+// worker whose share takes in a unit's start is charged for starting it; a
+// share boundary inside those rows hands the whole start to the later worker
+// (the earlier one then holds no piece of the unit).  With equal shares of
+// spans, a worker that holds two pieces gets correspondingly fewer entries.
+constexpr int kGroupPieceRows = 192;
+
+MLA_HD int group_unit_span(const Req& r, int G, int u) {
+  const int v = group_unit_len(r, G, u);
+  return v > 0 ? v + kGroupPieceRows : 0;
+}
+
+// Stream rows of request r in group mode (the sum of its units' spans).
 MLA_HD int64_t group_request_rows(const Req& r, int G) {
   int64_t s = 0;
   const int U = group_units(r, G);
-  for (int u = 0; u < U; ++u) s += group_unit_len(r, G, u);
+  for (int u = 0; u < U; ++u) s += group_unit_span(r, G, u);
   return s;
 }
 
-// Position in the group-mode stream: request b, its unit u, offset k.
+// Position in the group-mode stream: request b, its unit u, offset k within
+// the unit's span (entry k - kGroupPieceRows, or the unit's start before it).
 struct GCursor {
   int b, u, k;
   Req r;
@@ -288,7 +304,7 @@ MLA_HD void gcursor_in_request(GCursor& c, int b, const Req& r, int64_t off, int
   c.r = r;
   const int U = group_units(r, G);
   for (int u = 0; u < U; ++u) {
-    const int v = group_unit_len(r, G, u);
+    const int v = group_unit_span(r, G, u);
     if (off < v) {
       c.u = u;
       c.k = (int)off;
@@ -298,6 +314,13 @@ MLA_HD void gcursor_in_request(GCursor& c, int b, const Req& r, int64_t off, int
   }
   c.u = U;  // not reached for a valid offset
   c.k = 0;
+}
+
+// The entries [k0, k0 + len) of its unit that the stream rows [k, k + n) of a
+// span cover (len may be 0: rows that only charge the unit's start).
+MLA_HD void group_piece_entries(int k, int n, int& k0, int& len) {
+  k0 = imax(k - kGroupPieceRows, 0);
+  len = imax(k + n - kGroupPieceRows, 0) - k0;
 }
 
 // Move to the start of the next non-empty unit (unit lengths never shrink
@@ -319,7 +342,7 @@ MLA_HD bool gcursor_next_unit(GCursor& c, const ReqSource& src, int B, int G) {
 }
 
 MLA_HD int64_t gsnap_at(int64_t x, const GCursor& c, int G) {
-  return snap_position(x, c.k, group_unit_len(c.r, G, c.u));
+  return snap_position(x, c.k, group_unit_span(c.r, G, c.u));
 }
 
 }  // namespace mla

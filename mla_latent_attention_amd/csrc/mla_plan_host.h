@@ -1,7 +1,9 @@
 // mla_plan_host.h - host mirror of the device planners (plain C++, no HIP).
 //
 // Walks the same equal-share, boundary-snapped plan the decode kernels derive
-// on the device (mla_plan.h) and lists every worker's pieces, for the tests:
+// on the device (mla_plan.h) and lists every worker's pieces (group mode:
+// their entries, not the stream rows that charge a unit's start), for the
+// tests:
 // the C ABI exports it as mla_plan_host / mla_plan_groups_host, and a
 // sanitizer build of the tests includes it directly.
 #pragma once
@@ -132,26 +134,31 @@ inline int64_t plan_group_pieces_host(const int32_t* qo_indptr, const int32_t* k
     int piece = 0;
     while (pos < p1) {
       const int L = group_unit_len(c.r, G, c.u);
-      const int len = (int)lmin((int64_t)(L - c.k), p1 - pos);
-      if (len <= 0) return -1;
-      const bool complete = (c.k == 0 && len == L);
-      const int slot = complete ? -1 : slots * w + (piece == 0 ? 0 : slots / 2);
-      if (count < out_cap) {
-        int64_t* rec = out + 8 * count;
-        rec[0] = w;
-        rec[1] = c.b;
-        rec[2] = c.u;
-        rec[3] = c.k;
-        rec[4] = c.k + len;
-        rec[5] = L;
-        rec[6] = slot;
-        rec[7] = complete ? 1 : 0;
+      const int span = L + kGroupPieceRows;
+      const int n = (int)lmin((int64_t)(span - c.k), p1 - pos);
+      if (n <= 0) return -1;
+      int k0, len;
+      group_piece_entries(c.k, n, k0, len);
+      if (len > 0) {
+        const bool complete = (k0 == 0 && len == L);
+        const int slot = complete ? -1 : slots * w + (piece == 0 ? 0 : slots / 2);
+        if (count < out_cap) {
+          int64_t* rec = out + 8 * count;
+          rec[0] = w;
+          rec[1] = c.b;
+          rec[2] = c.u;
+          rec[3] = k0;
+          rec[4] = k0 + len;
+          rec[5] = L;
+          rec[6] = slot;
+          rec[7] = complete ? 1 : 0;
+        }
+        ++count;
+        ++piece;
       }
-      ++count;
-      pos += len;
-      c.k += len;
-      ++piece;
-      if (pos < p1 && c.k == L && !gcursor_next_unit(c, src, batch, G))
+      pos += n;
+      c.k += n;
+      if (pos < p1 && c.k == span && !gcursor_next_unit(c, src, batch, G))
         return -1;
     }
   }

@@ -2,8 +2,8 @@
 // by tests/test_host_sanitizers.py: random and adversarial call shapes through
 // the same host code the library exports as mla_plan_host /
 // mla_plan_groups_host, checking that every piece stays inside its unit, that
-// the pieces add up to the stream, and that bad input is refused, not read
-// out of bounds.
+// the pieces add up to every unit's entries, and that bad input is refused,
+// not read out of bounds.
 #include <stdint.h>
 #include <stdio.h>
 
@@ -31,7 +31,7 @@ std::vector<int32_t> indptr(const std::vector<int>& v) {
 
 // Runs one planner twice (count, then fill) and checks the pieces.
 template <class F>
-void check(F plan, int64_t stream_rows, int seed) {
+void check(F plan, int64_t stream_rows, int seed) {  // stream_rows: entries of all units
   const int64_t n = plan(nullptr, 0);
   expect(n >= 0, "planner refused valid input", seed);
   if (n < 0) return;
@@ -46,7 +46,7 @@ void check(F plan, int64_t stream_rows, int seed) {
     expect((r[7] == 1) == (r[6] == -1), "slot / completeness mismatch", seed);
     total += r[4] - r[3];
   }
-  expect(total == stream_rows, "pieces do not add up to the stream", seed);
+  expect(total == stream_rows, "pieces do not add up to the entries", seed);
 }
 
 }  // namespace
@@ -76,7 +76,12 @@ int main() {
     int64_t W = 0, Wg = 0;
     for (int b = 0; b < B; ++b) W += (int64_t)G * mla::request_rows(mla::load_req(src, b));
     src.causal = causal;
-    for (int b = 0; b < B; ++b) Wg += mla::group_request_rows(mla::load_req(src, b), G);
+    // Group mode: the pieces hold every unit's entries, not the leading stream
+    // rows that charge each non-empty unit's start.
+    for (int b = 0; b < B; ++b) {
+      const mla::Req r = mla::load_req(src, b);
+      for (int u = 0; u < mla::group_units(r, G); ++u) Wg += mla::group_unit_len(r, G, u);
+    }
     check([&](int64_t* o, int64_t cap) {
       return mla::plan_pieces_host(qo.data(), kv.data(), g, B, H, nw, w_cp, r_cp, o, cap);
     }, W, seed);

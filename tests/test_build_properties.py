@@ -5,9 +5,9 @@
   use puts spill traffic next to the gather stream (a spill inside the tile
   loop costs several per cent).  The bf16 kernel may keep a few per-piece
   values in scratch, never more than a small bound.
-* The group-mode kernel holds 256 accumulators per lane besides q; a few
-  per-piece values may sit in scratch, never more than a small bound.  It
-  writes m0, which its inline-asm LDS DMA reads
+* The group-mode kernel holds 256 accumulators per lane besides q; some
+  per-piece values may sit in scratch (a bounded amount), but its tile loop
+  (the blocks that hold the MFMA steps) touches no scratch.  It writes m0, which its inline-asm LDS DMA reads
   as the LDS destination, only in the instruction right before each DMA: the
   compiler itself then never sees a stale m0.
 * No MFMA accumulates onto the result of an MFMA of another kind: gfx950
@@ -79,7 +79,27 @@ def test_bf16_decode_kernel_scratch_is_small(compiled):
 
 def test_group_decode_kernel_scratch_is_small(compiled_groups):
     _, usage = compiled_groups
-    assert _scratch(usage, "mla_decode_groups_fp8_kernel") <= 64
+    assert _scratch(usage, "mla_decode_groups_fp8_kernel") <= 320
+
+
+def test_group_tile_loop_touches_no_scratch(compiled_groups):
+    """Every basic block holding P.V steps (the builtin MFMAs of the tile loop,
+    16 or more per block) is free of scratch loads and stores."""
+    asm, _ = compiled_groups
+    blocks, cur = [], []
+    for line in asm.splitlines():
+        t = line.strip()
+        if re.match(r"^\.LBB\d+_\d+:", t) or t.startswith(".Lfunc_end"):
+            blocks.append(cur)
+            cur = []
+        elif t and not t.startswith((";", ".")):
+            cur.append(t)
+    blocks.append(cur)
+    loops = [b for b in blocks if sum(1 for t in b if t.startswith("v_mfma")) >= 16]
+    assert len(loops) >= 3  # one per kernel build at least
+    for b in loops:
+        bad = [t for t in b if t.startswith("scratch_")]
+        assert not bad, bad[:4]
 
 
 def test_group_kernel_m0_written_only_for_its_dma(compiled_groups):

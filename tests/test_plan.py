@@ -16,6 +16,7 @@ MIN_WORKER_ROWS = 256
 SNAP_ROWS = 64
 GROUPS_PER_UNIT = 8  # group mode: row groups per unit
 GROUP_SLOTS = 16  # group mode: partial slots per worker (two pieces x 8 row groups)
+GROUP_PIECE_ROWS = 192  # group mode: a unit's span is its entries plus these leading rows
 
 
 def visible(n, qlen, j):
@@ -45,9 +46,10 @@ def units(qo, kv, G, rule=None):
 
 
 def group_units(qo, kv, G, causal=True, rule=None):
-    """Group mode: (request, unit, length, stream start) in stream order.  Unit u
-    of a request covers row groups 8u..8u+7 (row group = token * G + head
-    group) and is as long as its last row group sees."""
+    """Group mode: (request, unit, length, stream start, span) in stream order.
+    Unit u of a request covers row groups 8u..8u+7 (row group = token * G +
+    head group) and is as long as its last row group sees; in the stream it
+    takes GROUP_PIECE_ROWS more rows (ahead of its entries) when non-empty."""
     out, pos = [], 0
     U = GROUPS_PER_UNIT
     for b in range(len(qo) - 1):
@@ -61,16 +63,23 @@ def group_units(qo, kv, G, causal=True, rule=None):
                 v = visible(n, ql, last // G)
             else:
                 v = rule(b, n, ql, last // G)
-            out.append((b, u, v, pos))
-            pos += v
+            span = v + GROUP_PIECE_ROWS if v > 0 else 0
+            out.append((b, u, v, pos, span))
+            pos += span
     return out, pos
+
+
+def spans_of(us):
+    """(stream start, stream length) of each non-empty unit: the span in group
+    mode, the length otherwise."""
+    return [(e[3], e[4] if len(e) > 4 else e[2]) for e in us if e[2] > 0]
 
 
 def snapped_bounds(us, W, nw):
     """Worker boundaries: w*W//nw, moved onto a unit boundary within SNAP_ROWS
     (the nearer one; back on a tie)."""
-    starts = [st for _, _, v, st in us if v > 0]
-    lens = [v for _, _, v, _ in us if v > 0]
+    starts = [st for st, _ in spans_of(us)]
+    lens = [n for _, n in spans_of(us)]
     bounds = [0]
     for w in range(1, nw):
         x = w * W // nw
@@ -203,6 +212,10 @@ def test_rejects_bad_planner_input():
 
 
 def check_group_plan(qo, kv, H, nw_req, causal=True, dcp=None):
+    """The host planner's group-mode pieces equal the model's: worker w's
+    snapped share of the span stream, intersected with each unit's entries
+    (its span less the GROUP_PIECE_ROWS leading rows, which only charge the
+    unit's start), with the slot rule the combine relies on."""
     G = H // 16
     rule = None if dcp is None else dcp_rule(*dcp)
     us, W = group_units(qo, kv, G, causal, rule)
@@ -214,45 +227,48 @@ def check_group_plan(qo, kv, H, nw_req, causal=True, dcp=None):
     nw = min(nw_req, max(1, W // MIN_WORKER_ROWS))
     S = snapped_bounds(us, W, nw)
     assert all(a < b for a, b in zip(S, S[1:]))
+    want = []
+    for w in range(nw):
+        k = 0  # this worker's pieces so far
+        for b, u, v, st, span in us:
+            if v == 0:
+                continue
+            lo, hi = max(S[w], st + GROUP_PIECE_ROWS), min(S[w + 1], st + span)
+            if lo >= hi:
+                continue
+            k0, k1 = lo - st - GROUP_PIECE_ROWS, hi - st - GROUP_PIECE_ROWS
+            complete = k0 == 0 and k1 == v
+            slot = -1 if complete else GROUP_SLOTS * w + (0 if k == 0 else GROUP_SLOTS // 2)
+            want.append((w, b, u, k0, k1, v, slot, int(complete)))
+            k += 1
+    got = [tuple(int(x) for x in p) for p in pieces]
+    assert got == want
+    # every non-empty unit is tiled once, and a split unit's later workers
+    # hold it as their first piece, in consecutive order (the group combine
+    # reads slot 16 * w + row group of each of them)
     cover = {}
-    for w, b, u, kb, ke, ul, slot, comp in pieces:
-        assert 0 <= kb < ke <= ul
-        cover.setdefault((b, u), []).append((kb, ke, w, slot, comp))
-    owner = lambda p: int(np.searchsorted(S, p, side="right")) - 1  # noqa: E731
-    for b, u, v, start in us:
+    for w, b, u, kb, ke, ul, slot, comp in got:
+        cover.setdefault((b, u), []).append((kb, ke, w, slot))
+    for b, u, v, st, span in us:
         if v == 0:
             assert (b, u) not in cover
             continue
         segs = sorted(cover[(b, u)])
         assert segs[0][0] == 0 and segs[-1][1] == v
-        for (a0, a1, *_), (b0, b1, *_) in zip(segs, segs[1:]):
-            assert a1 == b0
-        if len(segs) == 1:
-            assert segs[0][4] == 1 and segs[0][3] == -1
-            continue
-        assert all(s[4] == 0 for s in segs)
-        # The group combine reads, for the i-th worker after the first, slots
-        # 16 * (w0 + i) + row group: those workers must hold the unit as their
-        # first piece, in consecutive order; the first worker's slots start at
-        # 16 * w0, or 16 * w0 + 8 when the unit is not its first piece.
-        wlo, whi = owner(start), owner(start + v - 1)
-        assert [s[2] for s in segs] == list(range(wlo, whi + 1))
-        first = GROUP_SLOTS * wlo + (GROUP_SLOTS // 2 if S[wlo] < start else 0)
-        assert segs[0][3] == first
-        assert [s[3] for s in segs[1:]] == [GROUP_SLOTS * w for w in range(wlo + 1, whi + 1)]
-    per_worker = np.zeros(nw, dtype=np.int64)
-    for w, b, u, kb, ke, *_ in pieces:
-        per_worker[w] += ke - kb
-    shares = np.array([S[w + 1] - S[w] for w in range(nw)])
-    assert np.array_equal(per_worker, shares)
+        assert all(x[1] == y[0] for x, y in zip(segs, segs[1:]))
+        assert [x[2] for x in segs] == list(range(segs[0][2], segs[0][2] + len(segs)))
+        assert [x[3] for x in segs[1:]] == [GROUP_SLOTS * x[2] for x in segs[1:]]
+    # equal shares, and no boundary within SNAP_ROWS of a span's ends
+    shares = np.diff(np.array(S))
     assert np.all(np.abs(shares - W / nw) <= 2 * SNAP_ROWS + 1)
-    slots = [p[6] for p in pieces if p[6] >= 0]
+    starts = [st for st, _ in spans_of(us)]
+    lens = [n for _, n in spans_of(us)]
+    for x in S[1:-1]:
+        i = int(np.searchsorted(starts, x, side="right")) - 1
+        kx = x - starts[i]
+        assert kx == 0 or (kx > SNAP_ROWS and lens[i] - kx > SNAP_ROWS)
+    slots = [p[6] for p in got if p[6] >= 0]
     assert len(slots) == len(set(slots))
-    for w in range(nw):
-        mine = pieces[pieces[:, 0] == w]
-        for i, p in enumerate(mine):
-            if p[7] == 0:
-                assert i in (0, len(mine) - 1)
     return pieces
 
 
@@ -267,13 +283,37 @@ def test_group_plan_dcp_share_workload():
     assert lens == [17_748, 17_749, 17_750]
 
 
+def test_group_plan_charges_each_unit_start():
+    """DCP share: the 16 workers whose share crosses a unit boundary run two
+    pieces; each unit's leading GROUP_PIECE_ROWS rows give them that many
+    fewer entries than a worker inside one unit."""
+    p = plan_groups_host(indptr([4] * 8), indptr([17_750] * 8), 96, 256, True)
+    entries, pieces = np.zeros(256, np.int64), np.zeros(256, np.int64)
+    for r in p:
+        entries[r[0]] += r[4] - r[3]
+        pieces[r[0]] += 1
+    assert np.bincount(pieces).tolist() == [0, 240, 16]
+    assert entries[pieces == 1].max() - entries[pieces == 2].max() >= GROUP_PIECE_ROWS - 2 * SNAP_ROWS
+
+
+def test_model_constants_match_the_planner_header():
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(__file__), "..", "mla_latent_attention_amd", "csrc",
+                            "mla_plan.h")).read()
+    for name, val in (("kMinWorkerRows", MIN_WORKER_ROWS), ("kSnapRows", SNAP_ROWS),
+                      ("kGroupsPerUnit", GROUPS_PER_UNIT), ("kGroupPieceRows", GROUP_PIECE_ROWS)):
+        m = re.search(r"constexpr int %s = (\d+);" % name, src)
+        assert m and int(m.group(1)) == val, name
+
+
 def test_group_units_mask_within_unit():
     """With 16 heads and 4 tokens, one unit holds all four tokens; its length
     is the last token's visible count, the others see fewer."""
     us, W = group_units(indptr([4]), indptr([100]), 1)
-    assert [(u, v) for _, u, v, _ in us] == [(0, 100)]
+    assert [(u, v) for _, u, v, *_ in us] == [(0, 100)]
     us, W = group_units(indptr([5]), indptr([100]), 2)  # 10 row groups: units of 8 and 2
-    assert [(u, v) for _, u, v, _ in us] == [(0, 99), (1, 100)]
+    assert [(u, v) for _, u, v, *_ in us] == [(0, 99), (1, 100)]
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -302,7 +342,7 @@ def test_group_plan_without_causal_mask():
     check_group_plan(indptr([7]), indptr([5000]), 64, 37, causal=False)
     check_group_plan(indptr([3]), indptr([0]), 32, 8, causal=False)
     us, _ = group_units(indptr([4]), indptr([100]), 1, causal=False)
-    assert [(u, v) for _, u, v, _ in us] == [(0, 100)]
+    assert [(u, v) for _, u, v, *_ in us] == [(0, 100)]
 
 
 # ---------------------------------------------------------------- DCP shards
