@@ -99,6 +99,22 @@ def test_small_shared_prefix_any_worker_count(nw):
     check(small_shared(), num_workers=nw, where=f"small nw={nw}")
 
 
+# Ragged group-mode call (96 heads, draft tokens): with 23, 37 or 58 workers
+# some share boundaries fall inside a unit's leading charge rows (checked on
+# the CPU in test_plan.py), so a worker is charged for a unit start it does
+# not run and the next worker takes the unit from its first entry.
+CHARGE_LENGTHS = [700, 1900, 260, 3000, 45, 1200]
+CHARGE_QLENS = [4, 2, 3, 1, 4, 2]
+
+
+@pytest.mark.parametrize("nw", [5, 23, 37, 58])
+def test_group_mode_share_boundaries_in_charge_rows(nw):
+    w = workloads.build("charge", CHARGE_LENGTHS, num_heads=96, real_heads=96, qlens=CHARGE_QLENS,
+                        pool_entries=1 << 14, kv_std=0.5, scale_range=(0.5, 2.0), seed=131,
+                        device=DEV)
+    check(w, num_workers=nw, where=f"charge rows nw={nw}")
+
+
 @pytest.mark.parametrize("heads", [16, 96])
 def test_one_long_request_split_over_many_workers(heads):
     """One request split over ~100-150 workers: the combine merges more than 16

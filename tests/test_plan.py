@@ -296,6 +296,21 @@ def test_group_plan_charges_each_unit_start():
     assert entries[pieces == 1].max() - entries[pieces == 2].max() >= GROUP_PIECE_ROWS - 2 * SNAP_ROWS
 
 
+def test_group_boundaries_fall_inside_charge_rows():
+    """The ragged call of the GPU test for charge rows: with 23, 37 and 58
+    workers some snapped share boundaries lie strictly inside a unit's
+    leading GROUP_PIECE_ROWS rows (and the plan is still exact)."""
+    qo, kv = indptr([4, 2, 3, 1, 4, 2]), indptr([700, 1900, 260, 3000, 45, 1200])
+    us, W = group_units(qo, kv, 6)
+    for nw_req in (23, 37, 58):
+        nw = min(nw_req, max(1, W // MIN_WORKER_ROWS))
+        S = snapped_bounds(us, W, nw)
+        inside = sum(1 for x in S[1:-1] for b, u, v, st, span in us
+                     if v > 0 and st < x < st + GROUP_PIECE_ROWS)
+        assert inside > 0, nw_req
+        check_group_plan(qo, kv, 96, nw_req)
+
+
 def test_model_constants_match_the_planner_header():
     import os
     import re
