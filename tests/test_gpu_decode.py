@@ -608,10 +608,22 @@ def test_dcp_interleaved_shards_and_merge(case):
     # The merged answer carries two bf16 roundings (each shard's o, then the
     # merge's), and the 3- and 9-position requests leave shards of one or two
     # entries, so |o| reaches ~2.5, where one bf16 ulp (2^-6) exceeds 1e-2:
-    # the absolute bound is one ulp at the largest |o| (row-normwise and lse
-    # bounds unchanged).
-    assert_gate(m, f"dcp {case}: 8 shards merged vs the full call",
-                abs_tol=bf16_abs_tol(m["ref_absmax"]))
+    # the absolute bound is one ulp at the largest |o|.  For the same reason
+    # the row-normwise bound is derived for the merge rather than taken from
+    # the merged row: every shard row is within 2^-7 of its own row maximum
+    # (checked above), the merge averages shard rows with weights that sum to
+    # one and rounds once to bf16, so a merged row is within 2^-7 of the
+    # largest of its shard rows' maxima plus 2^-9 of its own; shard rows of
+    # one or two entries can exceed the merged row, which averages more.
+    ok = (m["max_abs"] <= bf16_abs_tol(m["ref_absmax"]) and m["dead_rows_nonzero"] == 0
+          and m["lse_inf_mismatch"] == 0 and m["lse_nan"] == 0 and m["lse_abs"] <= 1e-3)
+    assert ok, f"dcp {case}: 8 shards merged vs the full call {m}"
+    shard_rowmax = torch.stack(parts_o).float()[:, toks].abs().amax(dim=(0, 3)).double().cpu().numpy()
+    err = np.abs(o_m.float()[toks].double().cpu().numpy() - o_ref).max(axis=-1)
+    bound = 2.0 ** -7 * shard_rowmax + 2.0 ** -9 * np.abs(o_ref).max(axis=-1)
+    worst = float((err / np.maximum(bound, 1e-30)).max())
+    say(f"[dcp] {case} merged: worst row error / derived bound = {worst:.3f}")
+    assert worst <= 1.0, f"dcp {case}: merged row error over its bound by {worst:.3f}"
 
 
 def test_dcp_bad_arguments_are_rejected():
