@@ -253,6 +253,9 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
 }
 
 struct Fp8Path {
+  // Split partials in bf16: half the bytes to write and read back, within
+  // the gate for the fp8 cache's outputs.
+  static constexpr bool kBf16Parts = true;
   static constexpr int kRowBytes = kRowDim;
   static constexpr int kTile = kFp8Tile;
   static constexpr int kVStride = kFp8VStride;
@@ -425,6 +428,9 @@ __device__ __forceinline__ void bf16_tile(WaveState& st, uint4 (&B)[18], TileIdx
 }
 
 struct Bf16Path {
+  // Split partials in fp32: bf16 caches reach |o| ~ 3-7 on one-entry and
+  // multi-token rows, where a second bf16 rounding exceeds the 1e-2 bound.
+  static constexpr bool kBf16Parts = false;
   static constexpr int kRowBytes = kBf16RowBytes;
   static constexpr int kTile = kBf16Tile;
   static constexpr int kVStride = kBf16VStride;
@@ -599,12 +605,20 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
     if (p.lse != nullptr && wv == 0 && gq == 0) p.lse[orow] = lse_val;
     return;
   }
-  float* dst = p.part_o + ((int64_t)slot * kGroup + n) * kLatent + dim0;
+  if constexpr (Path::kBf16Parts) {
+    // bf16 (round to nearest even) at the fp32 layout's element indices, in
+    // the first half of the region.
+    uint16_t* dst = (uint16_t*)p.part_o + ((int64_t)slot * kGroup + n) * kLatent + dim0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float* d = dst + Path::kDimStride * i;
-    *(float4*)d = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-    *(float4*)(d + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+    for (int i = 0; i < 4; ++i) store_bf16x8(dst + Path::kDimStride * i, acc[i]);
+  } else {
+    float* dst = p.part_o + ((int64_t)slot * kGroup + n) * kLatent + dim0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* d = dst + Path::kDimStride * i;
+      *(float4*)d = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+      *(float4*)(d + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+    }
   }
   if (wv == 0 && gq == 0) p.part_lse[(int64_t)slot * kGroup + n] = lse_val;
 }
@@ -847,7 +861,14 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShare
     p.lse[orow] = sum > 0.f ? M + fast_log2(sum) * kLn2 : neg_inf();
 }
 
+// The standard kernels' split combine: fp8 caches leave bf16 partials, bf16
+// caches fp32 ones.
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const DecodeParams p) {
+  __shared__ CombineShared sh;
+  combine_unit<2, true>(p, sh);
+}
+
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_fp32_kernel(const DecodeParams p) {
   __shared__ CombineShared sh;
   combine_unit<2, false>(p, sh);
 }
@@ -967,8 +988,11 @@ hipError_t launch_decode(const DecodeParams& p, int kv_dtype, bool group_mode, h
   if (group_mode && kv_dtype == 0)
     hipLaunchKernelGGL(mla_combine_groups_kernel, dim3(units, 2 * kGroup), dim3(kCombineThreads), 0,
                        stream, p);
-  else
+  else if (kv_dtype == 0)
     hipLaunchKernelGGL(mla_combine_kernel, dim3(units, 2 * kGroup), dim3(kCombineThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL(mla_combine_fp32_kernel, dim3(units, 2 * kGroup), dim3(kCombineThreads), 0,
                        stream, p);
   return hipGetLastError();
 }

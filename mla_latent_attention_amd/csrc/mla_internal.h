@@ -72,9 +72,9 @@ __host__ __device__ inline ReqSource source_of(const DecodeParams& p) {
 //            workers, w = 0 else; then one spare entry (index num_units) that
 //            takes the stores of lanes holding no descriptor, so that the
 //            group kernel writes descriptors without a divergent branch
-//   part_o   (slots * num_workers, 16, 512) fp32 partial outputs (group mode
-//            stores them as bf16 at the same element indices, in the first
-//            half of the region)
+//   part_o   (slots * num_workers, 16, 512) fp32 partial outputs (calls on an
+//            fp8 cache store them as bf16 at the same element indices, in the
+//            first half of the region)
 //   part_lse (slots * num_workers, 16) fp32 partial lse
 constexpr int kMaxWorkers = 1 << 16;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
