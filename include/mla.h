@@ -199,6 +199,12 @@ mla_status mla_decode_paged(const void* q, int q_dtype, const void* kv_pool, int
  *                 positions in total.
  *  cp_world_size  shards the positions are dealt over, 1..1024.
  *  cp_rank        this shard, 0 <= cp_rank < cp_world_size.
+ *  o_dtype        MLA_DTYPE_BF16: o is (num_q_tokens, num_heads, 512) bf16, as
+ *                 for mla_decode.  MLA_DTYPE_FP32: o is the same shape in fp32,
+ *                 and the call's internal split partials are kept in fp32 too,
+ *                 so a shard's answer reaches the merge unrounded; the merge
+ *                 (mla_merge_partials with FP32 parts) then rounds once, to the
+ *                 final bf16.  Any other value returns MLA_ERR_BAD_DTYPE.
  * Layout (caller's contract): positions are dealt round-robin, so this
  * shard's i-th entry of request b is the entry at full-list position
  * cp_rank + i * cp_world_size; it holds ceil((N_b - cp_rank) /
@@ -220,7 +226,8 @@ mla_status mla_decode_dcp(const void* q, int q_dtype, const void* kv_pool, int k
                           int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
                           const float* q_scale, const float* kv_scale, int return_lse,
                           float* lse, const int32_t* g_kv_indptr, int cp_world_size,
-                          int cp_rank, void* workspace, size_t workspace_bytes, void* stream);
+                          int cp_rank, int o_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /*
  * LSE-weighted merge of partial answers over disjoint KV shards (the DCP

@@ -141,9 +141,10 @@ def decode(
             _need(s, name, dev, torch.float32)
             if s.numel() != 1:
                 raise ValueError(f"{name} must hold one value")
+    o_dtype = torch.bfloat16 if _dcp is None else _dcp[3]
     if o is None:
-        o = torch.empty((T, H, LATENT_DIM), dtype=torch.bfloat16, device=dev)
-    _need(o, "o", dev, torch.bfloat16, (T, H, LATENT_DIM))
+        o = torch.empty((T, H, LATENT_DIM), dtype=o_dtype, device=dev)
+    _need(o, "o", dev, o_dtype, (T, H, LATENT_DIM))
     if return_lse:
         if lse is None:
             lse = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -173,10 +174,10 @@ def decode(
         status = L.mla_decode_ex(*head, _ptr(workspace), ws_len, int(num_workers), _stream(dev))
         _lib.check(status, "mla_decode")
     else:
-        g_kv_indptr, cp_world_size, cp_rank = _dcp
+        g_kv_indptr, cp_world_size, cp_rank, _ = _dcp
         _need(g_kv_indptr, "g_kv_indptr", dev, torch.int32, (B + 1,))
         status = L.mla_decode_dcp(*head, _ptr(g_kv_indptr), int(cp_world_size), int(cp_rank),
-                                  _ptr(workspace), ws_len, _stream(dev))
+                                  _storage_dtype(o), _ptr(workspace), ws_len, _stream(dev))
         _lib.check(status, "mla_decode_dcp")
     return (o, lse) if return_lse else o
 
@@ -225,6 +226,7 @@ def decode_dcp(
     g_kv_indptr: torch.Tensor,
     cp_world_size: int,
     cp_rank: int,
+    o_dtype: torch.dtype = torch.bfloat16,
     o: torch.Tensor | None = None,
     lse: torch.Tensor | None = None,
     max_seqlen_q: int | None = None,
@@ -233,10 +235,13 @@ def decode_dcp(
     """One DCP shard's decode (mla_decode_dcp): kv_indptr / kv_indices hold this
     shard's entries, the full-list positions cp_rank, cp_rank + cp_world_size, ...
     of each request; g_kv_indptr (B+1) int32 on the device gives the full lists'
-    offsets.  Returns what decode() returns."""
+    offsets.  o_dtype torch.float32 returns the shard's o in fp32 (for
+    merge_partials with fp32 parts).  Returns what decode() returns."""
+    if o_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("o_dtype must be torch.bfloat16 or torch.float32")
     return decode(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_lens, sm_scale,
                   q_scale, kv_scale, return_lse, o=o, lse=lse, max_seqlen_q=max_seqlen_q,
-                  workspace=workspace, _dcp=(g_kv_indptr, cp_world_size, cp_rank))
+                  workspace=workspace, _dcp=(g_kv_indptr, cp_world_size, cp_rank, o_dtype))
 
 
 def cascade_workspace_bytes(batch: int, num_q_tokens: int, num_heads: int,

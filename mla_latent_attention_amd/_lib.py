@@ -39,7 +39,8 @@ SIGNATURES = {
         _vp]),
     "mla_decode_cascade_workspace_bytes": (C.c_size_t, [C.c_int] * 4),
     "mla_decode_paged": (C.c_int, _DECODE_ARGS[:11] + [C.c_int] + _DECODE_ARGS[11:] + [_vp]),
-    "mla_decode_dcp": (C.c_int, _DECODE_ARGS[:20] + [_vp, C.c_int, C.c_int] + _DECODE_ARGS[20:] + [_vp]),
+    "mla_decode_dcp": (C.c_int, _DECODE_ARGS[:20] + [_vp, C.c_int, C.c_int, C.c_int]
+                       + _DECODE_ARGS[20:] + [_vp]),
     "mla_rope_quant_cache": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int, C.c_int, _vp, C.c_int,
                                        C.c_int, C.c_int, _vp, C.c_int64, _vp, _vp, _vp, _vp]),
     "mla_latent_to_v": (C.c_int, [_vp, _vp, _vp, C.c_int, C.c_int, C.c_int, _vp]),

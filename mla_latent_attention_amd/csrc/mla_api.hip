@@ -66,7 +66,7 @@ mla_status decode_impl(const void* q, int q_dtype, const void* kv_pool, int kv_d
                        float sm_scale, const float* q_scale, const float* kv_scale,
                        int return_lse, float* lse, const int32_t* g_kv_indptr, int cp_size,
                        int cp_rank, const int32_t* last_page_lens, int page_shift, void* workspace,
-                       size_t workspace_bytes, int num_workers, void* stream) {
+                       size_t workspace_bytes, int num_workers, void* stream, int o_fp32 = 0) {
   if (!q || !kv_pool || !o || !qo_indptr || !kv_indptr || !kv_indices)
     return MLA_ERR_NULL_POINTER;
   if (return_lse && !lse) return MLA_ERR_NULL_POINTER;
@@ -97,8 +97,11 @@ mla_status decode_impl(const void* q, int q_dtype, const void* kv_pool, int kv_d
   p.q = static_cast<const uint8_t*>(q);
   p.kv = static_cast<const uint8_t*>(kv_pool);
   p.pool_entries = pool_entries;
-  p.o = static_cast<uint16_t*>(o);
-  p.o32 = nullptr;
+  // An fp32 output (DCP shards to be merged) also keeps the split partials in
+  // fp32, so the result carries no bf16 rounding before the merge's own.
+  p.o = o_fp32 ? nullptr : static_cast<uint16_t*>(o);
+  p.o32 = o_fp32 ? static_cast<float*>(o) : nullptr;
+  p.part_fp32 = o_fp32 ? 1 : 0;
   p.qo_indptr = qo_indptr;
   p.kv_indptr = kv_indptr;
   p.kv_indices = kv_indices;
@@ -205,15 +208,18 @@ mla_status mla_decode_dcp(const void* q, int q_dtype, const void* kv_pool, int k
                           int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
                           const float* q_scale, const float* kv_scale, int return_lse,
                           float* lse, const int32_t* g_kv_indptr, int cp_world_size,
-                          int cp_rank, void* workspace, size_t workspace_bytes, void* stream) {
+                          int cp_rank, int o_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
   (void)kv_last_page_lens;
   if (!g_kv_indptr) return MLA_ERR_NULL_POINTER;
+  if (o_dtype != MLA_DTYPE_BF16 && o_dtype != MLA_DTYPE_FP32) return MLA_ERR_BAD_DTYPE;
   if (cp_world_size < 1 || cp_world_size > kMaxCpSize || cp_rank < 0 || cp_rank >= cp_world_size)
     return MLA_ERR_BAD_SHAPE;
   return decode_impl(q, q_dtype, kv_pool, kv_dtype, pool_entries, o, qo_indptr, kv_indptr,
                      kv_indices, kv_indices_len, batch, num_q_tokens, num_heads, max_seqlen_q,
                      sm_scale, q_scale, kv_scale, return_lse, lse, g_kv_indptr, cp_world_size,
-                     cp_rank, nullptr, 0, workspace, workspace_bytes, 0, stream);
+                     cp_rank, nullptr, 0, workspace, workspace_bytes, 0, stream,
+                     o_dtype == MLA_DTYPE_FP32 ? 1 : 0);
 }
 
 mla_status mla_decode(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,

@@ -605,7 +605,7 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
     if (p.lse != nullptr && wv == 0 && gq == 0) p.lse[orow] = lse_val;
     return;
   }
-  if constexpr (Path::kBf16Parts) {
+  if (Path::kBf16Parts && !p.part_fp32) {
     // bf16 (round to nearest even) at the fp32 layout's element indices, in
     // the first half of the region.
     uint16_t* dst = (uint16_t*)p.part_o + ((int64_t)slot * kGroup + n) * kLatent + dim0;
@@ -878,6 +878,13 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_groups_kernel(con
   combine_unit<16, true>(p, sh);
 }
 
+// Group mode with fp32 partials (calls whose output is fp32).
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_groups_fp32_kernel(
+    const DecodeParams p) {
+  __shared__ CombineShared sh;
+  combine_unit<16, false>(p, sh);
+}
+
 // ---------------------------------------------------------------- shard merge
 
 // One wave per (token, head) row, 8 dims per lane.  Shards are taken in
@@ -985,10 +992,13 @@ hipError_t launch_decode(const DecodeParams& p, int kv_dtype, bool group_mode, h
   }
   if (e != hipSuccess) return e;
   const unsigned units = (unsigned)(p.num_tokens * (p.num_heads / kGroup));
-  if (group_mode && kv_dtype == 0)
+  if (group_mode && kv_dtype == 0 && p.part_fp32)
+    hipLaunchKernelGGL(mla_combine_groups_fp32_kernel, dim3(units, 2 * kGroup),
+                       dim3(kCombineThreads), 0, stream, p);
+  else if (group_mode && kv_dtype == 0)
     hipLaunchKernelGGL(mla_combine_groups_kernel, dim3(units, 2 * kGroup), dim3(kCombineThreads), 0,
                        stream, p);
-  else if (kv_dtype == 0)
+  else if (kv_dtype == 0 && !p.part_fp32)
     hipLaunchKernelGGL(mla_combine_kernel, dim3(units, 2 * kGroup), dim3(kCombineThreads), 0,
                        stream, p);
   else

@@ -366,33 +366,46 @@ __device__ __forceinline__ void pair_step(WideState& st, PairP& cur, const PairP
   pair_pv<8>(st, prev, p0, p1, off, h);
 }
 
-// The 32 partial rows of a wave (bf16 of O^T * oscale) go to global memory
-// through LDS: a lane holds 8-byte pieces of its row scattered over 16 blocks,
-// so storing them directly makes every store instruction touch 32 rows 1 KB
-// apart, which issues slowly; staged, each store writes two whole 512-byte
-// half rows.  Row r = lane%32 of the wave is head r%16 of row group
-// wv + 4*(r/16), whose partial slot is slot_base + wv + 4*(r/16).  Uses ring
-// bytes [wv * kStageBytes, +kStageBytes): no wave reads the ring after its
-// tile loop, and the next piece waits for every wave before refilling it.
-constexpr int kStageStride = 528;                 // 512 bytes of a half row + 16 (bank spread)
+// The 32 partial rows of a wave (O^T * oscale, as bf16 or fp32) go to global
+// memory through LDS: a lane holds 16-byte pieces of its row scattered over 16
+// blocks, so storing them directly makes every store instruction touch 32 rows
+// 1 KB apart, which issues slowly; staged, each store writes two whole
+// 512-byte row pieces.  The rows pass in chunks of 512 bytes per row: two
+// halves of 256 dims in bf16, four quarters of 128 dims in fp32.  Row
+// r = lane%32 of the wave is head r%16 of row group wv + 4*(r/16), whose
+// partial slot is slot_base + wv + 4*(r/16).  Uses ring bytes
+// [wv * kStageBytes, +kStageBytes): no wave reads the ring after its tile
+// loop, and the next piece waits for every wave before refilling it.
+constexpr int kStageStride = 528;                 // 512 bytes of a row chunk + 16 (bank spread)
 constexpr int kStageBytes = 32 * kStageStride;  // one wave's 32 rows
 static_assert(kWaves * kStageBytes <= kGRing * kGTileBytes, "staging fits in the ring");
 
-__device__ __forceinline__ void store_partials(const WideState& st, float oscale, uint16_t* part,
+template <bool kF32>
+__device__ __forceinline__ void store_partials(const WideState& st, float oscale, void* part,
                                                int64_t slot_base, int wv, int lane) {
+  constexpr int kChunks = kF32 ? 4 : 2;    // passes over the staging rows
+  constexpr int kBlocks = 16 / kChunks;    // O^T blocks (32 dims each) per pass
+  constexpr int kElem = kF32 ? 4 : 2;      // bytes per stored value
   uint8_t* stage = g_ring + wv * kStageBytes;
   const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {  // dims [256 half, +256)
+  for (int chunk = 0; chunk < kChunks; ++chunk) {
 #pragma unroll
-    for (int b = 0; b < 8; ++b)
+    for (int b = 0; b < kBlocks; ++b)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int blk = 8 * half + b;
-        uint2 pk;
-        pk.x = pack_bf16x2(st.O[blk][4 * q4 + 0] * oscale, st.O[blk][4 * q4 + 1] * oscale);
-        pk.y = pack_bf16x2(st.O[blk][4 * q4 + 2] * oscale, st.O[blk][4 * q4 + 3] * oscale);
-        *(uint2*)(stage + r * kStageStride + 2 * (32 * b + 8 * q4 + 4 * h)) = pk;
+        const int blk = kBlocks * chunk + b;
+        uint8_t* dst = stage + r * kStageStride + kElem * (32 * b + 8 * q4 + 4 * h);
+        const float a0 = st.O[blk][4 * q4 + 0] * oscale, a1 = st.O[blk][4 * q4 + 1] * oscale;
+        const float a2 = st.O[blk][4 * q4 + 2] * oscale, a3 = st.O[blk][4 * q4 + 3] * oscale;
+        if constexpr (kF32) {
+          *(float4*)dst = make_float4(a0, a1, a2, a3);
+        } else {
+          uint2 pk;
+          pk.x = pack_bf16x2(a0, a1);
+          pk.y = pack_bf16x2(a2, a3);
+          *(uint2*)dst = pk;
+        }
       }
     wave_lds_sync();  // the wave's writes are in LDS before any lane reads another's
 #pragma unroll
@@ -400,9 +413,13 @@ __device__ __forceinline__ void store_partials(const WideState& st, float oscale
       const int rr = 2 * it + (lane >> 5), c = lane & 31;
       const uint4 v = *(const uint4*)(stage + rr * kStageStride + 16 * c);
       const int64_t slot = slot_base + wv + kWaves * (rr >> 4);
-      *(uint4*)(part + (slot * kGroup + (rr & 15)) * kLatent + 256 * half + 8 * c) = v;
+      const int64_t e0 = (slot * kGroup + (rr & 15)) * kLatent + (kLatent / kChunks) * chunk;
+      if constexpr (kF32)
+        *(uint4*)((float*)part + e0 + 4 * c) = v;
+      else
+        *(uint4*)((uint16_t*)part + e0 + 8 * c) = v;
     }
-    wave_lds_sync();  // reads done before the next half overwrites the rows
+    wave_lds_sync();  // reads done before the next chunk overwrites the rows
   }
 }
 
@@ -518,8 +535,12 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   for (int seg0 = 0; seg0 < len; seg0 += kGIdxSeg) {
     const int srows = imin(kGIdxSeg, len - seg0);
     if (seg0 > 0) __syncthreads();  // the previous segment is done with the indices
+    // The first kIdxBatch * kThreads indices of segment 0 came with q, but
+    // only for the first pass: a redo after a piece of several segments finds
+    // the last segment's indices there.
     stage_indices<kPaged, kThreads, kCascade>(sh.idx, p, src.template at<kPaged>(seg0),
-                                              seg0 == 0 ? kIdxBatch * kThreads : 0, srows);
+                                              (seg0 == 0 && pass == 0) ? kIdxBatch * kThreads : 0,
+                                              srows);
     __syncthreads();
     const int ntiles = (srows + kGTile - 1) / kGTile;
     // Ring of six tiles, consumed in pairs (P.V takes two tiles per step).  At
@@ -589,13 +610,16 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   const float oscale = empty ? 0.f : ks / Lsum;
   const float lse_val = empty ? neg_inf() : (st.m + fast_log2(Lsum)) * kLn2;
   if (!complete) {
-    // Partials are stored in bf16 (round to nearest even): every worker
-    // writes eight row groups of them at the end of a split piece, and their
-    // bytes, written and read back by the combine, rival the attention
-    // arithmetic.  Every lane takes part: the rows of a row group past the
+    // Partials are stored in bf16 (round to nearest even) unless the call
+    // asks for fp32 ones (an fp32 output): every worker writes eight row
+    // groups of them at the end of a split piece, and their bytes, written
+    // and read back by the combine, rival the attention arithmetic.  Every lane takes part: the rows of a row group past the
     // request's last (empty, weight 0) land in that row group's own slot,
     // which the combine never reads.  Lanes l and l+32 store the same lse.
-    store_partials(st, oscale, (uint16_t*)p.part_o, slot_base, wv, lane);
+    if (p.part_fp32)
+      store_partials<true>(st, oscale, p.part_o, slot_base, wv, lane);
+    else
+      store_partials<false>(st, oscale, p.part_o, slot_base, wv, lane);
     p.part_lse[(slot_base + ulocal) * kGroup + n16] = lse_val;
     return;
   }

@@ -14,7 +14,8 @@ struct DecodeParams {
   const uint8_t* kv;        // (pool_entries, 576)
   int64_t pool_entries;
   uint16_t* o;              // (T, H, 512) bf16
-  float* o32;               // if set, o is written here in fp32 instead (cascade passes)
+  float* o32;               // if set, o is written here in fp32 instead (cascade passes,
+                            // DCP shards asked for fp32 output)
   const int32_t* qo_indptr;  // (B+1)
   const int32_t* kv_indptr;  // (B+1)
   const int32_t* kv_indices;
@@ -26,7 +27,9 @@ struct DecodeParams {
   const float* q_scale;     // device scalar or nullptr (1.0)
   const float* kv_scale;    // device scalar or nullptr (1.0)
   float* lse;               // (T, H) or nullptr
-  float* part_o;            // workspace: (slots*num_workers, 16, 512) fp32 (bf16 in group mode)
+  float* part_o;            // workspace: (slots*num_workers, 16, 512) split partials
+  int part_fp32 = 0;        // 1: partials in fp32; 0: fp32 for a bf16 cache, bf16 for an
+                            // fp8 one (see the workspace layout below)
   float* part_lse;          // workspace: (slots*num_workers, 16) fp32
   int4* desc;               // workspace: (tokens * head groups) split-unit descriptors
   int num_workers;
@@ -74,7 +77,7 @@ __host__ __device__ inline ReqSource source_of(const DecodeParams& p) {
 //            group kernel writes descriptors without a divergent branch
 //   part_o   (slots * num_workers, 16, 512) fp32 partial outputs (calls on an
 //            fp8 cache store them as bf16 at the same element indices, in the
-//            first half of the region)
+//            first half of the region, unless part_fp32 is set)
 //   part_lse (slots * num_workers, 16) fp32 partial lse
 constexpr int kMaxWorkers = 1 << 16;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

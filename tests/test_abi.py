@@ -108,7 +108,7 @@ def _decode_dcp(**over):
     args = dict(
         q=FAKE, q_dtype=0, kv=FAKE, kv_dtype=0, pool=256, o=FAKE, qo=FAKE, kvp=FAKE, idx=FAKE,
         idx_len=164, lpl=None, batch=2, T=2, H=16, qmax=1, sm=0.072, qs=None, ks=None, rl=0,
-        lse=None, gkv=FAKE, cps=8, cpr=3, ws=FAKE, ws_len=1 << 30, stream=None,
+        lse=None, gkv=FAKE, cps=8, cpr=3, odt=1, ws=FAKE, ws_len=1 << 30, stream=None,
     )
     args.update(over)
     return _lib.lib().mla_decode_dcp(*args.values())
@@ -126,6 +126,8 @@ def _decode_dcp(**over):
         (dict(H=24), 4),
         (dict(qmax=65), 2),
         (dict(ws=None), 5),
+        (dict(odt=0), 3),
+        (dict(odt=7), 3),
     ],
 )
 def test_decode_dcp_rejects_bad_arguments_before_any_launch(over, status):

@@ -32,9 +32,9 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def run(w, num_workers=0, return_lse=True, q=None):
+def run(w, num_workers=0, return_lse=True, q=None, o_dtype=torch.bfloat16):
     """decode() on w's inputs; decode_paged() for a paged cache, decode_dcp()
-    for one DCP shard."""
+    for one DCP shard (o_dtype: the shard's output type)."""
     torch.cuda.synchronize()
     args = (w.q if q is None else q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
             w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale)
@@ -45,7 +45,7 @@ def run(w, num_workers=0, return_lse=True, q=None):
     elif w.g_kv_indptr is not None:
         assert num_workers == 0
         out = mla.decode_dcp(*args, return_lse=return_lse, g_kv_indptr=w.g_kv_indptr,
-                             cp_world_size=w.cp_size, cp_rank=w.cp_rank,
+                             cp_world_size=w.cp_size, cp_rank=w.cp_rank, o_dtype=o_dtype,
                              max_seqlen_q=w.max_seqlen_q)
     else:
         out = mla.decode(*args, return_lse=return_lse, max_seqlen_q=w.max_seqlen_q,
@@ -61,12 +61,13 @@ def oracle(w, requests=None):
     return toks, o, lse
 
 
-def check(w, requests=None, num_workers=0, where="", bf16_ulp_abs=False):
+def check(w, requests=None, num_workers=0, where="", bf16_ulp_abs=False,
+          o_dtype=torch.bfloat16):
     """Compare with the oracle.  bf16_ulp_abs widens the absolute bound to one
-    bf16 unit in the last place at the largest |o| where that exceeds 1e-2
-    (only for cases whose outputs leave the benchmark distributions)."""
+    bf16 unit in the last place at the largest |o| where |o| >= 4 (only for
+    cases whose outputs leave the benchmark distributions)."""
     say(f"[parity] {w.name} requests={requests} workers={num_workers}")
-    o, lse = run(w, num_workers)
+    o, lse = run(w, num_workers, o_dtype=o_dtype)
     toks, o_ref, lse_ref = oracle(w, requests)
     m = metrics(o[toks], o_ref, lse[toks], lse_ref)
     say(f"[parity] {w.name}: {m}")
@@ -264,6 +265,33 @@ def test_group_mode_single_row_group_requests(nw):
                         qlens=[1, 4, 1, 1, 1, 1], pool_entries=8192, kv_std=0.5,
                         scale_range=(0.5, 2.0), seed=19, device=DEV)
     check(w, num_workers=nw, where=f"group mode, one-row-group units, nw={nw}")
+
+
+@pytest.mark.parametrize("nw", [1, 2, 0])
+@pytest.mark.parametrize("heads", [64, 16])
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_scores_rising_far_above_the_first_tiles(sign, heads, nw):
+    """Request 0's later entries score ~426 base-2 units above its first 4,500.
+    With 64 heads (group mode) a piece that sees this redoes its pass with the
+    row's true maximum: one piece over both index segments (nw=1, 6,000
+    entries > 4,096 staged per segment), a piece straddling the jump (nw=2), or
+    the default split.  sign = -1 runs the same with a negative sm_scale (the
+    kernel moves the sign onto q).  With 16 heads the standard kernel's running
+    maximum takes the same jump."""
+    w = workloads.redo_case(sign, heads, device=DEV)
+    w.sm_scale = sign * w.sm_scale
+    _, _, m = check(w, num_workers=nw, where=f"redo sign={sign} heads={heads} nw={nw}")
+    assert m["ref_absmax"] > 0
+
+
+@pytest.mark.parametrize("heads", [16, 64])
+def test_zero_score_scale_gives_the_mean_of_v(heads):
+    """sm_scale = 0: every score is 0, so o is the mean of the visible V rows
+    and lse = ln n."""
+    w = workloads.build(f"zero-scale-h{heads}", [1, 700, 5000], num_heads=heads,
+                        real_heads=heads, pool_entries=1 << 13, kv_std=0.5, seed=93, device=DEV)
+    w.sm_scale = 0.0
+    check(w, where=f"zero scale heads={heads}")
 
 
 def test_group_mode_pad_heads_bitwise_and_deterministic():
@@ -591,6 +619,10 @@ DCP_CASES = {
 
 @pytest.mark.parametrize("case", sorted(DCP_CASES))
 def test_dcp_interleaved_shards_and_merge(case):
+    """Every shard against the oracle's shard rule, then the 8 shards merged
+    against the full call.  The shards return fp32 o (and keep fp32 split
+    partials), so the merged bf16 answer is rounded once, by the merge, and is
+    held to the same gate as a single call."""
     kw = DCP_CASES[case]
     full = workloads.build(f"dcp-{case}", [0, 3, 9, 700, 2501, 4096, 5003], pool_entries=1 << 14,
                            kv_std=0.5, scale_range=(0.5, 2.0), seed=71, device=DEV, **kw)
@@ -598,32 +630,27 @@ def test_dcp_interleaved_shards_and_merge(case):
     parts_o, parts_l = [], []
     for r in range(W):
         shard = workloads.dcp_shard(full, W, r)
-        o, lse, _ = check(shard, where=f"dcp {case} rank {r}")
+        o, lse, _ = check(shard, where=f"dcp {case} rank {r}", o_dtype=torch.float32)
+        assert o.dtype == torch.float32
         parts_o.append(o)
         parts_l.append(lse)
     o_m, lse_m = mla.merge_partials(torch.stack(parts_o), torch.stack(parts_l))
     toks, o_ref, lse_ref = oracle(full)
     m = metrics(o_m, o_ref, lse_m, lse_ref)
     say(f"[dcp] {case} merged: {m}")
-    # The merged answer carries two bf16 roundings (each shard's o, then the
-    # merge's), and the 3- and 9-position requests leave shards of one or two
-    # entries, so |o| reaches ~2.5, where one bf16 ulp (2^-6) exceeds 1e-2:
-    # the absolute bound is one ulp at the largest |o|.  For the same reason
-    # the row-normwise bound is derived for the merge rather than taken from
-    # the merged row: every shard row is within 2^-7 of its own row maximum
-    # (checked above), the merge averages shard rows with weights that sum to
-    # one and rounds once to bf16, so a merged row is within 2^-7 of the
-    # largest of its shard rows' maxima plus 2^-9 of its own; shard rows of
-    # one or two entries can exceed the merged row, which averages more.
-    ok = (m["max_abs"] <= bf16_abs_tol(m["ref_absmax"]) and m["dead_rows_nonzero"] == 0
-          and m["lse_inf_mismatch"] == 0 and m["lse_nan"] == 0 and m["lse_abs"] <= 1e-3)
-    assert ok, f"dcp {case}: 8 shards merged vs the full call {m}"
-    shard_rowmax = torch.stack(parts_o).float()[:, toks].abs().amax(dim=(0, 3)).double().cpu().numpy()
-    err = np.abs(o_m.float()[toks].double().cpu().numpy() - o_ref).max(axis=-1)
-    bound = 2.0 ** -7 * shard_rowmax + 2.0 ** -9 * np.abs(o_ref).max(axis=-1)
-    worst = float((err / np.maximum(bound, 1e-30)).max())
-    say(f"[dcp] {case} merged: worst row error / derived bound = {worst:.3f}")
-    assert worst <= 1.0, f"dcp {case}: merged row error over its bound by {worst:.3f}"
+    assert_gate(m, f"dcp {case}: 8 shards merged vs the full call")
+
+
+@pytest.mark.parametrize("case", sorted(DCP_CASES))
+def test_dcp_bf16_shard_outputs(case):
+    """The shards' default bf16 output: each shard is one call, held to the gate."""
+    kw = DCP_CASES[case]
+    full = workloads.build(f"dcp16-{case}", [0, 3, 9, 700, 2501, 4096, 5003],
+                           pool_entries=1 << 14, kv_std=0.5, scale_range=(0.5, 2.0), seed=72,
+                           device=DEV, **kw)
+    for r in (0, 5, 7):
+        o, _, _ = check(workloads.dcp_shard(full, 8, r), where=f"dcp bf16 out {case} rank {r}")
+        assert o.dtype == torch.bfloat16
 
 
 def test_dcp_bad_arguments_are_rejected():
@@ -746,6 +773,13 @@ def test_dcp_share_sampled():
     """One DCP8 rank at full size (rank 7 of 142,000 positions per request)."""
     w = workloads.dcp_share(DEV)
     check(w, requests=[0, 5])
+
+
+def test_dcp_local_share_sampled():
+    """The DCP8-shaped share with the bottom-right mask on the shard's own list
+    (batch 8, 96 heads, 4 draft tokens, 17,750 entries per request), sampled."""
+    w = workloads.dcp_local(DEV)
+    check(w, requests=[0, 6])
 
 
 def test_headline_batch16_paged128_sampled():

@@ -382,6 +382,39 @@ def dcp_share(device="cpu", cp_rank: int = DCP_SIZE - 1) -> Workload:
     return w
 
 
+def dcp_local(device="cpu") -> Workload:
+    """One GPU's DCP8-shaped share with the mask taken on the local list: batch 8,
+    96 heads, 4 query tokens per request (multi-token verification, causal among
+    the draft tokens, bottom-right on the shard's own 17,750 entries = 142,000 / 8),
+    fp8 KV N(0,0.5) in the 5,283,840-entry pool, q N(0,1), scales U[0.5,2],
+    return_lse on.  This is the plain mla_decode call on the shard's list."""
+    return build(
+        "dcp-local", [DCP_LOCAL] * 8, num_heads=96, real_heads=96, qlens=[4] * 8,
+        pool_entries=POOL_ENTRIES, dtype="fp8", kv_std=0.5, q_std=1.0,
+        scale_range=(0.5, 2.0), return_lse=True, seed=5500, device=device,
+    )
+
+
+def redo_case(sign: float = 1.0, num_heads: int = 64, device="cpu") -> Workload:
+    """A stress case for the score-range handling: two requests (6,000 and 700
+    entries, one query token, 16 * k heads, N(0,0.5) KV, N(0,1) q).  Every q row's
+    64 rope dims are set to 8.0, and the rope dims of request 0's entries at
+    positions >= 4,500 to 8.0 * sign, so those entries score about
+    64 * 64 * sm_scale * log2(e) ~ 426 base-2 units above the first 4,500 (for a
+    positive sm_scale and sign = 1; use sign = -1 with a negative sm_scale)."""
+    w = build(
+        f"redo-h{num_heads}-{'pos' if sign > 0 else 'neg'}", [6000, 700], num_heads=num_heads,
+        real_heads=num_heads, pool_entries=1 << 14, dtype="fp8", kv_std=0.5, q_std=1.0,
+        scale_range=None, seed=9100, device=device,
+    )
+    kvp = w.kv_indptr.cpu().tolist()
+    big = w.kv_indices[kvp[0] + 4500: kvp[1]].to(torch.int64)
+    code = int(torch.tensor(8.0 * sign).to(torch.float8_e4m3fn).view(torch.uint8).item())
+    w.kv_pool.view(torch.uint8)[big, LATENT_DIM:] = code  # byte writes: no fp8 index_put needed
+    w.q[:, :, LATENT_DIM:] = torch.tensor(8.0, device=device).to(w.q.dtype)
+    return w
+
+
 def merge_shards(
     num_parts: int = 8, num_tokens: int = 32, num_heads: int = 96, parts_dtype: str = "fp32",
     seed: int = 5100, device="cpu", kv_local: int = DCP_LOCAL,
