@@ -59,7 +59,8 @@ typedef enum {
   MLA_ERR_BAD_DTYPE = 3,
   MLA_ERR_UNSUPPORTED = 4,
   MLA_ERR_WORKSPACE_TOO_SMALL = 5,
-  MLA_ERR_HIP = 6
+  MLA_ERR_HIP = 6,
+  MLA_ERR_SCRATCH_TOO_SMALL = 7
 } mla_status;
 
 /* Width of one cache row and of the output (Sec. 2 "K3 MLA geometry"). */
@@ -129,6 +130,38 @@ mla_status mla_decode(const void* q, int q_dtype, const void* kv_pool, int kv_dt
                       int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
                       const float* q_scale, const float* kv_scale, int return_lse, float* lse,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments and results as mla_decode, without the workspace.  The call
+ * uses a fixed scratch array that the library holds on each device for the
+ * life of the process (mla_decode_noalloc_scratch_bytes(), 20 MiB), and
+ * allocates nothing, on the host or the device.
+ *
+ *  - A call whose workspace (mla_decode_workspace_bytes for its shape) exceeds
+ *    the scratch returns MLA_ERR_SCRATCH_TOO_SMALL and enqueues nothing.  On
+ *    MI355X (256 compute units) that admits standard-mode calls
+ *    (num_heads / 16 * max_seqlen_q < 4, e.g. the 16-head single-token call)
+ *    with up to about 250,000 (token, head group) units, and no group-mode call.
+ *  - The scratch is shared by every call on one device, and no byte of it needs
+ *    to be cleared between calls (each call writes every byte it reads), but
+ *    calls that overlap on one device (concurrent streams) race on it: order
+ *    them, or use mla_decode with separate workspaces.
+ *  - The first call on a device looks up the scratch's device address
+ *    (hipGetSymbolAddress) with that device current; an error there returns
+ *    MLA_ERR_HIP.
+ */
+mla_status mla_decode_noalloc(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                              int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                              const int32_t* kv_indptr, const int32_t* kv_indices,
+                              int64_t kv_indices_len, const int32_t* kv_last_page_lens, int batch,
+                              int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
+                              const float* q_scale, const float* kv_scale, int return_lse,
+                              float* lse, void* stream);
+
+/* Bytes of the fixed scratch mla_decode_noalloc uses on each device. */
+size_t mla_decode_noalloc_scratch_bytes(void);
 
 /*
  * mla_decode with an explicit number of worker workgroups (0 = the library's

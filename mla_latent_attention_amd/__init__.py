@@ -25,6 +25,7 @@ __all__ = [
     "decode_cascade",
     "decode_dcp",
     "decode_paged",
+    "decode_noalloc",
     "rope_quant_cache",
     "latent_to_v",
     "cascade_workspace_bytes",
@@ -179,6 +180,58 @@ def decode(
         status = L.mla_decode_dcp(*head, _ptr(g_kv_indptr), int(cp_world_size), int(cp_rank),
                                   _storage_dtype(o), _ptr(workspace), ws_len, _stream(dev))
         _lib.check(status, "mla_decode_dcp")
+    return (o, lse) if return_lse else o
+
+
+def decode_noalloc(
+    q: torch.Tensor,
+    kv_pool: torch.Tensor,
+    qo_indptr: torch.Tensor,
+    kv_indptr: torch.Tensor,
+    kv_indices: torch.Tensor,
+    kv_last_page_lens: torch.Tensor | None,
+    sm_scale: float,
+    q_scale: torch.Tensor | None = None,
+    kv_scale: torch.Tensor | None = None,
+    return_lse: bool = False,
+    *,
+    o: torch.Tensor,
+    lse: torch.Tensor | None = None,
+    max_seqlen_q: int,
+):
+    """decode() through mla_decode_noalloc: no workspace, nothing allocated.
+    The caller passes o (and lse with return_lse) and max_seqlen_q; the call
+    uses the library's fixed per-device scratch.  Returns what decode() returns."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a device tensor")
+    if q.dim() != 3 or q.shape[2] != ROW_DIM:
+        raise ValueError(f"q must be (T, H, {ROW_DIM})")
+    T, H, _ = q.shape
+    if kv_pool.dim() == 4:
+        kv_pool = kv_pool.view(-1, ROW_DIM)
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_DIM:
+        raise ValueError(f"kv_pool must be (N, {ROW_DIM})")
+    _need(q, "q", dev)
+    _need(kv_pool, "kv_pool", dev)
+    B = qo_indptr.numel() - 1
+    _need(qo_indptr, "qo_indptr", dev, torch.int32, (B + 1,))
+    _need(kv_indptr, "kv_indptr", dev, torch.int32, (B + 1,))
+    _need(kv_indices, "kv_indices", dev, torch.int32)
+    for name, s in (("q_scale", q_scale), ("kv_scale", kv_scale)):
+        if s is not None:
+            _need(s, name, dev, torch.float32)
+    _need(o, "o", dev, torch.bfloat16, (T, H, LATENT_DIM))
+    if return_lse:
+        if lse is None:
+            raise ValueError("return_lse needs the caller's lse")
+        _need(lse, "lse", dev, torch.float32, (T, H))
+    status = _lib.lib().mla_decode_noalloc(
+        _ptr(q), _storage_dtype(q), _ptr(kv_pool), _storage_dtype(kv_pool), kv_pool.shape[0],
+        _ptr(o), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices), kv_indices.numel(), None,
+        B, T, H, int(max_seqlen_q), float(sm_scale), _ptr(q_scale), _ptr(kv_scale),
+        1 if return_lse else 0, _ptr(lse) if return_lse else None, _stream(dev))
+    _lib.check(status, "mla_decode_noalloc")
     return (o, lse) if return_lse else o
 
 

@@ -16,6 +16,7 @@ STATUS = {
     4: "MLA_ERR_UNSUPPORTED",
     5: "MLA_ERR_WORKSPACE_TOO_SMALL",
     6: "MLA_ERR_HIP",
+    7: "MLA_ERR_SCRATCH_TOO_SMALL",
 }
 DTYPE_FP8, DTYPE_BF16, DTYPE_FP32 = 0, 1, 2
 
@@ -29,6 +30,8 @@ _DECODE_ARGS = [
 SIGNATURES = {
     "mla_decode": (C.c_int, _DECODE_ARGS + [_vp]),
     "mla_decode_ex": (C.c_int, _DECODE_ARGS + [C.c_int, _vp]),
+    "mla_decode_noalloc": (C.c_int, _DECODE_ARGS[:20] + [_vp]),
+    "mla_decode_noalloc_scratch_bytes": (C.c_size_t, []),
     "mla_decode_workspace_bytes": (C.c_size_t, [C.c_int] * 4),
     "mla_decode_workspace_bytes_ex": (C.c_size_t, [C.c_int] * 5),
     "mla_merge_partials": (C.c_int, [_vp, C.c_int, _vp, C.c_int, C.c_int, C.c_int, _vp, _vp, _vp]),

@@ -42,6 +42,31 @@ bool shape_ok(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
   return true;
 }
 
+// Fixed device scratch for mla_decode_noalloc, the entry point for callers
+// that cannot allocate: it holds the call's workspace (split descriptors and
+// partials).  Each device holds its own copy of the array for the life of the
+// process.  In host code `scratch` only names the symbol; its device address
+// comes from hipGetSymbolAddress, per device, and only that address is ever
+// handed to a kernel.
+constexpr size_t kNoAllocScratchBytes = size_t(20) << 20;  // 20 MiB
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // device address per device, once found
+
+// Device address of this device's scratch (set up on the first call on the
+// device, with that device current), or nullptr if HIP fails.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+    (void)hipGetLastError();  // leave no sticky error for the caller's next HIP call
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
 using mla::kMaxWorkers;
 constexpr int kMaxCpSize = 1024;  // DCP shards accepted by mla_decode_dcp
 constexpr int kMaxPageShift = 12;  // page sizes accepted by mla_decode_paged: 1 .. 4096
@@ -143,6 +168,9 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: num_heads must be a multiple of 16";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: workspace missing or too small";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case MLA_ERR_SCRATCH_TOO_SMALL:
+      return "MLA_ERR_SCRATCH_TOO_SMALL: the call needs more workspace than the fixed scratch "
+             "of mla_decode_noalloc holds";
     default: return "MLA_ERR_UNKNOWN";
   }
 }
@@ -234,6 +262,36 @@ mla_status mla_decode(const void* q, int q_dtype, const void* kv_pool, int kv_dt
                        num_heads, max_seqlen_q, sm_scale, q_scale, kv_scale, return_lse, lse,
                        workspace, workspace_bytes, 0, stream);
 }
+
+mla_status mla_decode_noalloc(const void* q, int q_dtype, const void* kv_pool, int kv_dtype,
+                              int64_t pool_entries, void* o, const int32_t* qo_indptr,
+                              const int32_t* kv_indptr, const int32_t* kv_indices,
+                              int64_t kv_indices_len, const int32_t* kv_last_page_lens, int batch,
+                              int num_q_tokens, int num_heads, int max_seqlen_q, float sm_scale,
+                              const float* q_scale, const float* kv_scale, int return_lse,
+                              float* lse, void* stream) {
+  // The same checks as mla_decode first (nothing below allocates), then the
+  // size check against the fixed scratch.
+  if (!q || !kv_pool || !o || !qo_indptr || !kv_indptr || !kv_indices)
+    return MLA_ERR_NULL_POINTER;
+  if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return MLA_ERR_BAD_SHAPE;
+  if (num_heads <= 0 || num_heads % mla::kGroup != 0) return MLA_ERR_UNSUPPORTED;
+  const int cus = current_cu_count();
+  if (cus <= 0) return MLA_ERR_HIP;
+  const size_t need = mla::workspace_bytes(workers_for(num_heads, max_seqlen_q, cus),
+                                           (int64_t)num_q_tokens * (num_heads / mla::kGroup),
+                                           slots_for(num_heads, max_seqlen_q));
+  if (need > kNoAllocScratchBytes) return MLA_ERR_SCRATCH_TOO_SMALL;
+  void* ws = device_scratch();
+  if (ws == nullptr) return MLA_ERR_HIP;
+  (void)kv_last_page_lens;
+  return decode_impl(q, q_dtype, kv_pool, kv_dtype, pool_entries, o, qo_indptr, kv_indptr,
+                     kv_indices, kv_indices_len, batch, num_q_tokens, num_heads, max_seqlen_q,
+                     sm_scale, q_scale, kv_scale, return_lse, lse, nullptr, 1, 0, nullptr, 0, ws,
+                     kNoAllocScratchBytes, 0, stream);
+}
+
+size_t mla_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 namespace {
 
