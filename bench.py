@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode µs/call + HBM GB/s (% of 8 TB/s), bs16 kv≈68K fp8, 1 GPU"
 CONFIG_NAMES = ("c24_batch24_fp8", "mixed_batch64_fp8", "mixed_batch64_bf16",
-                "dcp_share_96heads_qlen4_fp8", "c16_shared_prefix_cascade_fp8",
+                "dcp_local_96heads_qlen4_fp8", "dcp_share_96heads_qlen4_fp8",
+                "dcp_share_96heads_qlen4_fp8_f32out", "c16_shared_prefix_cascade_fp8",
                 "merge_8_shards_fp32", "merge_8_shards_bf16", "c16_layer_step_rope_decode_v")
 PEAK_GBS = 8000.0
 
@@ -147,18 +148,21 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
 
     out = {}
     cases = [
-        ("c24_batch24_fp8", lambda: workloads.c24(dev), 0.5),
-        ("mixed_batch64_fp8", lambda: workloads.mixed(dev, "fp8"), 1.0),
-        ("mixed_batch64_bf16", lambda: workloads.mixed(dev, "bf16"), 1.0),
-        ("dcp_share_96heads_qlen4_fp8", lambda: workloads.dcp_share(dev), 0.5),
+        ("c24_batch24_fp8", lambda: workloads.c24(dev), 0.5, torch.bfloat16),
+        ("mixed_batch64_fp8", lambda: workloads.mixed(dev, "fp8"), 1.0, torch.bfloat16),
+        ("mixed_batch64_bf16", lambda: workloads.mixed(dev, "bf16"), 1.0, torch.bfloat16),
+        ("dcp_local_96heads_qlen4_fp8", lambda: workloads.dcp_local(dev), 0.5, torch.bfloat16),
+        ("dcp_share_96heads_qlen4_fp8", lambda: workloads.dcp_share(dev), 0.5, torch.bfloat16),
+        ("dcp_share_96heads_qlen4_fp8_f32out", lambda: workloads.dcp_share(dev), 0.5,
+         torch.float32),
     ]
-    for name, make, std in cases:
+    for name, make, std, o_dtype in cases:
         if only is not None and name != only:
             continue
         base = make()
         layers = extra_layers(base, n_layers, std, 7000, dev)
         T, H = base.num_tokens, base.num_heads
-        o = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+        o = torch.empty((T, H, 512), dtype=o_dtype, device=dev)
         lse = torch.empty((T, H), dtype=torch.float32, device=dev) if base.return_lse else None
         ws = mla.new_workspace(mla.workspace_bytes(base.batch, T, H, base.max_seqlen_q), dev)
 
@@ -167,8 +171,8 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
                 return lambda: mla.decode_dcp(
                     w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_lens,
                     w.sm_scale, w.q_scale, w.kv_scale, return_lse=w.return_lse,
-                    g_kv_indptr=w.g_kv_indptr, cp_world_size=w.cp_size, cp_rank=w.cp_rank, o=o,
-                    lse=lse, max_seqlen_q=w.max_seqlen_q, workspace=ws)
+                    g_kv_indptr=w.g_kv_indptr, cp_world_size=w.cp_size, cp_rank=w.cp_rank,
+                    o_dtype=o_dtype, o=o, lse=lse, max_seqlen_q=w.max_seqlen_q, workspace=ws)
             return lambda: mla.decode(w.q, w.kv_pool, w.qo_indptr, w.kv_indptr, w.kv_indices,
                                       w.kv_last_page_lens, w.sm_scale, w.q_scale, w.kv_scale,
                                       return_lse=w.return_lse, o=o, lse=lse,
@@ -181,8 +185,9 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
                      "GB_s": round(nbytes / wall / 1e9, 2),
                      "pct_of_8TBs": round(100 * nbytes / wall / 1e9 / PEAK_GBS, 2),
                      "TFLOP_s": round(flops / wall / 1e12, 2),
-                     "algorithmic_bytes_per_call": nbytes, "kv_rows": base.total_kv,
-                     "dtype": base.dtype, "calls": n}
+                     "algorithmic_bytes_per_call": nbytes, "flops_per_call": flops,
+                     "kv_rows": base.total_kv, "dtype": base.dtype,
+                     "o_dtype": str(o_dtype).replace("torch.", ""), "calls": n}
         del layers, base, o, lse, ws
         torch.cuda.empty_cache()
     name = "c16_shared_prefix_cascade_fp8"
@@ -222,7 +227,7 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
         lse = torch.empty((32, 96), dtype=torch.float32, device=dev)
         calls = [(lambda op=op, lp=lp: mla.merge_partials(op, lp, o=o, lse=lse))
                  for op, lp in sets]
-        wall, ev, n = time_graph(calls, steps, warmup)
+        wall, ev, n = time_graph(calls, steps, warmup, per_graph=8)
         nbytes = accounting.merge_bytes(8, 32, 96, parts_dtype)
         out[f"merge_8_shards_{parts_dtype}"] = {
             "us_per_call": round(wall * 1e6, 2), "event_us": stats_us(ev),
@@ -278,7 +283,7 @@ def layer_step_line(mla, dev, steps, warmup, n_layers=4):
     for name, calls in (("rope_quant_cache", [rope(w, s) for w, s in zip(layers, sur)]),
                         ("latent_to_v", [bmm(s) for s in sur]),
                         ("layer_step", [step(w, s) for w, s in zip(layers, sur)])):
-        wall, ev, n = time_graph(calls, steps, warmup)
+        wall, ev, n = time_graph(calls, steps, warmup, per_graph=1 if name == "layer_step" else 8)
         res[name] = {"us_per_call": round(wall * 1e6, 2), "event_us": stats_us(ev), "calls": n}
     rope_bytes = (T * H * (512 + 64) * 2 + T * 576 * 2 + T * 8 + T * 256
                   + T * Hp * 576 + T * 576)
@@ -308,8 +313,15 @@ def make_calls(mla, layers, o, ws):
     return [call_for(w) for w in layers]
 
 
-def time_graph(calls, steps, warmup):
-    """Capture all calls once and replay; (wall s/call, event s/call per replay, calls)."""
+def time_graph(calls, steps, warmup, per_graph=1):
+    """Capture the calls in HIP graphs of `per_graph` consecutive calls each
+    (cycling through `calls`), replay graphs for `warmup` calls untimed, then
+    for exactly `steps` calls (rounded up to whole graphs), with an event on
+    the launch stream between consecutive graphs.  One call per graph for the
+    decode calls (each is ~100 us of GPU work, far more than a graph launch
+    costs the host); several for calls of a few us, which a launch per call
+    would starve.  Returns (wall s per call over the timed calls, per-call
+    event seconds (graph interval / per_graph), calls timed)."""
     import torch
 
     side = torch.cuda.Stream()
@@ -319,28 +331,32 @@ def time_graph(calls, steps, warmup):
             c()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for c in calls:
-            c()
     L = len(calls)
-    reps = max(1, steps // L)
-    for _ in range(max(1, warmup // L)):
-        g.replay()
+    graphs = []
+    for j in range(max(1, -(-L // per_graph))):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(per_graph):
+                calls[(j * per_graph + i) % L]()
+        graphs.append(g)
+    ng = len(graphs)
+    reps = max(1, -(-steps // per_graph))
+    for i in range(-(-warmup // per_graph)):
+        graphs[i % ng].replay()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev[0].record()
     for i in range(reps):
-        starts[i].record()
-        g.replay()
-        ends[i].record()
+        graphs[i % ng].replay()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / (reps * L)
-    ev = [s.elapsed_time(e) * 1e-3 / L for s, e in zip(starts, ends)]
-    del g
-    return wall, ev, reps * L
+    n = reps * per_graph
+    wall = (time.perf_counter() - t0) / n
+    per_call = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 / per_graph for i in range(reps)]
+    del graphs
+    return wall, per_call, n
 
 
 def time_eager(calls, steps, warmup):

@@ -875,14 +875,14 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_fp32_kernel(const
 
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_groups_kernel(const DecodeParams p) {
   __shared__ CombineShared sh;
-  combine_unit<16, true>(p, sh);
+  combine_unit<2 * kGroupsPerUnit, true>(p, sh);
 }
 
 // Group mode with fp32 partials (calls whose output is fp32).
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_groups_fp32_kernel(
     const DecodeParams p) {
   __shared__ CombineShared sh;
-  combine_unit<16, false>(p, sh);
+  combine_unit<2 * kGroupsPerUnit, false>(p, sh);
 }
 
 // ---------------------------------------------------------------- shard merge
