@@ -283,7 +283,7 @@ def layer_step_line(mla, dev, steps, warmup, n_layers=4):
     for name, calls in (("rope_quant_cache", [rope(w, s) for w, s in zip(layers, sur)]),
                         ("latent_to_v", [bmm(s) for s in sur]),
                         ("layer_step", [step(w, s) for w, s in zip(layers, sur)])):
-        wall, ev, n = time_graph(calls, steps, warmup, per_graph=1 if name == "layer_step" else 8)
+        wall, ev, n = time_graph(calls, steps, warmup, per_graph=8)
         res[name] = {"us_per_call": round(wall * 1e6, 2), "event_us": stats_us(ev), "calls": n}
     rope_bytes = (T * H * (512 + 64) * 2 + T * 576 * 2 + T * 8 + T * 256
                   + T * Hp * 576 + T * 576)
@@ -313,15 +313,21 @@ def make_calls(mla, layers, o, ws):
     return [call_for(w) for w in layers]
 
 
-def time_graph(calls, steps, warmup, per_graph=1):
+def graph_width(steps, most=8):
+    """Calls per captured graph: the largest divisor of `steps` up to `most`,
+    so that whole graphs make exactly `steps` calls."""
+    return max(d for d in range(1, most + 1) if steps % d == 0)
+
+
+def time_graph(calls, steps, warmup, per_graph=None):
     """Capture the calls in HIP graphs of `per_graph` consecutive calls each
-    (cycling through `calls`), replay graphs for `warmup` calls untimed, then
-    for exactly `steps` calls (rounded up to whole graphs), with an event on
-    the launch stream between consecutive graphs.  One call per graph for the
-    decode calls (each is ~100 us of GPU work, far more than a graph launch
-    costs the host); several for calls of a few us, which a launch per call
-    would starve.  Returns (wall s per call over the timed calls, per-call
-    event seconds (graph interval / per_graph), calls timed)."""
+    (cycling through `calls`; default graph_width(steps)), replay graphs for
+    `warmup` calls untimed, then for `steps` calls (exactly, when per_graph
+    divides it), with an event on the launch stream between consecutive
+    graphs.  Several calls per graph, as in a model step captured whole: a
+    graph launch per call leaves a gap of several us between calls that a
+    step's own kernels do not have.  Returns (wall s per call over the timed
+    calls, per-call event seconds (graph interval / per_graph), calls timed)."""
     import torch
 
     side = torch.cuda.Stream()
@@ -331,6 +337,8 @@ def time_graph(calls, steps, warmup, per_graph=1):
             c()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    if per_graph is None:
+        per_graph = graph_width(steps)
     L = len(calls)
     graphs = []
     for j in range(max(1, -(-L // per_graph))):

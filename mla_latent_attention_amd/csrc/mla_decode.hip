@@ -50,8 +50,7 @@ struct alignas(16) DecodeShared {
   int64_t red[kWaves];
   float m[kWaves][16];
   float l[kWaves][16];
-  int pb[2];
-  int64_t pcum[2];
+  PlanHit hits[2];
 };
 
 // The unit (query token, head group) a piece belongs to.
@@ -266,7 +265,7 @@ struct Fp8Path {
   template <bool kPaged>
   static __device__ __forceinline__ void load_q(Q& q, const DecodeParams& p, DecodeShared& sh,
                                                 const UnitRef& u, RowSrc idx, int n) {
-    const int lane = threadIdx.x & 63;
+    const int lane = opaque((int)threadIdx.x) & 63;  // address built here, not held
     const uint8_t* qrow = p.q +
                           ((int64_t)u.t * p.num_heads + u.g * kGroup + (lane & 15)) * kRowBytes +
                           16 * (lane >> 4);
@@ -548,29 +547,33 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
   }
 
   // ---- merge the 4 waves' online-softmax states
+  // The per-lane LDS and output addresses from here on are rebuilt from an
+  // opaque thread id.
+  const int etid = opaque(tid), elane = etid & 63, ewv = etid >> 6, en = elane & 15,
+            egq = elane >> 4;
   st.l += __shfl_xor(st.l, 16);
   st.l += __shfl_xor(st.l, 32);
   __syncthreads();  // every wave is done with its V staging
-  if (gq == 0) {
-    sh.m[wv][n] = st.m;
-    sh.l[wv][n] = st.l;
+  if (egq == 0) {
+    sh.m[ewv][en] = st.m;
+    sh.l[ewv][en] = st.l;
   }
   v4f* comb = (v4f*)sh.buf;
 #pragma unroll
-  for (int b = 0; b < 32; ++b) comb[(wv * 32 + b) * 64 + lane] = st.O[b];
+  for (int b = 0; b < 32; ++b) comb[(ewv * 32 + b) * 64 + elane] = st.O[b];
   __syncthreads();
 
   float mw[kWaves], M = neg_inf();
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    mw[w] = sh.m[w][n];
+    mw[w] = sh.m[w][en];
     M = fmaxf(M, mw[w]);
   }
   float fw[kWaves], L = 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     fw[w] = (mw[w] == neg_inf()) ? 0.f : fast_exp2(mw[w] - M);
-    L += sh.l[w][n] * fw[w];
+    L += sh.l[w][en] * fw[w];
   }
   const float oscale = ks / (Path::kPScale * L);
 
@@ -581,14 +584,14 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
   for (int bb = 0; bb < 8; ++bb) {
     v4f a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) a += fw[w] * comb[(w * 32 + 8 * wv + bb) * 64 + lane];
+    for (int w = 0; w < kWaves; ++w) a += fw[w] * comb[(w * 32 + 8 * ewv + bb) * 64 + elane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][bb] = a[i] * oscale;
   }
-  const int dim0 = Path::first_dim(wv, gq);
+  const int dim0 = Path::first_dim(ewv, egq);
   const float lse_val = (M + fast_log2(L)) * kLn2;
   if (slot < 0) {
-    const int64_t orow = (int64_t)u.t * p.num_heads + u.g * kGroup + n;
+    const int64_t orow = (int64_t)u.t * p.num_heads + u.g * kGroup + en;
     if (p.o32 != nullptr) {
       float* d32 = p.o32 + orow * kLatent + dim0;
 #pragma unroll
@@ -602,17 +605,17 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
 #pragma unroll
       for (int i = 0; i < 4; ++i) store_bf16x8(dst + Path::kDimStride * i, acc[i]);
     }
-    if (p.lse != nullptr && wv == 0 && gq == 0) p.lse[orow] = lse_val;
+    if (p.lse != nullptr && ewv == 0 && egq == 0) p.lse[orow] = lse_val;
     return;
   }
   if (Path::kBf16Parts && !p.part_fp32) {
     // bf16 (round to nearest even) at the fp32 layout's element indices, in
     // the first half of the region.
-    uint16_t* dst = (uint16_t*)p.part_o + ((int64_t)slot * kGroup + n) * kLatent + dim0;
+    uint16_t* dst = (uint16_t*)p.part_o + ((int64_t)slot * kGroup + en) * kLatent + dim0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) store_bf16x8(dst + Path::kDimStride * i, acc[i]);
   } else {
-    float* dst = p.part_o + ((int64_t)slot * kGroup + n) * kLatent + dim0;
+    float* dst = p.part_o + ((int64_t)slot * kGroup + en) * kLatent + dim0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float* d = dst + Path::kDimStride * i;
@@ -620,44 +623,42 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
       *(float4*)(d + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
     }
   }
-  if (wv == 0 && gq == 0) p.part_lse[(int64_t)slot * kGroup + n] = lse_val;
+  if (ewv == 0 && egq == 0) p.part_lse[(int64_t)slot * kGroup + en] = lse_val;
 }
 
 // One worker: locate its share of the KV stream and run its pieces.
 template <class Path, bool kPaged>
 __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShared& sh) {
   const int G = p.num_heads / kGroup;
+  // The scales first: their loads overlap the planner's.
+  const float qs = p.q_scale ? *p.q_scale : 1.0f;
+  const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
 
-  // Pass 1 over requests: stream length W; zero this block's empty tokens.
-  const ReqSource src = source_of<kPaged>(p);
-  int64_t acc = 0;
-  for (int b = threadIdx.x; b < p.batch; b += kThreads) {
-    const Req r = load_req(src, b);
-    acc += (int64_t)G * request_rows(r);
-    const int nempty = req_empty_tokens(r);
-    for (int j = 0; j < nempty; ++j)
-      if ((r.q_base + j) % (int)gridDim.x == (int)blockIdx.x) zero_token(p, r.q_base + j);
-  }
-  const int64_t W = uniform(block_sum_i64(acc, sh.red));
+  // This worker's range [p0, p1) of the stream: the equal-share boundaries,
+  // each snapped to a unit boundary within kSnapRows (0 and W are boundaries
+  // already).  The lookup also zeroes the empty tokens this block owns.
   const int w = blockIdx.x;
-  if (W == 0) return;
-  const int nw = effective_workers(W, p.num_workers);
-  if (w >= nw) return;
-  // This worker's range [p0, p1): the equal-share boundaries, each snapped to
-  // a unit boundary within kSnapRows (0 and W are boundaries already).
-  const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
-  const int64_t xs[2] = {x0, x1 < W ? x1 : -1};
-  plan_locate2<kPaged>(p, [G](const Req& r) { return (int64_t)G * request_rows(r); }, xs, sh.red, sh.pb,
-               sh.pcum);
-  const int b0 = uniform(sh.pb[0]), b1 = uniform(sh.pb[1]);
-  if (b0 < 0 || b1 == -1) return;  // not reached with consistent indptr
+  int64_t W, x0, x1;
+  int nw;
+  PlanHit hit[2];
+  if (!plan_lookup<kPaged, kThreads, false>(
+          p, [G](const Req& r) { return (int64_t)G * request_rows(r); },
+          [&p](const Req& r) {
+            const int nempty = req_empty_tokens(r);
+            for (int j = 0; j < nempty; ++j)
+              if ((r.q_base + j) % (int)gridDim.x == (int)blockIdx.x) zero_token(p, r.q_base + j);
+          },
+          w, sh.red, sh.hits, W, nw, x0, x1, hit))
+    return;
+  if (hit[0].b < 0 || (x1 < W && hit[1].b < 0)) return;  // not reached with consistent indptr
+  const ReqSource src = source_of<kPaged>(p);
   Cursor c;
-  cursor_in_request(c, b0, load_req(src, b0), x0 - uniform(sh.pcum[0]), G);
+  cursor_in_request(c, hit[0].b, hit[0].r, x0 - hit[0].cum, G);
   uniformize(c);
   int64_t p1 = W;
   if (x1 < W) {
     Cursor c1;
-    cursor_in_request(c1, b1, load_req(src, b1), x1 - uniform(sh.pcum[1]), G);
+    cursor_in_request(c1, hit[1].b, hit[1].r, x1 - hit[1].cum, G);
     uniformize(c1);
     p1 = snap_at(x1, c1);
   }
@@ -669,8 +670,6 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
     if (!cursor_next_unit(c, src, p.batch, G)) return;
     uniformize(c);
   }
-  const float qs = p.q_scale ? *p.q_scale : 1.0f;
-  const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
   const float cs = p.sm_scale * kLog2e * qs * ks;
 
   int64_t pos = p0;
@@ -692,12 +691,13 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
       // later worker w' up to the last.  (Written before the piece runs, so
       // none of this stays live across its tile loop.)
       int* d = (int*)(p.desc + ((int64_t)u.t * G + u.g));
+      const int wv = opaque(w);  // moved to a vector register here, not held
       if (c.k == 0) {
-        d[0] = w;
+        d[0] = wv;
         d[2] = slot;
         d[3] = complete ? 0 : 1;
       }
-      if (!complete && c.k + len == v) d[1] = w;
+      if (!complete && c.k + len == v) d[1] = wv;
     }
     decode_piece<Path, kPaged>(p, sh, u, row_src<kPaged>(c.r, c.k), len, slot, cs, ks);
     pos += len;

@@ -58,8 +58,7 @@ struct alignas(16) GroupShared {
   int32_t idx[kGIdxSeg];  // kv_indices of the current segment of the piece
   int flag[kWaves];       // per-wave "redo the piece" votes
   int64_t red[kWaves];
-  int pb[2];
-  int64_t pcum[2];
+  PlanHit hits[2];
 };
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -658,35 +657,32 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
 template <bool kPaged, bool kCascade>
 __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared& sh) {
   const int G = p.num_heads / kGroup;
+  // The scales first: their loads overlap the planner's.
+  const float qs = p.q_scale ? *p.q_scale : 1.0f;
+  const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
 
-  // Pass 1 over requests: stream length W; zero this block's empty tokens.
-  const ReqSource src = source_of<kPaged, kCascade>(p);
-  int64_t acc = 0;
-  for (int b = threadIdx.x; b < p.batch; b += kThreads) {
-    const Req r = load_req(src, b);
-    acc += group_request_rows(r, G);
-    const int nempty = req_empty_tokens(r);
-    for (int jj = 0; jj < nempty; ++jj)
-      if ((r.q_base + jj) % (int)gridDim.x == (int)blockIdx.x) zero_token(p, r.q_base + jj);
-  }
-  const int64_t W = uniform(block_sum_i64(acc, sh.red));
   const int w = blockIdx.x;
-  if (W == 0) return;
-  const int nw = effective_workers(W, p.num_workers);
-  if (w >= nw) return;
-  const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
-  const int64_t xs[2] = {x0, x1 < W ? x1 : -1};
-  plan_locate2<kPaged, kThreads, kCascade>(p, [G](const Req& r) { return group_request_rows(r, G); },
-                                           xs, sh.red, sh.pb, sh.pcum);
-  const int b0 = uniform(sh.pb[0]), b1 = uniform(sh.pb[1]);
-  if (b0 < 0 || b1 == -1) return;  // not reached with consistent indptr
+  int64_t W, x0, x1;
+  int nw;
+  PlanHit hit[2];
+  if (!plan_lookup<kPaged, kThreads, kCascade>(
+          p, [G](const Req& r) { return group_request_rows(r, G); },
+          [&p](const Req& r) {
+            const int nempty = req_empty_tokens(r);
+            for (int jj = 0; jj < nempty; ++jj)
+              if ((r.q_base + jj) % (int)gridDim.x == (int)blockIdx.x) zero_token(p, r.q_base + jj);
+          },
+          w, sh.red, sh.hits, W, nw, x0, x1, hit))
+    return;
+  if (hit[0].b < 0 || (x1 < W && hit[1].b < 0)) return;  // not reached with consistent indptr
+  const ReqSource src = source_of<kPaged, kCascade>(p);
   GCursor c;
-  gcursor_in_request(c, b0, load_req(src, b0), x0 - uniform(sh.pcum[0]), G);
+  gcursor_in_request(c, hit[0].b, hit[0].r, x0 - hit[0].cum, G);
   uniformize(c);
   int64_t p1 = W;
   if (x1 < W) {
     GCursor c1;
-    gcursor_in_request(c1, b1, load_req(src, b1), x1 - uniform(sh.pcum[1]), G);
+    gcursor_in_request(c1, hit[1].b, hit[1].r, x1 - hit[1].cum, G);
     uniformize(c1);
     p1 = gsnap_at(x1, c1, G);
   }
@@ -698,8 +694,6 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
     if (!gcursor_next_unit(c, src, p.batch, G)) return;
     uniformize(c);
   }
-  const float qs = p.q_scale ? *p.q_scale : 1.0f;
-  const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
   const float cs = p.sm_scale * kLog2e * qs * ks;
 
   // Walk the share in stream rows (unit spans); each span's leading

@@ -79,6 +79,14 @@ __device__ __forceinline__ int64_t uniform(int64_t x) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
+// A value the compiler cannot see through.  Per-lane address arithmetic of an
+// epilogue built from it stays in the epilogue instead of being hoisted out of
+// the enclosing loop, where it would hold vector registers the tile loop needs.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ void uniformize(Req& r) {
   r.kv_base = uniform(r.kv_base);
   r.n = uniform(r.n);
@@ -161,6 +169,86 @@ __device__ void plan_locate2(const DecodeParams& p, RowsOf rows_of, const int64_
     if (sb[0] != -1 && sb[1] != -1) break;
   }
   __syncthreads();
+}
+
+// The requests holding stream positions x0 = worker_begin(w, W, nw) and x1
+// (the next worker's start), where request b holds rows_of(b) stream rows.
+// Batches of at most kT requests take one request per thread: one read of
+// each request, one block-wide scan that gives W and every request's first
+// stream position, and the two requests handed over through LDS (bounds
+// included), so the lookup costs one memory round trip.  Larger batches scan
+// twice (plan_locate2) and read the two requests again.  Empty tokens of the
+// requests this block reads are zeroed on the way (zero_empty).  Returns
+// false if this worker has nothing to do (W == 0 or w >= nw).
+struct PlanHit {
+  int b;        // request (-1: none)
+  int64_t cum;  // its first stream position
+  Req r;
+};
+
+template <bool kPaged, int kT, bool kCascade, class RowsOf, class ZeroEmpty>
+__device__ __forceinline__ bool plan_lookup(const DecodeParams& p, RowsOf rows_of,
+                                            ZeroEmpty zero_empty, int w, int64_t* red,
+                                            PlanHit* hits, int64_t& W, int& nw, int64_t& x0,
+                                            int64_t& x1, PlanHit (&out)[2]) {
+  const ReqSource src = source_of<kPaged, kCascade>(p);
+  if (p.batch <= kT) {
+    const int b = threadIdx.x;
+    Req r{};
+    int64_t R = 0;
+    if (b < p.batch) {
+      r = load_req(src, b);
+      R = rows_of(r);
+      zero_empty(r);
+    }
+    int64_t total;
+    const int64_t cum = block_excl_scan_i64<kT>(R, red, total);
+    W = uniform(total);
+    if (W == 0) return false;
+    nw = effective_workers(W, p.num_workers);
+    if (w >= nw) return false;
+    x0 = worker_begin(w, W, nw);
+    x1 = worker_begin(w + 1, W, nw);
+    if (threadIdx.x < 2) hits[threadIdx.x].b = -1;
+    __syncthreads();
+    if (R > 0 && x0 >= cum && x0 < cum + R) hits[0] = PlanHit{b, cum, r};
+    if (R > 0 && x1 < W && x1 >= cum && x1 < cum + R) hits[1] = PlanHit{b, cum, r};
+    __syncthreads();
+  } else {
+    int64_t acc = 0;
+    for (int b = threadIdx.x; b < p.batch; b += kT) {
+      const Req r = load_req(src, b);
+      acc += rows_of(r);
+      zero_empty(r);
+    }
+    W = uniform(block_sum_i64<kT>(acc, red));
+    if (W == 0) return false;
+    nw = effective_workers(W, p.num_workers);
+    if (w >= nw) return false;
+    x0 = worker_begin(w, W, nw);
+    x1 = worker_begin(w + 1, W, nw);
+    const int64_t xs[2] = {x0, x1 < W ? x1 : -1};
+    __shared__ int lb[2];
+    __shared__ int64_t lcum[2];
+    plan_locate2<kPaged, kT, kCascade>(p, rows_of, xs, red, lb, lcum);
+    // Threads 0 and 1 fetch the two requests found.
+    if (threadIdx.x < 2) {
+      const int i = threadIdx.x;
+      const int b = lb[i];
+      hits[i].b = b;
+      hits[i].cum = lcum[i];
+      if (b >= 0) hits[i].r = load_req(src, b);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    out[i].b = uniform(hits[i].b);
+    out[i].cum = uniform(hits[i].cum);
+    out[i].r = hits[i].r;
+    uniformize(out[i].r);
+  }
+  return true;
 }
 
 // ---------------------------------------------------------------- softmax state

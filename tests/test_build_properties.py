@@ -79,7 +79,7 @@ def test_bf16_decode_kernel_scratch_is_small(compiled):
 
 def test_group_decode_kernel_scratch_is_small(compiled_groups):
     _, usage = compiled_groups
-    assert _scratch(usage, "mla_decode_groups_fp8_kernel") <= 336
+    assert _scratch(usage, "mla_decode_groups_fp8_kernel") <= 368
 
 
 def test_group_tile_loop_touches_no_scratch(compiled_groups):
