@@ -71,20 +71,22 @@ typedef enum {
 
 /*
  * Workspace bytes mla_decode needs on the current device for this call shape.
- * The workspace holds fp32 partial answers of the KV splits and one 16-byte
- * split descriptor per (query token, head group); its size depends only on
- * the device's compute-unit count and the arguments below, not on KV lengths
- * or the storage type.  Returns 0 for invalid shapes.
+ * The workspace holds the partial answers of the KV splits (o rows and their
+ * lse) and one 16-byte split descriptor per (query token, head group); its
+ * size depends only on the device's compute-unit count and the arguments
+ * below, not on KV lengths or the storage type.  Returns 0 for invalid shapes.
  *
  * Two kernels serve mla_decode.  The standard one gives each worker
  * workgroup a contiguous range of (token, head group) rows, at most two of
- * them partial (two 16x512 fp32 partial slots per worker), one worker per
- * compute unit.  When num_heads / 16 * max_seqlen_q >= 4 and the storage is
- * FP8, the group-mode kernel instead walks 8 row groups of one request over a
- * single shared KV range, so each gathered cache row feeds 128 query rows; it
- * also runs one worker per compute unit, with sixteen partial slots each (held
- * in bf16).  The workspace is sized for the larger layout whenever the shape
- * qualifies.
+ * them partial (two 16x512 partial slots per worker), one worker per compute
+ * unit.  When num_heads / 16 * max_seqlen_q >= 4 and the storage is FP8, the
+ * group-mode kernel instead walks 8 row groups of one request over a single
+ * shared KV range, so each gathered cache row feeds 128 query rows; it also
+ * runs one worker per compute unit, with sixteen partial slots each.
+ * Partial o rows are stored in bf16 for an FP8 cache with a bf16 output and in
+ * fp32 otherwise (a bf16 cache, or an fp32 output as mla_decode_dcp can ask
+ * for); the slots are sized for fp32 either way.  The workspace is sized for
+ * the group-mode layout whenever the shape qualifies.
  */
 size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, int max_seqlen_q);
 
@@ -300,8 +302,11 @@ const char* mla_status_string(int status);
  *  must hold at least qlen_b - 1 entries (a token's masked entries then all
  *  lie in the suffix); this is the caller's contract, not checked.
  *  workspace: at least mla_decode_cascade_workspace_bytes(...) bytes.
- *  Runs three steps on `stream`: the prefix pass, the suffix pass (each with
- *  its split combine) and an LSE merge of the two into o / lse.
+ *  Runs three kernels on `stream`: one group-mode decode launch that takes
+ *  the prefix pass (every token against the shared prefix) and the suffix
+ *  pass (each request against its own suffix) as one balanced work stream,
+ *  writing fp32 o / lse for each pass into the workspace; its split combine;
+ *  and an LSE merge of the two passes into o / lse.
  */
 size_t mla_decode_cascade_workspace_bytes(int batch, int num_q_tokens, int num_heads,
                                           int max_seqlen_q);
