@@ -279,10 +279,22 @@ def layer_step_line(mla, dev, steps, warmup, n_layers=4):
         r, d, b = rope(w, s), dec(w), bmm(s)
         return lambda: (r(), d(), b())
 
+    ws_step = mla.new_workspace(
+        mla._lib.lib().mla_decode_step_workspace_bytes(w0.batch, T, Hp, 1), dev)
+
+    def fused(w, s):
+        return lambda: mla.decode_step(s.q_latent, s.q_pe, s.k_latent, s.k_pe, s.positions,
+                                       s.cos_sin, slots, w.kv_pool, w.qo_indptr, w.kv_indptr,
+                                       w.kv_indices, w.sm_scale, s.w_uv, num_heads_pad=Hp,
+                                       q_scale=w.q_scale, kv_scale=w.kv_scale, o_latent=o,
+                                       out=v, max_seqlen_q=1, workspace=ws_step)
+
     res = {}
     for name, calls in (("rope_quant_cache", [rope(w, s) for w, s in zip(layers, sur)]),
                         ("latent_to_v", [bmm(s) for s in sur]),
-                        ("layer_step", [step(w, s) for w, s in zip(layers, sur)])):
+                        ("decode", [dec(w) for w in layers]),
+                        ("layer_step", [step(w, s) for w, s in zip(layers, sur)]),
+                        ("layer_step_fused", [fused(w, s) for w, s in zip(layers, sur)])):
         wall, ev, n = time_graph(calls, steps, warmup, per_graph=8)
         res[name] = {"us_per_call": round(wall * 1e6, 2), "event_us": stats_us(ev), "calls": n}
     rope_bytes = (T * H * (512 + 64) * 2 + T * 576 * 2 + T * 8 + T * 256
@@ -292,8 +304,14 @@ def layer_step_line(mla, dev, steps, warmup, n_layers=4):
     res["latent_to_v"]["algorithmic_bytes_per_call"] = bmm_bytes
     res["latent_to_v"]["GB_s"] = round(bmm_bytes / (res["latent_to_v"]["us_per_call"] * 1e-6) / 1e9, 2)
     res["layer_step"]["decode_bytes_per_call"] = accounting.workload_bytes(w0)
+    res["layer_step_fused"]["over_decode_us"] = round(
+        res["layer_step_fused"]["us_per_call"] - res["decode"]["us_per_call"], 2)
+    res["layer_step"]["over_decode_us"] = round(
+        res["layer_step"]["us_per_call"] - res["decode"]["us_per_call"], 2)
     res["workload"] = (f"c16 (T={T}, {H} heads padded to {Hp}): rope + fp8 + cache write of the new "
-                       f"entries, the decode, then o (T,{H},512) x W_uv ({H},128,512)")
+                       f"entries, the decode, then o (T,{H},512) x W_uv ({H},128,512); "
+                       f"layer_step: three calls (mla_rope_quant_cache, mla_decode, "
+                       f"mla_latent_to_v); layer_step_fused: mla_decode_step (two launches)")
     del layers, sur
     torch.cuda.empty_cache()
     return res

@@ -375,6 +375,54 @@ mla_status mla_latent_to_v(const void* o_latent, const void* w_uv, void* out, in
                            int num_heads, int num_heads_pad, void* stream);
 
 /*
+ * One decode step of an MLA layer with the steps either side folded in
+ * ("[Kimi-K3 MLA TP8] MLA performance", Sec. 3: the fused rope / concat /
+ * fp8 op that produces q and writes the step's new cache entries, the decode,
+ * and the batched GEMM to v_head_dim; Sec. 2 geometry).  The same results as
+ *   mla_rope_quant_cache(q_latent, q_pe, k_latent, k_pe, positions, cos_sin,
+ *                        max_pos, rope_style, q_fp8, num_q_tokens, num_heads,
+ *                        num_heads_pad, kv_pool, pool_entries, slot_mapping,
+ *                        q_scale, kv_scale);
+ *   mla_decode(q_fp8, FP8, kv_pool, FP8, ..., o_latent, ..., num_heads_pad, ...);
+ *   mla_latent_to_v(o_latent, w_uv, out, num_q_tokens, num_heads, num_heads_pad);
+ * in three launches instead of four: a prologue kernel, one block per decode
+ * worker, does a share of the rope / fp8 / cache-write step (q rows into the
+ * workspace) and computes that worker's plan; the decode kernel starts from
+ * the stored plan; one kernel after it merges split rows and applies w_uv.  The new cache entries, o_latent, lse and out equal the
+ * three-call chain's bit for bit.
+ *
+ *  Arguments as for mla_rope_quant_cache (num_heads = the real heads,
+ *  num_heads_pad a positive multiple of 16), mla_decode (FP8 cache, page_size
+ *  1) and mla_latent_to_v, all device memory except the sizes and sm_scale.
+ *  o_latent (num_q_tokens, num_heads_pad, 512) bf16 is written as mla_decode's
+ *  o; out (num_q_tokens, num_heads, 128) bf16 as mla_latent_to_v's.
+ *  Contract (not checked): token j of a request with qlen tokens and n
+ *  entries has its new entry listed at position n - qlen + j of the request's
+ *  kv_indices, and that index equals slot_mapping of the token (or the token's
+ *  slot is negative or >= pool_entries, and nothing is written); other rows
+ *  of the pool are not written during the call.
+ *  workspace: at least mla_decode_step_workspace_bytes(batch, num_q_tokens,
+ *  num_heads_pad, max_seqlen_q) bytes (the decode's workspace, the fp8 q
+ *  rows and the workers' plans); contents on entry do not matter.
+ * Errors: NULL pointers (MLA_ERR_NULL_POINTER); num_heads_pad not a positive
+ * multiple of 16 (MLA_ERR_UNSUPPORTED); the shape checks of the three calls
+ * (MLA_ERR_BAD_SHAPE); a small workspace (MLA_ERR_WORKSPACE_TOO_SMALL).
+ */
+size_t mla_decode_step_workspace_bytes(int batch, int num_q_tokens, int num_heads_pad,
+                                       int max_seqlen_q);
+
+mla_status mla_decode_step(const void* q_latent, const void* q_pe, const void* k_latent,
+                           const void* k_pe, const int32_t* positions, const float* cos_sin,
+                           int max_pos, int rope_style, const int32_t* slot_mapping,
+                           void* kv_pool, int64_t pool_entries, const int32_t* qo_indptr,
+                           const int32_t* kv_indptr, const int32_t* kv_indices,
+                           int64_t kv_indices_len, int batch, int num_q_tokens, int num_heads,
+                           int num_heads_pad, int max_seqlen_q, float sm_scale,
+                           const float* q_scale, const float* kv_scale, const void* w_uv,
+                           void* o_latent, void* out, int return_lse, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Host mirror of the work planner, for tests: given host copies of qo_indptr
  * and kv_indptr, fill `out` (capacity `out_cap` pieces, 8 int64 each:
  * worker, token, head_group, kv_begin, kv_end, unit_len, slot, is_complete)

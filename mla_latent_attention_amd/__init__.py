@@ -28,6 +28,7 @@ __all__ = [
     "decode_noalloc",
     "rope_quant_cache",
     "latent_to_v",
+    "decode_step",
     "cascade_workspace_bytes",
     "new_workspace",
     "MLAError",
@@ -503,3 +504,75 @@ def latent_to_v(o_latent, w_uv, *, out=None):
                                         _stream(dev))
     _lib.check(status, "mla_latent_to_v")
     return out
+
+
+def decode_step(q_latent, q_pe, k_latent, k_pe, positions, cos_sin, slot_mapping, kv_pool,
+                qo_indptr, kv_indptr, kv_indices, sm_scale, w_uv, *, num_heads_pad: int,
+                rope_style: int = 0, q_scale=None, kv_scale=None, return_lse: bool = False,
+                o_latent=None, out=None, lse=None, max_seqlen_q: int | None = None,
+                workspace=None):
+    """One decode step of an MLA layer (mla_decode_step): the rope / fp8 /
+    cache-write step, the decode and the latent -> v map in two launches.
+    Returns out (T, H, 128) bf16, and o_latent (T, num_heads_pad, 512) bf16
+    (and lse (T, num_heads_pad) if return_lse); kv_pool's new entries are
+    written.  Arguments as for rope_quant_cache, decode (fp8 pool, page size 1)
+    and latent_to_v; w_uv (H, 128, 512) bf16 gives the real head count."""
+    dev = q_latent.device
+    if q_latent.dim() != 3 or q_latent.shape[2] != LATENT_DIM:
+        raise ValueError("q_latent must be (T, H, 512)")
+    T, H, _ = q_latent.shape
+    Hp = int(num_heads_pad)
+    _need(q_latent, "q_latent", dev, torch.bfloat16)
+    _need(q_pe, "q_pe", dev, torch.bfloat16, (T, H, 64))
+    _need(k_latent, "k_latent", dev, torch.bfloat16, (T, LATENT_DIM))
+    _need(k_pe, "k_pe", dev, torch.bfloat16, (T, 64))
+    _need(positions, "positions", dev, torch.int32, (T,))
+    _need(slot_mapping, "slot_mapping", dev, torch.int32, (T,))
+    _need(cos_sin, "cos_sin", dev, torch.float32)
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != 64:
+        raise ValueError("cos_sin must be (max_pos, 64)")
+    if kv_pool.dim() == 4:
+        kv_pool = kv_pool.view(-1, ROW_DIM)
+    _need(kv_pool, "kv_pool", dev, torch.float8_e4m3fn)
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_DIM:
+        raise ValueError("kv_pool must be (N, 576)")
+    B = qo_indptr.numel() - 1
+    _need(qo_indptr, "qo_indptr", dev, torch.int32, (B + 1,))
+    _need(kv_indptr, "kv_indptr", dev, torch.int32, (B + 1,))
+    _need(kv_indices, "kv_indices", dev, torch.int32)
+    _need(w_uv, "w_uv", dev, torch.bfloat16, (H, 128, LATENT_DIM))
+    for name, s in (("q_scale", q_scale), ("kv_scale", kv_scale)):
+        if s is not None:
+            _need(s, name, dev, torch.float32)
+            if s.numel() != 1:
+                raise ValueError(f"{name} must hold one value")
+    if o_latent is None:
+        o_latent = torch.empty((T, Hp, LATENT_DIM), dtype=torch.bfloat16, device=dev)
+    _need(o_latent, "o_latent", dev, torch.bfloat16, (T, Hp, LATENT_DIM))
+    if out is None:
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", dev, torch.bfloat16, (T, H, 128))
+    if return_lse:
+        if lse is None:
+            lse = torch.empty((T, Hp), dtype=torch.float32, device=dev)
+        _need(lse, "lse", dev, torch.float32, (T, Hp))
+    if max_seqlen_q is None:
+        max_seqlen_q = int((qo_indptr[1:] - qo_indptr[:-1]).max().item()) if B > 0 else 1
+    if workspace is None:
+        need = _lib.lib().mla_decode_step_workspace_bytes(B, T, Hp, int(max_seqlen_q))
+        if need == 0:
+            raise ValueError("unsupported decode_step shape")
+        workspace = new_workspace(need, dev)
+    _need(workspace, "workspace", dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    status = _lib.lib().mla_decode_step(
+        _ptr(q_latent), _ptr(q_pe), _ptr(k_latent), _ptr(k_pe), _ptr(positions), _ptr(cos_sin),
+        cos_sin.shape[0], int(rope_style), _ptr(slot_mapping), _ptr(kv_pool), kv_pool.shape[0],
+        _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices), kv_indices.numel(), B, T, H, Hp,
+        int(max_seqlen_q), float(sm_scale), _ptr(q_scale), _ptr(kv_scale), _ptr(w_uv),
+        _ptr(o_latent), _ptr(out), 1 if return_lse else 0, _ptr(lse) if return_lse else None,
+        _ptr(workspace), ws_len, _stream(dev))
+    _lib.check(status, "mla_decode_step")
+    if return_lse:
+        return out, o_latent, lse
+    return out, o_latent

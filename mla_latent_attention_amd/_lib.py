@@ -47,6 +47,11 @@ SIGNATURES = {
     "mla_rope_quant_cache": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int, C.c_int, _vp, C.c_int,
                                        C.c_int, C.c_int, _vp, C.c_int64, _vp, _vp, _vp, _vp]),
     "mla_latent_to_v": (C.c_int, [_vp, _vp, _vp, C.c_int, C.c_int, C.c_int, _vp]),
+    "mla_decode_step_workspace_bytes": (C.c_size_t, [C.c_int] * 4),
+    "mla_decode_step": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int, C.c_int, _vp, _vp,
+                                  C.c_int64, _vp, _vp, _vp, C.c_int64, C.c_int, C.c_int, C.c_int,
+                                  C.c_int, C.c_int, C.c_float, _vp, _vp, _vp, _vp, _vp, C.c_int,
+                                  _vp, _vp, C.c_size_t, _vp]),
     "mla_plan_host": (C.c_int64, [_vp, _vp, _vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, _vp,
                                   C.c_int64]),
     "mla_plan_groups_host": (C.c_int64, [_vp, _vp, _vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,

@@ -295,6 +295,16 @@ size_t mla_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 namespace {
 
+// The layer step's workspace after the decode's: the fp8 q rows (T, H_pad,
+// 576) the prologue builds, then one plan per worker.
+size_t step_q_bytes(int num_q_tokens, int num_heads_pad) {
+  return mla::align256((size_t)num_q_tokens * num_heads_pad * mla::kRowDim);
+}
+size_t step_extra_bytes(int num_q_tokens, int num_heads_pad, int num_workers) {
+  return step_q_bytes(num_q_tokens, num_heads_pad) +
+         mla::align256((size_t)num_workers * sizeof(mla::WorkerPlan));
+}
+
 // Cascade workspace: the group-mode decode workspace for the one-launch call
 // (2T virtual tokens), followed by its fp32 outputs, parts (2, T, H, 512) and
 // lse_parts (2, T, H): prefix first, suffix second (fp32 keeps the merge from
@@ -456,6 +466,93 @@ mla_status mla_rope_quant_cache(const void* q_latent, const void* q_pe, const vo
           cos_sin, max_pos, rope_style, static_cast<uint8_t*>(q_out), num_q_tokens, num_heads,
           num_heads_pad, static_cast<uint8_t*>(kv_pool), pool_entries, slot_mapping, q_scale,
           kv_scale, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+size_t mla_decode_step_workspace_bytes(int batch, int num_q_tokens, int num_heads_pad,
+                                       int max_seqlen_q) {
+  if (!shape_ok(batch, num_q_tokens, num_heads_pad, max_seqlen_q)) return 0;
+  if (num_heads_pad % mla::kGroup != 0) return 0;
+  const int cus = current_cu_count();
+  if (cus <= 0) return 0;
+  const int64_t num_units = (int64_t)num_q_tokens * (num_heads_pad / mla::kGroup);
+  return mla::align256(mla::workspace_bytes(cus, num_units, mla::slots_per_worker(false))) +
+         step_extra_bytes(num_q_tokens, num_heads_pad, cus);
+}
+
+mla_status mla_decode_step(const void* q_latent, const void* q_pe, const void* k_latent,
+                           const void* k_pe, const int32_t* positions, const float* cos_sin,
+                           int max_pos, int rope_style, const int32_t* slot_mapping,
+                           void* kv_pool, int64_t pool_entries, const int32_t* qo_indptr,
+                           const int32_t* kv_indptr, const int32_t* kv_indices,
+                           int64_t kv_indices_len, int batch, int num_q_tokens, int num_heads,
+                           int num_heads_pad, int max_seqlen_q, float sm_scale,
+                           const float* q_scale, const float* kv_scale, const void* w_uv,
+                           void* o_latent, void* out, int return_lse, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q_latent || !q_pe || !k_latent || !k_pe || !positions || !cos_sin || !slot_mapping ||
+      !kv_pool || !qo_indptr || !kv_indptr || !kv_indices || !w_uv || !o_latent || !out)
+    return MLA_ERR_NULL_POINTER;
+  if (return_lse && !lse) return MLA_ERR_NULL_POINTER;
+  if (num_heads_pad <= 0 || num_heads_pad % mla::kGroup != 0) return MLA_ERR_UNSUPPORTED;
+  if (num_heads < 1 || num_heads > num_heads_pad || max_pos < 1 ||
+      (rope_style != 0 && rope_style != 1))
+    return MLA_ERR_BAD_SHAPE;
+  if (!shape_ok(batch, num_q_tokens, num_heads_pad, max_seqlen_q)) return MLA_ERR_BAD_SHAPE;
+  if (pool_entries < 1 || kv_indices_len < 0 || kv_indices_len > 0x7FFFFFFF)
+    return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)num_q_tokens * num_heads_pad > 0x7FFFFFFF) return MLA_ERR_BAD_SHAPE;
+  const int cus = current_cu_count();
+  if (cus <= 0) return MLA_ERR_HIP;
+  const int G = num_heads_pad / mla::kGroup;
+  const int64_t num_units = (int64_t)num_q_tokens * G;
+  const int slots = mla::slots_per_worker(false);
+  const size_t dec_bytes = mla::align256(mla::workspace_bytes(cus, num_units, slots));
+  if (!workspace ||
+      workspace_bytes < dec_bytes + step_extra_bytes(num_q_tokens, num_heads_pad, cus))
+    return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+  mla::DecodeParams p;
+  p.q_out = static_cast<uint8_t*>(workspace) + dec_bytes;  // built by the call
+  p.q = p.q_out;
+  p.plans = reinterpret_cast<mla::WorkerPlan*>(p.q_out + step_q_bytes(num_q_tokens, num_heads_pad));
+  p.kv = static_cast<const uint8_t*>(kv_pool);
+  p.kv_out = static_cast<uint8_t*>(kv_pool);
+  p.pool_entries = pool_entries;
+  p.o = static_cast<uint16_t*>(o_latent);
+  p.o32 = nullptr;
+  p.part_fp32 = 0;
+  p.qo_indptr = qo_indptr;
+  p.kv_indptr = kv_indptr;
+  p.kv_indices = kv_indices;
+  p.kv_indices_len = (int)kv_indices_len;
+  p.batch = batch;
+  p.num_tokens = num_q_tokens;
+  p.num_heads = num_heads_pad;
+  p.sm_scale = sm_scale;
+  p.q_scale = q_scale;
+  p.kv_scale = kv_scale;
+  p.lse = return_lse ? lse : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  p.desc = reinterpret_cast<int4*>(ws);
+  p.part_o = reinterpret_cast<float*>(ws + mla::desc_bytes(num_units));
+  p.part_lse = reinterpret_cast<float*>(ws + mla::desc_bytes(num_units) +
+                                        mla::part_o_bytes(cus, slots));
+  p.num_workers = cus;
+  p.causal = 1;
+  p.q_latent = static_cast<const uint16_t*>(q_latent);
+  p.q_pe = static_cast<const uint16_t*>(q_pe);
+  p.k_latent = static_cast<const uint16_t*>(k_latent);
+  p.k_pe = static_cast<const uint16_t*>(k_pe);
+  p.positions = positions;
+  p.cos_sin = cos_sin;
+  p.max_pos = max_pos;
+  p.rope_style = rope_style;
+  p.real_heads = num_heads;
+  p.slot_mapping = slot_mapping;
+  if (mla::launch_decode_step(p, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out),
+                              static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include "mla_device.h"
+#include "mla_rope.h"
 
 namespace mla {
 
@@ -627,16 +628,14 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
 }
 
 // One worker: locate its share of the KV stream and run its pieces.
-template <class Path, bool kPaged>
-__device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShared& sh) {
+// This worker's range [p0, p1) of the stream and the cursor at p0: the
+// equal-share boundaries, each snapped to a unit boundary within kSnapRows
+// (0 and W are boundaries already).  The lookup also zeroes the empty tokens
+// this block owns.  False: the worker has nothing to do.  All threads call it.
+template <bool kPaged>
+__device__ __forceinline__ bool plan_worker(const DecodeParams& p, int64_t* red, PlanHit* hits,
+                                            Cursor& c, int64_t& p0, int64_t& p1) {
   const int G = p.num_heads / kGroup;
-  // The scales first: their loads overlap the planner's.
-  const float qs = p.q_scale ? *p.q_scale : 1.0f;
-  const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
-
-  // This worker's range [p0, p1) of the stream: the equal-share boundaries,
-  // each snapped to a unit boundary within kSnapRows (0 and W are boundaries
-  // already).  The lookup also zeroes the empty tokens this block owns.
   const int w = blockIdx.x;
   int64_t W, x0, x1;
   int nw;
@@ -648,28 +647,52 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShare
             for (int j = 0; j < nempty; ++j)
               if ((r.q_base + j) % (int)gridDim.x == (int)blockIdx.x) zero_token(p, r.q_base + j);
           },
-          w, sh.red, sh.hits, W, nw, x0, x1, hit))
-    return;
-  if (hit[0].b < 0 || (x1 < W && hit[1].b < 0)) return;  // not reached with consistent indptr
+          w, red, hits, W, nw, x0, x1, hit))
+    return false;
+  if (hit[0].b < 0 || (x1 < W && hit[1].b < 0)) return false;  // not with consistent indptr
   const ReqSource src = source_of<kPaged>(p);
-  Cursor c;
   cursor_in_request(c, hit[0].b, hit[0].r, x0 - hit[0].cum, G);
   uniformize(c);
-  int64_t p1 = W;
+  p1 = W;
   if (x1 < W) {
     Cursor c1;
     cursor_in_request(c1, hit[1].b, hit[1].r, x1 - hit[1].cum, G);
     uniformize(c1);
     p1 = snap_at(x1, c1);
   }
-  const int64_t p0 = snap_at(x0, c);
-  if (p0 >= p1) return;
+  p0 = snap_at(x0, c);
+  if (p0 >= p1) return false;
   if (p0 < x0) {
     c.k = 0;  // moved back to the start of its unit
   } else if (p0 > x0) {  // moved forward past the end of its unit
-    if (!cursor_next_unit(c, src, p.batch, G)) return;
+    if (!cursor_next_unit(c, src, p.batch, G)) return false;
     uniformize(c);
   }
+  return true;
+}
+
+// kPlanned: the plan comes from p.plans (the layer step's prologue kernel
+// computed it) instead of the planner.
+template <class Path, bool kPaged, bool kPlanned = false>
+__device__ __forceinline__ void decode_worker(const DecodeParams& p, DecodeShared& sh) {
+  const int G = p.num_heads / kGroup;
+  // The scales first: their loads overlap the planner's.
+  const float qs = p.q_scale ? *p.q_scale : 1.0f;
+  const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
+  const int w = blockIdx.x;
+  Cursor c;
+  int64_t p0, p1;
+  if constexpr (kPlanned) {
+    const WorkerPlan& wp = p.plans[w];
+    if (!uniform(wp.ok)) return;
+    p0 = uniform(wp.p0);
+    p1 = uniform(wp.p1);
+    c = wp.c;
+    uniformize(c);
+  } else {
+    if (!plan_worker<kPaged>(p, sh.red, sh.hits, c, p0, p1)) return;
+  }
+  const ReqSource src = source_of<kPaged>(p);
   const float cs = p.sm_scale * kLog2e * qs * ks;
 
   int64_t pos = p0;
@@ -722,6 +745,52 @@ void mla_decode_bf16_kernel(const DecodeParams p) {
   decode_worker<Bf16Path, false>(p, sh);
 }
 
+// The layer step's decode (fp8, page_size 1): the standard kernel on the plan
+// and q rows the step's prologue kernel left in the workspace.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_fp8_planned_kernel(const DecodeParams p) {
+  __shared__ DecodeShared sh;
+  decode_worker<Fp8Path, false, true>(p, sh);
+}
+
+// The layer step's prologue, one block per decode worker: a 1/gridDim share of
+// the rope / fp8 / cache-write step (q rows of every padded head and each
+// token's new cache entry, in chunks of 8 codes), then the worker's plan,
+// stored for the decode kernel.  The stores of both reach the decode at the
+// kernel boundary.
+struct PrologueShared {
+  int64_t red[kWaves];
+  PlanHit hits[2];
+};
+
+__global__ __launch_bounds__(kThreads) void mla_step_prologue_kernel(const DecodeParams p) {
+  __shared__ PrologueShared sh;
+  const int Hp = p.num_heads;
+  const int64_t per_token = (int64_t)(Hp + 1) * kChunksPerRow;
+  const int64_t items = (int64_t)p.num_tokens * per_token;
+  const int64_t share = (items + gridDim.x - 1) / gridDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * share;
+  const int64_t i1 = i0 + share < items ? i0 + share : items;
+  for (int64_t it = i0 + threadIdx.x; it < i1; it += kThreads) {
+    const int t = (int)(it / per_token);
+    const int rem = (int)(it - (int64_t)t * per_token);
+    const int row = rem / kChunksPerRow;
+    rope_quant_item(p.q_latent, p.q_pe, p.k_latent, p.k_pe, p.positions, p.cos_sin, p.max_pos,
+                    p.rope_style, p.q_out, p.real_heads, Hp, p.kv_out, p.pool_entries,
+                    p.slot_mapping, p.q_scale, p.kv_scale, t, row, rem - row * kChunksPerRow);
+  }
+  Cursor c;
+  int64_t p0 = 0, p1 = 0;
+  const bool ok = plan_worker<false>(p, sh.red, sh.hits, c, p0, p1);
+  if (threadIdx.x == 0) {
+    WorkerPlan& wp = p.plans[blockIdx.x];
+    wp.ok = ok ? 1 : 0;
+    wp.p0 = p0;
+    wp.p1 = p1;
+    wp.c = c;
+  }
+}
+
 // Paged-cache builds (page_size > 1).
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_fp8_paged_kernel(const DecodeParams p) {
@@ -752,23 +821,27 @@ constexpr int kCombineWaves = 4;
 constexpr int kCombineThreads = 64 * kCombineWaves;
 constexpr int kCombineBatch = 16;
 
+template <int kHalves>
 struct CombineShared {
-  float4 acc[kCombineWaves][64];
+  float4 acc[kCombineWaves][kHalves][64];
   float m[kCombineWaves];
   float sum[kCombineWaves];
 };
 
-template <int kSlots, bool kBf16Parts>
-__device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShared& sh) {
-  const int64_t u = blockIdx.x;
-  const int4 d = p.desc[u];
-  if (d.w == 0) return;
-  const int G = p.num_heads / kGroup;
+// The merge of row n of split unit d (its descriptor) over its slots, for
+// kHalves consecutive 256-dim halves from h0: lane l takes dims
+// 256 (h0 + i) + 4l .. + 3 of half i.  On return the wave that holds the
+// result (wave 0; the return value says which) has the unnormalised sums in
+// acc, the row's running maximum in M and its weight sum in sum.  All four
+// waves of the block must call it (the many-slot path meets at a barrier);
+// every element goes through the same operations whatever kHalves is.
+template <int kSlots, bool kBf16Parts, int kHalves>
+__device__ __forceinline__ bool combine_row(const DecodeParams& p, CombineShared<kHalves>& sh,
+                                            const int4 d, int n, int h0,
+                                            float4 (&acc)[kHalves], float& M, float& sum) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int n = blockIdx.y >> 1, h = blockIdx.y & 1;
   const int w0 = d.x, S = d.y - d.x + 1;
   const bool many = S > kCombineBatch;  // uniform over the block
-  if (!many && wv != 0) return;
   const int pos = d.z % (kSlots / 2);
   auto slot_of = [&](int i) -> int64_t {
     return i == 0 ? (int64_t)d.z : (int64_t)kSlots * (w0 + i) + pos;
@@ -776,24 +849,30 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShare
 
   // Slots in batches: every load of a batch is issued before any is used,
   // with an online rescale across batches.  A slot whose lse is -inf (its
-  // piece held none of the row's visible entries) gets weight 0.
-  float M = neg_inf(), sum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // piece held none of the row's visible entries) gets weight 0.  With at
+  // most kCombineBatch slots only wave 0 has a batch.
+  M = neg_inf();
+  sum = 0.f;
+#pragma unroll
+  for (int hf = 0; hf < kHalves; ++hf) acc[hf] = make_float4(0.f, 0.f, 0.f, 0.f);
   const int step = many ? kCombineWaves * kCombineBatch : kCombineBatch;
   for (int i0 = wv * kCombineBatch; i0 < S; i0 += step) {
-    float4 x[kCombineBatch];
+    float4 x[kCombineBatch][kHalves];
     float ls[kCombineBatch];
 #pragma unroll
     for (int j = 0; j < kCombineBatch; ++j) {  // past-the-end slots reload the last one, weight 0
       const int64_t slot = slot_of(imin(i0 + j, S - 1));
       ls[j] = p.part_lse[slot * kGroup + n];
-      const int64_t e0 = (slot * kGroup + n) * kLatent + 256 * h + 4 * lane;
-      if constexpr (kBf16Parts) {
-        const uint2 b = *(const uint2*)((const uint16_t*)p.part_o + e0);
-        x[j] = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
-                           __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
-      } else {
-        x[j] = *(const float4*)(p.part_o + e0);
+#pragma unroll
+      for (int hf = 0; hf < kHalves; ++hf) {
+        const int64_t e0 = (slot * kGroup + n) * kLatent + 256 * (h0 + hf) + 4 * lane;
+        if constexpr (kBf16Parts) {
+          const uint2 b = *(const uint2*)((const uint16_t*)p.part_o + e0);
+          x[j][hf] = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                                 __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+        } else {
+          x[j][hf] = *(const float4*)(p.part_o + e0);
+        }
       }
     }
     // Keep the scheduler from interleaving these loads with their uses, which
@@ -806,55 +885,81 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShare
     if (bm == neg_inf()) continue;  // nothing visible yet: acc and sum stay 0
     const float alpha = (M == neg_inf()) ? 0.f : fast_exp2((M - bm) * kLog2e);
     sum *= alpha;
-    acc.x *= alpha;
-    acc.y *= alpha;
-    acc.z *= alpha;
-    acc.w *= alpha;
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf) {
+      acc[hf].x *= alpha;
+      acc[hf].y *= alpha;
+      acc[hf].z *= alpha;
+      acc[hf].w *= alpha;
+    }
     M = bm;
 #pragma unroll
     for (int j = 0; j < kCombineBatch; ++j) {
       const float wt = (i0 + j < S) ? fast_exp2((ls[j] - M) * kLog2e) : 0.f;
       sum += wt;
-      acc.x += wt * x[j].x;
-      acc.y += wt * x[j].y;
-      acc.z += wt * x[j].z;
-      acc.w += wt * x[j].w;
+#pragma unroll
+      for (int hf = 0; hf < kHalves; ++hf) {
+        acc[hf].x += wt * x[j][hf].x;
+        acc[hf].y += wt * x[j][hf].y;
+        acc[hf].z += wt * x[j][hf].z;
+        acc[hf].w += wt * x[j][hf].w;
+      }
     }
   }
   if (many) {
-    sh.acc[wv][lane] = acc;
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf) sh.acc[wv][hf][lane] = acc[hf];
     if (lane == 0) {
       sh.m[wv] = M;
       sh.sum[wv] = sum;
     }
     __syncthreads();
-    if (wv != 0) return;
+    if (wv != 0) return false;
     M = neg_inf();
 #pragma unroll
     for (int i = 0; i < kCombineWaves; ++i) M = fmaxf(M, sh.m[i]);
     sum = 0.f;
-    acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf) acc[hf] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < kCombineWaves; ++i) {
       const float wt = (sh.m[i] == neg_inf()) ? 0.f : fast_exp2((sh.m[i] - M) * kLog2e);
-      const float4 a = sh.acc[i][lane];
       sum += wt * sh.sum[i];
-      acc.x += wt * a.x;
-      acc.y += wt * a.y;
-      acc.z += wt * a.z;
-      acc.w += wt * a.w;
+#pragma unroll
+      for (int hf = 0; hf < kHalves; ++hf) {
+        const float4 a = sh.acc[i][hf][lane];
+        acc[hf].x += wt * a.x;
+        acc[hf].y += wt * a.y;
+        acc[hf].z += wt * a.z;
+        acc[hf].w += wt * a.w;
+      }
     }
   }
+  return wv == 0;
+}
+
+template <int kSlots, bool kBf16Parts>
+__device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShared<1>& sh) {
+  const int64_t u = blockIdx.x;
+  const int4 d = p.desc[u];
+  if (d.w == 0) return;
+  const int G = p.num_heads / kGroup;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = blockIdx.y >> 1, h = blockIdx.y & 1;
+  if (d.y - d.x + 1 <= kCombineBatch && wv != 0) return;  // one wave merges up to a batch
+  float4 acc[1];
+  float M, sum;
+  if (!combine_row<kSlots, kBf16Parts, 1>(p, sh, d, n, h, acc, M, sum)) return;
   const float inv = sum > 0.f ? 1.0f / sum : 0.f;  // a row that sees nothing: o = 0, lse = -inf
   const int64_t t = u / G, g = u % G;
   const int64_t orow = t * p.num_heads + g * kGroup + n;
   if (p.o32 != nullptr) {
     *(float4*)(p.o32 + orow * kLatent + 256 * h + 4 * lane) =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        make_float4(acc[0].x * inv, acc[0].y * inv, acc[0].z * inv, acc[0].w * inv);
   } else {
     uint2 pk;
-    pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
-    pk.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    pk.x = pack_bf16x2(acc[0].x * inv, acc[0].y * inv);
+    pk.y = pack_bf16x2(acc[0].z * inv, acc[0].w * inv);
     *(uint2*)(p.o + orow * kLatent + 256 * h + 4 * lane) = pk;
   }
   if (p.lse != nullptr && h == 0 && lane == 0)
@@ -864,25 +969,100 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShare
 // The standard kernels' split combine: fp8 caches leave bf16 partials, bf16
 // caches fp32 ones.
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const DecodeParams p) {
-  __shared__ CombineShared sh;
+  __shared__ CombineShared<1> sh;
   combine_unit<2, true>(p, sh);
 }
 
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_fp32_kernel(const DecodeParams p) {
-  __shared__ CombineShared sh;
+  __shared__ CombineShared<1> sh;
   combine_unit<2, false>(p, sh);
 }
 
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_groups_kernel(const DecodeParams p) {
-  __shared__ CombineShared sh;
+  __shared__ CombineShared<1> sh;
   combine_unit<2 * kGroupsPerUnit, true>(p, sh);
 }
 
 // Group mode with fp32 partials (calls whose output is fp32).
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_groups_fp32_kernel(
     const DecodeParams p) {
-  __shared__ CombineShared sh;
+  __shared__ CombineShared<1> sh;
   combine_unit<2 * kGroupsPerUnit, false>(p, sh);
+}
+
+// The fused layer step's tail: the split combine and the latent -> v map in
+// one launch ("[Kimi-K3 MLA TP8] MLA performance", Sec. 3: a batched GEMM maps
+// each head's 512-dim latent output to v_head_dim = 128, Sec. 2).  grid
+// (T * H_pad) blocks of four waves, block (t, h): row h of token t's unit is
+// merged from its partials if the unit was split (the same arithmetic as
+// mla_combine_kernel, written to o and lse) or read back from o if the decode
+// wrote it whole; then, for a real head, out[t, h, :] = o[t, h, :] . W[h]^T on
+// v_mfma_f32_16x16x32_bf16 with the bf16 row in every A row and the same
+// operand order and k steps as mla_latent_to_v_kernel, so each output is the
+// one that kernel gives for this row.  Wave w computes outputs
+// [32w, 32w + 32); its W operands are in flight from the block's start.
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_v_kernel(const DecodeParams p,
+                                                                        const uint16_t* w_uv,
+                                                                        uint16_t* vout) {
+  __shared__ CombineShared<2> sh;
+  __shared__ __align__(16) uint16_t orow[kLatent];
+  const int Hp = p.num_heads, G = Hp / kGroup;
+  const int t = blockIdx.x / Hp, h = blockIdx.x - t * Hp;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const bool real = h < p.real_heads;
+
+  uint4 b[2][16];
+  if (real) {
+    const uint16_t* wrow = w_uv + ((int64_t)h * 128 + 32 * wv + (lane & 15)) * kLatent + 8 * (lane >> 4);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int s = 0; s < 16; ++s) b[nt][s] = *(const uint4*)(wrow + nt * 16 * kLatent + 32 * s);
+  }
+
+  const int64_t u = (int64_t)t * G + h / kGroup;
+  const int n = h % kGroup;
+  const int64_t orow_g = (int64_t)t * Hp + h;
+  const int4 d = p.desc[u];
+  if (d.w == 0) {  // a complete unit: the decode wrote the row
+    if (wv == 0) *(uint4*)(orow + 8 * lane) = *(const uint4*)(p.o + orow_g * kLatent + 8 * lane);
+  } else {
+    float4 acc[2];
+    float M, sum;
+    if (combine_row<2, true, 2>(p, sh, d, n, 0, acc, M, sum)) {
+      const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint2 pk;
+        pk.x = pack_bf16x2(acc[hf].x * inv, acc[hf].y * inv);
+        pk.y = pack_bf16x2(acc[hf].z * inv, acc[hf].w * inv);
+        *(uint2*)(p.o + orow_g * kLatent + 256 * hf + 4 * lane) = pk;
+        *(uint2*)(orow + 256 * hf + 4 * lane) = pk;
+      }
+      if (p.lse != nullptr && lane == 0)
+        p.lse[orow_g] = sum > 0.f ? M + fast_log2(sum) * kLn2 : neg_inf();
+    }
+  }
+  __syncthreads();
+  if (!real) return;
+  v4f acc2[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const uint4 a = *(const uint4*)(orow + 8 * (lane >> 4) + 32 * s);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      acc2[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(a), as_v8bf(b[nt][s]), acc2[nt],
+                                                         0, 0, 0);
+  }
+  // Element 0 of lanes 0..15: A row 0, output dim 32 wv + 16 nt + lane.
+  if (lane < 16) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      uint32_t x = __float_as_uint(acc2[nt][0]);
+      x += 0x7FFFu + ((x >> 16) & 1u);  // round to nearest even
+      vout[((int64_t)t * p.real_heads + h) * 128 + 32 * wv + 16 * nt + lane] = (uint16_t)(x >> 16);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- shard merge
@@ -1004,6 +1184,20 @@ hipError_t launch_decode(const DecodeParams& p, int kv_dtype, bool group_mode, h
   else
     hipLaunchKernelGGL(mla_combine_fp32_kernel, dim3(units, 2 * kGroup), dim3(kCombineThreads), 0,
                        stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const DecodeParams& p, const uint16_t* w_uv, uint16_t* vout,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(mla_step_prologue_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_decode_fp8_planned_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream,
+                     p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_combine_v_kernel, dim3((unsigned)(p.num_tokens * p.num_heads)),
+                     dim3(kCombineThreads), 0, stream, p, w_uv, vout);
   return hipGetLastError();
 }
 

@@ -9,6 +9,15 @@
 
 namespace mla {
 
+// A decode worker's share as the planner leaves it (the layer step's prologue
+// kernel stores one per worker): stream range [p0, p1) and the cursor at p0;
+// ok = 0: nothing to do.
+struct WorkerPlan {
+  int64_t p0, p1;
+  Cursor c;
+  int ok;
+};
+
 struct DecodeParams {
   const uint8_t* q;         // (T, H, 576) elements of the storage type
   const uint8_t* kv;        // (pool_entries, 576)
@@ -45,6 +54,21 @@ struct DecodeParams {
   // prefix), the rest from kv_indices2 (the suffixes); -1: off.
   int cascade_prefix = -1;
   const int32_t* kv_indices2 = nullptr;
+  // Layer step (mla_decode_step; only its prologue kernel reads these): the
+  // rope / fp8 / cache-write step's inputs and outputs.
+  const uint16_t* q_latent = nullptr;  // (T, real_heads, 512) bf16
+  const uint16_t* q_pe = nullptr;      // (T, real_heads, 64) bf16, before rotation
+  const uint16_t* k_latent = nullptr;  // (T, 512) bf16: the tokens' new entries
+  const uint16_t* k_pe = nullptr;      // (T, 64) bf16, before rotation
+  const int32_t* positions = nullptr;  // (T), clamped to [0, max_pos)
+  const float* cos_sin = nullptr;      // (max_pos, 64): 32 cos then 32 sin
+  int max_pos = 0;
+  int rope_style = 0;                  // 0: dims (2j, 2j+1) rotate; 1: dims (j, j+32)
+  int real_heads = 0;                  // heads of q_latent / q_pe; the rest are padding
+  const int32_t* slot_mapping = nullptr;  // (T) pool slot of each token's new entry
+  uint8_t* kv_out = nullptr;           // the pool again, writable
+  uint8_t* q_out = nullptr;            // (T, H, 576) fp8 q built by the call (q reads it)
+  WorkerPlan* plans = nullptr;         // (num_workers) plans of the planned decode build
 };
 
 // The planner's view of the call's requests.  Builds without kPaged /
@@ -101,6 +125,10 @@ hipError_t launch_decode_groups(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_merge(const void* o_parts, int parts_fp32, const float* lse_parts, int num_parts,
                         int64_t rows, uint16_t* o, float* lse, hipStream_t stream);
+// The fused layer step: the fused fp8 decode (standard kernel) and the
+// combine + latent -> v kernel (mla_decode.hip).
+hipError_t launch_decode_step(const DecodeParams& p, const uint16_t* w_uv, uint16_t* vout,
+                              hipStream_t stream);
 
 // Steps either side of the decode (mla_surround.hip).
 hipError_t launch_rope_quant_cache(const uint16_t* q_latent, const uint16_t* q_pe,

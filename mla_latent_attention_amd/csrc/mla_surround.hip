@@ -20,6 +20,7 @@
 #include <stdint.h>
 
 #include "mla_internal.h"
+#include "mla_rope.h"
 
 namespace mla {
 
@@ -29,61 +30,7 @@ typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
 
-constexpr int kRopeDim = 64;
-constexpr int kRopeHalf = 32;
-constexpr int kChunk = 8;                      // outputs per thread
-constexpr int kChunksPerRow = kRowDim / kChunk;  // 72
 constexpr int kRopeThreads = 256;
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-// float -> OCP e4m3fn code, round to nearest even, finite values beyond the
-// largest (448) saturate to it, NaN stays NaN.  Integer arithmetic on the
-// fp32 bits, so the result does not depend on a hardware conversion mode.
-__device__ __forceinline__ uint32_t e4m3fn_code(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;  // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |f| >= 448 (and inf): saturate
-  const int e = (int)(a >> 23) - 127;
-  if (e < -6) {
-    // Subnormal range: multiples of 2^-9.  |f| * 2^9 is exact; rint rounds
-    // half to even; 8 * 2^-9 = 2^-6 is code 0x08, the smallest normal.
-    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);
-    return sign | (uint32_t)m;
-  }
-  uint32_t mant = a & 0x7FFFFFu;
-  uint32_t m3 = mant >> 20;
-  const uint32_t rest = mant & 0xFFFFFu;  // the 20 dropped bits
-  if (rest > 0x80000u || (rest == 0x80000u && (m3 & 1u))) ++m3;
-  uint32_t code = ((uint32_t)(e + 7) << 3) + m3;  // a mantissa carry bumps the exponent
-  if (code > 0x7Eu) code = 0x7Eu;
-  return sign | code;
-}
-
-// The rotated value of rope dim i (0..63) of row x at a position whose
-// cos / sin of angle j are cs[j] / cs[32 + j].  style 0: dims (2j, 2j+1)
-// rotate together; style 1: dims (j, j+32).  Products and sums are rounded
-// one at a time (no fused multiply-add), so the value, and the fp8 code it
-// rounds to, is the same on any device.
-__device__ __forceinline__ float rope_dim(const uint16_t* x, const float* cs, int i, int style) {
-#pragma clang fp contract(off)
-  int j, a, b;
-  if (style == 0) {
-    j = i >> 1;
-    a = 2 * j;
-    b = 2 * j + 1;
-  } else {
-    j = i & (kRopeHalf - 1);
-    a = j;
-    b = j + kRopeHalf;
-  }
-  const float c = cs[j], s = cs[kRopeHalf + j];
-  const float xa = bf16_to_f32(x[a]), xb = bf16_to_f32(x[b]);
-  if (i == a) return xa * c - xb * s;
-  return xb * c + xa * s;
-}
 
 }  // namespace
 
@@ -99,43 +46,9 @@ __global__ __launch_bounds__(kRopeThreads) void mla_rope_quant_cache_kernel(
   const int k = blockIdx.y * kRopeThreads + threadIdx.x;
   const int row = k / kChunksPerRow, chunk = k - row * kChunksPerRow;
   if (row > num_heads_pad) return;
-  const int d0 = chunk * kChunk;
-  int pos = positions[t];
-  pos = pos < 0 ? 0 : (pos >= max_pos ? max_pos - 1 : pos);
-  const float* cs = cos_sin + (int64_t)pos * kRopeDim;
-
-  const uint16_t* lat;  // this row's 512 latent dims
-  const uint16_t* pe;   // and its 64 rope dims
-  uint8_t* dst;
-  float scale;
-  if (row < num_heads_pad) {
-    dst = q_out + ((int64_t)t * num_heads_pad + row) * kRowDim + d0;
-    if (row >= num_heads) {  // pad head: zero codes
-      *(uint2*)dst = make_uint2(0u, 0u);
-      return;
-    }
-    lat = q_latent + ((int64_t)t * num_heads + row) * kLatent;
-    pe = q_pe + ((int64_t)t * num_heads + row) * kRopeDim;
-    scale = q_scale ? *q_scale : 1.0f;
-  } else {
-    const int slot = slot_mapping[t];
-    if (slot < 0 || slot >= pool_entries) return;  // no cache write for this token
-    dst = kv_pool + (int64_t)slot * kRowDim + d0;
-    lat = k_latent + (int64_t)t * kLatent;
-    pe = k_pe + (int64_t)t * kRopeDim;
-    scale = kv_scale ? *kv_scale : 1.0f;
-  }
-  uint32_t codes[kChunk];
-#pragma unroll
-  for (int e = 0; e < kChunk; ++e) {
-    const int d = d0 + e;
-    const float v = d < kLatent ? bf16_to_f32(lat[d]) : rope_dim(pe, cs, d - kLatent, rope_style);
-    codes[e] = e4m3fn_code(v / scale);  // stored = real / scale, correctly rounded
-  }
-  uint2 pk;
-  pk.x = codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24);
-  pk.y = codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24);
-  *(uint2*)dst = pk;
+  rope_quant_item(q_latent, q_pe, k_latent, k_pe, positions, cos_sin, max_pos, rope_style, q_out,
+                  num_heads, num_heads_pad, kv_pool, pool_entries, slot_mapping, q_scale, kv_scale,
+                  t, row, chunk);
 }
 
 // grid (ceil(T / 16), H, 2), block 256: wave wv of block (mt, h, nh) computes

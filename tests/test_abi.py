@@ -187,3 +187,29 @@ def test_rope_quant_cache_rejects_bad_arguments(over, status):
 )
 def test_latent_to_v_rejects_bad_arguments(args, status):
     assert _lib.lib().mla_latent_to_v(*args) == status
+
+
+def _step(**over):
+    args = dict(ql=FAKE, qp=FAKE, kl=FAKE, kp=FAKE, pos=FAKE, cs=FAKE, max_pos=100, style=0,
+                slots=FAKE, pool=FAKE, n=1 << 20, qo=FAKE, kvp=FAKE, kvi=FAKE, kvi_len=1000,
+                B=16, T=16, H=12, Hp=16, mq=1, sm=0.07, qs=None, ks=None, w=FAKE, o=FAKE,
+                out=FAKE, ret_lse=0, lse=None, ws=FAKE, ws_len=1 << 30, stream=None)
+    args.update(over)
+    return _lib.lib().mla_decode_step(*args.values())
+
+
+@pytest.mark.parametrize(
+    "over,status",
+    [(dict(ql=None), 1), (dict(slots=None), 1), (dict(w=None), 1), (dict(out=None), 1),
+     (dict(o=None), 1), (dict(ret_lse=1), 1), (dict(Hp=24), 4), (dict(Hp=0), 4),
+     (dict(H=20), 2), (dict(H=0), 2), (dict(style=2), 2), (dict(max_pos=0), 2), (dict(T=0), 2),
+     (dict(mq=65), 2), (dict(n=0), 2), (dict(kvi_len=-1), 2)],
+)
+def test_decode_step_rejects_bad_arguments_before_any_launch(over, status):
+    assert _step(**over) == status
+
+
+def test_decode_step_workspace_size_rejects_bad_shapes():
+    L = _lib.lib()
+    assert L.mla_decode_step_workspace_bytes(16, 16, 24, 1) == 0
+    assert L.mla_decode_step_workspace_bytes(16, 0, 16, 1) == 0
