@@ -645,7 +645,7 @@ __device__ __forceinline__ bool plan_worker(const DecodeParams& p, int64_t* red,
           [&p](const Req& r) {
             const int nempty = req_empty_tokens(r);
             for (int j = 0; j < nempty; ++j)
-              if ((r.q_base + j) % (int)gridDim.x == (int)blockIdx.x) zero_token(p, r.q_base + j);
+              if ((r.q_base + j) % p.num_workers == (int)blockIdx.x) zero_token(p, r.q_base + j);
           },
           w, red, hits, W, nw, x0, x1, hit))
     return false;
@@ -753,11 +753,12 @@ void mla_decode_fp8_planned_kernel(const DecodeParams p) {
   decode_worker<Fp8Path, false, true>(p, sh);
 }
 
-// The layer step's prologue, one block per decode worker: a 1/gridDim share of
-// the rope / fp8 / cache-write step (q rows of every padded head and each
-// token's new cache entry, in chunks of 8 codes), then the worker's plan,
-// stored for the decode kernel.  The stores of both reach the decode at the
-// kernel boundary.
+// The layer step's prologue: blocks 0 .. num_workers-1 compute and store the
+// decode workers' plans (and zero the empty tokens, as the decode's planner
+// does); the blocks after them do the rope / fp8 / cache-write step, one
+// chunk of 8 codes per thread (q rows of every padded head, then each token's
+// new cache entry), so both run side by side.  The stores reach the decode at
+// the kernel boundary.
 struct PrologueShared {
   int64_t red[kWaves];
   PlanHit hits[2];
@@ -765,19 +766,18 @@ struct PrologueShared {
 
 __global__ __launch_bounds__(kThreads) void mla_step_prologue_kernel(const DecodeParams p) {
   __shared__ PrologueShared sh;
-  const int Hp = p.num_heads;
-  const int64_t per_token = (int64_t)(Hp + 1) * kChunksPerRow;
-  const int64_t items = (int64_t)p.num_tokens * per_token;
-  const int64_t share = (items + gridDim.x - 1) / gridDim.x;
-  const int64_t i0 = (int64_t)blockIdx.x * share;
-  const int64_t i1 = i0 + share < items ? i0 + share : items;
-  for (int64_t it = i0 + threadIdx.x; it < i1; it += kThreads) {
+  if ((int)blockIdx.x >= p.num_workers) {
+    const int Hp = p.num_heads;
+    const int per_token = (Hp + 1) * kChunksPerRow;
+    const int64_t it = (int64_t)(blockIdx.x - p.num_workers) * kThreads + threadIdx.x;
+    if (it >= (int64_t)p.num_tokens * per_token) return;
     const int t = (int)(it / per_token);
     const int rem = (int)(it - (int64_t)t * per_token);
     const int row = rem / kChunksPerRow;
     rope_quant_item(p.q_latent, p.q_pe, p.k_latent, p.k_pe, p.positions, p.cos_sin, p.max_pos,
                     p.rope_style, p.q_out, p.real_heads, Hp, p.kv_out, p.pool_entries,
                     p.slot_mapping, p.q_scale, p.kv_scale, t, row, rem - row * kChunksPerRow);
+    return;
   }
   Cursor c;
   int64_t p0 = 0, p1 = 0;
@@ -1189,7 +1189,11 @@ hipError_t launch_decode(const DecodeParams& p, int kv_dtype, bool group_mode, h
 
 hipError_t launch_decode_step(const DecodeParams& p, const uint16_t* w_uv, uint16_t* vout,
                               hipStream_t stream) {
-  hipLaunchKernelGGL(mla_step_prologue_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream, p);
+  const int64_t rope_items = (int64_t)p.num_tokens * (p.num_heads + 1) * kChunksPerRow;
+  const int64_t blocks = p.num_workers + (rope_items + kThreads - 1) / kThreads;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mla_step_prologue_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_decode_fp8_planned_kernel, dim3(p.num_workers), dim3(kThreads), 0, stream,
