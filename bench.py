@@ -41,7 +41,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--layers", type=int, default=8, help="distinct layer caches cycled per step")
-    ap.add_argument("--variant", default="shared", choices=["shared", "unshared", "blocked"])
+    ap.add_argument("--variant", default="shared",
+                    choices=["shared", "unshared", "blocked", "paged128", "paged128_unshared"],
+                    help="index layout of the timed call (paged128*: mla_decode_paged with "
+                         "128-slot pages, the prefix's pages shared or not)")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the extra timing lines")
@@ -536,11 +539,10 @@ def measured_traffic(variant):
             with open(os.path.join(ROOT, path), "rb") as f:
                 if hashlib.sha256(f.read()).hexdigest() != want:
                     return None
-    except (OSError, KeyError, ValueError, AttributeError):
+        v = rec["variants"][variant]
+        return int(v["fetch_bytes_per_call"]) + int(v["write_bytes_per_call"])
+    except (OSError, KeyError, ValueError, AttributeError, TypeError):
         return None
-    if variant != rec.get("variant"):
-        return None
-    return int(rec["fetch_bytes_per_call"]) + int(rec["write_bytes_per_call"])
 
 
 def stats_us(ev):
@@ -576,7 +578,11 @@ def main():
         line = config_lines(mla, dev, max(64, a.steps // 4), 8, only=a.only)
         print(json.dumps({"config_only": a.only, **line[a.only]}), flush=True)
         return
-    layers = make_layers(a.layers, a.variant, dev)
+    if a.variant.startswith("paged128"):
+        layers = with_pages(make_layers(a.layers, "shared", dev), 128, dev,
+                            shared=a.variant == "paged128")
+    else:
+        layers = make_layers(a.layers, a.variant, dev)
     w0 = layers[0]
     nbytes = accounting.workload_bytes(w0)
     flops = accounting.workload_flops(w0)
@@ -620,7 +626,9 @@ def main():
         "event_us_per_call": stats_us(ev),
         "roofline": {
             "bound": "hbm",
-            "kernel": "mla_decode call: mla_decode_fp8_kernel + mla_combine_kernel",
+            "kernel": ("mla_decode call: " + ("mla_decode_fp8_paged_kernel" if w0.page_size > 1
+                                              else "mla_decode_fp8_kernel")
+                       + " + mla_combine_kernel"),
             "achieved": round(achieved, 2),
             "peak": PEAK_GBS,
             "unit": "GB/s",
@@ -661,7 +669,7 @@ def main():
         del calls, layers
         torch.cuda.empty_cache()
         out["configs"] = config_lines(mla, dev, max(64, a.steps // 4), 8)
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and w0.page_size == 1:
         o_chk, lse_chk = mla.decode(w0.q, w0.kv_pool, w0.qo_indptr, w0.kv_indptr, w0.kv_indices,
                                     w0.kv_last_page_lens, w0.sm_scale, w0.q_scale, w0.kv_scale,
                                     return_lse=True, max_seqlen_q=1)
