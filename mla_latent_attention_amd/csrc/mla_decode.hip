@@ -118,10 +118,16 @@ __device__ __forceinline__ const uint4* stage_q(uint8_t* dst_bytes, const uint8_
 
 // ---- fp8 e4m3 path: 32-row tiles of 576-byte rows.
 //
-// Lane l gathers tile rows (l%16) and (16 + l%16), bytes [64c + 16*(l/16), +16)
-// for c = 0..8: two K-blocks of 32 dims of the A operand of
-// v_mfma_f32_16x16x32_fp8_fp8 per load, so Q.K^T runs from registers as
-// S^T (kv x 16 rows) = K . Q^T.  The latent 512 bytes go to a per-wave LDS
+// Lane l (row n = l%16, group g = l/16) gathers tile rows n and 16 + n: for
+// s = 0..3 the 32 bytes [128s + 32g, +32) of the latent dims, the operand of
+// one v_mfma_scale_f32_16x16x128_f8f6f4 step (unit E8M0 scales), and the 16
+// rope bytes [512 + 16g, +16), the operands of two v_mfma_f32_16x16x32_fp8_fp8
+// steps, so Q.K^T runs from registers as S^T (kv x 16 rows) = K . Q^T in
+// 4 x 32 + 2 x 16 = 160 cycles per 16 kv rows (eighteen 16x16x32 steps took
+// 288).  q holds the same bytes of its rows, so the dims pair up whatever
+// order the matrix cores sum them in.  The two step kinds keep separate
+// accumulators (an MFMA must not read another kind's result as its
+// accumulator), added at the end.  The latent 512 bytes go to a per-wave LDS
 // tile; P.V reads 16 bytes from each of 8 rows and transposes 4x4 byte blocks
 // (v_perm) into the V^T A operand: O^T (512 x 16 rows) += V^T . P^T.  P enters
 // as two e4m3 terms, P*128 = hi + lo, which keeps ~8 significant bits of P (a
@@ -139,18 +145,31 @@ __device__ __forceinline__ TileIdx fp8_fetch_idx(const int32_t* sidx, int rows, 
   return t;
 }
 
+// Byte offset of load c (0..8) of a row for lane group g: latent bytes
+// [128(c/2) + 32g + 16(c%2), +16) for c < 8, rope bytes [512 + 16g, +16).
+__device__ __forceinline__ int fp8_load_offset(int c, int g) {
+  return c < 8 ? 128 * (c >> 1) + 32 * g + 16 * (c & 1) : kLatent + 16 * g;
+}
+
 __device__ __forceinline__ void fp8_issue_rows(uint4 (&B)[18], const uint8_t* kv,
                                                int64_t pool_entries, TileIdx ti, int gq) {
-  const uint8_t* s0 = row_ptr<kRowDim>(kv, pool_entries, ti.i0, gq);
-  const uint8_t* s1 = row_ptr<kRowDim>(kv, pool_entries, ti.i1, gq);
+  const uint8_t* s0 = row_ptr<kRowDim>(kv, pool_entries, ti.i0, 0);
+  const uint8_t* s1 = row_ptr<kRowDim>(kv, pool_entries, ti.i1, 0);
 #pragma unroll
-  for (int c = 0; c < 9; ++c) B[c] = *(const uint4*)(s0 + 64 * c);
+  for (int c = 0; c < 9; ++c) B[c] = *(const uint4*)(s0 + fp8_load_offset(c, gq));
 #pragma unroll
-  for (int c = 0; c < 9; ++c) B[9 + c] = *(const uint4*)(s1 + 64 * c);
+  for (int c = 0; c < 9; ++c) B[9 + c] = *(const uint4*)(s1 + fp8_load_offset(c, gq));
+}
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v8i as_v8i(uint4 a, uint4 b) {
+  return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
 struct Fp8Q {
-  long lo[9], hi[9];  // q row lane%16, bytes [64c + 16*(lane/16), +8) and [+8, +16)
+  v8i m[4];   // q row lane%16, latent bytes [128s + 32*(lane/16), +32)
+  long r[2];  // its rope bytes [512 + 16*(lane/16), +8) and [+8, +16)
 };
 
 // One 32-row tile: S^T = K.Q^T, online softmax, O^T += V^T.P^T.  With kRefill,
@@ -162,24 +181,28 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
                                          const int32_t* sidx, int rows, int tile, float cs, int n,
                                          int gq) {
   v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  v4f t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < 9; ++c) {
-    const long qlo = q.lo[c], qhi = q.hi[c];
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].x, B[c].y), qlo, s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].x, B[9 + c].y), qlo, s1, 0, 0,
-                                                    0);
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[c].z, B[c].w), qhi, s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[9 + c].z, B[9 + c].w), qhi, s1, 0, 0,
-                                                    0);
+  for (int k = 0; k < 4; ++k) {
+    s0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as_v8i(B[2 * k], B[2 * k + 1]), q.m[k],
+                                                           s0, 0, 0, 0, 127, 0, 127);
+    s1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as_v8i(B[9 + 2 * k], B[10 + 2 * k]),
+                                                           q.m[k], s1, 0, 0, 0, 127, 0, 127);
   }
+  t0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[8].x, B[8].y), q.r[0], t0, 0, 0, 0);
+  t1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[17].x, B[17].y), q.r[0], t1, 0, 0, 0);
+  t0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[8].z, B[8].w), q.r[1], t0, 0, 0, 0);
+  t1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(B[17].z, B[17].w), q.r[1], t1, 0, 0, 0);
 
   // Stage the latent 512 bytes of both 16-row blocks in this wave's LDS tile.
   wave_lds_sync();  // the previous tile's V reads are complete
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    *(uint4*)(vst + n * kFp8VStride + 64 * c + 16 * gq) = B[c];
-    *(uint4*)(vst + (16 + n) * kFp8VStride + 64 * c + 16 * gq) = B[9 + c];
+    *(uint4*)(vst + n * kFp8VStride + fp8_load_offset(c, gq)) = B[c];
+    *(uint4*)(vst + (16 + n) * kFp8VStride + fp8_load_offset(c, gq)) = B[9 + c];
   }
+  s0 += t0;
+  s1 += t1;
   if constexpr (kRefill) {
     fp8_issue_rows(B, p.kv, p.pool_entries, next, gq);
     next = fp8_fetch_idx(sidx, rows, tile + 4 * kWaves, n);
@@ -267,18 +290,16 @@ struct Fp8Path {
   static __device__ __forceinline__ void load_q(Q& q, const DecodeParams& p, DecodeShared& sh,
                                                 const UnitRef& u, RowSrc idx, int n) {
     const int lane = opaque((int)threadIdx.x) & 63;  // address built here, not held
-    const uint8_t* qrow = p.q +
-                          ((int64_t)u.t * p.num_heads + u.g * kGroup + (lane & 15)) * kRowBytes +
-                          16 * (lane >> 4);
+    const uint8_t* qrow =
+        p.q + ((int64_t)u.t * p.num_heads + u.g * kGroup + (lane & 15)) * kRowBytes;
     uint4 x[9];
 #pragma unroll
-    for (int c = 0; c < 9; ++c) x[c] = *(const uint4*)(qrow + 64 * c);
+    for (int c = 0; c < 9; ++c) x[c] = *(const uint4*)(qrow + fp8_load_offset(c, lane >> 4));
     stage_first_indices<kPaged>(sh.idx, p, idx, n);
 #pragma unroll
-    for (int c = 0; c < 9; ++c) {
-      q.lo[c] = as_long(x[c].x, x[c].y);
-      q.hi[c] = as_long(x[c].z, x[c].w);
-    }
+    for (int k = 0; k < 4; ++k) q.m[k] = as_v8i(x[2 * k], x[2 * k + 1]);
+    q.r[0] = as_long(x[8].x, x[8].y);
+    q.r[1] = as_long(x[8].z, x[8].w);
   }
   static __device__ __forceinline__ TileIdx fetch_idx(const int32_t* sidx, int rows, int tile,
                                                       int n) {
