@@ -31,6 +31,7 @@ METRIC = "MLA decode µs/call + HBM GB/s (% of 8 TB/s), bs16 kv≈68K fp8, 1 GPU
 CONFIG_NAMES = ("c24_batch24_fp8", "mixed_batch64_fp8", "mixed_batch64_bf16",
                 "dcp_local_96heads_qlen4_fp8", "dcp_share_96heads_qlen4_fp8",
                 "dcp_share_96heads_qlen4_fp8_f32out", "c16_shared_prefix_cascade_fp8",
+                "c16_shared_prefix_cascade_fp8_12heads",
                 "merge_8_shards_fp32", "merge_8_shards_bf16", "c16_layer_step_rope_decode_v")
 PEAK_GBS = 8000.0
 
@@ -193,14 +194,20 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
                      "o_dtype": str(o_dtype).replace("torch.", ""), "calls": n}
         del layers, base, o, lse, ws
         torch.cuda.empty_cache()
-    name = "c16_shared_prefix_cascade_fp8"
-    if only is None or only == name:
+    for name, heads in (("c16_shared_prefix_cascade_fp8", None),
+                        ("c16_shared_prefix_cascade_fp8_12heads", 12)):
+        if only is not None and only != name:
+            continue
         # The headline call through decode_cascade: the 63,911 shared entries
-        # given once, each request's own entries as its suffix.
+        # given once, each request's own entries as its suffix; with 12 heads
+        # the real heads are passed unpadded (q (16, 12, 576)).
         base = workloads.c16(dev, "shared")
         layers = extra_layers(base, n_layers, 0.5, 7000, dev)
+        if heads is not None:
+            layers = [workloads.Workload(**{**w.__dict__, "q": w.q[:, :heads].contiguous(),
+                                            "num_heads": heads}) for w in layers]
         pre, sptr, suf = workloads.split_prefix(base, workloads.SHARED_PREFIX)
-        T, H = base.num_tokens, base.num_heads
+        T, H = base.num_tokens, layers[0].num_heads
         o = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
         ws = mla.new_workspace(mla.cascade_workspace_bytes(base.batch, T, H, 1), dev)
 
@@ -218,7 +225,7 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
                      "cascade_bytes_per_call": unique,
                      "GB_s_cascade_bytes": round(unique / wall / 1e9, 2),
                      "TFLOP_s": round(accounting.workload_flops(base) / wall / 1e12, 2),
-                     "kv_rows": base.total_kv, "dtype": "fp8", "calls": n}
+                     "heads": H, "kv_rows": base.total_kv, "dtype": "fp8", "calls": n}
         del layers, base, o, ws, pre, sptr, suf
         torch.cuda.empty_cache()
     for parts_dtype in ("fp32", "bf16"):

@@ -298,7 +298,12 @@ const char* mla_status_string(int status);
  *  Arguments as for mla_decode, with kv_indptr / kv_indices replaced by
  *  prefix_indices (prefix_len) int32 and suffix_indptr (batch+1) /
  *  suffix_indices (suffix_indices_len) int32, all device memory.
- *  Supported: FP8 q and KV only.  Causal draft tokens: every request's suffix
+ *  Supported: FP8 q and KV only.  num_heads may be any count from 1 to 4,096:
+ *  the query rows (token, head) are packed 16 to a matrix tile whatever the
+ *  head count, so a model's 12 real heads are passed unpadded, q
+ *  (num_q_tokens, 12, 576) and o (num_q_tokens, 12, 512), and no tile row is
+ *  spent on padding ("[Kimi-K3 MLA TP8] MLA performance", Sec. 5.1: with 12
+ *  heads padded to 16, a quarter of the Q tile is zero).  Causal draft tokens: every request's suffix
  *  must hold at least qlen_b - 1 entries (a token's masked entries then all
  *  lie in the suffix); this is the caller's contract, not checked.
  *  workspace: at least mla_decode_cascade_workspace_bytes(...) bytes.

@@ -138,11 +138,7 @@ mla_status decode_impl(const void* q, int q_dtype, const void* kv_pool, int kv_d
   p.q_scale = q_scale;
   p.kv_scale = kv_scale;
   p.lse = return_lse ? lse : nullptr;
-  char* ws = static_cast<char*>(workspace);
-  p.desc = reinterpret_cast<int4*>(ws);
-  p.part_o = reinterpret_cast<float*>(ws + mla::desc_bytes(num_units));
-  p.part_lse = reinterpret_cast<float*>(ws + mla::desc_bytes(num_units) +
-                                        mla::part_o_bytes(num_workers, slots));
+  mla::set_workspace(p, static_cast<char*>(workspace), num_units, num_workers, slots);
   p.num_workers = num_workers;
   p.causal = 1;
   p.g_kv_indptr = g_kv_indptr;
@@ -313,10 +309,18 @@ struct CascadeLayout {
   size_t decode_bytes, parts_off, lse_off, total;
 };
 
+// The cascade takes any head count (rows are packed 16 to a row group, so
+// 12 real heads need no padding) within the plain call's other limits.
+bool cascade_shape_ok(int batch, int num_q_tokens, int num_heads, int max_seqlen_q) {
+  if (num_heads < 1 || num_heads > 4096) return false;
+  const int padded = mla::kGroup * mla::group_slots_per_token(num_heads);
+  return shape_ok(batch, num_q_tokens, padded, max_seqlen_q) &&
+         (int64_t)2 * num_q_tokens * num_heads <= 0x7FFFFFFF;
+}
+
 CascadeLayout cascade_layout(int batch, int num_q_tokens, int num_heads, int max_seqlen_q,
                              int cus) {
-  const int G = num_heads / mla::kGroup;
-  const int64_t units = 2 * (int64_t)num_q_tokens * G;
+  const int64_t units = 2 * (int64_t)num_q_tokens * mla::group_slots_per_token(num_heads);
   CascadeLayout l;
   l.decode_bytes = mla::align256(mla::workspace_bytes(cus, units, mla::slots_per_worker(true)));
   l.parts_off = l.decode_bytes;
@@ -327,19 +331,12 @@ CascadeLayout cascade_layout(int batch, int num_q_tokens, int num_heads, int max
   return l;
 }
 
-void set_workspace(mla::DecodeParams& p, char* ws, int64_t units, int slots) {
-  p.desc = reinterpret_cast<int4*>(ws);
-  p.part_o = reinterpret_cast<float*>(ws + mla::desc_bytes(units));
-  p.part_lse = reinterpret_cast<float*>(ws + mla::desc_bytes(units) +
-                                        mla::part_o_bytes(p.num_workers, slots));
-}
 
 }  // namespace
 
 size_t mla_decode_cascade_workspace_bytes(int batch, int num_q_tokens, int num_heads,
                                           int max_seqlen_q) {
-  if (!shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
-  if (num_heads % mla::kGroup) return 0;
+  if (!cascade_shape_ok(batch, num_q_tokens, num_heads, max_seqlen_q)) return 0;
   const int cus = current_cu_count();
   if (cus <= 0) return 0;
   return cascade_layout(batch, num_q_tokens, num_heads, max_seqlen_q, cus).total;
@@ -359,9 +356,8 @@ mla_status mla_decode_cascade(const void* q, int q_dtype, const void* kv_pool, i
   if (suffix_indices_len > 0 && !suffix_indices) return MLA_ERR_NULL_POINTER;
   if (return_lse && !lse) return MLA_ERR_NULL_POINTER;
   if (q_dtype != MLA_DTYPE_FP8_E4M3FN || kv_dtype != MLA_DTYPE_FP8_E4M3FN) return MLA_ERR_BAD_DTYPE;
-  if (num_heads <= 0 || num_heads % mla::kGroup != 0) return MLA_ERR_UNSUPPORTED;
   const int T = num_q_tokens;
-  if (!shape_ok(batch, T, num_heads, max_seqlen_q)) return MLA_ERR_BAD_SHAPE;
+  if (!cascade_shape_ok(batch, T, num_heads, max_seqlen_q)) return MLA_ERR_BAD_SHAPE;
   if (pool_entries < 1 || prefix_len < 0 || suffix_indices_len < 0 ||
       prefix_len + suffix_indices_len > 0x7FFFFFFF || T > (1 << 29) || batch > (1 << 29))
     return MLA_ERR_BAD_SHAPE;
@@ -369,8 +365,7 @@ mla_status mla_decode_cascade(const void* q, int q_dtype, const void* kv_pool, i
   if (cus <= 0) return MLA_ERR_HIP;
   const CascadeLayout lay = cascade_layout(batch, T, num_heads, max_seqlen_q, cus);
   if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  const int G = num_heads / mla::kGroup;
-  const int64_t units = (int64_t)T * G;
+  const int64_t units = (int64_t)T * mla::group_slots_per_token(num_heads);
   char* ws = static_cast<char*>(workspace);
   float* parts = reinterpret_cast<float*>(ws + lay.parts_off);
   float* lse_parts = reinterpret_cast<float*>(ws + lay.lse_off);
@@ -407,7 +402,7 @@ mla_status mla_decode_cascade(const void* q, int q_dtype, const void* kv_pool, i
   p.batch = batch + 1;
   p.num_tokens = 2 * T;
   p.causal = 1;
-  set_workspace(p, ws, 2 * units, mla::slots_per_worker(true));
+  mla::set_workspace(p, ws, 2 * units, p.num_workers, mla::slots_per_worker(true));
   if (mla::launch_decode(p, 0, true, st) != hipSuccess) return MLA_ERR_HIP;
 
   // LSE merge of the two passes (a pass that saw nothing has lse = -inf).
@@ -534,11 +529,7 @@ mla_status mla_decode_step(const void* q_latent, const void* q_pe, const void* k
   p.q_scale = q_scale;
   p.kv_scale = kv_scale;
   p.lse = return_lse ? lse : nullptr;
-  char* ws = static_cast<char*>(workspace);
-  p.desc = reinterpret_cast<int4*>(ws);
-  p.part_o = reinterpret_cast<float*>(ws + mla::desc_bytes(num_units));
-  p.part_lse = reinterpret_cast<float*>(ws + mla::desc_bytes(num_units) +
-                                        mla::part_o_bytes(cus, slots));
+  mla::set_workspace(p, static_cast<char*>(workspace), num_units, cus, slots);
   p.num_workers = cus;
   p.causal = 1;
   p.q_latent = static_cast<const uint16_t*>(q_latent);

@@ -963,17 +963,29 @@ template <int kSlots, bool kBf16Parts>
 __device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShared<1>& sh) {
   const int64_t u = blockIdx.x;
   const int4 d = p.desc[u];
+  // Group mode: the row group's first token and head and its row count (rows
+  // are packed when the head count is not a multiple of 16), loaded beside
+  // the descriptor rather than after it.
+  int2 rr = make_int2(0, 0);
+  if constexpr (kSlots != 2) rr = p.desc_rows[u];
   if (d.w == 0) return;
-  const int G = p.num_heads / kGroup;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = blockIdx.y >> 1, h = blockIdx.y & 1;
+  // The row's place in o: unit u = token * G + head group in the standard
+  // kernels, the descriptor's rows in group mode.
+  int64_t orow;
+  if constexpr (kSlots == 2) {
+    const int G = p.num_heads / kGroup;
+    orow = (u / G) * p.num_heads + (u % G) * kGroup + n;
+  } else {
+    if (n >= (rr.y & 31)) return;  // past the last row of a partial row group
+    orow = (int64_t)rr.x * p.num_heads + (rr.y >> 5) + n;
+  }
   if (d.y - d.x + 1 <= kCombineBatch && wv != 0) return;  // one wave merges up to a batch
   float4 acc[1];
   float M, sum;
   if (!combine_row<kSlots, kBf16Parts, 1>(p, sh, d, n, h, acc, M, sum)) return;
   const float inv = sum > 0.f ? 1.0f / sum : 0.f;  // a row that sees nothing: o = 0, lse = -inf
-  const int64_t t = u / G, g = u % G;
-  const int64_t orow = t * p.num_heads + g * kGroup + n;
   if (p.o32 != nullptr) {
     *(float4*)(p.o32 + orow * kLatent + 256 * h + 4 * lane) =
         make_float4(acc[0].x * inv, acc[0].y * inv, acc[0].z * inv, acc[0].w * inv);
@@ -1192,7 +1204,9 @@ hipError_t launch_decode(const DecodeParams& p, int kv_dtype, bool group_mode, h
     return hipErrorNotSupported;
   }
   if (e != hipSuccess) return e;
-  const unsigned units = (unsigned)(p.num_tokens * (p.num_heads / kGroup));
+  const unsigned units =
+      (unsigned)(p.num_tokens * (group_mode ? group_slots_per_token(p.num_heads)
+                                            : p.num_heads / kGroup));
   if (group_mode && kv_dtype == 0 && p.part_fp32)
     hipLaunchKernelGGL(mla_combine_groups_fp32_kernel, dim3(units, 2 * kGroup),
                        dim3(kCombineThreads), 0, stream, p);

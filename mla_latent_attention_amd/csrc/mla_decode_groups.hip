@@ -423,54 +423,66 @@ __device__ __forceinline__ void store_partials(const WideState& st, float oscale
 }
 
 // One piece: entries [k0, k0 + len) of unit c.u of request c.b (unit
-// length L).  slot_base < 0: the piece is the whole unit and every row group
-// writes o / lse; else row group i of the unit writes partial slot
-// slot_base + i.
+// length L; H heads, the request's rows packed 16 to a row group).
+// slot_base < 0: the piece is the whole unit and every row writes o / lse;
+// else row group i of the unit writes partial slot slot_base + i.
 template <bool kPaged, bool kCascade>
 __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& sh,
-                                            const GCursor& c, int k0, int G, int L, int len,
+                                            const GCursor& c, int k0, int H, int L, int len,
                                             int slot_base, int w, float cs, float ks) {
   const int tid = threadIdx.x, wv = uniform(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, hq = lane & 31, half = hq >> 4, n16 = hq & 15;
-  const int R = c.r.qlen * G;
+  const int NR = c.r.qlen * H;              // the request's query rows
+  const int RG = group_row_groups(c.r, H);  // and row groups
   const bool complete = slot_base < 0;
 
-  // The wave's two row groups (uniform), then this lane's.
-  int rows_h[2], vis_h[2];
+  // The wave's two row groups (uniform): the entries their last rows see
+  // (the most any of their rows sees) and their first rows see (the fewest;
+  // 0 if the row group is not full).  Rows are token-major, so a row group's
+  // visible counts rise from its first row to its last.
+  int rows_h[2], vis_h[2], first_h[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int rgk = kGroupsPerUnit * c.u + wv + kWaves * k;
-    const int jk = imin(rgk, R - 1) / G;
-    vis_h[k] = rgk < R ? req_visible(c.r, jk) : 0;
+    const bool ok = rgk < RG;
+    vis_h[k] = ok ? req_visible(c.r, group_last_token(c.r, H, rgk)) : 0;
+    const int vfirst = (ok && kGroup * rgk + kGroup <= NR)
+                           ? req_visible(c.r, imin(kGroup * rgk, NR - 1) / H) : 0;
     rows_h[k] = imax(0, imin(vis_h[k] - k0, len));
+    first_h[k] = imax(0, imin(vfirst - k0, len));
   }
-  const int wave_rows = imax(rows_h[0], rows_h[1]);
-  const int full_rows = imin(rows_h[0], rows_h[1]);
+  const int wave_rows = uniform(imax(rows_h[0], rows_h[1]));
+  const int full_rows = uniform(imin(first_h[0], first_h[1]));
   const int ulocal = wv + kWaves * half;  // this lane's row group within the unit
   const int rg = kGroupsPerUnit * c.u + ulocal;
-  const bool valid = rg < R;
-  const int rgc = imin(rg, R - 1);
-  const int j = rgc / G, g = rgc - j * G;
+  const int row = kGroup * rg + n16;      // this lane's query row within the request
+  const bool valid = row < NR;
+  const int rowc = imin(row, NR - 1);
+  const int j = rowc / H, hh = rowc - j * H;  // its token and head
   const int t = c.r.q_base + j;
   // The q row: in a one-launch cascade call tokens T .. 2T-1 (the suffix
   // requests) are the caller's tokens 0 .. T-1 again.
   const int qtok = (kCascade && t >= (p.num_tokens >> 1)) ? t - (p.num_tokens >> 1) : t;
-  const int vw = half ? vis_h[1] : vis_h[0];
-  const int rows_w = half ? rows_h[1] : rows_h[0];
+  const int vw = valid ? req_visible(c.r, j) : 0;
+  const int rows_w = imax(0, imin(vw - k0, len));
 
   // Split-unit descriptor of each row group (see mla_decode.hip): written by
-  // the workers holding the unit's first and last pieces.  Every lane stores
-  // (the conditions are uniform); lanes that hold no row group's descriptor
-  // store to the spare entry after the last, so that no divergent branch
-  // exists here: the compiler has placed a register spill under such a
-  // branch's narrowed exec mask, saving only the branch's lanes.
+  // the workers holding the unit's first and last pieces, with the row
+  // group's output rows (its first token and head, and its row count).
+  // Every lane stores (the conditions are uniform); lanes that hold no row
+  // group's descriptor store to the spare entry after the last, so that no
+  // divergent branch exists here: the compiler has placed a register spill
+  // under such a branch's narrowed exec mask, saving only the branch's lanes.
   {
-    const bool mine = (lane == 0 || lane == 16) && valid && vw > 0;
-    int* d = (int*)(p.desc + (mine ? (int64_t)t * G + g : (int64_t)p.num_tokens * G));
+    const int Gs = group_slots_per_token(H);
+    const bool mine = (lane == 0 || lane == 16) && rg < RG && (half ? vis_h[1] : vis_h[0]) > 0;
+    const int64_t e = mine ? (int64_t)c.r.q_base * Gs + rg : (int64_t)p.num_tokens * Gs;
+    int* d = (int*)(p.desc + e);
     if (k0 == 0) {
       d[0] = w;
       d[2] = complete ? 0 : slot_base + ulocal;
       d[3] = complete ? 0 : 1;
+      p.desc_rows[e] = make_int2(t, hh * 32 + imin(kGroup, NR - kGroup * rg));
     }
     if (!complete && k0 + len == L) d[1] = w;
   }
@@ -482,8 +494,7 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   const RowSrc src = row_src<kPaged>(c.r, k0);
   v8i_t q[9];
   {
-    const uint8_t* qrow =
-        p.q + ((int64_t)qtok * p.num_heads + g * kGroup + n16) * kRowDim + 32 * h;
+    const uint8_t* qrow = p.q + ((int64_t)qtok * H + hh) * kRowDim + 32 * h;
     uint4 xq[18];
 #pragma unroll
     for (int i = 0; i < 18; ++i) xq[i] = *(const uint4*)(qrow + 64 * (i >> 1) + 16 * (i & 1));
@@ -623,9 +634,9 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
     return;
   }
   if (!valid) return;
-  if (vw == 0) return;  // the row group sees nothing: o / lse written elsewhere
+  if (vw == 0) return;  // the row sees nothing: o / lse written elsewhere
   {
-    const int64_t orow = (int64_t)t * p.num_heads + g * kGroup + n16;
+    const int64_t orow = (int64_t)t * H + hh;
     if (p.o32 != nullptr) {
       float* d32 = p.o32 + orow * kLatent + 4 * h;
 #pragma unroll
@@ -656,7 +667,7 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
 // One worker: locate its share of the group-mode stream and run its pieces.
 template <bool kPaged, bool kCascade>
 __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared& sh) {
-  const int G = p.num_heads / kGroup;
+  const int H = p.num_heads;
   // The scales first: their loads overlap the planner's.
   const float qs = p.q_scale ? *p.q_scale : 1.0f;
   const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
@@ -666,32 +677,28 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
   int nw;
   PlanHit hit[2];
   if (!plan_lookup<kPaged, kThreads, kCascade>(
-          p, [G](const Req& r) { return group_request_rows(r, G); },
-          [&p](const Req& r) {
-            const int nempty = req_empty_tokens(r);
-            for (int jj = 0; jj < nempty; ++jj)
-              if ((r.q_base + jj) % (int)gridDim.x == (int)blockIdx.x) zero_token(p, r.q_base + jj);
-          },
+          p, [H](const Req& r) { return group_request_rows(r, H); },
+          [&p, H](const Req& r) { clear_group_request(p, r, H); },
           w, sh.red, sh.hits, W, nw, x0, x1, hit))
     return;
   if (hit[0].b < 0 || (x1 < W && hit[1].b < 0)) return;  // not reached with consistent indptr
   const ReqSource src = source_of<kPaged, kCascade>(p);
   GCursor c;
-  gcursor_in_request(c, hit[0].b, hit[0].r, x0 - hit[0].cum, G);
+  gcursor_in_request(c, hit[0].b, hit[0].r, x0 - hit[0].cum, H);
   uniformize(c);
   int64_t p1 = W;
   if (x1 < W) {
     GCursor c1;
-    gcursor_in_request(c1, hit[1].b, hit[1].r, x1 - hit[1].cum, G);
+    gcursor_in_request(c1, hit[1].b, hit[1].r, x1 - hit[1].cum, H);
     uniformize(c1);
-    p1 = gsnap_at(x1, c1, G);
+    p1 = gsnap_at(x1, c1, H);
   }
-  const int64_t p0 = gsnap_at(x0, c, G);
+  const int64_t p0 = gsnap_at(x0, c, H);
   if (p0 >= p1) return;
   if (p0 < x0) {
     c.k = 0;
   } else if (p0 > x0) {
-    if (!gcursor_next_unit(c, src, p.batch, G)) return;
+    if (!gcursor_next_unit(c, src, p.batch, H)) return;
     uniformize(c);
   }
   const float cs = p.sm_scale * kLog2e * qs * ks;
@@ -702,7 +709,7 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
   int64_t pos = p0;
   int piece = 0;
   while (pos < p1) {
-    const int L = group_unit_len(c.r, G, c.u);
+    const int L = group_unit_len(c.r, H, c.u);
     const int span = L + kGroupPieceRows;
     const int n = (int)lmin((int64_t)(span - c.k), p1 - pos);
     if (n <= 0) break;  // not reached with a consistent plan
@@ -712,14 +719,14 @@ __device__ __forceinline__ void group_worker(const DecodeParams& p, GroupShared&
       const bool complete = (k0 == 0 && len == L);
       const int slot_base =
           complete ? -1 : kGSlotsPerPiece * (2 * w + (piece == 0 ? 0 : 1));
-      group_piece<kPaged, kCascade>(p, sh, c, uniform(k0), G, L, uniform(len), slot_base, w, cs,
+      group_piece<kPaged, kCascade>(p, sh, c, uniform(k0), H, L, uniform(len), slot_base, w, cs,
                                     ks);
       ++piece;
     }
     pos += n;
     c.k += n;
     if (pos < p1 && c.k == span) {
-      if (!gcursor_next_unit(c, src, p.batch, G)) break;
+      if (!gcursor_next_unit(c, src, p.batch, H)) break;
       uniformize(c);
     }
   }

@@ -396,9 +396,8 @@ __device__ __forceinline__ void stage_indices(int32_t* dst, const DecodeParams& 
 
 // Query rows that see no entry get o = 0, lse = -inf; the block owning token t
 // (t mod gridDim.x) writes them.  Rare: empty requests or early draft tokens.
-__device__ void zero_token(const DecodeParams& p, int t) {
-  const int G = p.num_heads / kGroup;
-  for (int g = 0; g < G; ++g) p.desc[(int64_t)t * G + g] = make_int4(0, 0, 0, 0);
+// o = 0 and lse = -inf for every head of token t (a token that sees nothing).
+__device__ void zero_token_rows(const DecodeParams& p, int t) {
   for (int h = 0; h < p.num_heads; ++h) {
     const int64_t orow = (int64_t)t * p.num_heads + h;
     if (p.o32 != nullptr) {
@@ -410,6 +409,36 @@ __device__ void zero_token(const DecodeParams& p, int t) {
     }
     if (p.lse != nullptr) p.lse[orow] = neg_inf();
   }
+}
+
+// The standard kernels' empty token: its head groups' descriptors say
+// "not split", and its rows are zeroed.
+__device__ void zero_token(const DecodeParams& p, int t) {
+  const int G = p.num_heads / kGroup;
+  for (int g = 0; g < G; ++g) p.desc[(int64_t)t * G + g] = make_int4(0, 0, 0, 0);
+  zero_token_rows(p, t);
+}
+
+// Group mode's empty-row bookkeeping for request r (H heads): the rows of its
+// tokens that see nothing, and "not split" descriptors for the entries no
+// piece writes: its leading row groups whose rows all see nothing (only when
+// some of its tokens see nothing; visible counts rise with the token) and its
+// unused entries (entry q_base * Gs + rg, rg in [row groups, qlen * Gs)).
+// Each token and entry is dealt to one block (index mod the worker count).
+__device__ void clear_group_request(const DecodeParams& p, const Req& r, int H) {
+  const int nempty = req_empty_tokens(r);
+  for (int j = 0; j < nempty; ++j)
+    if ((r.q_base + j) % p.num_workers == (int)blockIdx.x) zero_token_rows(p, r.q_base + j);
+  const int Gs = group_slots_per_token(H);
+  const int RG = group_row_groups(r, H);
+  int dark = 0;  // leading row groups that see nothing
+  if (nempty > 0)
+    while (dark < RG && group_last_token(r, H, dark) < nempty) ++dark;
+  const int base = r.q_base * Gs;
+  for (int rg = 0; rg < dark; ++rg)
+    if ((base + rg) % p.num_workers == (int)blockIdx.x) p.desc[base + rg] = make_int4(0, 0, 0, 0);
+  for (int rg = RG; rg < r.qlen * Gs; ++rg)
+    if ((base + rg) % p.num_workers == (int)blockIdx.x) p.desc[base + rg] = make_int4(0, 0, 0, 0);
 }
 
 }  // namespace mla

@@ -41,6 +41,8 @@ struct DecodeParams {
                             // fp8 one (see the workspace layout below)
   float* part_lse;          // workspace: (slots*num_workers, 16) fp32
   int4* desc;               // workspace: (tokens * head groups) split-unit descriptors
+  int2* desc_rows = nullptr;  // group mode: {first token, first head * 32 + rows} of each
+                              // descriptor's row group (rows 1..16; packed heads)
   int num_workers;
   int causal;               // 1: bottom-right causal; 0: every token of a request sees all
                             // of its entries
@@ -102,10 +104,15 @@ __host__ __device__ inline ReqSource source_of(const DecodeParams& p) {
 //   part_o   (slots * num_workers, 16, 512) fp32 partial outputs (calls on an
 //            fp8 cache store them as bf16 at the same element indices, in the
 //            first half of the region, unless part_fp32 is set)
+//            (then, group mode, desc_rows: int2 per entry, the output rows of
+//            the entry's row group, written with its descriptor)
 //   part_lse (slots * num_workers, 16) fp32 partial lse
 constexpr int kMaxWorkers = 1 << 16;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-inline size_t desc_bytes(int64_t num_units) { return align256(size_t(num_units + 1) * 16); }
+inline size_t desc_entries_bytes(int64_t num_units) { return align256(size_t(num_units + 1) * 16); }
+inline size_t desc_bytes(int64_t num_units) {
+  return desc_entries_bytes(num_units) + align256(size_t(num_units + 1) * 8);
+}
 inline size_t part_o_bytes(int num_workers, int slots) {
   return align256(size_t(slots) * num_workers * 16 * 512 * 4);
 }
@@ -115,6 +122,15 @@ inline size_t part_lse_bytes(int num_workers, int slots) {
 inline size_t workspace_bytes(int num_workers, int64_t num_units, int slots) {
   return desc_bytes(num_units) + part_o_bytes(num_workers, slots) +
          part_lse_bytes(num_workers, slots);
+}
+
+// Points the call's descriptors, partials and their lse into workspace ws.
+inline void set_workspace(DecodeParams& p, char* ws, int64_t num_units, int num_workers, int slots) {
+  p.desc = reinterpret_cast<int4*>(ws);
+  p.desc_rows = reinterpret_cast<int2*>(ws + desc_entries_bytes(num_units));
+  p.part_o = reinterpret_cast<float*>(ws + desc_bytes(num_units));
+  p.part_lse = reinterpret_cast<float*>(ws + desc_bytes(num_units) +
+                                        part_o_bytes(num_workers, slots));
 }
 
 // kv_dtype: 0 = fp8 e4m3fn, 1 = bf16.  group_mode selects the group-mode

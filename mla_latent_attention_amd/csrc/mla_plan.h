@@ -242,9 +242,13 @@ MLA_HD bool cursor_next_unit(Cursor& c, const ReqSource& src, int B, int G) {
 
 // ---- Group mode: a unit is kGroupsPerUnit consecutive row groups of one
 // request, processed by one workgroup over one shared KV range (each wave two
-// row groups).  Row group rg = j * G + g (token j, head group g); unit u covers
-// row groups [8u, 8u + 8) of the request's qlen * G and is as long as the
-// last of them sees (the others mask the entries they may not see).  Used when
+// row groups).  The request's query rows (token j, head h), qlen * H of them,
+// are numbered j * H + h and cut into row groups of 16 (the last may be
+// partial): with H a multiple of 16, row group rg is token rg / G, head group
+// rg % G; with any other H (12 real heads, unpadded) a row group may hold rows
+// of two or more tokens, and no MFMA row is spent on padding.  Unit u covers
+// row groups [8u, 8u + 8) and is as long as its last row sees (the other rows
+// mask the entries they may not see).  Used when
 // a request may hold four or more row groups (many heads or several query
 // tokens), where a unit per row group would gather the same rows once per row
 // group; a unit with fewer than eight leaves some MFMA rows idle, which costs
@@ -260,13 +264,27 @@ MLA_HD bool use_group_mode(int G, int max_seqlen_q) {
   return (int64_t)G * max_seqlen_q >= kGroupModeMinRows;
 }
 
-MLA_HD int group_units(const Req& r, int G) {
-  return (r.qlen * G + kGroupsPerUnit - 1) / kGroupsPerUnit;
+// Row groups of request r with H heads per token.
+MLA_HD int group_row_groups(const Req& r, int H) { return (r.qlen * H + kGroup - 1) / kGroup; }
+
+// Row-group entries per query token in the descriptor layout: request r's
+// row group rg has entry q_base * group_slots_per_token(H) + rg (a request's
+// ceil(qlen * H / 16) row groups never exceed its tokens' qlen * ceil(H / 16)
+// entries; entries past them are unused).
+MLA_HD int group_slots_per_token(int H) { return (H + kGroup - 1) / kGroup; }
+
+MLA_HD int group_units(const Req& r, int H) {
+  return (group_row_groups(r, H) + kGroupsPerUnit - 1) / kGroupsPerUnit;
 }
 
-MLA_HD int group_unit_len(const Req& r, int G, int u) {
-  const int last = imin(kGroupsPerUnit * u + kGroupsPerUnit - 1, r.qlen * G - 1);
-  return req_visible(r, last / G);
+// Token of the last row of row group rg.
+MLA_HD int group_last_token(const Req& r, int H, int rg) {
+  return imin(kGroup * rg + kGroup - 1, r.qlen * H - 1) / H;
+}
+
+MLA_HD int group_unit_len(const Req& r, int H, int u) {
+  const int last = imin(kGroupsPerUnit * u + kGroupsPerUnit - 1, group_row_groups(r, H) - 1);
+  return req_visible(r, group_last_token(r, H, last));
 }
 
 // A group-mode piece has fixed work worth about kGroupPieceRows rows of its
@@ -279,16 +297,16 @@ MLA_HD int group_unit_len(const Req& r, int G, int u) {
 // spans, a worker that holds two pieces gets correspondingly fewer entries.
 constexpr int kGroupPieceRows = 192;
 
-MLA_HD int group_unit_span(const Req& r, int G, int u) {
-  const int v = group_unit_len(r, G, u);
+MLA_HD int group_unit_span(const Req& r, int H, int u) {
+  const int v = group_unit_len(r, H, u);
   return v > 0 ? v + kGroupPieceRows : 0;
 }
 
 // Stream rows of request r in group mode (the sum of its units' spans).
-MLA_HD int64_t group_request_rows(const Req& r, int G) {
+MLA_HD int64_t group_request_rows(const Req& r, int H) {
   int64_t s = 0;
-  const int U = group_units(r, G);
-  for (int u = 0; u < U; ++u) s += group_unit_span(r, G, u);
+  const int U = group_units(r, H);
+  for (int u = 0; u < U; ++u) s += group_unit_span(r, H, u);
   return s;
 }
 
@@ -299,12 +317,12 @@ struct GCursor {
   Req r;
 };
 
-MLA_HD void gcursor_in_request(GCursor& c, int b, const Req& r, int64_t off, int G) {
+MLA_HD void gcursor_in_request(GCursor& c, int b, const Req& r, int64_t off, int H) {
   c.b = b;
   c.r = r;
-  const int U = group_units(r, G);
+  const int U = group_units(r, H);
   for (int u = 0; u < U; ++u) {
-    const int v = group_unit_span(r, G, u);
+    const int v = group_unit_span(r, H, u);
     if (off < v) {
       c.u = u;
       c.k = (int)off;
@@ -325,24 +343,24 @@ MLA_HD void group_piece_entries(int k, int n, int& k0, int& len) {
 
 // Move to the start of the next non-empty unit (unit lengths never shrink
 // within a request).  Returns false past the end.
-MLA_HD bool gcursor_next_unit(GCursor& c, const ReqSource& src, int B, int G) {
+MLA_HD bool gcursor_next_unit(GCursor& c, const ReqSource& src, int B, int H) {
   c.k = 0;
-  if (++c.u < group_units(c.r, G)) return true;
+  if (++c.u < group_units(c.r, H)) return true;
   for (int b = c.b + 1; b < B; ++b) {
     const Req r = load_req(src, b);
-    if (group_request_rows(r, G) > 0) {
+    if (group_request_rows(r, H) > 0) {
       c.b = b;
       c.r = r;
       c.u = 0;
-      while (group_unit_len(r, G, c.u) == 0) ++c.u;
+      while (group_unit_len(r, H, c.u) == 0) ++c.u;
       return true;
     }
   }
   return false;
 }
 
-MLA_HD int64_t gsnap_at(int64_t x, const GCursor& c, int G) {
-  return snap_position(x, c.k, group_unit_span(c.r, G, c.u));
+MLA_HD int64_t gsnap_at(int64_t x, const GCursor& c, int H) {
+  return snap_position(x, c.k, group_unit_span(c.r, H, c.u));
 }
 
 }  // namespace mla

@@ -92,18 +92,18 @@ inline int64_t plan_group_pieces_host(const int32_t* qo_indptr, const int32_t* k
                                       const int32_t* g_kv_indptr, int batch, int num_heads,
                                       int num_workers, int causal, int cp_world_size,
                                       int cp_rank, int64_t* out, int64_t out_cap) {
-  if (!qo_indptr || !kv_indptr || batch < 1 || num_heads < kGroup || num_heads % kGroup ||
-      num_workers < 1 || (out_cap > 0 && !out))
+  if (!qo_indptr || !kv_indptr || batch < 1 || num_heads < 1 || num_workers < 1 ||
+      (out_cap > 0 && !out))
     return -1;
   if (cp_world_size < 1 || cp_rank < 0 || cp_rank >= cp_world_size) return -1;
-  const int G = num_heads / kGroup;
+  const int H = num_heads;  // any count: rows are packed 16 to a row group
   const int T = qo_indptr[batch];
   const int kv_cap = kv_indptr[batch];
   if (T < 0 || kv_cap < 0) return -1;
   const ReqSource src{qo_indptr, kv_indptr, g_kv_indptr, kv_cap, T, causal ? 1 : 0, cp_world_size,
                       cp_rank, nullptr, 0, -1};
   std::vector<int64_t> cum(batch + 1, 0);
-  for (int b = 0; b < batch; ++b) cum[b + 1] = cum[b] + group_request_rows(load_req(src, b), G);
+  for (int b = 0; b < batch; ++b) cum[b + 1] = cum[b] + group_request_rows(load_req(src, b), H);
   const int64_t W = cum[batch];
   if (W == 0) return 0;
   const int nw = effective_workers(W, num_workers);
@@ -112,7 +112,7 @@ inline int64_t plan_group_pieces_host(const int32_t* qo_indptr, const int32_t* k
   auto locate = [&](int64_t x, GCursor& c) {
     int b = 0;
     while (!(cum[b] <= x && x < cum[b + 1])) ++b;
-    gcursor_in_request(c, b, load_req(src, b), x - cum[b], G);
+    gcursor_in_request(c, b, load_req(src, b), x - cum[b], H);
   };
   for (int w = 0; w < nw; ++w) {
     const int64_t x0 = worker_begin(w, W, nw), x1 = worker_begin(w + 1, W, nw);
@@ -121,19 +121,19 @@ inline int64_t plan_group_pieces_host(const int32_t* qo_indptr, const int32_t* k
     int64_t p1 = W;
     if (x1 < W) {
       locate(x1, c1);
-      p1 = gsnap_at(x1, c1, G);
+      p1 = gsnap_at(x1, c1, H);
     }
-    const int64_t p0 = gsnap_at(x0, c, G);
+    const int64_t p0 = gsnap_at(x0, c, H);
     if (p0 >= p1) continue;
     if (p0 < x0) {
       c.k = 0;
     } else if (p0 > x0) {
-      if (!gcursor_next_unit(c, src, batch, G)) continue;
+      if (!gcursor_next_unit(c, src, batch, H)) continue;
     }
     int64_t pos = p0;
     int piece = 0;
     while (pos < p1) {
-      const int L = group_unit_len(c.r, G, c.u);
+      const int L = group_unit_len(c.r, H, c.u);
       const int span = L + kGroupPieceRows;
       const int n = (int)lmin((int64_t)(span - c.k), p1 - pos);
       if (n <= 0) return -1;
@@ -158,7 +158,7 @@ inline int64_t plan_group_pieces_host(const int32_t* qo_indptr, const int32_t* k
       }
       pos += n;
       c.k += n;
-      if (pos < p1 && c.k == span && !gcursor_next_unit(c, src, batch, G))
+      if (pos < p1 && c.k == span && !gcursor_next_unit(c, src, batch, H))
         return -1;
     }
   }

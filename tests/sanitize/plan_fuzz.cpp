@@ -77,16 +77,18 @@ int main() {
     for (int b = 0; b < B; ++b) W += (int64_t)G * mla::request_rows(mla::load_req(src, b));
     src.causal = causal;
     // Group mode: the pieces hold every unit's entries, not the leading stream
-    // rows that charge each non-empty unit's start.
+    // rows that charge each non-empty unit's start.  Its rows are packed, so
+    // any head count is allowed there.
+    const int Hg = (seed & 1) ? H : U(1, 100);
     for (int b = 0; b < B; ++b) {
       const mla::Req r = mla::load_req(src, b);
-      for (int u = 0; u < mla::group_units(r, G); ++u) Wg += mla::group_unit_len(r, G, u);
+      for (int u = 0; u < mla::group_units(r, Hg); ++u) Wg += mla::group_unit_len(r, Hg, u);
     }
     check([&](int64_t* o, int64_t cap) {
       return mla::plan_pieces_host(qo.data(), kv.data(), g, B, H, nw, w_cp, r_cp, o, cap);
     }, W, seed);
     check([&](int64_t* o, int64_t cap) {
-      return mla::plan_group_pieces_host(qo.data(), kv.data(), g, B, H, nw, causal, w_cp, r_cp, o,
+      return mla::plan_group_pieces_host(qo.data(), kv.data(), g, B, Hg, nw, causal, w_cp, r_cp, o,
                                          cap);
     }, Wg, seed);
   }

@@ -395,6 +395,34 @@ def test_cascade_multi_token_many_heads():
     check_cascade(w, 2000)
 
 
+@pytest.mark.parametrize("H,qlens", [(12, None), (12, [2, 1, 3, 1]), (20, [1, 2, 1, 1]),
+                                     (1, [3, 1, 1, 2]), (44, None)])
+def test_cascade_unpadded_heads_match_oracle(H, qlens):
+    """Any head count, unpadded: query rows (token, head) are packed 16 to a
+    row group, so a row group can hold rows of two or more tokens (each masked
+    by its own token's visible count under draft tokens)."""
+    w = workloads.build(f"casc-h{H}", [2600, 2100, 3300, 2050], num_heads=H, real_heads=H,
+                        qlens=qlens, pool_entries=16384, kv_std=0.5, scale_range=(0.5, 2.0),
+                        shared_prefix=2000, seed=40 + H, device=DEV)
+    check_cascade(w, 2000, where=f"cascade, {H} unpadded heads, qlens {qlens}")
+
+
+def test_cascade_unpadded_12_heads_equal_the_padded_call_on_the_real_heads():
+    """12 unpadded heads against the same q padded to 16 with zero heads: the
+    real heads agree within the gate (different tile packings, same rows)."""
+    w = workloads.build("casc-pad", [2600, 2100, 3300, 2050], num_heads=16, real_heads=12,
+                        pool_entries=16384, kv_std=0.5, scale_range=(0.5, 2.0),
+                        shared_prefix=2000, seed=51, device=DEV)
+    w12 = workloads.Workload(**{**w.__dict__, "q": w.q[:, :12].contiguous(), "num_heads": 12,
+                                "real_heads": 12, "name": "casc-pad-12"})
+    o16, lse16 = run_cascade(w, 2000)
+    o12, lse12 = run_cascade(w12, 2000)
+    m = metrics(o12, o16[:, :12].float().cpu().numpy().astype(np.float64), lse12,
+                lse16[:, :12].cpu().numpy())
+    say(f"[cascade 12 vs 16] {m}")
+    assert_gate(m, "cascade 12 unpadded heads vs padded to 16")
+
+
 def test_cascade_graph_replay_matches_eager_bitwise():
     w = small_shared(12)
     pre, sptr, suf = workloads.split_prefix(w, 2000)
@@ -793,6 +821,17 @@ def test_headline_batch16_cascade_sampled():
     w = workloads.c16(DEV, "shared", return_lse=True)
     check_cascade(w, workloads.SHARED_PREFIX, requests=[0, 7, 15])
     del w
+
+
+def test_headline_batch16_cascade_12_unpadded_heads_sampled():
+    """The batch-16 call's 12 real heads passed unpadded to the cascade (its
+    prefix pass packs 16 tokens x 12 heads into 12 row groups, not 16)."""
+    w = workloads.c16(DEV, "shared", return_lse=True)
+    w12 = workloads.Workload(**{**w.__dict__, "q": w.q[:, :12].contiguous(), "num_heads": 12,
+                                "real_heads": 12, "name": "c16-12heads"})
+    del w
+    check_cascade(w12, workloads.SHARED_PREFIX, requests=[0, 7, 15])
+    del w12
 
 
 def test_captured_argument_layout_is_accepted():

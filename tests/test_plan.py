@@ -45,24 +45,26 @@ def units(qo, kv, G, rule=None):
     return out, pos
 
 
-def group_units(qo, kv, G, causal=True, rule=None):
+def group_units(qo, kv, H, causal=True, rule=None):
     """Group mode: (request, unit, length, stream start, span) in stream order.
-    Unit u of a request covers row groups 8u..8u+7 (row group = token * G +
-    head group) and is as long as its last row group sees; in the stream it
-    takes GROUP_PIECE_ROWS more rows (ahead of its entries) when non-empty."""
+    A request's ql * H query rows (token j, head h) are numbered j * H + h and
+    cut into row groups of 16; unit u covers row groups 8u..8u+7 and is as
+    long as its last row sees; in the stream it takes GROUP_PIECE_ROWS more
+    rows (ahead of its entries) when non-empty."""
     out, pos = [], 0
     U = GROUPS_PER_UNIT
     for b in range(len(qo) - 1):
         n, ql = kv[b + 1] - kv[b], qo[b + 1] - qo[b]
-        R = ql * G
+        R = -(-(ql * H) // 16)
         for u in range(-(-R // U)):
-            last = min(U * u + U - 1, R - 1)
+            last_rg = min(U * u + U - 1, R - 1)
+            tok = min(16 * last_rg + 15, ql * H - 1) // H
             if not causal:
                 v = n
             elif rule is None:
-                v = visible(n, ql, last // G)
+                v = visible(n, ql, tok)
             else:
-                v = rule(b, n, ql, last // G)
+                v = rule(b, n, ql, tok)
             span = v + GROUP_PIECE_ROWS if v > 0 else 0
             out.append((b, u, v, pos, span))
             pos += span
@@ -216,9 +218,8 @@ def check_group_plan(qo, kv, H, nw_req, causal=True, dcp=None):
     snapped share of the span stream, intersected with each unit's entries
     (its span less the GROUP_PIECE_ROWS leading rows, which only charge the
     unit's start), with the slot rule the combine relies on."""
-    G = H // 16
     rule = None if dcp is None else dcp_rule(*dcp)
-    us, W = group_units(qo, kv, G, causal, rule)
+    us, W = group_units(qo, kv, H, causal, rule)
     kw = {} if dcp is None else dict(g_kv_indptr=dcp[0], cp_world_size=dcp[1], cp_rank=dcp[2])
     pieces = plan_groups_host(qo, kv, H, nw_req, causal, **kw)
     if W == 0:
@@ -301,7 +302,7 @@ def test_group_boundaries_fall_inside_charge_rows():
     workers some snapped share boundaries lie strictly inside a unit's
     leading GROUP_PIECE_ROWS rows (and the plan is still exact)."""
     qo, kv = indptr([4, 2, 3, 1, 4, 2]), indptr([700, 1900, 260, 3000, 45, 1200])
-    us, W = group_units(qo, kv, 6)
+    us, W = group_units(qo, kv, 96)
     for nw_req in (23, 37, 58):
         nw = min(nw_req, max(1, W // MIN_WORKER_ROWS))
         S = snapped_bounds(us, W, nw)
@@ -325,10 +326,25 @@ def test_model_constants_match_the_planner_header():
 def test_group_units_mask_within_unit():
     """With 16 heads and 4 tokens, one unit holds all four tokens; its length
     is the last token's visible count, the others see fewer."""
-    us, W = group_units(indptr([4]), indptr([100]), 1)
+    us, W = group_units(indptr([4]), indptr([100]), 16)
     assert [(u, v) for _, u, v, *_ in us] == [(0, 100)]
-    us, W = group_units(indptr([5]), indptr([100]), 2)  # 10 row groups: units of 8 and 2
+    us, W = group_units(indptr([5]), indptr([100]), 32)  # 10 row groups: units of 8 and 2
     assert [(u, v) for _, u, v, *_ in us] == [(0, 99), (1, 100)]
+
+
+def test_group_units_pack_unpadded_heads():
+    """12 heads: token j's rows are 12j .. 12j + 11, so row group 0 holds token 0
+    and the first four heads of token 1; 16 tokens make 12 row groups (1.5
+    units) instead of 16; a unit's length is its last row's token's."""
+    us, W = group_units(indptr([16]), indptr([1000]), 12, causal=False)
+    assert [(u, v) for _, u, v, *_ in us] == [(0, 1000), (1, 1000)]
+    us, W = group_units(indptr([11]), indptr([1000]), 12)  # 132 rows: 9 row groups
+    # unit 0: row groups 0-7 end at row 127, token 10; unit 1: row group 8, token 10
+    assert [(u, v) for _, u, v, *_ in us] == [(0, 1000), (1, 1000)]
+    us, W = group_units(indptr([3]), indptr([50]), 12)  # 36 rows: 3 row groups, one unit
+    assert [(u, v) for _, u, v, *_ in us] == [(0, 50)]
+    us, W = group_units(indptr([1, 1]), indptr([30, 40]), 20)  # 20 rows: two row groups each
+    assert [(b, u, v) for b, u, v, *_ in us] == [(0, 0, 30), (1, 0, 40)]
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -338,7 +354,7 @@ def test_group_random_ragged_plans(seed):
     lengths = rng.integers(0, 5000, size=B)
     lengths[rng.random(B) < 0.2] = 0
     qlens = rng.integers(1, 6, size=B)
-    H = 16 * int(rng.integers(1, 7))
+    H = 16 * int(rng.integers(1, 7)) if seed % 2 == 0 else int(rng.integers(1, 100))
     check_group_plan(indptr(qlens), indptr(lengths), H, int(rng.integers(1, 600)))
 
 
@@ -356,8 +372,11 @@ def test_group_plan_without_causal_mask():
     assert set(pieces[:, 5].tolist()) == {63_911}
     check_group_plan(indptr([7]), indptr([5000]), 64, 37, causal=False)
     check_group_plan(indptr([3]), indptr([0]), 32, 8, causal=False)
-    us, _ = group_units(indptr([4]), indptr([100]), 1, causal=False)
+    us, _ = group_units(indptr([4]), indptr([100]), 16, causal=False)
     assert [(u, v) for _, u, v, *_ in us] == [(0, 100)]
+    # the cascade's prefix pass with 12 unpadded heads: 16 tokens, 192 rows
+    pieces = check_group_plan(indptr([16]), indptr([63_911]), 12, 256, causal=False)
+    assert set(pieces[:, 2].tolist()) == {0, 1}
 
 
 # ---------------------------------------------------------------- DCP shards
