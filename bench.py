@@ -31,7 +31,7 @@ METRIC = "MLA decode µs/call + HBM GB/s (% of 8 TB/s), bs16 kv≈68K fp8, 1 GPU
 CONFIG_NAMES = ("c24_batch24_fp8", "mixed_batch64_fp8", "mixed_batch64_bf16",
                 "dcp_local_96heads_qlen4_fp8", "dcp_share_96heads_qlen4_fp8",
                 "dcp_share_96heads_qlen4_fp8_f32out", "c16_shared_prefix_cascade_fp8",
-                "c16_shared_prefix_cascade_fp8_12heads",
+                "c16_shared_prefix_cascade_fp8_12heads", "c32_shared_prefix_cascade_fp8_12_vs_16",
                 "merge_8_shards_fp32", "merge_8_shards_bf16", "c16_layer_step_rope_decode_v")
 PEAK_GBS = 8000.0
 
@@ -227,6 +227,37 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
                      "TFLOP_s": round(accounting.workload_flops(base) / wall / 1e12, 2),
                      "heads": H, "kv_rows": base.total_kv, "dtype": "fp8", "calls": n}
         del layers, base, o, ws, pre, sptr, suf
+        torch.cuda.empty_cache()
+    name = "c32_shared_prefix_cascade_fp8_12_vs_16"
+    if only is None or only == name:
+        # Batch 32 through decode_cascade with the 12 real heads padded to 16
+        # and unpadded: the prefix pass's 32 x 12 query rows fill 3 units of
+        # 128 rows, the padded 32 x 16 fill 4.
+        base = workloads.c32(dev)
+        pre, sptr, suf = workloads.split_prefix(base, workloads.SHARED_PREFIX)
+        T = base.num_tokens
+        res = {}
+        for heads in (16, 12):
+            layers = extra_layers(base, n_layers, 0.5, 7500, dev)
+            if heads == 12:
+                layers = [workloads.Workload(**{**w.__dict__, "q": w.q[:, :12].contiguous(),
+                                                "num_heads": 12}) for w in layers]
+            o = torch.empty((T, heads, 512), dtype=torch.bfloat16, device=dev)
+            ws = mla.new_workspace(mla.cascade_workspace_bytes(base.batch, T, heads, 1), dev)
+            calls = [(lambda w=w: mla.decode_cascade(w.q, w.kv_pool, w.qo_indptr, pre, sptr, suf,
+                                                     w.sm_scale, w.q_scale, w.kv_scale, o=o,
+                                                     max_seqlen_q=1, workspace=ws))
+                     for w in layers]
+            wall, ev, n = time_graph(calls, steps, warmup)
+            res[f"heads_{heads}"] = {"us_per_call": round(wall * 1e6, 2), "event_us": stats_us(ev),
+                                     "calls": n}
+            del layers, o, ws, calls
+        res["kv_rows"] = base.total_kv
+        res["workload"] = ("batch 32, kv ~68,430, shared 63,911-entry prefix, fp8, through "
+                           "mla_decode_cascade: heads_16 = 12 real heads padded with 4 zero heads, "
+                           "heads_12 = the 12 real heads unpadded")
+        out[name] = res
+        del base, pre, sptr, suf
         torch.cuda.empty_cache()
     for parts_dtype in ("fp32", "bf16"):
         if only is not None and only != f"merge_8_shards_{parts_dtype}":

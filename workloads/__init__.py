@@ -302,6 +302,19 @@ def c16(device="cpu", variant: str = "shared", return_lse: bool = False) -> Work
     )
 
 
+def c32(device="cpu") -> Workload:
+    """The batch-16 call's request shape at batch 32 (shared 63,911-entry
+    prefix + 4,089 unique + 430 + (b mod 5) decoded), fp8, 16 heads (12 real +
+    4 zero): a batch whose 12-head query rows fill fewer group-mode units than
+    its padded ones (384 rows: 3 units of 128 against 4)."""
+    lengths = [SHARED_PREFIX + UNIQUE_INPUT + 430 + (b % 5) for b in range(32)]
+    return build(
+        "c32", lengths, num_heads=16, real_heads=12, pool_entries=POOL_ENTRIES, dtype="fp8",
+        kv_std=0.5, q_std=1.0, scale_range=(0.5, 2.0), shared_prefix=SHARED_PREFIX,
+        index_buffer=INDEX_BUFFER, return_lse=False, seed=2500, device=device,
+    )
+
+
 def c24_lengths() -> list[int]:
     g = _gen(3000, "cpu")
     dec = torch.randint(0, 351, (24,), generator=g).tolist()
