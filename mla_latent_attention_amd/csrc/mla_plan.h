@@ -288,14 +288,15 @@ MLA_HD int group_unit_len(const Req& r, int H, int u) {
 }
 
 // A group-mode piece has fixed work worth about kGroupPieceRows rows of its
-// tile loop (q and index staging, the first tile loads, eight row groups of
-// partial stores), so in the work stream every non-empty unit is that many
-// rows longer than its entries: its span.  The extra rows come first, so the
+// tile loop (q and index staging, the first tile loads, the last pair's P.V,
+// eight row groups of partial stores), so in the work stream every non-empty
+// unit is that many rows longer than its entries: its span.  The extra rows come first, so the
 // worker whose share takes in a unit's start is charged for starting it; a
 // share boundary inside those rows hands the whole start to the later worker
 // (the earlier one then holds no piece of the unit).  With equal shares of
 // spans, a worker that holds two pieces gets correspondingly fewer entries.
-constexpr int kGroupPieceRows = 192;
+// (Timestamps per workgroup put a second piece at ~38K cycles, ~10 tiles.)
+constexpr int kGroupPieceRows = 320;
 
 MLA_HD int group_unit_span(const Req& r, int H, int u) {
   const int v = group_unit_len(r, H, u);

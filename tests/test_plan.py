@@ -16,7 +16,7 @@ MIN_WORKER_ROWS = 256
 SNAP_ROWS = 64
 GROUPS_PER_UNIT = 8  # group mode: row groups per unit
 GROUP_SLOTS = 16  # group mode: partial slots per worker (two pieces x 8 row groups)
-GROUP_PIECE_ROWS = 192  # group mode: a unit's span is its entries plus these leading rows
+GROUP_PIECE_ROWS = 320  # group mode: a unit's span is its entries plus these leading rows
 
 
 def visible(n, qlen, j):
