@@ -32,7 +32,10 @@
  *   - Device-side contents (indptr monotonicity, index ranges) are the
  *     caller's contract.  The kernels clamp every index they read to the
  *     buffer it addresses, so a violation gives wrong numbers, never an
- *     out-of-bounds access.
+ *     out-of-bounds access.  mla_check_inputs reports violations on request;
+ *     a library built with MLA_DEBUG_CHECKS defined (libmla_debug.so) runs
+ *     that check inside every decode entry point, synchronises, and returns
+ *     MLA_ERR_BAD_INPUT, enqueuing nothing else, when it finds one.
  *   - Concurrent calls on different streams need distinct workspaces.
  */
 #ifndef MLA_H_
@@ -60,7 +63,8 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 4,
   MLA_ERR_WORKSPACE_TOO_SMALL = 5,
   MLA_ERR_HIP = 6,
-  MLA_ERR_SCRATCH_TOO_SMALL = 7
+  MLA_ERR_SCRATCH_TOO_SMALL = 7,
+  MLA_ERR_BAD_INPUT = 8
 } mla_status;
 
 /* Width of one cache row and of the output (Sec. 2 "K3 MLA geometry"). */
@@ -285,6 +289,57 @@ mla_status mla_merge_partials(const void* o_parts, int parts_dtype, const float*
 
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(int status);
+
+/*
+ * Device-side check of a decode call's index arguments, the parts of the call
+ * the host validation cannot see (Sec. 4.1 "Arguments" and Sec. 5.2: CSR
+ * qo_indptr / kv_indptr over a list of pool entries, or of page numbers for a
+ * paged cache).  Enqueues, on `stream`, a write of 0 to *status followed by a
+ * pass that ORs in one bit per kind of violation found:
+ *   MLA_CHECK_QO_INDPTR      qo_indptr[0] != 0, a decrease, a request with
+ *                            more than max_seqlen_q tokens, or
+ *                            qo_indptr[batch] != num_q_tokens;
+ *   MLA_CHECK_KV_INDPTR      kv_indptr[0] != 0, a decrease, or
+ *                            kv_indptr[batch] > kv_indices_len;
+ *   MLA_CHECK_KV_INDEX       an entry of kv_indices[0 .. kv_indptr[batch])
+ *                            outside [0, pool_entries / page_size);
+ *   MLA_CHECK_LAST_PAGE_LEN  (when kv_last_page_lens is given) page_size 1:
+ *                            a length other than 1 (0 allowed for an empty
+ *                            request); page_size > 1: a request with pages
+ *                            whose length is outside 1 .. page_size;
+ *   MLA_CHECK_DCP_LENGTHS    (when g_kv_indptr is given, as for
+ *                            mla_decode_dcp) g_kv_indptr[0] != 0, a
+ *                            decrease, or a request whose local list does not
+ *                            hold exactly its share of positions (those p <
+ *                            its global length with p mod cp_world_size ==
+ *                            cp_rank).
+ * 0 means none found.  Inputs are read only within the sizes passed (batch + 1
+ * indptr entries, kv_indices_len indices), whatever they hold.  For
+ * mla_decode_cascade, check the suffix lists as the batch and the prefix as a
+ * batch of one request.  The call itself allocates nothing and does not
+ * synchronise; read *status after the stream has reached it.
+ *
+ *  status  device int, written by the check (caller-owned).
+ *  page_size 1, 2, 4, ..., 4096; pool_entries >= 1 (rows of the pool).
+ *  g_kv_indptr may be NULL (then cp_world_size and cp_rank are ignored).
+ *
+ * Errors (nothing enqueued): MLA_ERR_NULL_POINTER (qo_indptr, kv_indptr,
+ * status, or kv_indices with kv_indices_len > 0), MLA_ERR_BAD_SHAPE (batch <
+ * 1, num_q_tokens < 0, max_seqlen_q < 1, kv_indices_len < 0, pool_entries <
+ * 1, page_size not a power of two in range, cp_rank outside
+ * 0 .. cp_world_size - 1).  MLA_ERR_HIP if the launch fails.
+ */
+#define MLA_CHECK_QO_INDPTR 1
+#define MLA_CHECK_KV_INDPTR 2
+#define MLA_CHECK_KV_INDEX 4
+#define MLA_CHECK_LAST_PAGE_LEN 8
+#define MLA_CHECK_DCP_LENGTHS 16
+mla_status mla_check_inputs(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, int64_t kv_indices_len,
+                            const int32_t* kv_last_page_lens, int page_size,
+                            int64_t pool_entries, int batch, int num_q_tokens, int max_seqlen_q,
+                            const int32_t* g_kv_indptr, int cp_world_size, int cp_rank,
+                            int* status, void* stream);
 
 /*
  * Shared-prefix (cascade) decode ("[Kimi-K3 MLA TP8] MLA performance",

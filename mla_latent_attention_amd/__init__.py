@@ -29,6 +29,7 @@ __all__ = [
     "rope_quant_cache",
     "latent_to_v",
     "decode_step",
+    "check_inputs",
     "cascade_workspace_bytes",
     "new_workspace",
     "MLAError",
@@ -401,6 +402,44 @@ PLAN_FIELDS = ("worker", "token", "head_group", "kv_begin", "kv_end", "unit_len"
 
 GROUP_PLAN_FIELDS = ("worker", "request", "unit", "kv_begin", "kv_end", "unit_len", "slot_base",
                      "complete")
+
+
+def check_inputs(qo_indptr, kv_indptr, kv_indices, pool_entries: int, *, max_seqlen_q: int,
+                 num_q_tokens: int | None = None, kv_last_page_lens=None, page_size: int = 1,
+                 g_kv_indptr=None, cp_world_size: int = 1, cp_rank: int = 0,
+                 status: torch.Tensor | None = None):
+    """Device-side check of a decode call's index arguments (mla_check_inputs).
+
+    Enqueues the check on the current stream; with status=None it allocates a
+    one-int device word, waits for the check and returns the set of violated
+    contracts (names such as "MLA_CHECK_KV_INDEX"; empty if none).  With a
+    caller-provided status (1 int32 on the device) it only enqueues the check
+    and returns None: the word holds the bits once the stream reaches it."""
+    dev = qo_indptr.device
+    B = qo_indptr.numel() - 1
+    _need(qo_indptr, "qo_indptr", dev, torch.int32, (B + 1,))
+    _need(kv_indptr, "kv_indptr", dev, torch.int32, (B + 1,))
+    _need(kv_indices, "kv_indices", dev, torch.int32)
+    if kv_last_page_lens is not None:
+        _need(kv_last_page_lens, "kv_last_page_lens", dev, torch.int32, (B,))
+    if g_kv_indptr is not None:
+        _need(g_kv_indptr, "g_kv_indptr", dev, torch.int32, (B + 1,))
+    if num_q_tokens is None:
+        num_q_tokens = int(qo_indptr[-1].item())
+    wait = status is None
+    if wait:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    _need(status, "status", dev, torch.int32, (1,))
+    rc = _lib.lib().mla_check_inputs(
+        _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices), kv_indices.numel(),
+        _ptr(kv_last_page_lens), int(page_size), int(pool_entries), B, int(num_q_tokens),
+        int(max_seqlen_q), _ptr(g_kv_indptr), int(cp_world_size), int(cp_rank), _ptr(status),
+        _stream(dev))
+    _lib.check(rc, "mla_check_inputs")
+    if not wait:
+        return None
+    bits = int(status.item())
+    return {name for bit, name in _lib.CHECK_BITS.items() if bits & bit}
 
 
 def _plan(fn, qo_indptr, kv_indptr, num_heads, num_workers, g_kv_indptr=None):

@@ -1,4 +1,7 @@
-"""Build step: compile the HIP sources under csrc/ into the in-tree libmla.so.
+"""Build step: compile the HIP sources under csrc/ into the in-tree libmla.so,
+and the same sources with MLA_DEBUG_CHECKS defined into libmla_debug.so (every
+decode entry point first checks its index arguments on the device and
+synchronises; see mla_check_inputs in include/mla.h).
 
 hipcc cross-compiles for gfx950 without a GPU present.  Packed-fp32 VALU
 instructions are disabled for the device code (-packed-fp32-ops); the host
@@ -15,7 +18,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["mla_decode.hip", "mla_decode_groups.hip", "mla_surround.hip", "mla_api.hip"]
+LIB_DEBUG = os.path.join(HERE, "libmla_debug.so")
+SOURCES = ["mla_decode.hip", "mla_decode_groups.hip", "mla_surround.hip", "mla_check.hip",
+           "mla_api.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -37,19 +42,29 @@ def hipcc() -> str:
 
 
 def build_library(verbose: bool = False) -> str:
-    """Compile libmla.so (always recompiles) and return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    """Compile libmla.so and libmla_debug.so (always recompiles; the two builds
+    run side by side) and return the path of libmla.so."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    jobs = []
+    for out, extra in ((LIB, []), (LIB_DEBUG, ["-DMLA_DEBUG_CHECKS"])):
+        cmd = [hipcc(), *FLAGS, *extra, *srcs, "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                           text=True)))
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    failed = []
+    for out, proc in jobs:
+        _, stderr = proc.communicate()
+        err = "\n".join(l for l in stderr.splitlines() if noise not in l)
+        if proc.returncode != 0:
+            failed.append(f"{os.path.basename(out)}: hipcc failed ({proc.returncode}):\n{err}")
+        elif verbose and err.strip():
+            print(err, file=sys.stderr)
+    if failed:
+        raise RuntimeError("\n".join(failed))
+    for out, _ in jobs:
+        os.replace(out + ".tmp", out)
     return LIB
 
 

@@ -67,6 +67,54 @@ void* device_scratch() {
   return ptr;
 }
 
+#ifdef MLA_DEBUG_CHECKS
+// The debug build's check result: one word per device, written by the check
+// kernel and read back by the entry point that launched it.
+static __device__ int debug_status;
+
+// Runs the device-side index check on `stream`, waits for it, and returns
+// MLA_ERR_BAD_INPUT if it found a violation (the debug build only: this
+// synchronises, which the release entry points never do).
+mla_status debug_check(mla::CheckParams c, void* stream) {
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(debug_status)) != hipSuccess || ptr == nullptr) {
+    (void)hipGetLastError();
+    return MLA_ERR_HIP;
+  }
+  c.status = static_cast<int*>(ptr);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mla::launch_check_inputs(c, st) != hipSuccess) return MLA_ERR_HIP;
+  int found = 0;
+  if (hipMemcpyAsync(&found, ptr, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return MLA_ERR_HIP;
+  return found != 0 ? MLA_ERR_BAD_INPUT : MLA_OK;
+}
+#endif
+
+mla::CheckParams check_params(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                              const int32_t* kv_indices, int64_t kv_indices_len,
+                              const int32_t* last_page_lens, int page_shift, int64_t pool_entries,
+                              int batch, int num_q_tokens, int max_seqlen_q,
+                              const int32_t* g_kv_indptr, int cp_size, int cp_rank) {
+  mla::CheckParams c;
+  c.qo_indptr = qo_indptr;
+  c.kv_indptr = kv_indptr;
+  c.kv_indices = kv_indices;
+  c.last_page_lens = last_page_lens;
+  c.g_kv_indptr = g_kv_indptr;
+  c.kv_indices_len = kv_indices_len;
+  c.pool_entries = pool_entries;
+  c.batch = batch;
+  c.num_q_tokens = num_q_tokens;
+  c.max_seqlen_q = max_seqlen_q;
+  c.page_shift = page_shift;
+  c.cp_size = g_kv_indptr != nullptr ? cp_size : 1;
+  c.cp_rank = g_kv_indptr != nullptr ? cp_rank : 0;
+  c.status = nullptr;
+  return c;
+}
+
 using mla::kMaxWorkers;
 constexpr int kMaxCpSize = 1024;  // DCP shards accepted by mla_decode_dcp
 constexpr int kMaxPageShift = 12;  // page sizes accepted by mla_decode_paged: 1 .. 4096
@@ -146,6 +194,16 @@ mla_status decode_impl(const void* q, int q_dtype, const void* kv_pool, int kv_d
   p.cp_rank = cp_rank;
   p.last_page_lens = page_shift > 0 ? last_page_lens : nullptr;
   p.page_shift = page_shift;
+#ifdef MLA_DEBUG_CHECKS
+  {
+    const mla_status s = debug_check(
+        check_params(qo_indptr, kv_indptr, kv_indices, kv_indices_len, p.last_page_lens,
+                     page_shift, pool_entries, batch, num_q_tokens, max_seqlen_q, g_kv_indptr,
+                     cp_size, cp_rank),
+        stream);
+    if (s != MLA_OK) return s;
+  }
+#endif
   if (mla::launch_decode(p, kdt, group_mode, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
@@ -167,6 +225,9 @@ const char* mla_status_string(int status) {
     case MLA_ERR_SCRATCH_TOO_SMALL:
       return "MLA_ERR_SCRATCH_TOO_SMALL: the call needs more workspace than the fixed scratch "
              "of mla_decode_noalloc holds";
+    case MLA_ERR_BAD_INPUT:
+      return "MLA_ERR_BAD_INPUT: the index arguments break the call's contract (found by the "
+             "device-side check)";
     default: return "MLA_ERR_UNKNOWN";
   }
 }
@@ -403,6 +464,20 @@ mla_status mla_decode_cascade(const void* q, int q_dtype, const void* kv_pool, i
   p.num_tokens = 2 * T;
   p.causal = 1;
   mla::set_workspace(p, ws, 2 * units, p.num_workers, mla::slots_per_worker(true));
+#ifdef MLA_DEBUG_CHECKS
+  {
+    // The suffix lists as the batch, then the prefix list whole.
+    mla_status s = debug_check(check_params(qo_indptr, suffix_indptr, suffix_indices,
+                                            suffix_indices_len, nullptr, 0, pool_entries, batch,
+                                            T, max_seqlen_q, nullptr, 1, 0),
+                               stream);
+    if (s == MLA_OK && prefix_len > 0)
+      s = debug_check(check_params(nullptr, nullptr, prefix_indices, prefix_len, nullptr, 0,
+                                   pool_entries, 1, 0, 1, nullptr, 1, 0),
+                      stream);
+    if (s != MLA_OK) return s;
+  }
+#endif
   if (mla::launch_decode(p, 0, true, st) != hipSuccess) return MLA_ERR_HIP;
 
   // LSE merge of the two passes (a pass that saw nothing has lse = -inf).
@@ -542,8 +617,43 @@ mla_status mla_decode_step(const void* q_latent, const void* q_pe, const void* k
   p.rope_style = rope_style;
   p.real_heads = num_heads;
   p.slot_mapping = slot_mapping;
+#ifdef MLA_DEBUG_CHECKS
+  {
+    const mla_status s = debug_check(
+        check_params(qo_indptr, kv_indptr, kv_indices, kv_indices_len, nullptr, 0, pool_entries,
+                     batch, num_q_tokens, max_seqlen_q, nullptr, 1, 0),
+        stream);
+    if (s != MLA_OK) return s;
+  }
+#endif
   if (mla::launch_decode_step(p, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out),
                               static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+mla_status mla_check_inputs(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, int64_t kv_indices_len,
+                            const int32_t* kv_last_page_lens, int page_size,
+                            int64_t pool_entries, int batch, int num_q_tokens, int max_seqlen_q,
+                            const int32_t* g_kv_indptr, int cp_world_size, int cp_rank,
+                            int* status, void* stream) {
+  if (!qo_indptr || !kv_indptr || !status || (kv_indices_len > 0 && !kv_indices))
+    return MLA_ERR_NULL_POINTER;
+  int shift = 0;
+  while (shift <= kMaxPageShift && (1 << shift) != page_size) ++shift;
+  if (page_size < 1 || shift > kMaxPageShift) return MLA_ERR_BAD_SHAPE;
+  if (batch < 1 || num_q_tokens < 0 || max_seqlen_q < 1 || kv_indices_len < 0 ||
+      pool_entries < 1)
+    return MLA_ERR_BAD_SHAPE;
+  if (g_kv_indptr != nullptr &&
+      (cp_world_size < 1 || cp_world_size > kMaxCpSize || cp_rank < 0 || cp_rank >= cp_world_size))
+    return MLA_ERR_BAD_SHAPE;
+  mla::CheckParams c = check_params(qo_indptr, kv_indptr, kv_indices, kv_indices_len,
+                                    kv_last_page_lens, shift, pool_entries, batch, num_q_tokens,
+                                    max_seqlen_q, g_kv_indptr, cp_world_size, cp_rank);
+  c.status = status;
+  if (mla::launch_check_inputs(c, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -146,6 +146,26 @@ hipError_t launch_merge(const void* o_parts, int parts_fp32, const float* lse_pa
 hipError_t launch_decode_step(const DecodeParams& p, const uint16_t* w_uv, uint16_t* vout,
                               hipStream_t stream);
 
+// Device-side check of a call's index arguments (mla_check.hip): bits of
+// MLA_CHECK_* OR-ed into *status (cleared first).
+struct CheckParams {
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* last_page_lens;  // nullptr: not checked
+  const int32_t* g_kv_indptr;     // nullptr: not a DCP shard
+  int64_t kv_indices_len;
+  int64_t pool_entries;
+  int batch;
+  int num_q_tokens;
+  int max_seqlen_q;
+  int page_shift;
+  int cp_size;
+  int cp_rank;
+  int* status;
+};
+hipError_t launch_check_inputs(const CheckParams& c, hipStream_t stream);
+
 // Steps either side of the decode (mla_surround.hip).
 hipError_t launch_rope_quant_cache(const uint16_t* q_latent, const uint16_t* q_pe,
                                    const uint16_t* k_latent, const uint16_t* k_pe,

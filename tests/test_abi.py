@@ -27,8 +27,9 @@ def test_header_declares_the_boundary():
         assert required in names
 
 
-def test_library_exports_every_declared_symbol():
-    L = _lib.lib()
+@pytest.mark.parametrize("which", ["release", "debug"])
+def test_library_exports_every_declared_symbol(which):
+    L = _lib.lib() if which == "release" else _lib.debug_lib()
     for name in declared_functions():
         assert hasattr(L, name), f"{name} declared in mla.h but not exported"
         assert name in _lib.SIGNATURES, f"binding has no signature for {name}"
@@ -39,6 +40,13 @@ def test_status_strings():
     for code, name in _lib.STATUS.items():
         assert L.mla_status_string(code).decode().startswith(name)
     assert L.mla_status_string(99).decode() == "MLA_ERR_UNKNOWN"
+
+
+def test_check_bits_match_the_header():
+    text = open(HEADER).read()
+    bits = {int(v): k for k, v in re.findall(r"#define (MLA_CHECK_\w+) (\d+)", text)}
+    assert bits == _lib.CHECK_BITS
+    assert re.search(r"MLA_ERR_BAD_INPUT = 8", text)
 
 
 def test_workspace_size_is_pure_and_bounded():
@@ -213,3 +221,28 @@ def test_decode_step_workspace_size_rejects_bad_shapes():
     L = _lib.lib()
     assert L.mla_decode_step_workspace_bytes(16, 16, 24, 1) == 0
     assert L.mla_decode_step_workspace_bytes(16, 0, 16, 1) == 0
+
+
+def _check(**over):
+    args = dict(qo=FAKE, kvp=FAKE, kvi=FAKE, kvi_len=1000, lpl=None, page=1, pool=1 << 20, B=16,
+                T=16, mq=1, g=None, cp=1, rank=0, status=FAKE, stream=None)
+    args.update(over)
+    return _lib.lib().mla_check_inputs(*args.values())
+
+
+@pytest.mark.parametrize(
+    "over,status",
+    [(dict(qo=None), 1), (dict(kvp=None), 1), (dict(status=None), 1), (dict(kvi=None), 1),
+     (dict(page=0), 2), (dict(page=3), 2), (dict(page=8192), 2), (dict(B=0), 2),
+     (dict(T=-1), 2), (dict(mq=0), 2), (dict(kvi_len=-1), 2), (dict(pool=0), 2),
+     (dict(g=FAKE, cp=0), 2), (dict(g=FAKE, cp=4, rank=4), 2), (dict(g=FAKE, cp=4, rank=-1), 2)],
+)
+def test_check_inputs_rejects_bad_arguments_before_any_launch(over, status):
+    assert _check(**over) == status
+
+
+def test_check_inputs_allows_an_empty_index_list_without_a_pointer():
+    # kv_indices may be NULL when the list is empty; the call then gets as far
+    # as the launch, which needs a GPU, so only the argument checks are run
+    # here: a NULL status still fails first.
+    assert _check(kvi=None, kvi_len=0, status=None) == 1
