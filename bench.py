@@ -446,6 +446,43 @@ def time_eager(calls, steps, warmup):
     return wall, ev, steps
 
 
+def time_cold(calls, steps, mode, flush_bytes=512 << 20):
+    """Each call timed alone with HIP events, after a pass over a scratch
+    buffer of flush_bytes (outside the events) that evicts the 256 MiB
+    last-level cache, as when the other layers of a model step run between two
+    calls of a layer.  mode "read" reads the buffer (a sum), so the cache is
+    left holding clean lines; mode "write" fills it, so the call first has to
+    write back the cache's dirty lines as it evicts them.  Returns the
+    per-call event seconds."""
+    import torch
+
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    scratch.fill_(1.0)
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def flush(i):
+        if mode == "read":
+            torch.sum(scratch, dim=0, out=sink)
+        else:
+            scratch.fill_(float(i & 7))
+
+    for i in range(2):
+        flush(i)
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        flush(i)
+        starts[i].record()
+        calls[i % len(calls)]()
+        ends[i].record()
+    torch.cuda.synchronize()
+    ev = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
+    del scratch, sink
+    return ev
+
+
 def cpu_baseline(w, n_req, gpu_out=None):
     """The float64 oracle on `n_req` full-length requests of the same call.
     gpu_out = (o, lse) of the same call on the GPU: its error against the
@@ -683,6 +720,16 @@ def main():
             wall_e, ev_e, _ = time_eager(calls, max(16, a.steps // 4), 4)
             variants["eager_calls_incl_host_overhead"] = {"us_per_call": round(wall_e * 1e6, 2),
                                                           "event_us": stats_us(ev_e)}
+        # Cold (the survey's protocol): every call timed alone after a pass
+        # over 512 MiB that evicts the 256 MiB last-level cache; per-call
+        # events, median.
+        for mode in ("read", "write"):
+            st_c = stats_us(time_cold(calls, 32, mode))
+            med_c = st_c["median"] * 1e-6
+            variants[f"cold_after_512MiB_{mode}"] = {
+                "us_per_call": st_c["median"], "event_us": st_c,
+                "GB_s": round(nbytes / med_c / 1e9, 2),
+                "pct_of_8TBs": round(100 * nbytes / med_c / 1e9 / PEAK_GBS, 2)}
         for var in ("unshared", "blocked"):
             if var == a.variant:
                 continue
