@@ -87,9 +87,9 @@ typedef enum {
  * group-mode kernel instead walks 8 row groups of one request over a single
  * shared KV range, so each gathered cache row feeds 128 query rows; it also
  * runs one worker per compute unit, with sixteen partial slots each.
- * Partial o rows are stored in bf16 for an FP8 cache with a bf16 output and in
- * fp32 otherwise (a bf16 cache, or an fp32 output as mla_decode_dcp can ask
- * for); the slots are sized for fp32 either way.  The workspace is sized for
+ * Partial o rows are stored in fp16, divided by kv_scale, for an FP8 cache
+ * with a bf16 output and in fp32 otherwise (a bf16 cache, or an fp32 output as
+ * mla_decode_dcp can ask for); the slots are sized for fp32 either way.  The workspace is sized for
  * the group-mode layout whenever the shape qualifies.
  */
 size_t mla_decode_workspace_bytes(int batch, int num_q_tokens, int num_heads, int max_seqlen_q);

@@ -276,9 +276,9 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
 }
 
 struct Fp8Path {
-  // Split partials in bf16: half the bytes to write and read back, within
-  // the gate for the fp8 cache's outputs.
-  static constexpr bool kBf16Parts = true;
+  // Split partials in fp16 without the kv scale (pack_f16x2): half the bytes
+  // of fp32 to write and read back, within the gate for the merged rows.
+  static constexpr bool kHalfParts = true;
   static constexpr int kRowBytes = kRowDim;
   static constexpr int kTile = kFp8Tile;
   static constexpr int kVStride = kFp8VStride;
@@ -449,9 +449,9 @@ __device__ __forceinline__ void bf16_tile(WaveState& st, uint4 (&B)[18], TileIdx
 }
 
 struct Bf16Path {
-  // Split partials in fp32: bf16 caches reach |o| ~ 3-7 on one-entry and
-  // multi-token rows, where a second bf16 rounding exceeds the 1e-2 bound.
-  static constexpr bool kBf16Parts = false;
+  // Split partials in fp32: a bf16 cache's rows are not bounded by the e4m3
+  // range that keeps fp16 partials finite.
+  static constexpr bool kHalfParts = false;
   static constexpr int kRowBytes = kBf16RowBytes;
   static constexpr int kTile = kBf16Tile;
   static constexpr int kVStride = kBf16VStride;
@@ -597,7 +597,9 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
     fw[w] = (mw[w] == neg_inf()) ? 0.f : fast_exp2(mw[w] - M);
     L += sh.l[w][en] * fw[w];
   }
-  const float oscale = ks / (Path::kPScale * L);
+  // fp16 split partials leave out the kv scale (the combine applies it).
+  const bool half_parts = Path::kHalfParts && slot >= 0 && !p.part_fp32;
+  const float oscale = (half_parts ? 1.0f : ks) / (Path::kPScale * L);
 
   // This wave writes O^T blocks [8wv, 8wv + 8); element i of block 8wv + bb is
   // dim first_dim + kDimStride*i + bb.
@@ -630,12 +632,12 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
     if (p.lse != nullptr && ewv == 0 && egq == 0) p.lse[orow] = lse_val;
     return;
   }
-  if (Path::kBf16Parts && !p.part_fp32) {
-    // bf16 (round to nearest even) at the fp32 layout's element indices, in
-    // the first half of the region.
+  if (half_parts) {
+    // fp16 at the fp32 layout's element indices, in the first half of the
+    // region.
     uint16_t* dst = (uint16_t*)p.part_o + ((int64_t)slot * kGroup + en) * kLatent + dim0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) store_bf16x8(dst + Path::kDimStride * i, acc[i]);
+    for (int i = 0; i < 4; ++i) store_f16x8(dst + Path::kDimStride * i, acc[i]);
   } else {
     float* dst = p.part_o + ((int64_t)slot * kGroup + en) * kLatent + dim0;
 #pragma unroll
@@ -856,7 +858,7 @@ struct CombineShared {
 // acc, the row's running maximum in M and its weight sum in sum.  All four
 // waves of the block must call it (the many-slot path meets at a barrier);
 // every element goes through the same operations whatever kHalves is.
-template <int kSlots, bool kBf16Parts, int kHalves>
+template <int kSlots, bool kHalfParts, int kHalves>
 __device__ __forceinline__ bool combine_row(const DecodeParams& p, CombineShared<kHalves>& sh,
                                             const int4 d, int n, int h0,
                                             float4 (&acc)[kHalves], float& M, float& sum) {
@@ -887,10 +889,10 @@ __device__ __forceinline__ bool combine_row(const DecodeParams& p, CombineShared
 #pragma unroll
       for (int hf = 0; hf < kHalves; ++hf) {
         const int64_t e0 = (slot * kGroup + n) * kLatent + 256 * (h0 + hf) + 4 * lane;
-        if constexpr (kBf16Parts) {
+        if constexpr (kHalfParts) {
           const uint2 b = *(const uint2*)((const uint16_t*)p.part_o + e0);
-          x[j][hf] = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
-                                 __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+          const float2 lo = unpack_f16x2(b.x), hi = unpack_f16x2(b.y);
+          x[j][hf] = make_float4(lo.x, lo.y, hi.x, hi.y);
         } else {
           x[j][hf] = *(const float4*)(p.part_o + e0);
         }
@@ -959,7 +961,7 @@ __device__ __forceinline__ bool combine_row(const DecodeParams& p, CombineShared
   return wv == 0;
 }
 
-template <int kSlots, bool kBf16Parts>
+template <int kSlots, bool kHalfParts>
 __device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShared<1>& sh) {
   const int64_t u = blockIdx.x;
   const int4 d = p.desc[u];
@@ -984,8 +986,10 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShare
   if (d.y - d.x + 1 <= kCombineBatch && wv != 0) return;  // one wave merges up to a batch
   float4 acc[1];
   float M, sum;
-  if (!combine_row<kSlots, kBf16Parts, 1>(p, sh, d, n, h, acc, M, sum)) return;
-  const float inv = sum > 0.f ? 1.0f / sum : 0.f;  // a row that sees nothing: o = 0, lse = -inf
+  if (!combine_row<kSlots, kHalfParts, 1>(p, sh, d, n, h, acc, M, sum)) return;
+  // fp16 partials carry no kv scale: applied here, with the normalisation.
+  const float ks = kHalfParts && p.kv_scale != nullptr ? *p.kv_scale : 1.0f;
+  const float inv = sum > 0.f ? ks / sum : 0.f;  // a row that sees nothing: o = 0, lse = -inf
   if (p.o32 != nullptr) {
     *(float4*)(p.o32 + orow * kLatent + 256 * h + 4 * lane) =
         make_float4(acc[0].x * inv, acc[0].y * inv, acc[0].z * inv, acc[0].w * inv);
@@ -999,7 +1003,7 @@ __device__ __forceinline__ void combine_unit(const DecodeParams& p, CombineShare
     p.lse[orow] = sum > 0.f ? M + fast_log2(sum) * kLn2 : neg_inf();
 }
 
-// The standard kernels' split combine: fp8 caches leave bf16 partials, bf16
+// The standard kernels' split combine: fp8 caches leave fp16 partials, bf16
 // caches fp32 ones.
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const DecodeParams p) {
   __shared__ CombineShared<1> sh;
@@ -1063,7 +1067,8 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_v_kernel(const De
     float4 acc[2];
     float M, sum;
     if (combine_row<2, true, 2>(p, sh, d, n, 0, acc, M, sum)) {
-      const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+      const float ks = p.kv_scale != nullptr ? *p.kv_scale : 1.0f;  // fp16 partials carry none
+      const float inv = sum > 0.f ? ks / sum : 0.f;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         uint2 pk;

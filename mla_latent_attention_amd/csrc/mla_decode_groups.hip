@@ -365,12 +365,12 @@ __device__ __forceinline__ void pair_step(WideState& st, PairP& cur, const PairP
   pair_pv<8>(st, prev, p0, p1, off, h);
 }
 
-// The 32 partial rows of a wave (O^T * oscale, as bf16 or fp32) go to global
+// The 32 partial rows of a wave (O^T * oscale, as fp16 or fp32) go to global
 // memory through LDS: a lane holds 16-byte pieces of its row scattered over 16
 // blocks, so storing them directly makes every store instruction touch 32 rows
 // 1 KB apart, which issues slowly; staged, each store writes two whole
 // 512-byte row pieces.  The rows pass in chunks of 512 bytes per row: two
-// halves of 256 dims in bf16, four quarters of 128 dims in fp32.  Row
+// halves of 256 dims in fp16, four quarters of 128 dims in fp32.  Row
 // r = lane%32 of the wave is head r%16 of row group wv + 4*(r/16), whose
 // partial slot is slot_base + wv + 4*(r/16).  Uses ring bytes
 // [wv * kStageBytes, +kStageBytes): no wave reads the ring after its tile
@@ -401,8 +401,8 @@ __device__ __forceinline__ void store_partials(const WideState& st, float oscale
           *(float4*)dst = make_float4(a0, a1, a2, a3);
         } else {
           uint2 pk;
-          pk.x = pack_bf16x2(a0, a1);
-          pk.y = pack_bf16x2(a2, a3);
+          pk.x = pack_f16x2(a0, a1);
+          pk.y = pack_f16x2(a2, a3);
           *(uint2*)dst = pk;
         }
       }
@@ -620,16 +620,18 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   const float oscale = empty ? 0.f : ks / Lsum;
   const float lse_val = empty ? neg_inf() : (st.m + fast_log2(Lsum)) * kLn2;
   if (!complete) {
-    // Partials are stored in bf16 (round to nearest even) unless the call
-    // asks for fp32 ones (an fp32 output): every worker writes eight row
-    // groups of them at the end of a split piece, and their bytes, written
-    // and read back by the combine, rival the attention arithmetic.  Every lane takes part: the rows of a row group past the
-    // request's last (empty, weight 0) land in that row group's own slot,
-    // which the combine never reads.  Lanes l and l+32 store the same lse.
+    // Partials are stored in fp16 (round to nearest even), without the kv
+    // scale (the combine applies it), unless the call asks for fp32 ones (an
+    // fp32 output): every worker writes eight row groups of them at the end
+    // of a split piece, and their bytes, written and read back by the
+    // combine, rival the attention arithmetic.  Every lane takes part: the
+    // rows of a row group past the request's last (empty, weight 0) land in
+    // that row group's own slot, which the combine never reads.  Lanes l and
+    // l+32 store the same lse.
     if (p.part_fp32)
       store_partials<true>(st, oscale, p.part_o, slot_base, wv, lane);
     else
-      store_partials<false>(st, oscale, p.part_o, slot_base, wv, lane);
+      store_partials<false>(st, empty ? 0.f : 1.0f / Lsum, p.part_o, slot_base, wv, lane);
     p.part_lse[(slot_base + ulocal) * kGroup + n16] = lse_val;
     return;
   }

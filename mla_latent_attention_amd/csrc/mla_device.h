@@ -45,6 +45,23 @@ __device__ __forceinline__ u32 pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(u32, __builtin_convertvector(v2f32_t{a, b}, v2bf16_t));
 }
 
+// Split partials of the fp8 kernels are stored as fp16 (11 significant bits,
+// against bf16's 8: with a bf16 partial the merged row carries two bf16
+// roundings, up to one bf16 unit, 0.0156 at |o| in [2, 4), where the 1e-2
+// bound allows one; with fp16 the pair stays under 0.0098), of values
+// without the kv scale, so that they stay within fp16's range (|o / kv_scale|
+// <= 448, the largest e4m3 value).  Round to nearest even.
+// (Two scalar conversions, not the packed one: with the packed conversion the
+// standard fp8 kernel's epilogue no longer fits its registers.)
+__device__ __forceinline__ u32 pack_f16x2(float a, float b) {
+  return (u32)__builtin_bit_cast(uint16_t, (_Float16)a) |
+         ((u32)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+__device__ __forceinline__ float2 unpack_f16x2(u32 w) {
+  return make_float2((float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)),
+                     (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)));
+}
+
 __device__ __forceinline__ long as_long(u32 lo, u32 hi) {
   return (long)((uint64_t)lo | ((uint64_t)hi << 32));
 }
@@ -357,6 +374,15 @@ __device__ __forceinline__ void stage_first_indices(int32_t* idx_dst, const Deco
   }
 #pragma unroll
   for (int j = 0; j < kIdxBatch; ++j) idx_dst[imin(j * kT + (int)threadIdx.x, n - 1)] = iv[j];
+}
+
+__device__ __forceinline__ void store_f16x8(uint16_t* dst, const float (&a)[8]) {
+  uint4 pk;
+  pk.x = pack_f16x2(a[0], a[1]);
+  pk.y = pack_f16x2(a[2], a[3]);
+  pk.z = pack_f16x2(a[4], a[5]);
+  pk.w = pack_f16x2(a[6], a[7]);
+  *(uint4*)dst = pk;
 }
 
 __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&a)[8]) {

@@ -37,7 +37,7 @@ struct DecodeParams {
   const float* kv_scale;    // device scalar or nullptr (1.0)
   float* lse;               // (T, H) or nullptr
   float* part_o;            // workspace: (slots*num_workers, 16, 512) split partials
-  int part_fp32 = 0;        // 1: partials in fp32; 0: fp32 for a bf16 cache, bf16 for an
+  int part_fp32 = 0;        // 1: partials in fp32; 0: fp32 for a bf16 cache, fp16 for an
                             // fp8 one (see the workspace layout below)
   float* part_lse;          // workspace: (slots*num_workers, 16) fp32
   int4* desc;               // workspace: (tokens * head groups) split-unit descriptors
@@ -102,8 +102,9 @@ __host__ __device__ inline ReqSource source_of(const DecodeParams& p) {
 //            takes the stores of lanes holding no descriptor, so that the
 //            group kernel writes descriptors without a divergent branch
 //   part_o   (slots * num_workers, 16, 512) fp32 partial outputs (calls on an
-//            fp8 cache store them as bf16 at the same element indices, in the
-//            first half of the region, unless part_fp32 is set)
+//            fp8 cache store them as fp16 divided by kv_scale, at the same
+//            element indices, in the first half of the region, unless
+//            part_fp32 is set)
 //            (then, group mode, desc_rows: int2 per entry, the output rows of
 //            the entry's row group, written with its descriptor)
 //   part_lse (slots * num_workers, 16) fp32 partial lse
