@@ -51,6 +51,7 @@ struct alignas(16) DecodeShared {
   int64_t red[kWaves];
   float m[kWaves][16];
   float l[kWaves][16];
+  float dl[kWaves][16];
   PlanHit hits[2];
 };
 
@@ -226,19 +227,33 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
   u32 h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
   h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], h1, true);
   float r[8];
-  r[0] = x[0] - __builtin_amdgcn_cvt_f32_fp8(h0, 0);
-  r[1] = x[1] - __builtin_amdgcn_cvt_f32_fp8(h0, 1);
-  r[2] = x[2] - __builtin_amdgcn_cvt_f32_fp8(h0, 2);
-  r[3] = x[3] - __builtin_amdgcn_cvt_f32_fp8(h0, 3);
-  r[4] = x[4] - __builtin_amdgcn_cvt_f32_fp8(h1, 0);
-  r[5] = x[5] - __builtin_amdgcn_cvt_f32_fp8(h1, 1);
-  r[6] = x[6] - __builtin_amdgcn_cvt_f32_fp8(h1, 2);
-  r[7] = x[7] - __builtin_amdgcn_cvt_f32_fp8(h1, 3);
+  {
+    const v2f32_t a = __builtin_amdgcn_cvt_pk_f32_fp8(h0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(h0, true);
+    const v2f32_t c = __builtin_amdgcn_cvt_pk_f32_fp8(h1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(h1, true);
+    r[0] = x[0] - a[0];
+    r[1] = x[1] - a[1];
+    r[2] = x[2] - b[0];
+    r[3] = x[3] - b[1];
+    r[4] = x[4] - c[0];
+    r[5] = x[5] - c[1];
+    r[6] = x[6] - d[0];
+    r[7] = x[7] - d[1];
+  }
   u32 l0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
   l0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], l0, true);
   u32 l1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[4], r[5], 0, false);
   l1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], l1, true);
   const long phi = as_long(h0, h1), plo = as_long(l0, l1);
+  // o is normalised by the sum of the weights the MFMAs use (hi + lo, not P):
+  // the split's rounding then moves o towards the entries it favours instead
+  // of scaling it, an error bounded by |V - o| rather than |V|.  The lse
+  // keeps the sum of P.
+  {
+    const v2f32_t a = __builtin_amdgcn_cvt_pk_f32_fp8(l0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(l0, true);
+    const v2f32_t c = __builtin_amdgcn_cvt_pk_f32_fp8(l1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(l1, true);
+    st.dl += ((a[0] - r[0]) + (a[1] - r[1])) + ((b[0] - r[2]) + (b[1] - r[3])) +
+             (((c[0] - r[4]) + (c[1] - r[5])) + ((d[0] - r[6]) + (d[1] - r[7])));
+  }
 
   // O^T += V^T . P^T; the kv row of operand byte k is kappa(gq, k):
   // 4gq + k for k < 4, 16 + 4gq + (k - 4) otherwise.
@@ -517,6 +532,7 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
   for (int b = 0; b < 32; ++b) st.O[b] = v4f{0.f, 0.f, 0.f, 0.f};
   st.m = neg_inf();
   st.l = 0.f;
+  st.dl = 0.f;
 
   uint8_t* vst = sh.buf + wv * Path::kTile * Path::kVStride;
   for (int seg0 = 0; seg0 < rows; seg0 += kIdxSeg) {
@@ -575,10 +591,13 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
             egq = elane >> 4;
   st.l += __shfl_xor(st.l, 16);
   st.l += __shfl_xor(st.l, 32);
+  st.dl += __shfl_xor(st.dl, 16);
+  st.dl += __shfl_xor(st.dl, 32);
   __syncthreads();  // every wave is done with its V staging
   if (egq == 0) {
     sh.m[ewv][en] = st.m;
     sh.l[ewv][en] = st.l;
+    sh.dl[ewv][en] = st.dl;
   }
   v4f* comb = (v4f*)sh.buf;
 #pragma unroll
@@ -591,15 +610,17 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, DecodeShared
     mw[w] = sh.m[w][en];
     M = fmaxf(M, mw[w]);
   }
-  float fw[kWaves], L = 0.f;
+  float fw[kWaves], L = 0.f, DL = 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     fw[w] = (mw[w] == neg_inf()) ? 0.f : fast_exp2(mw[w] - M);
     L += sh.l[w][en] * fw[w];
+    DL += sh.dl[w][en] * fw[w];
   }
   // fp16 split partials leave out the kv scale (the combine applies it).
+  // o over the weights' sum, L * kPScale + DL (the lse takes L).
   const bool half_parts = Path::kHalfParts && slot >= 0 && !p.part_fp32;
-  const float oscale = (half_parts ? 1.0f : ks) / (Path::kPScale * L);
+  const float oscale = (half_parts ? 1.0f : ks) / __builtin_fmaf(Path::kPScale, L, DL);
 
   // This wave writes O^T blocks [8wv, 8wv + 8); element i of block 8wv + bb is
   // dim first_dim + kDimStride*i + bb.

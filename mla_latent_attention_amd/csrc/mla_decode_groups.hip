@@ -150,7 +150,8 @@ struct WideState {
   v16f O[16];
   float m;
   float mx;
-  float l;
+  float l;   // sum of P (the lse's)
+  float lw;  // sum of the weights the MFMAs use, hi + lo (o's normaliser)
   bool big;
 };
 
@@ -280,17 +281,21 @@ __device__ __forceinline__ void tile_softmax(WideState& st, PairP& pp, const v16
   int e = (int)__builtin_ceilf(fminf(fmaxf(rel, -200.f), 200.f)) - 8;
   e = imin(imax(e, -127), 127);
   const float nref = -(st.m + (float)e);
-  float x[16], ps[4] = {0.f, 0.f, 0.f, 0.f};
+  // (Sums start at -0, which x + -0 = x lets the compiler drop.)
+  float x[16], ps[4] = {-0.f, -0.f, -0.f, -0.f}, dw = -0.f;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     x[v] = fast_exp2(__builtin_fmaf(r[v], cs, nref));
     ps[v & 3] += x[v];
   }
-  st.l += __builtin_ldexpf((ps[0] + ps[1]) + (ps[2] + ps[3]), e);
   pp.e[kTau] = e;
   // fp8 hi part, then the residual as fp8 lo (same block scale).  Each
   // packing's first write keeps the upper half of its destination, given a
-  // register that is dead by then, so no zeroing move is needed.
+  // register that is dead by then, so no zeroing move is needed.  o is
+  // normalised by the sum of the weights the MFMAs use (hi + lo, not P): the
+  // split's rounding then moves o towards the entries it favours instead of
+  // scaling it, an error bounded by |V - o| rather than |V|.  The lse keeps
+  // the sum of P.
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 0], x[4 * w + 1], __float_as_int(r[4 * w]),
@@ -302,9 +307,15 @@ __device__ __forceinline__ void tile_softmax(WideState& st, PairP& pp, const v16
     const float d2 = x[4 * w + 2] - h23[0], d3 = x[4 * w + 3] - h23[1];
     int lw = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, __float_as_int(d0), false);
     lw = __builtin_amdgcn_cvt_pk_fp8_f32(d2, d3, lw, true);
+    const v2f_t l01 = __builtin_amdgcn_cvt_pk_f32_fp8(lw, false);
+    const v2f_t l23 = __builtin_amdgcn_cvt_pk_f32_fp8(lw, true);
+    dw += (l01[0] - d0) + (l01[1] - d1) + ((l23[0] - d2) + (l23[1] - d3));
     pp.hi[4 * kTau + w] = hw;
     pp.lo[4 * kTau + w] = lw;
   }
+  const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  st.l += __builtin_ldexpf(psum, e);
+  st.lw += __builtin_ldexpf(psum + dw, e);
 }
 
 // O^T += V^T . P^T over the pair's 64 rows for dim blocks [kB0, kB0 + 8) on
@@ -540,6 +551,7 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
 #pragma unroll
     for (int i = 0; i < 16; ++i) st.O[b][i] = 0.f;
   st.l = 0.f;
+  st.lw = 0.f;
   st.big = false;
 
   for (int seg0 = 0; seg0 < len; seg0 += kGIdxSeg) {
@@ -610,14 +622,17 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   }
   }
 
-  float Lsum = st.l;
+  float Lsum = st.l, Wsum = st.lw;
   {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(Lsum), __float_as_uint(Lsum),
                                                      false, false);
     Lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const auto sv = __builtin_amdgcn_permlane32_swap(__float_as_uint(Wsum), __float_as_uint(Wsum),
+                                                     false, false);
+    Wsum = __uint_as_float(sv[0]) + __uint_as_float(sv[1]);
   }
   const bool empty = rows_w == 0;  // in a split piece: contributes weight 0
-  const float oscale = empty ? 0.f : ks / Lsum;
+  const float oscale = empty ? 0.f : ks / Wsum;
   const float lse_val = empty ? neg_inf() : (st.m + fast_log2(Lsum)) * kLn2;
   if (!complete) {
     // Partials are stored in fp16 (round to nearest even), without the kv
@@ -631,7 +646,7 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
     if (p.part_fp32)
       store_partials<true>(st, oscale, p.part_o, slot_base, wv, lane);
     else
-      store_partials<false>(st, empty ? 0.f : 1.0f / Lsum, p.part_o, slot_base, wv, lane);
+      store_partials<false>(st, empty ? 0.f : 1.0f / Wsum, p.part_o, slot_base, wv, lane);
     p.part_lse[(slot_base + ulocal) * kGroup + n16] = lse_val;
     return;
   }

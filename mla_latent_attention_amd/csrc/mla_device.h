@@ -275,6 +275,9 @@ struct WaveState {
               // scaled by the path's kPScale
   float m;    // (possibly stale) running max of base-2 scores of row lane%16
   float l;    // this lane's partial sum of 2^(s - m)
+  float dl;   // fp8 path: this lane's sum of (hi + lo) - P * kPScale, the split's
+              // rounding of the weights (o is normalised by l + dl / kPScale,
+              // the lse takes l)
 };
 
 // Online-softmax update for row lane%16 from this lane's N scores (already
@@ -295,9 +298,10 @@ __device__ __forceinline__ void softmax_update(WaveState& st, float (&x)[N]) {
 #pragma unroll
     for (int b = 0; b < 32; ++b) st.O[b] *= alpha;
     st.l *= alpha;
+    st.dl *= alpha;
     st.m = mset;
   }
-  float psum = 0.f;
+  float psum = -0.f;  // x + -0 = x: the first add folds away
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     x[i] = fast_exp2(x[i] - st.m);
