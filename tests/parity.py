@@ -24,19 +24,16 @@ LSE_TOL = 1e-3
 
 
 def bf16_abs_tol(ref_absmax: float) -> float:
-    """1e-2 while |o| < 2; from |o| >= 2 one bf16 unit in the last place at the
-    largest |o|: half for the output's own rounding, half for the arithmetic
-    before it.
+    """1e-2 while |o| < 4; from |o| >= 4 one bf16 unit in the last place at the
+    largest |o|.
 
-    Below 2 a bf16 output's rounding (half an ulp, at most 2^-8) leaves more
-    than 6e-3 of 1e-2 to the arithmetic.  On [2, 4) that half ulp is 2^-7 and
-    leaves 2.2e-3, less than the fp8 path's P.V error (P as two e4m3 terms
-    keeps about 8 significant bits: up to ~2^-9 of |V| before the rounding);
-    from 4 on the half ulp alone exceeds 1e-2.  Only for inputs outside the
-    benchmark distributions (whose outputs stay within +-2)."""
+    Below 4 a bf16 output's own rounding (half an ulp, at most 2^-7 on [2, 4))
+    fits inside 1e-2.  From 4 on that half ulp alone is >= 2^-6 > 1e-2, so no
+    bf16 output can meet 1e-2 there; the bound becomes one ulp: half for the
+    output's rounding and half for the arithmetic before it."""
     import math
 
-    if ref_absmax < 2.0:
+    if ref_absmax < 4.0:
         return ABS_TOL
     ulp = 2.0 ** (math.floor(math.log2(ref_absmax)) - 7)
     return max(ABS_TOL, ulp)

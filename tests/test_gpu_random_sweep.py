@@ -75,8 +75,8 @@ def draw(seed):
     return mode, lengths, kw, extra
 
 
-@pytest.mark.parametrize("seed", range(24))
-def test_random_call_matches_oracle(seed):
+def run_case(seed):
+    """Run case `seed` through the C ABI and the oracle: (metrics, mode, kwargs)."""
     mode, lengths, kw, extra = draw(seed)
     say(f"[sweep {seed}] {mode} lengths={lengths} {kw} {extra}")
     P = kw.get("page_size", 1)
@@ -109,5 +109,10 @@ def test_random_call_matches_oracle(seed):
     toks = a["tokens"]
     m = metrics(o[toks], o_ref, lse[toks], lse_ref)
     say(f"[sweep {seed}] {m}")
-    # The draws leave the benchmark distributions (scales up to 2 lift |o| past 2).
+    return m, mode, kw
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_call_matches_oracle(seed):
+    m, mode, _ = run_case(seed)
     assert_gate(m, f"sweep {seed} ({mode})", abs_tol=bf16_abs_tol(m["ref_absmax"]))
