@@ -248,12 +248,8 @@ __device__ __forceinline__ void fp8_tile(WaveState& st, uint4 (&B)[18], TileIdx&
   // the split's rounding then moves o towards the entries it favours instead
   // of scaling it, an error bounded by |V - o| rather than |V|.  The lse
   // keeps the sum of P.
-  {
-    const v2f32_t a = __builtin_amdgcn_cvt_pk_f32_fp8(l0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(l0, true);
-    const v2f32_t c = __builtin_amdgcn_cvt_pk_f32_fp8(l1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(l1, true);
-    st.dl += ((a[0] - r[0]) + (a[1] - r[1])) + ((b[0] - r[2]) + (b[1] - r[3])) +
-             (((c[0] - r[4]) + (c[1] - r[5])) + ((d[0] - r[6]) + (d[1] - r[7])));
-  }
+  st.dl = add_fp8x4(l1, add_fp8x4(l0, st.dl)) -
+          (((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7])));
 
   // O^T += V^T . P^T; the kv row of operand byte k is kappa(gq, k):
   // 4gq + k for k < 4, 16 + 4gq + (k - 4) otherwise.

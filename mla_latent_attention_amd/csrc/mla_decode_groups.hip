@@ -305,11 +305,9 @@ __device__ __forceinline__ void tile_softmax(WideState& st, PairP& pp, const v16
     const v2f_t h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
     const float d0 = x[4 * w + 0] - h01[0], d1 = x[4 * w + 1] - h01[1];
     const float d2 = x[4 * w + 2] - h23[0], d3 = x[4 * w + 3] - h23[1];
-    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, __float_as_int(d0), false);
+    int lw = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, __float_as_int(x[4 * w]), false);
     lw = __builtin_amdgcn_cvt_pk_fp8_f32(d2, d3, lw, true);
-    const v2f_t l01 = __builtin_amdgcn_cvt_pk_f32_fp8(lw, false);
-    const v2f_t l23 = __builtin_amdgcn_cvt_pk_f32_fp8(lw, true);
-    dw += (l01[0] - d0) + (l01[1] - d1) + ((l23[0] - d2) + (l23[1] - d3));
+    dw = add_fp8x4(lw, dw) - ((d0 + d1) + (d2 + d3));
     pp.hi[4 * kTau + w] = hw;
     pp.lo[4 * kTau + w] = lw;
   }

@@ -380,6 +380,17 @@ __device__ __forceinline__ void stage_first_indices(int32_t* idx_dst, const Deco
   for (int j = 0; j < kIdxBatch; ++j) idx_dst[imin(j * kT + (int)threadIdx.x, n - 1)] = iv[j];
 }
 
+// acc plus the four e4m3 values packed in w: each pair widened to f16 (exact)
+// and summed by an f32 dot product with (1, 1).
+typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float add_fp8x4(u32 w, float acc) {
+  const v2h_t one = {(_Float16)1.0f, (_Float16)1.0f};
+  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false), one, acc,
+                               false);
+  return __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true), one, acc,
+                                false);
+}
+
 __device__ __forceinline__ void store_f16x8(uint16_t* dst, const float (&a)[8]) {
   uint4 pk;
   pk.x = pack_f16x2(a[0], a[1]);
