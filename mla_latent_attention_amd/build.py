@@ -68,5 +68,32 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+# The plain-C caller of the C ABI that a GPU test runs (host code only: gcc,
+# C11, linked against libmla.so and the HIP runtime, found through rpath).
+ROOT = os.path.dirname(HERE)
+C_DRIVER_SRC = os.path.join(ROOT, "tests", "native", "c_abi_decode.c")
+C_DRIVER = os.path.splitext(C_DRIVER_SRC)[0]
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_c_driver(verbose: bool = False) -> str | None:
+    """Compile tests/native/c_abi_decode.c against the built libmla.so (None
+    when the tests are not present)."""
+    if not os.path.exists(C_DRIVER_SRC):
+        return None
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           f"-I{ROCM}/include", f"-I{os.path.join(ROOT, 'include')}", C_DRIVER_SRC,
+           "-o", C_DRIVER + ".tmp", f"-L{HERE}", "-lmla", f"-L{ROCM}/lib", "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/../../mla_latent_attention_amd", f"-Wl,-rpath,{ROCM}/lib"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(C_DRIVER + ".tmp", C_DRIVER)
+    return C_DRIVER
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_c_driver(verbose=True))

@@ -246,3 +246,21 @@ def test_check_inputs_allows_an_empty_index_list_without_a_pointer():
     # as the launch, which needs a GPU, so only the argument checks are run
     # here: a NULL status still fails first.
     assert _check(kvi=None, kvi_len=0, status=None) == 1
+
+
+def test_header_and_plain_c_caller_compile_as_c11():
+    """include/mla.h is a C header: the plain-C caller the GPU tests run
+    compiles with gcc in C11 mode, warnings as errors."""
+    import shutil
+    import subprocess
+
+    from mla_latent_attention_amd import build
+
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.exists(os.path.join(build.ROCM, "include", "hip")):
+        pytest.skip("gcc or the ROCm headers are not installed")
+    res = subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                          "-D__HIP_PLATFORM_AMD__", f"-I{build.ROCM}/include",
+                          f"-I{os.path.join(build.ROOT, 'include')}", build.C_DRIVER_SRC],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
