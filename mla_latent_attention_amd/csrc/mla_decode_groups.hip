@@ -577,13 +577,15 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
     // the previous pair's P.V (matrix cores), which are independent, can issue
     // interleaved.  A tile past this wave's rows is scored fully masked (P = 0
     // changes no state), and the first step's P.V runs with P = 0.
-    PairP prev;
-    prev.hi = v8i_t{};
-    prev.lo = v8i_t{};
-    prev.e[0] = prev.e[1] = 0;
+    // The P operands of consecutive pairs alternate between pa and pb (the
+    // loop runs two pairs per iteration), so no step copies one into the other.
+    PairP pa, pb;
+    pb.hi = v8i_t{};
+    pb.lo = v8i_t{};
+    pb.e[0] = pb.e[1] = 0;
     const uint8_t* pb0 = g_ring;
     const uint8_t* pb1 = g_ring;
-    for (int t = 0; t < ntiles; t += 2) {
+    auto step = [&](int t, PairP& cur, const PairP& prev) {
       wait_tiles_in_flight(0);  // this wave's loads of tiles t, t+1 (the last it issued)
       __syncthreads();  // tiles t, t+1 are in LDS; every wave is done with t-4, t-3
 #pragma unroll
@@ -594,16 +596,24 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
       const int base0 = seg0 + t * kGTile, base1 = base0 + kGTile;
       // lim1 <= 0 also masks a missing odd tile: its rows lie past the piece.
       const int lim1 = t + 1 < ntiles ? rows_w - base1 : 0;
-      PairP cur;
       pair_step(st, cur, prev, q, b0, b1, pb0, pb1, off, sc, rows_w - base0, lim1,
                 t + 1 < ntiles && base1 + kGTile <= full_rows, csa, h);
-      prev = cur;
       pb0 = b0;
       pb1 = b1;
+    };
+    bool last_in_a = false;  // which of pa, pb holds the last pair's P
+    for (int t = 0; t < ntiles; t += 4) {
+      step(t, pa, pb);
+      if (t + 2 >= ntiles) {
+        last_in_a = true;
+        break;
+      }
+      step(t + 2, pb, pa);
     }
+    if (last_in_a) pb = pa;
     if (seg0 + (((ntiles - 1) >> 1) << 1) * kGTile < wave_rows) {  // the last pair
-      pair_pv<0>(st, prev, pb0, pb1, off, h);
-      pair_pv<8>(st, prev, pb0, pb1, off, h);
+      pair_pv<0>(st, pb, pb0, pb1, off, h);
+      pair_pv<8>(st, pb, pb0, pb1, off, h);
     }
     __builtin_amdgcn_s_waitcnt(kVmcntNone);  // every ring load has landed
     __syncthreads();
