@@ -641,6 +641,15 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
   }
   const bool empty = rows_w == 0;  // in a split piece: contributes weight 0
   const float oscale = empty ? 0.f : ks / Wsum;
+  // The lane's row, rebuilt here from an opaque copy of the thread id, so that
+  // none of its indices stays live across the tile loop.
+  const int elane = opaque(tid) & 63;
+  const int eh = elane >> 5, en16 = elane & 15;
+  const int eulocal = wv + kWaves * ((elane & 31) >> 4);
+  const int erow = kGroup * (kGroupsPerUnit * c.u + eulocal) + en16;
+  const int erowc = imin(erow, NR - 1);
+  const int ej = erowc / H;
+  const int64_t eorow = (int64_t)(c.r.q_base + ej) * H + (erowc - ej * H);
   const float lse_val = empty ? neg_inf() : (st.m + fast_log2(Lsum)) * kLn2;
   if (!complete) {
     // Partials are stored in fp16 (round to nearest even), without the kv
@@ -652,16 +661,17 @@ __device__ __forceinline__ void group_piece(const DecodeParams& p, GroupShared& 
     // that row group's own slot, which the combine never reads.  Lanes l and
     // l+32 store the same lse.
     if (p.part_fp32)
-      store_partials<true>(st, oscale, p.part_o, slot_base, wv, lane);
+      store_partials<true>(st, oscale, p.part_o, slot_base, wv, elane);
     else
-      store_partials<false>(st, empty ? 0.f : 1.0f / Wsum, p.part_o, slot_base, wv, lane);
-    p.part_lse[(slot_base + ulocal) * kGroup + n16] = lse_val;
+      store_partials<false>(st, empty ? 0.f : 1.0f / Wsum, p.part_o, slot_base, wv, elane);
+    p.part_lse[(slot_base + eulocal) * kGroup + en16] = lse_val;
     return;
   }
-  if (!valid) return;
-  if (vw == 0) return;  // the row sees nothing: o / lse written elsewhere
+  if (erow >= NR) return;
+  if (req_visible(c.r, ej) == 0) return;  // the row sees nothing: o / lse written elsewhere
   {
-    const int64_t orow = (int64_t)t * H + hh;
+    const int64_t orow = eorow;
+    const int h = eh;
     if (p.o32 != nullptr) {
       float* d32 = p.o32 + orow * kLatent + 4 * h;
 #pragma unroll
