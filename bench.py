@@ -34,6 +34,7 @@ CONFIG_NAMES = ("c24_batch24_fp8", "mixed_batch64_fp8", "mixed_batch64_bf16",
                 "c16_shared_prefix_cascade_fp8_12heads", "c32_shared_prefix_cascade_fp8_12_vs_16",
                 "merge_8_shards_fp32", "merge_8_shards_bf16", "c16_layer_step_rope_decode_v")
 PEAK_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0  # dense fp8 MFMA (the decode's Q.K and P.V run on fp8 MFMA)
 
 
 def parse():
@@ -189,6 +190,7 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
                      "GB_s": round(nbytes / wall / 1e9, 2),
                      "pct_of_8TBs": round(100 * nbytes / wall / 1e9 / PEAK_GBS, 2),
                      "TFLOP_s": round(flops / wall / 1e12, 2),
+                     "pct_of_fp8_peak": round(100 * flops / wall / 1e12 / PEAK_FP8_TFLOPS, 2),
                      "algorithmic_bytes_per_call": nbytes, "flops_per_call": flops,
                      "kv_rows": base.total_kv, "dtype": base.dtype,
                      "o_dtype": str(o_dtype).replace("torch.", ""), "calls": n}
@@ -225,6 +227,8 @@ def config_lines(mla, dev, steps, warmup, n_layers=4, only=None):
                      "cascade_bytes_per_call": unique,
                      "GB_s_cascade_bytes": round(unique / wall / 1e9, 2),
                      "TFLOP_s": round(accounting.workload_flops(base) / wall / 1e12, 2),
+                     "pct_of_fp8_peak": round(100 * accounting.workload_flops(base) / wall / 1e12
+                                              / PEAK_FP8_TFLOPS, 2),
                      "heads": H, "kv_rows": base.total_kv, "dtype": "fp8", "calls": n}
         del layers, base, o, ws, pre, sptr, suf
         torch.cuda.empty_cache()
